@@ -1,0 +1,375 @@
+#!/usr/bin/env python3
+"""Benchmark of the sharded relay hot path on one MI355X.
+
+One step is one pass of every relay kernel of the method over one batch of
+synthetic input at one message size M (per-active-rank input bytes, bf16):
+
+  A=2 allreduce  (H=6, numChunks=8):  6 helper reductions + 2 active epilogues
+  A=2 reduce-scatter:                 2 owner epilogues (recvCount = M/4 elems)
+  A=4 allreduce  (H=4, 500 permille): 4 helper reductions + 4 active slices
+  A=4 reduce-scatter (H=4):           4 helper pass-1 + 4 owner pass-2 launches
+  A=4 all-to-all (H=4, numChunks=5):  4 packs + 4 unpacks (segmentCount = M/8)
+
+Inputs are resident in HBM before timing starts.  ``value`` is the step's
+algorithmic bytes (every input element read once, every output element
+written once) divided by the measured step time, in GB/s (10^9 bytes/s).
+Each launch is bracketed by HIP events on the stream it runs on; the kernel
+with the largest share of the step's time is reported against the 8 TB/s HBM
+peak in ``roofline``.  ``cpu_baseline`` times the CPU oracle (single thread)
+on one step of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--message-mib M]
+  python bench.py --sweep [--sweep-out FILE]   # per-row GB/s, 2 MiB .. 1 GiB
+"""
+import argparse
+import hashlib
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "achieved HBM GB/s (and % of peak) of relay reduce/pack kernels, 2MB-1GB msgs"
+MIB = 1 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--message-mib", type=float, default=64.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--sweep", action="store_true", help="per-row sweep instead of the step benchmark")
+    p.add_argument("--sweep-sizes", default="2,4,8,16,32,64,128,256,512,1024")
+    p.add_argument("--sweep-reps", type=int, default=20)
+    p.add_argument("--sweep-out", default=None)
+    return p.parse_args()
+
+
+# --------------------------------------------------------------------------
+# workload
+# --------------------------------------------------------------------------
+
+def host_inputs(M):
+    """Seeded host inputs of every row at message M (pack_rr_helper_amd.synth)."""
+    from pack_rr_helper_amd import synth
+    n = M // 2
+    return {
+        "ar2": [synth.as_bf16_bits(synth.normal(n, 1, a)) for a in range(2)],
+        "rs2": [synth.as_bf16_bits(synth.normal(n, 1, 10 + a)) for a in range(2)],
+        "ar4": [synth.as_bf16_bits(synth.uniform(n, -2, 2, 3, a)) for a in range(4)],
+        "rs4": [synth.as_bf16_bits(synth.normal(n, 2, s)) for s in range(4)],
+        "a2a": [synth.bits16(n, 4, s) for s in range(4)],
+    }
+
+
+def build_rows(inp, rows=("ar2", "rs2", "ar4", "rs4", "a2a")):
+    import pack_rr_helper_amd as rr
+    from pack_rr_helper_amd import synth
+    from pack_rr_helper_amd import workloads as W
+    dev = lambda arrs, code=rr.BF16: [synth.to_device(a, code) for a in arrs]
+    out = {}
+    if "ar2" in rows:
+        out["ar2"] = W.AR2(dev(inp["ar2"]), rr.BF16, rr.AVG)
+    if "rs2" in rows:
+        out["rs2"] = W.RS2(dev(inp["rs2"]), rr.BF16, rr.AVG)
+    if "ar4" in rows:
+        out["ar4"] = W.AR4(dev(inp["ar4"]), rr.BF16, rr.AVG)
+    if "rs4" in rows:
+        out["rs4"] = W.RS4(dev(inp["rs4"]), rr.BF16, rr.SUM)
+    if "a2a" in rows:
+        out["a2a"] = W.A2A(dev(inp["a2a"], None), rr.BF16)
+    return out
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle, single thread, one step of the same workload
+# --------------------------------------------------------------------------
+
+def cpu_baseline(inp):
+    """Seconds and algorithmic bytes of one step through the oracle."""
+    import numpy as np
+    import oracle as orc
+
+    t_total, nbytes = 0.0, 0
+
+    def timed(fn, b):
+        nonlocal t_total, nbytes
+        t = time.perf_counter()
+        fn()
+        t_total += time.perf_counter() - t
+        nbytes += b
+
+    BF, AVG, SUM, AR, RS, A2A = orc.BF16, orc.AVG, orc.SUM, orc.ALLREDUCE, orc.REDUCE_SCATTER, orc.ALLTOALL
+    x = inp["ar2"]
+    g = orc.geometry(2, 6, 8, 0, x[0].size, AR, BF)
+    c = g["chunk"]
+    for k in range(6):
+        timed(lambda: orc.ar2_helper(BF, AVG, x[0][k * c:(k + 1) * c], x[1][k * c:(k + 1) * c]), 3 * c * 2)
+    out = np.zeros_like(x[0])
+    for a in range(2):
+        timed(lambda: orc.ar_active(BF, AVG, 2, 6, 8, 0, x[0].size, a, x, out), 3 * g["direct_len"] * 2)
+    x = inp["rs2"]
+    R = x[0].size // 2
+    timed(lambda: orc.rs2_active(BF, AVG, x[0][:R], x[1][:R]), 3 * R * 2)
+    timed(lambda: orc.rs2_active(BF, AVG, x[0][R:], x[1][R:]), 3 * R * 2)
+    x = inp["ar4"]
+    g = orc.geometry(4, 4, 0, 500, x[0].size, AR, BF)
+    c = g["chunk"]
+    for h in range(4):
+        timed(lambda: orc.ar4_helper(BF, AVG, [v[h * c:(h + 1) * c] for v in x]), 5 * c * 2)
+    out = np.zeros_like(x[0])
+    for a in range(4):
+        n = g["dslice"] if a < 3 else g["direct_len"] - 3 * g["dslice"]
+        timed(lambda: orc.ar_active(BF, AVG, 4, 4, 0, 500, x[0].size, a, x, out), 5 * n * 2)
+    x = inp["rs4"]
+    R = x[0].size // 4
+    c = orc.geometry(4, 4, 0, 500, R, RS, BF)["chunk"]
+    for h in range(4):
+        scratch = np.concatenate([x[s][o * R + h * c:o * R + (h + 1) * c]
+                                  for o in range(4) for s in range(4) if s != o])
+        timed(lambda: orc.rs4_pass1(BF, 4, c, scratch), 16 * c * 2)
+    reds = [np.ascontiguousarray(x[0][:c]) for _ in range(4)]
+    for o in range(4):
+        blk = [v[o * R:(o + 1) * R] for v in x]
+        timed(lambda: orc.rs4_pass2(BF, SUM, 4, 4, 500, R, o, blk, reds), (3 * 4 * c + 5 * (R - 4 * c)) * 2)
+    x = inp["a2a"]
+    seg = x[0].size // 4
+    c = orc.geometry(4, 4, 5, 0, seg, A2A, BF)["chunk"]
+    outs = [np.zeros(4 * seg, np.uint16) for _ in range(4)]
+    for h in range(4):
+        packed = []
+        timed(lambda: packed.extend(orc.a2a_pack(2, 4, seg, c, h, x)), 24 * c * 2)
+        timed(lambda: orc.a2a_unpack(2, 4, seg, c, h, packed, outs), 24 * c * 2)
+    return t_total, nbytes
+
+
+# --------------------------------------------------------------------------
+# traffic from the committed rocprofv3 counter summary
+# --------------------------------------------------------------------------
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in ("rr_kernels.hip", "rr_internal.h"):
+        with open(os.path.join(ROOT, "pack_rr_helper_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, message_mib):
+    """HBM bytes per launch of `kernel` from profiles/traffic.json, or None if
+    absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k or k.get("message_mib") != message_mib:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+# --------------------------------------------------------------------------
+# main benchmark
+# --------------------------------------------------------------------------
+
+def step_bench(args):
+    import torch
+    import pack_rr_helper_amd as rr
+    rr.load()
+    torch.cuda.set_device(0)
+    M = int(args.message_mib * MIB)
+    print(f"[bench] generating inputs, M={args.message_mib} MiB", file=sys.stderr, flush=True)
+    inp = host_inputs(M)
+    wls = build_rows(inp)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    calls = [c for wl in wls.values() for c in wl.calls(stream)]
+    step_bytes = sum(b for _, _, b, _ in calls)
+
+    print(f"[bench] warmup {args.warmup} steps, {len(calls)} launches per step", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        for _, _, _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for s in range(args.steps):
+        for (e0, e1), (_, _, _, fn) in zip(ev[s], calls):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)", file=sys.stderr,
+          flush=True)
+
+    per_row, per_kernel = {}, {}
+    for s in range(args.steps):
+        for (e0, e1), (row, kern, b, _) in zip(ev[s], calls):
+            ms = e0.elapsed_time(e1)
+            r = per_row.setdefault(row, [0.0, 0, 0])
+            r[0] += ms
+            r[1] += b
+            r[2] += 1
+            k = per_kernel.setdefault(kern, [0.0, 0, 0])
+            k[0] += ms
+            k[1] += b
+            k[2] += 1
+    dom = max(per_kernel, key=lambda k: per_kernel[k][0])
+    d_ms, d_b, d_n = per_kernel[dom]
+    achieved = (d_b / d_n) / (d_ms / d_n * 1e-3) / 1e9
+    traffic = traffic_for(dom, args.message_mib)
+
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / PEAK_GBS, 2),
+        "config": {
+            "workload": (f"relay hot path, {args.message_mib:g} MiB per-rank bf16 message: A=2 allreduce "
+                         "(H=6) + A=2 reduce-scatter + A=4 allreduce (H=4, 500 permille) + A=4 "
+                         "reduce-scatter + A=4 all-to-all pack/unpack, one GPU"),
+            "message_bytes": M,
+            "launches_per_step": len(calls),
+            "algorithmic_bytes_per_step": step_bytes,
+            "rows_gbs": {row: round(b / (ms * 1e-3) / 1e9, 1) for row, (ms, b, n) in per_row.items()},
+            "rows_us_per_launch": {row: round(1e3 * ms / n, 2) for row, (ms, b, n) in per_row.items()},
+        },
+        "roofline": {
+            "kernel": dom,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": d_b // d_n,
+            "avg_launch_us": round(1e3 * d_ms / d_n, 3),
+            "launches": d_n,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on one step of the same workload", file=sys.stderr, flush=True)
+        t, b, reps = 0.0, 0, 0
+        while t < 10.0 and reps < 10:
+            dt, db = cpu_baseline(inp)
+            t, b, reps = t + dt, b + db, reps + 1
+        result["cpu_baseline"] = {
+            "value": round(b / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{reps} full step(s) (every row, {args.message_mib:g} MiB message, {b} algorithmic "
+                       f"bytes) through the scalar C oracle, single thread, {t:.1f} s; host "
+                       f"{platform.processor() or platform.machine()}"),
+        }
+    print(json.dumps(result), flush=True)
+
+
+# --------------------------------------------------------------------------
+# sweep: per-row GB/s at 2 MiB .. 1 GiB
+# --------------------------------------------------------------------------
+
+def sweep(args):
+    import torch
+    import pack_rr_helper_amd as rr
+    from pack_rr_helper_amd import workloads as W
+    rr.load()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")  # > the 256 MB MALL
+    out = open(args.sweep_out, "w") if args.sweep_out else sys.stdout
+    gen = torch.Generator(device="cuda")
+    for mib in [float(v) for v in args.sweep_sizes.split(",")]:
+        M = int(mib * MIB)
+        n = M // 2
+        for row in ("ar2", "rs2", "ar4", "rs4", "a2a"):
+            gen.manual_seed(hash((row, M)) & 0xFFFFFFFF)
+            ranks = 2 if row in ("ar2", "rs2") else 4
+            if row == "a2a":
+                xs = [torch.randint(-32768, 32767, (n,), dtype=torch.int16, device="cuda", generator=gen)
+                      for _ in range(ranks)]
+            else:
+                xs = [torch.randn(n, device="cuda", generator=gen).to(torch.bfloat16) for _ in range(ranks)]
+            wl = {"ar2": lambda: W.AR2(xs, rr.BF16, rr.AVG), "rs2": lambda: W.RS2(xs, rr.BF16, rr.AVG),
+                  "ar4": lambda: W.AR4(xs, rr.BF16, rr.AVG), "rs4": lambda: W.RS4(xs, rr.BF16, rr.SUM),
+                  "a2a": lambda: W.A2A(xs, rr.BF16)}[row]()
+            for role in sorted({c[0] for c in wl.calls(stream)}):
+                cs = [c for c in wl.calls(stream) if c[0] == role]
+                times = []
+                for rep in range(args.sweep_reps + 3):
+                    flush.zero_()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    cs[0][3]()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    if rep >= 3:
+                        times.append(e0.elapsed_time(e1) * 1e-3)
+                b = cs[0][2]
+                rec = {"message_mib": mib, "row": role, "kernel": cs[0][1], "bytes_per_launch": b,
+                       "us_min": round(min(times) * 1e6, 2), "us_median": round(statistics.median(times) * 1e6, 2),
+                       "gbs_best": round(b / min(times) / 1e9, 1),
+                       "gbs_median": round(b / statistics.median(times) / 1e9, 1),
+                       "pct_peak_median": round(100 * b / statistics.median(times) / 1e9 / PEAK_GBS, 1)}
+                print(json.dumps(rec), file=out, flush=True)
+            del wl, xs
+            torch.cuda.empty_cache()
+        # calibration: a plain device-to-device copy of M bytes through torch
+        a = torch.empty(M, dtype=torch.uint8, device="cuda")
+        bb = torch.empty_like(a)
+        times = []
+        for rep in range(args.sweep_reps + 3):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            bb.copy_(a)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rep >= 3:
+                times.append(e0.elapsed_time(e1) * 1e-3)
+        print(json.dumps({"message_mib": mib, "row": "torch_copy_calibration", "bytes_per_launch": 2 * M,
+                          "gbs_median": round(2 * M / statistics.median(times) / 1e9, 1)}), file=out, flush=True)
+        del a, bb
+        torch.cuda.empty_cache()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
+              "requested). The relay's local kernels shard per rank; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.sweep:
+        sweep(args)
+    else:
+        step_bench(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,230 @@
+/*
+ * rr.h -- C ABI of the MI355X (gfx950) kernels for the per-GPU local work of the
+ * link-balanced sharded relay collectives, as described in the pull request
+ * "Link-balance the sharded relay schedules (up to 3.2x vs NCCL)" (torchrec #4570)
+ * and the commit messages of its stack.
+ *
+ * Terms follow the pull request:
+ *   A          active ranks per sparse group (2 or 4)
+ *   H          helpers per group: the other local ranks, local_size - A (>= 1)
+ *   numChunks  relay chunk divisor (A=2: H+2 in the link-balanced schedule;
+ *              A=4 all-to-all: H+1)
+ *   permille   A=4 allreduce / reduce-scatter offload fraction in 1/1000
+ *              (500 = the balanced split of summary section 4)
+ *   count      the per-group element count the kernel receives: the per-rank
+ *              element count for allreduce, recvCount for reduce-scatter,
+ *              segmentCount for all-to-all
+ *
+ * Conventions for every entry point:
+ *   - Buffers are device memory owned by the caller (for example torch
+ *     tensors).  The library allocates, frees, retains and synchronises
+ *     nothing; it never reads a buffer on the host.
+ *   - Pointer arguments of the form `const void* const* p` are HOST arrays of
+ *     DEVICE pointers.
+ *   - Kernels are enqueued on `stream` (a hipStream_t passed as void*; NULL =
+ *     the null stream) and run asynchronously.
+ *   - Buffer sizes are the caller's contract (they are stated per entry
+ *     point); the library cannot check them.
+ *   - Every call validates its arguments before any HIP call and returns an
+ *     rr_status; a thread-local message is available from rr_last_error().
+ *     No exception crosses the ABI.  RR_EHIP means a HIP launch failed.
+ *   - A relay chunk of zero elements (count below numChunks * 128, or an A=4
+ *     allreduce under the 2 MiB floor) is not an error: the group is served by
+ *     the direct path, helper work is a no-op and returns RR_OK (the zero-chunk
+ *     direct-fallback commit of the stack).
+ *   - Reductions read the buffer dtype, accumulate in fp32 in ascending source
+ *     rank order, multiply once by the op scale (SUM 1, AVG 1/A) and round once
+ *     to the buffer dtype (round-to-nearest-even).  A NaN result is a NaN of
+ *     unspecified payload.  Pack and unpack copy raw bit patterns.
+ */
+#ifndef RR_H
+#define RR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RR_ABI_VERSION 1
+
+typedef enum {
+    RR_OK = 0,
+    RR_EINVAL = 1,        /* argument outside the method's domain */
+    RR_EALIAS = 2,        /* forbidden overlap between inputs and outputs */
+    RR_EUNSUPPORTED = 3,  /* valid in the method, not provided by this library */
+    RR_EHIP = 4           /* the HIP runtime reported an error */
+} rr_status;
+
+typedef enum { RR_F32 = 0, RR_BF16 = 1 } rr_dtype;
+
+/* Only SUM and AVG exist in the method (reduce-scatter core commit). */
+typedef enum { RR_SUM = 0, RR_AVG = 1 } rr_op;
+
+typedef enum { RR_ALLREDUCE = 0, RR_REDUCE_SCATTER = 1, RR_ALLTOALL = 2 } rr_coll;
+
+typedef struct {
+    int32_t A;
+    int32_t H;
+    int32_t numChunks;
+    int32_t permille;
+    int64_t count;
+} rr_relay;
+
+/* Geometry of one group, in elements.  The relay region comes first:
+ * helper k owns [k*chunk, (k+1)*chunk) of every buffer it relays, so
+ * relay_total = H*chunk; the direct region is [direct_off, direct_off +
+ * direct_len) = [relay_total, count). */
+typedef struct {
+    int64_t chunk;        /* per-helper relay chunk (A=4 allreduce: oChunk); 0 = pure direct */
+    int64_t relay_total;
+    int64_t direct_off;
+    int64_t direct_len;
+    int64_t dirA_off, dirA_len; /* A=2: the direct piece riding with relay group 1 */
+    int64_t dirB_off, dirB_len; /* A=2: the direct piece riding with relay group 2 */
+    int64_t dslice;       /* A=4 allreduce / reduce-scatter: direct slice per active
+                             (active A-1 also takes direct_len - A*dslice) */
+    int64_t helper_elems; /* helper scratch contract for this collective */
+    int32_t pure_direct;
+    int32_t reserved;
+} rr_geom;
+
+/* ABI version compiled into the library (RR_ABI_VERSION). */
+int rr_abi_version(void);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *rr_last_error(void);
+
+/*
+ * rr_geometry -- the chunk geometry of one group (summary section 1 for A=2,
+ * section 4 for the A=4 allreduce, section 6 for the A=4 reduce-scatter, the
+ * all-to-all distributed-layer commit for the all-to-all chunk, and the
+ * zero-chunk direct-fallback commit for chunk == 0).
+ *   A=2, any collective: numChunks >= H+2; chunk = align_down(count/numChunks, 128);
+ *     dirA = the chunk at index H, dirB = the rest of the buffer.  chunk == 0:
+ *     dirA = [0, count/2), dirB = the remainder.  helper_elems = 2*chunk (two
+ *     slots; the allreduce helper writes its reduced chunk over slot 0).
+ *   A=4 allreduce: chunk = align_down(count*permille/(1000*H), 128); 0 when
+ *     count*elemsize < 2 MiB.  helper_elems = 2*count, which covers the
+ *     (A+1)*chunk the flat helper-reduce-and-broadcast needs.
+ *   A=4 reduce-scatter: chunk = align_down(recvCount*permille/(1000*H), 128);
+ *     helper_elems = 2*recvCount, holding A*(A-1) input chunks and A reduced
+ *     chunks (RR_EINVAL if A*A*chunk exceeds it).
+ *   A=4 all-to-all: numChunks >= H+1; chunk = align_down(segmentCount/numChunks, 128);
+ *     helper_elems = A*(A-1)*chunk, one chunk per (destination, source) pair.
+ * Errors: RR_EINVAL for A not in {2,4}, H < 1, count < 0, numChunks or
+ * permille out of range, unknown collective or dtype, null pointers.
+ */
+rr_status rr_geometry(const rr_relay *relay, int coll, int dtype, rr_geom *out);
+
+/*
+ * rr_passthrough_helper_size -- the helper buffer size for passthrough helpers
+ * used by the distributed layer: min(count_g, A * align_down(count_g / num_chunks, 128))
+ * elements, count_g being the count the kernel receives (reduce-scatter tests
+ * commit and all-to-all distributed-layer commit).  Returns -1 if count_g < 0,
+ * A < 1 or num_chunks < 1.
+ */
+int64_t rr_passthrough_helper_size(int64_t count_g, int32_t A, int32_t num_chunks);
+
+/*
+ * rr_helper_reduce -- reduce-at-helper for the allreduce (summary section 2
+ * for A=2; section 4 and the 4-active allreduce commit, "flat
+ * helper-reduce-and-broadcast", for A=4).
+ *   coll must be RR_ALLREDUCE: the A=2 reduce-scatter helpers are passthrough
+ *   (their two slots feed different outputs and are not summable), the A=4
+ *   reduce-scatter helper uses rr_rs_multi_reduce, and all-to-all has no
+ *   reduction -- all three return RR_EINVAL.
+ *   helper:  k in [0, H); selects nothing in memory (the slots are given) but
+ *            is validated against the geometry.
+ *   slots:   nSlots == A device pointers; slots[a] holds active a's copy of
+ *            relay chunk k (chunk elements each, buffer dtype).
+ *   out:     chunk elements: out[i] = RND(scale * sum_a slots[a][i]), scale 1
+ *            (SUM) or 1/A (AVG).  The helper returns it unchanged to every
+ *            active, whose relay region then needs no further work.
+ *   Aliasing: out may equal one of the slots exactly (the A=2 helper buffer
+ *   holds just the two slots); any other overlap is RR_EALIAS.
+ */
+rr_status rr_helper_reduce(const rr_relay *relay, int coll, int dtype, int op,
+                           int helper, const void *const *slots, int nSlots,
+                           void *out, void *stream);
+
+/*
+ * rr_active_add_scale -- the active rank's fused add + scale epilogue.
+ *   RR_ALLREDUCE (A=2 or 4): in[s] (nIn == A) is source rank s's full count-
+ *     element buffer; out is active `activeIdx`'s count-element output.
+ *     A=2 writes the whole direct region [direct_off, count) (dirA and dirB,
+ *     summary section 1); A=4 writes active activeIdx's direct slice (the
+ *     intra-link reduce-scatter of section 4).  out[i] = RND(scale * sum_s in[s][i]).
+ *     Elements outside that region are not touched (the relay region holds
+ *     what the helpers returned).
+ *   RR_REDUCE_SCATTER (A=2 only): in[s] (nIn == 2) is source s's block destined
+ *     for owner activeIdx (recvCount elements: the own block, and the other
+ *     active's block as assembled from the helpers' passthrough forwards and
+ *     the direct exchange); out is the owner's recvCount-element output, all of
+ *     which is written.  This fuses the add + scale of the relayed chunks and
+ *     the final reduction of the direct chunks (reduce-scatter core commit,
+ *     phases 3 and 5) into one pass.  A=4 uses rr_rs_multi_reduce (RR_EINVAL).
+ *   Aliasing: out may equal in[activeIdx] exactly (in-place); any other overlap
+ *   is RR_EALIAS.
+ */
+rr_status rr_active_add_scale(const rr_relay *relay, int coll, int dtype, int op,
+                              int activeIdx, const void *const *in, int nIn,
+                              void *out, void *stream);
+
+/*
+ * rr_rs_multi_reduce -- the A=4 reduce-scatter "two fused multi-input passes"
+ * of the flat reduce-at-helper schedule (summary section 6).  A must be 4.
+ *   pass 1, at helper idx (in [0, H)): nIn == 1; in[0] is the helper scratch
+ *     holding one chunk per (owner o, source) pair at element offset
+ *     (o*(A-1) + j)*chunk, j indexing the sources other than o in ascending
+ *     order.  out (A*chunk elements, owner-major) receives
+ *     out[o*chunk + i] = RND(sum_j scratch[(o*(A-1)+j)*chunk + i]) -- unscaled,
+ *     the owner applies the scale.  Within the 2*recvCount contract out
+ *     conventionally sits at scratch + A*(A-1)*chunk.  out must not overlap
+ *     the A*(A-1) input chunks (RR_EALIAS).
+ *   pass 2, at owner idx (in [0, A)): nIn == A + H; in[s] (s < A) is source s's
+ *     recvCount-element block destined for owner idx (in[idx] is the owner's
+ *     own block); in[A+h] is helper h's reduced chunk for this owner (chunk
+ *     elements).  out (recvCount elements):
+ *       offload slice h, [h*chunk, (h+1)*chunk): RND(scale*(in[idx][i] + in[A+h][i-h*chunk]))
+ *       direct region [H*chunk, recvCount):      RND(scale*sum_s in[s][i])
+ *     out may equal in[idx] exactly (in-place); any other overlap is RR_EALIAS.
+ *     With chunk == 0 the whole output is the direct sum and in[A..A+H-1]
+ *     are not read.
+ */
+rr_status rr_rs_multi_reduce(const rr_relay *relay, int dtype, int op, int pass,
+                             int idx, const void *const *in, int nIn, void *out,
+                             void *stream);
+
+/*
+ * rr_a2a_pack -- strided gather that coalesces helper slice h's all-to-all
+ * traffic per destination (the reverted all-to-all paragraph of the summary:
+ * "both ends are strided by segmentCount").  Out-of-place only.
+ *   src[s] (A pointers): source s's input, A segments of count elements,
+ *     segment d destined for rank d.
+ *   dst[d] (A pointers): (A-1)*chunk elements; chunk j holds the slice
+ *     [helper*chunk, (helper+1)*chunk) of segment d of the j-th source other
+ *     than d, sources ascending:
+ *       dst[d][j*chunk + i] = src[s_j][d*count + helper*chunk + i].
+ *   Bit copies of dtype-sized elements.  chunk == 0: no-op.  Any overlap
+ *   between a dst range and a src range or another dst range is RR_EALIAS.
+ */
+rr_status rr_a2a_pack(const rr_relay *relay, int dtype, int helper,
+                      const void *const *src, void *const *dst, void *stream);
+
+/*
+ * rr_a2a_unpack -- the inverse scatter on receive:
+ *       out[d][s_j*count + helper*chunk + i] = recv[d][j*chunk + i]
+ *   recv[d]: (A-1)*chunk elements as packed for destination d; out[d]: rank d's
+ *   A*count-element output.  Only helper slice positions of the segments from
+ *   other ranks are written.  Any overlap between an out slice and a recv
+ *   range or another out slice is RR_EALIAS.
+ */
+rr_status rr_a2a_unpack(const rr_relay *relay, int dtype, int helper,
+                        const void *const *recv, void *const *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RR_H */

@@ -1,0 +1,242 @@
+"""Python binding of librr.so, the gfx950 C-ABI library for the per-GPU hot path
+of the link-balanced sharded relay collectives (torchrec pull request #4570,
+"Link-balance the sharded relay schedules").
+
+The functions carry the C entry points' names and only marshal arguments:
+torch device tensors become device pointers, ``stream`` defaults to torch's
+current stream, and every step runs in the library's HIP kernels.  The binding
+checks what the C ABI cannot see -- that every tensor lives on the GPU, is
+contiguous, has the buffer dtype and is large enough -- and raises
+``ValueError`` for a rejected argument and ``RuntimeError`` for a HIP failure
+or a missing library.  There is no CPU fallback.
+
+Pointer/layout semantics of each call are documented in include/rr.h.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = [
+    "Relay", "RRError", "F32", "BF16", "SUM", "AVG", "ALLREDUCE", "REDUCE_SCATTER", "ALLTOALL",
+    "library_path", "load", "rr_abi_version", "rr_geometry", "rr_passthrough_helper_size",
+    "rr_helper_reduce", "rr_active_add_scale", "rr_rs_multi_reduce", "rr_a2a_pack",
+    "rr_a2a_unpack",
+]
+
+F32, BF16 = 0, 1
+SUM, AVG = 0, 1
+ALLREDUCE, REDUCE_SCATTER, ALLTOALL = 0, 1, 2
+RR_OK, RR_EINVAL, RR_EALIAS, RR_EUNSUPPORTED, RR_EHIP = 0, 1, 2, 3, 4
+_STATUS = {1: "RR_EINVAL", 2: "RR_EALIAS", 3: "RR_EUNSUPPORTED", 4: "RR_EHIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "librr.so")
+
+
+class RRError(ValueError):
+    """A call the library rejected; ``status`` is the rr_status code."""
+
+    def __init__(self, status, msg):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class _Relay(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_int32), ("H", ctypes.c_int32), ("numChunks", ctypes.c_int32),
+                ("permille", ctypes.c_int32), ("count", ctypes.c_int64)]
+
+
+class _Geom(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "chunk", "relay_total", "direct_off", "direct_len", "dirA_off", "dirA_len",
+        "dirB_off", "dirB_len", "dslice", "helper_elems")] + [
+        ("pure_direct", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Relay:
+    """One group's relay parameters in the pull request's terms (see rr.h)."""
+    A: int
+    H: int
+    numChunks: int = 0
+    permille: int = 500
+    count: int = 0
+
+    def _c(self):
+        return _Relay(self.A, self.H, self.numChunks, self.permille, self.count)
+
+
+_lib = None
+
+
+def load():
+    """Load librr.so (built by pack_rr_helper_amd/build.py); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(
+            f"{library_path} is missing: build it with `python -m pack_rr_helper_amd.build` "
+            "(the relay hot path has no CPU fallback)")
+    L = ctypes.CDLL(library_path)
+    vp, i32, i64, pp = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_void_p)
+    rp = ctypes.POINTER(_Relay)
+    ci = ctypes.c_int
+    for name, res, args in [
+        ("rr_abi_version", ci, []),
+        ("rr_last_error", ctypes.c_char_p, []),
+        ("rr_geometry", ci, [rp, ci, ci, ctypes.POINTER(_Geom)]),
+        ("rr_passthrough_helper_size", i64, [i64, i32, i32]),
+        ("rr_helper_reduce", ci, [rp, ci, ci, ci, ci, pp, ci, vp, vp]),
+        ("rr_active_add_scale", ci, [rp, ci, ci, ci, ci, pp, ci, vp, vp]),
+        ("rr_rs_multi_reduce", ci, [rp, ci, ci, ci, ci, pp, ci, vp, vp]),
+        ("rr_a2a_pack", ci, [rp, ci, ci, pp, pp, vp]),
+        ("rr_a2a_unpack", ci, [rp, ci, ci, pp, pp, vp]),
+    ]:
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    _lib = L
+    return L
+
+
+def _raise(st):
+    if st == RR_OK:
+        return
+    msg = load().rr_last_error().decode(errors="replace")
+    if st == RR_EHIP:
+        raise RuntimeError(f"RR_EHIP: {msg}")
+    raise RRError(st, msg)
+
+
+# --------------------------------------------------------------------------
+# marshalling
+# --------------------------------------------------------------------------
+
+_TORCH_DT = {F32: (torch.float32,), BF16: (torch.bfloat16,)}
+_BITS_DT = {4: (torch.float32, torch.int32, torch.uint32),
+            2: (torch.bfloat16, torch.float16, torch.int16, torch.uint16)}
+
+
+def _esize(dtype):
+    if dtype not in (F32, BF16):
+        raise RRError(RR_EINVAL, f"unknown dtype {dtype}")
+    return 4 if dtype == F32 else 2
+
+
+def _dev(t, what, dtype, min_elems, bits=False):
+    """Device pointer of tensor t after the checks the C ABI cannot make."""
+    if not isinstance(t, torch.Tensor):
+        raise RRError(RR_EINVAL, f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise RRError(RR_EINVAL, f"{what} is on {t.device}, the kernels need device memory")
+    ok_dt = _BITS_DT[_esize(dtype)] if bits else _TORCH_DT[dtype]
+    if t.dtype not in ok_dt:
+        raise RRError(RR_EINVAL, f"{what} has dtype {t.dtype}, expected one of {ok_dt}")
+    if not t.is_contiguous():
+        raise RRError(RR_EINVAL, f"{what} must be contiguous")
+    if t.numel() < min_elems:
+        raise RRError(RR_EINVAL, f"{what} holds {t.numel()} elements, needs {min_elems}")
+    return t.data_ptr()
+
+
+def _ptrs(ts, what, dtype, min_elems, bits=False):
+    if isinstance(ts, torch.Tensor):
+        ts = [ts]
+    ts = list(ts)
+    arr = (ctypes.c_void_p * max(len(ts), 1))()
+    for i, t in enumerate(ts):
+        arr[i] = _dev(t, f"{what}[{i}]", dtype, min_elems[i] if isinstance(min_elems, list) else min_elems,
+                      bits)
+    return arr, len(ts)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+# --------------------------------------------------------------------------
+# entry points
+# --------------------------------------------------------------------------
+
+def rr_abi_version():
+    return load().rr_abi_version()
+
+
+def rr_geometry(relay, coll, dtype):
+    """The group's geometry as a dict (see rr_geom in rr.h)."""
+    g = _Geom()
+    r = relay._c()
+    _raise(load().rr_geometry(ctypes.byref(r), coll, dtype, ctypes.byref(g)))
+    return {n: getattr(g, n) for n, _ in _Geom._fields_ if n != "reserved"}
+
+
+def rr_passthrough_helper_size(count_g, A, num_chunks):
+    v = load().rr_passthrough_helper_size(count_g, A, num_chunks)
+    if v < 0:
+        raise RRError(RR_EINVAL, "count_g < 0, A < 1 or num_chunks < 1")
+    return v
+
+
+def rr_helper_reduce(relay, coll, dtype, op, helper, slots, out, stream=None):
+    g = rr_geometry(relay, coll, dtype) if coll == ALLREDUCE else {"chunk": 0}
+    n = g["chunk"]
+    arr, k = _ptrs(slots, "slots", dtype, n)
+    o = _dev(out, "out", dtype, n)
+    r = relay._c()
+    _raise(load().rr_helper_reduce(ctypes.byref(r), coll, dtype, op, helper, arr, k,
+                                   ctypes.c_void_p(o), _stream(stream)))
+
+
+def rr_active_add_scale(relay, coll, dtype, op, active_idx, inputs, out, stream=None):
+    arr, k = _ptrs(inputs, "in", dtype, relay.count)
+    o = _dev(out, "out", dtype, relay.count)
+    r = relay._c()
+    _raise(load().rr_active_add_scale(ctypes.byref(r), coll, dtype, op, active_idx, arr, k,
+                                      ctypes.c_void_p(o), _stream(stream)))
+
+
+def rr_rs_multi_reduce(relay, dtype, op, pass_, idx, inputs, out, stream=None):
+    g = rr_geometry(relay, REDUCE_SCATTER, dtype)
+    A, H, c, R = relay.A, relay.H, g["chunk"], relay.count
+    inputs = list(inputs) if not isinstance(inputs, torch.Tensor) else [inputs]
+    if pass_ == 1:
+        need, out_need = [A * (A - 1) * c] * len(inputs), A * c
+    else:
+        need = [R if i < A else c for i in range(len(inputs))]
+        out_need = R
+    arr, k = _ptrs(inputs, "in", dtype, need)
+    o = _dev(out, "out", dtype, out_need)
+    r = relay._c()
+    _raise(load().rr_rs_multi_reduce(ctypes.byref(r), dtype, op, pass_, idx, arr, k,
+                                     ctypes.c_void_p(o), _stream(stream)))
+
+
+def _a2a_sizes(relay, dtype):
+    g = rr_geometry(relay, ALLTOALL, dtype)
+    return relay.A * relay.count, (relay.A - 1) * g["chunk"]
+
+
+def rr_a2a_pack(relay, dtype, helper, src, dst, stream=None):
+    full, packed = _a2a_sizes(relay, dtype)
+    if len(src) != relay.A or len(dst) != relay.A:
+        raise RRError(RR_EINVAL, f"pack takes A={relay.A} sources and A destinations")
+    s, _ = _ptrs(src, "src", dtype, full, bits=True)
+    d, _ = _ptrs(dst, "dst", dtype, packed, bits=True)
+    r = relay._c()
+    _raise(load().rr_a2a_pack(ctypes.byref(r), dtype, helper, s, d, _stream(stream)))
+
+
+def rr_a2a_unpack(relay, dtype, helper, recv, out, stream=None):
+    full, packed = _a2a_sizes(relay, dtype)
+    if len(recv) != relay.A or len(out) != relay.A:
+        raise RRError(RR_EINVAL, f"unpack takes A={relay.A} receive buffers and A outputs")
+    s, _ = _ptrs(recv, "recv", dtype, packed, bits=True)
+    d, _ = _ptrs(out, "out", dtype, full, bits=True)
+    r = relay._c()
+    _raise(load().rr_a2a_unpack(ctypes.byref(r), dtype, helper, s, d, _stream(stream)))

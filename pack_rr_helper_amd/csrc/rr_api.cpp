@@ -1,0 +1,674 @@
+// rr_api.cpp -- the C ABI declared in include/rr.h: argument validation,
+// relay geometry, and the translation of each relay step into the segment
+// tables the gfx950 kernels execute (rr_kernels.hip).
+//
+// Everything here runs on the host and returns before any HIP call when the
+// arguments are rejected.  Nothing is allocated: segment tables travel in the
+// kernel arguments.
+#include "rr.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "rr_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+rr_status fail(rr_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+rr_status ok()
+{
+    g_err[0] = '\0';
+    return RR_OK;
+}
+
+int64_t elem_size(int dtype) { return dtype == RR_F32 ? 4 : 2; }
+
+int64_t align_down_128(int64_t x) { return (x / 128) * 128; }
+
+uintptr_t addr(const void *p) { return reinterpret_cast<uintptr_t>(p); }
+
+// ---------------------------------------------------------------------------
+// Geometry (pull request summary sections 1, 4 and 6; zero-chunk fallback)
+// ---------------------------------------------------------------------------
+
+rr_status compute_geometry(const rr_relay *r, int coll, int dtype, rr_geom *g)
+{
+    if (!r)
+        return fail(RR_EINVAL, "relay descriptor is null");
+    memset(g, 0, sizeof *g);
+    const int A = r->A, H = r->H;
+    if (A != 2 && A != 4)
+        return fail(RR_EINVAL, "A=%d: the relay supports 2 or 4 active ranks per group", A);
+    if (H < 1)
+        return fail(RR_EINVAL, "H=%d: a relay group needs at least one helper", H);
+    if (r->count < 0)
+        return fail(RR_EINVAL, "count=%lld is negative", (long long)r->count);
+    if (coll < RR_ALLREDUCE || coll > RR_ALLTOALL)
+        return fail(RR_EINVAL, "unknown collective %d", coll);
+    if (dtype != RR_F32 && dtype != RR_BF16)
+        return fail(RR_EINVAL, "unknown dtype %d", dtype);
+
+    const int64_t es = elem_size(dtype);
+    int64_t chunk = 0;
+    if (A == 2) {
+        if (r->numChunks < H + 2)
+            return fail(RR_EINVAL,
+                        "numChunks=%d: the two-group A=2 schedule needs at least H+2=%d chunks",
+                        r->numChunks, H + 2);
+        chunk = align_down_128(r->count / r->numChunks);
+    } else if (coll == RR_ALLTOALL) {
+        if (r->numChunks < H + 1)
+            return fail(RR_EINVAL, "numChunks=%d: all-to-all needs at least H+1=%d chunks",
+                        r->numChunks, H + 1);
+        chunk = align_down_128(r->count / r->numChunks);
+    } else {
+        if (r->permille <= 0 || r->permille > 1000)
+            return fail(RR_EINVAL, "permille=%d must be in (0, 1000]", r->permille);
+        const bool under_floor = coll == RR_ALLREDUCE && r->count * es < (int64_t(2) << 20);
+        chunk = under_floor ? 0 : align_down_128(r->count * r->permille / (int64_t(1000) * H));
+        if (coll == RR_REDUCE_SCATTER && int64_t(A) * A * chunk > 2 * r->count)
+            return fail(RR_EINVAL,
+                        "permille=%d: A*(A-1) input chunks plus A reduced chunks exceed the "
+                        "2*recvCount helper contract",
+                        r->permille);
+    }
+
+    g->chunk = chunk;
+    g->pure_direct = chunk == 0;
+    g->relay_total = int64_t(H) * chunk;
+    g->direct_off = g->relay_total;
+    g->direct_len = r->count - g->relay_total;
+    if (A == 2) {
+        if (chunk > 0) {
+            g->dirA_off = int64_t(H) * chunk;
+            g->dirA_len = chunk;
+            g->dirB_off = int64_t(H + 1) * chunk;
+            g->dirB_len = r->count - g->dirB_off;
+        } else {
+            g->dirA_off = 0;
+            g->dirA_len = r->count / 2;
+            g->dirB_off = g->dirA_len;
+            g->dirB_len = r->count - g->dirA_len;
+        }
+        g->helper_elems = int64_t(A) * chunk;
+    } else if (coll == RR_ALLTOALL) {
+        g->helper_elems = int64_t(A) * (A - 1) * chunk;
+    } else {
+        g->dslice = g->direct_len / A;
+        g->helper_elems = 2 * r->count;
+    }
+    return RR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Byte ranges and aliasing
+// ---------------------------------------------------------------------------
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+    bool empty() const { return hi <= lo; }
+};
+
+Range range_of(const void *p, int64_t off_elems, int64_t n_elems, int64_t es)
+{
+    const uintptr_t lo = addr(p) + uintptr_t(off_elems * es);
+    return Range{lo, lo + uintptr_t(n_elems * es)};
+}
+
+bool overlap(Range a, Range b)
+{
+    return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool same(Range a, Range b) { return a.lo == b.lo && a.hi == b.hi; }
+
+rr_status check_ptr(const void *p, int64_t es, const char *what, int idx)
+{
+    if (!p)
+        return fail(RR_EINVAL, "%s[%d] is null", what, idx);
+    if (addr(p) % uintptr_t(es))
+        return fail(RR_EINVAL, "%s[%d]=%p is not aligned to the %lld-byte element", what, idx,
+                    p, (long long)es);
+    return RR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Reduction segments
+// ---------------------------------------------------------------------------
+
+struct RedItem {
+    const void *in[rr::kMaxIn];
+    int k;
+    void *out;
+    int64_t n;
+};
+
+// An element-wise output is safe when its range equals an input's range
+// exactly (each lane reads its inputs before writing the same elements) or is
+// disjoint from it; everything else is a forbidden alias.  Outputs must also
+// be disjoint from every other item's inputs and outputs.
+rr_status check_items(const RedItem *items, int nitems, int64_t es)
+{
+    for (int i = 0; i < nitems; ++i) {
+        const Range o = range_of(items[i].out, 0, items[i].n, es);
+        for (int j = 0; j < nitems; ++j) {
+            for (int k = 0; k < items[j].k; ++k) {
+                const Range x = range_of(items[j].in[k], 0, items[j].n, es);
+                if (!overlap(o, x))
+                    continue;
+                if (i == j && same(o, x))
+                    continue;
+                return fail(RR_EALIAS,
+                            "output range overlaps an input range other than an exact in-place alias");
+            }
+            if (j != i && overlap(o, range_of(items[j].out, 0, items[j].n, es)))
+                return fail(RR_EALIAS, "two output ranges overlap");
+        }
+    }
+    return RR_OK;
+}
+
+class RedLauncher {
+public:
+    RedLauncher(bool bf16, hipStream_t st) : bf16_(bf16), st_(st)
+    {
+        memset(&b_, 0, sizeof b_);
+        b_.bf16 = bf16;
+    }
+
+    // Splits one element-wise item into an unaligned head, a 16-byte
+    // vector body and a tail when every pointer agrees modulo 16 bytes;
+    // otherwise the whole item takes the element-wise path.
+    void add(const RedItem &it, float scale, int64_t es)
+    {
+        if (it.n <= 0)
+            return;
+        const uintptr_t m = addr(it.out) % 16;
+        bool agree = true;
+        for (int k = 0; k < it.k; ++k)
+            agree = agree && (addr(it.in[k]) % 16 == m);
+        if (!agree) {
+            piece(it, 0, it.n, false, scale, es);
+            return;
+        }
+        const int64_t ve = 16 / es;
+        const int64_t head = std::min<int64_t>(it.n, int64_t((16 - m) % 16) / es);
+        const int64_t body = ((it.n - head) / ve) * ve;
+        piece(it, 0, head, false, scale, es);
+        piece(it, head, body, true, scale, es);
+        piece(it, head + body, it.n - head - body, false, scale, es);
+    }
+
+    hipError_t finish()
+    {
+        flush();
+        return err_;
+    }
+
+private:
+    void piece(const RedItem &it, int64_t off, int64_t n, bool vec, float scale, int64_t es)
+    {
+        while (n > 0) {
+            rr::RedSeg s{};
+            for (int k = 0; k < it.k; ++k)
+                s.in[k] = static_cast<const char *>(it.in[k]) + off * es;
+            s.out = static_cast<char *>(it.out) + off * es;
+            s.k = it.k;
+            s.vec = vec;
+            s.scale = scale;
+            s.n = n;
+            if (b_.nseg == rr::kMaxRedSegs || tiles_ >= rr::kMaxTilesPerLaunch)
+                flush();
+            const int64_t per_tile = rr::red_tile_elems(vec, bf16_);
+            const int64_t room = rr::kMaxTilesPerLaunch - tiles_;
+            if ((s.n + per_tile - 1) / per_tile > room)
+                s.n = room * per_tile;
+            b_.tile0[b_.nseg] = int32_t(tiles_);
+            b_.seg[b_.nseg++] = s;
+            tiles_ += (s.n + per_tile - 1) / per_tile;
+            off += s.n;
+            n -= s.n;
+        }
+    }
+
+    void flush()
+    {
+        if (b_.nseg == 0)
+            return;
+        const hipError_t e = rr::launch_reduce(b_, tiles_, st_);
+        if (e != hipSuccess && err_ == hipSuccess)
+            err_ = e;
+        memset(&b_, 0, sizeof b_);
+        b_.bf16 = bf16_;
+        tiles_ = 0;
+    }
+
+    rr::RedBatch b_;
+    int64_t tiles_ = 0;
+    bool bf16_;
+    hipStream_t st_;
+    hipError_t err_ = hipSuccess;
+};
+
+rr_status run_reduce(const RedItem *items, int nitems, int dtype, float scale, void *stream)
+{
+    const int64_t es = elem_size(dtype);
+    rr_status st = check_items(items, nitems, es);
+    if (st != RR_OK)
+        return st;
+    RedLauncher L(dtype == RR_BF16, static_cast<hipStream_t>(stream));
+    for (int i = 0; i < nitems; ++i)
+        L.add(items[i], scale, es);
+    const hipError_t e = L.finish();
+    if (e != hipSuccess)
+        return fail(RR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+float op_scale(int op, int A) { return op == RR_AVG ? 1.0f / float(A) : 1.0f; }
+
+rr_status check_common(const rr_relay *r, int coll, int dtype, int op, rr_geom *g)
+{
+    rr_status st = compute_geometry(r, coll, dtype, g);
+    if (st != RR_OK)
+        return st;
+    if (op != RR_SUM && op != RR_AVG)
+        return fail(RR_EINVAL, "op=%d: the relay supports SUM and AVG only", op);
+    return RR_OK;
+}
+
+rr_status check_array(const void *const *arr, int n, int64_t es, const char *what)
+{
+    if (!arr)
+        return fail(RR_EINVAL, "%s pointer array is null", what);
+    for (int i = 0; i < n; ++i) {
+        rr_status st = check_ptr(arr[i], es, what, i);
+        if (st != RR_OK)
+            return st;
+    }
+    return RR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Copy segments (all-to-all pack / unpack)
+// ---------------------------------------------------------------------------
+
+class CopyLauncher {
+public:
+    explicit CopyLauncher(hipStream_t st) : st_(st)
+    {
+        memset(q_, 0, sizeof q_);
+        q_[1].shifted = true;
+    }
+
+    // Head bytes up to the destination's 16-byte boundary, a 16-byte body
+    // (aligned, or realigned from a source at another offset), and a tail.
+    void add(const void *src, void *dst, int64_t nbytes)
+    {
+        if (nbytes <= 0)
+            return;
+        const unsigned char *s = static_cast<const unsigned char *>(src);
+        unsigned char *d = static_cast<unsigned char *>(dst);
+        const int64_t head = std::min<int64_t>(nbytes, int64_t((16 - addr(d) % 16) % 16));
+        const int64_t body = ((nbytes - head) / 16) * 16;
+        piece(s, d, head, rr::kCopyBytes, 0);
+        const unsigned char *bs = s + head;
+        const uintptr_t delta = addr(bs) % 16;
+        if (delta == 0)
+            piece(bs, d + head, body, rr::kCopyAligned, 0);
+        else
+            piece(bs - delta, d + head, body, rr::kCopyShifted, int32_t(delta));
+        piece(s + head + body, d + head + body, nbytes - head - body, rr::kCopyBytes, 0);
+    }
+
+    hipError_t finish()
+    {
+        flush(q_[0]);
+        flush(q_[1]);
+        return err_;
+    }
+
+private:
+    struct Queue {
+        rr::CopyBatch b;
+        int64_t tiles;
+        bool shifted;
+    };
+
+    void piece(const unsigned char *src, unsigned char *dst, int64_t nbytes, int32_t mode,
+               int32_t shift)
+    {
+        Queue &q = q_[mode == rr::kCopyShifted ? 1 : 0];
+        while (nbytes > 0) {
+            rr::CopySeg s{};
+            s.src = src;
+            s.dst = dst;
+            s.nbytes = nbytes;
+            s.mode = mode;
+            s.shift = shift;
+            if (q.b.nseg == rr::kMaxCopySegs || q.tiles >= rr::kMaxTilesPerLaunch)
+                flush(q);
+            const int64_t per_tile = rr::copy_tile_bytes(mode);
+            const int64_t room = rr::kMaxTilesPerLaunch - q.tiles;
+            if ((s.nbytes + per_tile - 1) / per_tile > room)
+                s.nbytes = room * per_tile;
+            q.b.tile0[q.b.nseg] = int32_t(q.tiles);
+            q.b.seg[q.b.nseg++] = s;
+            q.tiles += (s.nbytes + per_tile - 1) / per_tile;
+            // a shifted body's source pointer is its aligned base: advancing
+            // it by whole 16-byte vectors keeps both the base and the shift
+            src += s.nbytes;
+            dst += s.nbytes;
+            nbytes -= s.nbytes;
+        }
+    }
+
+    void flush(Queue &q)
+    {
+        if (q.b.nseg == 0)
+            return;
+        const hipError_t e = rr::launch_copy(q.b, q.tiles, q.shifted, st_);
+        if (e != hipSuccess && err_ == hipSuccess)
+            err_ = e;
+        const bool shifted = q.shifted;
+        memset(&q, 0, sizeof q);
+        q.shifted = shifted;
+    }
+
+    Queue q_[2];
+    hipStream_t st_;
+    hipError_t err_ = hipSuccess;
+};
+
+// All-to-all chunk moves of helper slice h: for destination d and the j-th
+// source s_j != d, (source segment d of s_j at slice h) <-> (chunk j of the
+// per-destination buffer of d).
+struct A2AMove {
+    int d, s, j;
+};
+
+int a2a_moves(int A, A2AMove *mv)
+{
+    int n = 0;
+    for (int d = 0; d < A; ++d) {
+        int j = 0;
+        for (int s = 0; s < A; ++s) {
+            if (s == d)
+                continue;
+            mv[n++] = A2AMove{d, s, j++};
+        }
+    }
+    return n;
+}
+
+rr_status check_a2a(const rr_relay *r, int dtype, int helper, rr_geom *g)
+{
+    rr_status st = compute_geometry(r, RR_ALLTOALL, dtype, g);
+    if (st != RR_OK)
+        return st;
+    if (helper < 0 || helper >= r->H)
+        return fail(RR_EINVAL, "helper=%d outside [0, H=%d)", helper, r->H);
+    return RR_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// Exported entry points
+// ===========================================================================
+
+extern "C" {
+
+int rr_abi_version(void) { return RR_ABI_VERSION; }
+
+const char *rr_last_error(void) { return g_err; }
+
+rr_status rr_geometry(const rr_relay *relay, int coll, int dtype, rr_geom *out)
+{
+    if (!out)
+        return fail(RR_EINVAL, "output geometry pointer is null");
+    rr_status st = compute_geometry(relay, coll, dtype, out);
+    return st == RR_OK ? ok() : st;
+}
+
+int64_t rr_passthrough_helper_size(int64_t count_g, int32_t A, int32_t num_chunks)
+{
+    if (count_g < 0 || A < 1 || num_chunks < 1)
+        return -1;
+    const int64_t slots = int64_t(A) * align_down_128(count_g / num_chunks);
+    return std::min(count_g, slots);
+}
+
+rr_status rr_helper_reduce(const rr_relay *relay, int coll, int dtype, int op, int helper,
+                           const void *const *slots, int nSlots, void *out, void *stream)
+{
+    rr_geom g;
+    rr_status st = check_common(relay, coll, dtype, op, &g);
+    if (st != RR_OK)
+        return st;
+    if (coll == RR_REDUCE_SCATTER)
+        return fail(RR_EINVAL,
+                    relay->A == 2
+                        ? "A=2 reduce-scatter helpers are passthrough: slot 0 and slot 1 feed "
+                          "different outputs and are not summable"
+                        : "the A=4 reduce-scatter helper reduces with rr_rs_multi_reduce pass 1");
+    if (coll == RR_ALLTOALL)
+        return fail(RR_EINVAL, "all-to-all performs no reduction");
+    const int A = relay->A;
+    if (nSlots != A)
+        return fail(RR_EINVAL, "nSlots=%d: the allreduce helper sums exactly A=%d slots", nSlots, A);
+    if (helper < 0 || helper >= relay->H)
+        return fail(RR_EINVAL, "helper=%d outside [0, H=%d)", helper, relay->H);
+    if (g.chunk == 0)
+        return ok();  // pure direct: the helper has nothing to reduce
+    const int64_t es = elem_size(dtype);
+    if ((st = check_array(slots, nSlots, es, "slots")) != RR_OK)
+        return st;
+    if ((st = check_ptr(out, es, "out", 0)) != RR_OK)
+        return st;
+    RedItem it{};
+    for (int a = 0; a < A; ++a)
+        it.in[a] = slots[a];
+    it.k = A;
+    it.out = out;
+    it.n = g.chunk;
+    return run_reduce(&it, 1, dtype, op_scale(op, A), stream);
+}
+
+rr_status rr_active_add_scale(const rr_relay *relay, int coll, int dtype, int op, int activeIdx,
+                              const void *const *in, int nIn, void *out, void *stream)
+{
+    rr_geom g;
+    rr_status st = check_common(relay, coll, dtype, op, &g);
+    if (st != RR_OK)
+        return st;
+    const int A = relay->A;
+    if (coll == RR_ALLTOALL)
+        return fail(RR_EINVAL, "all-to-all performs no reduction");
+    if (coll == RR_REDUCE_SCATTER && A != 2)
+        return fail(RR_EINVAL, "the A=4 reduce-scatter owner reduces with rr_rs_multi_reduce pass 2");
+    if (nIn != A)
+        return fail(RR_EINVAL, "nIn=%d: the active epilogue sums one input per active (A=%d)", nIn, A);
+    if (activeIdx < 0 || activeIdx >= A)
+        return fail(RR_EINVAL, "activeIdx=%d outside [0, A=%d)", activeIdx, A);
+    const int64_t es = elem_size(dtype);
+    if ((st = check_array(in, nIn, es, "in")) != RR_OK)
+        return st;
+    if ((st = check_ptr(out, es, "out", 0)) != RR_OK)
+        return st;
+
+    int64_t lo = 0, n = relay->count;  // reduce-scatter: the whole block
+    if (coll == RR_ALLREDUCE) {
+        lo = g.direct_off;
+        n = g.direct_len;
+        if (A > 2) {
+            lo = g.direct_off + int64_t(activeIdx) * g.dslice;
+            n = activeIdx == A - 1 ? g.direct_off + g.direct_len - lo : g.dslice;
+        }
+    }
+    RedItem it{};
+    for (int s = 0; s < A; ++s)
+        it.in[s] = static_cast<const char *>(in[s]) + lo * es;
+    it.k = A;
+    it.out = static_cast<char *>(out) + lo * es;
+    it.n = n;
+    return run_reduce(&it, 1, dtype, op_scale(op, A), stream);
+}
+
+rr_status rr_rs_multi_reduce(const rr_relay *relay, int dtype, int op, int pass, int idx,
+                             const void *const *in, int nIn, void *out, void *stream)
+{
+    rr_geom g;
+    rr_status st = check_common(relay, RR_REDUCE_SCATTER, dtype, op, &g);
+    if (st != RR_OK)
+        return st;
+    const int A = relay->A, H = relay->H;
+    if (A != 4)
+        return fail(RR_EINVAL,
+                    "the two multi-input passes belong to the A=4 reduce-scatter; A=2 helpers "
+                    "are passthrough and the owner uses rr_active_add_scale");
+    const int64_t es = elem_size(dtype);
+    const int64_t c = g.chunk;
+    if (pass == 1) {
+        if (idx < 0 || idx >= H)
+            return fail(RR_EINVAL, "pass 1: helper idx=%d outside [0, H=%d)", idx, H);
+        if (nIn != 1)
+            return fail(RR_EINVAL, "pass 1 takes the helper scratch as its single input (nIn=%d)", nIn);
+        if (c == 0)
+            return ok();
+        if ((st = check_array(in, 1, es, "in")) != RR_OK)
+            return st;
+        if ((st = check_ptr(out, es, "out", 0)) != RR_OK)
+            return st;
+        if (overlap(range_of(out, 0, A * c, es), range_of(in[0], 0, int64_t(A) * (A - 1) * c, es)))
+            return fail(RR_EALIAS, "pass 1 output overlaps the A*(A-1) input chunks of the scratch");
+        RedItem items[4]{};
+        for (int o = 0; o < A; ++o) {
+            for (int j = 0; j < A - 1; ++j)
+                items[o].in[j] = static_cast<const char *>(in[0]) + (int64_t(o) * (A - 1) + j) * c * es;
+            items[o].k = A - 1;
+            items[o].out = static_cast<char *>(out) + int64_t(o) * c * es;
+            items[o].n = c;
+        }
+        return run_reduce(items, A, dtype, 1.0f, stream);
+    }
+    if (pass != 2)
+        return fail(RR_EINVAL, "pass=%d: the reduction has two passes (1 helper, 2 owner)", pass);
+    if (idx < 0 || idx >= A)
+        return fail(RR_EINVAL, "pass 2: owner idx=%d outside [0, A=%d)", idx, A);
+    if (nIn != A + H)
+        return fail(RR_EINVAL, "pass 2 takes A blocks and H reduced chunks (nIn=%d, expected %d)",
+                    nIn, A + H);
+    if ((st = check_array(in, A, es, "in")) != RR_OK)
+        return st;
+    if (c > 0 && (st = check_array(in + A, H, es, "in[A+h]")) != RR_OK)
+        return st;
+    if ((st = check_ptr(out, es, "out", 0)) != RR_OK)
+        return st;
+    if (H + 1 > 24)
+        return fail(RR_EUNSUPPORTED, "H=%d exceeds this library's segment table", H);
+    RedItem items[25]{};
+    int n = 0;
+    for (int h = 0; h < H && c > 0; ++h, ++n) {
+        items[n].in[0] = static_cast<const char *>(in[idx]) + int64_t(h) * c * es;
+        items[n].in[1] = in[A + h];
+        items[n].k = 2;
+        items[n].out = static_cast<char *>(out) + int64_t(h) * c * es;
+        items[n].n = c;
+    }
+    for (int s = 0; s < A; ++s)
+        items[n].in[s] = static_cast<const char *>(in[s]) + g.direct_off * es;
+    items[n].k = A;
+    items[n].out = static_cast<char *>(out) + g.direct_off * es;
+    items[n].n = g.direct_len;
+    ++n;
+    return run_reduce(items, n, dtype, op_scale(op, A), stream);
+}
+
+rr_status rr_a2a_pack(const rr_relay *relay, int dtype, int helper, const void *const *src,
+                      void *const *dst, void *stream)
+{
+    rr_geom g;
+    rr_status st = check_a2a(relay, dtype, helper, &g);
+    if (st != RR_OK)
+        return st;
+    if (g.chunk == 0)
+        return ok();
+    const int A = relay->A;
+    const int64_t es = elem_size(dtype), seg = relay->count, c = g.chunk;
+    if ((st = check_array(src, A, es, "src")) != RR_OK)
+        return st;
+    if ((st = check_array(const_cast<const void *const *>(dst), A, es, "dst")) != RR_OK)
+        return st;
+    for (int d = 0; d < A; ++d) {
+        const Range rd = range_of(dst[d], 0, int64_t(A - 1) * c, es);
+        for (int s = 0; s < A; ++s)
+            if (overlap(rd, range_of(src[s], 0, int64_t(A) * seg, es)))
+                return fail(RR_EALIAS, "all-to-all is out-of-place: dst[%d] overlaps src[%d]", d, s);
+        for (int e = 0; e < d; ++e)
+            if (overlap(rd, range_of(dst[e], 0, int64_t(A - 1) * c, es)))
+                return fail(RR_EALIAS, "dst[%d] overlaps dst[%d]", d, e);
+    }
+    A2AMove mv[16];
+    const int nm = a2a_moves(A, mv);
+    CopyLauncher L(static_cast<hipStream_t>(stream));
+    for (int m = 0; m < nm; ++m)
+        L.add(static_cast<const char *>(src[mv[m].s]) + (int64_t(mv[m].d) * seg + int64_t(helper) * c) * es,
+              static_cast<char *>(dst[mv[m].d]) + int64_t(mv[m].j) * c * es, c * es);
+    const hipError_t e = L.finish();
+    if (e != hipSuccess)
+        return fail(RR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+rr_status rr_a2a_unpack(const rr_relay *relay, int dtype, int helper, const void *const *recv,
+                        void *const *out, void *stream)
+{
+    rr_geom g;
+    rr_status st = check_a2a(relay, dtype, helper, &g);
+    if (st != RR_OK)
+        return st;
+    if (g.chunk == 0)
+        return ok();
+    const int A = relay->A;
+    const int64_t es = elem_size(dtype), seg = relay->count, c = g.chunk;
+    if ((st = check_array(recv, A, es, "recv")) != RR_OK)
+        return st;
+    if ((st = check_array(const_cast<const void *const *>(out), A, es, "out")) != RR_OK)
+        return st;
+    for (int d = 0; d < A; ++d) {
+        const Range ro = range_of(out[d], 0, int64_t(A) * seg, es);
+        for (int s = 0; s < A; ++s)
+            if (overlap(ro, range_of(recv[s], 0, int64_t(A - 1) * c, es)))
+                return fail(RR_EALIAS, "all-to-all is out-of-place: out[%d] overlaps recv[%d]", d, s);
+        for (int e = 0; e < d; ++e)
+            if (overlap(ro, range_of(out[e], 0, int64_t(A) * seg, es)))
+                return fail(RR_EALIAS, "out[%d] overlaps out[%d]", d, e);
+    }
+    A2AMove mv[16];
+    const int nm = a2a_moves(A, mv);
+    CopyLauncher L(static_cast<hipStream_t>(stream));
+    for (int m = 0; m < nm; ++m)
+        L.add(static_cast<const char *>(recv[mv[m].d]) + int64_t(mv[m].j) * c * es,
+              static_cast<char *>(out[mv[m].d]) + (int64_t(mv[m].s) * seg + int64_t(helper) * c) * es,
+              c * es);
+    const hipError_t e = L.finish();
+    if (e != hipSuccess)
+        return fail(RR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

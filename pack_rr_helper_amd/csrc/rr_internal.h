@@ -1,0 +1,97 @@
+// rr_internal.h -- launch descriptors shared by the C-ABI layer (rr_api.cpp)
+// and the gfx950 kernels (rr_kernels.hip).  Not part of the public ABI.
+//
+// Every relay step is a streaming element-wise operation: a K-input
+// fp32-accumulated sum with one scale and one rounding, or a raw copy of
+// chunks between strided and contiguous layouts.  A launch therefore carries a
+// small table of independent "segments" in its kernel arguments; each
+// workgroup processes one fixed-size tile of one segment.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace rr {
+
+constexpr int kBlock = 256;          // threads per workgroup (4 wave64)
+constexpr int kMaxIn = 4;            // inputs per reduction segment (A <= 4)
+constexpr int kMaxRedSegs = 24;      // segments per reduction launch
+constexpr int kMaxCopySegs = 64;     // segments per copy launch
+constexpr int64_t kMaxTilesPerLaunch = int64_t(1) << 22;
+
+#ifndef RR_UNROLL
+#define RR_UNROLL 4                  // 16-byte vectors per thread per input
+#endif
+#ifndef RR_LOAD_NT
+#define RR_LOAD_NT 1                 // inputs are read exactly once
+#endif
+#ifndef RR_STORE_NT
+#define RR_STORE_NT 1                // outputs are written exactly once
+#endif
+
+#ifndef RR_COPY_UNROLL
+#define RR_COPY_UNROLL 8             // 16-byte vectors per thread in a copy tile
+#endif
+
+constexpr int kUnroll = RR_UNROLL;
+constexpr int kScalarPerThread = 4;  // elements per thread in a scalar tile
+constexpr int kCopyUnroll = RR_COPY_UNROLL;
+constexpr int kShiftUnroll = 4;      // realigned copies hold two words per vector
+constexpr int kCopyBytesPerThread = 16;
+
+// One reduction segment: out[i] = RND(scale * fold_k in[k][i]) for i < n.
+// vec == 1: every pointer is 16-byte aligned and n is a multiple of the
+// elements in 16 bytes; vec == 0: element-wise path (heads, tails, and
+// segments whose pointers disagree modulo 16 bytes).
+struct RedSeg {
+    const void *in[kMaxIn];
+    void *out;
+    int64_t n;
+    int32_t k;
+    int32_t vec;
+    float scale;
+    int32_t pad;
+};
+
+struct RedBatch {
+    int32_t tile0[kMaxRedSegs];  // first tile of each segment within this launch
+    int32_t nseg;
+    int32_t bf16;                // element type: 1 bf16, 0 fp32
+    RedSeg seg[kMaxRedSegs];
+};
+
+enum CopyMode : int32_t { kCopyBytes = 0, kCopyAligned = 1, kCopyShifted = 2 };
+
+// One copy segment of nbytes.  kCopyAligned: src and dst 16-byte aligned,
+// nbytes a multiple of 16.  kCopyShifted: dst 16-byte aligned, nbytes a
+// multiple of 16, and the source starts `shift` bytes (1..15) past the
+// 16-byte aligned address `src`.  kCopyBytes: anything (heads and tails
+// shorter than 16 bytes).
+struct CopySeg {
+    const unsigned char *src;
+    unsigned char *dst;
+    int64_t nbytes;
+    int32_t mode;
+    int32_t shift;
+};
+
+struct CopyBatch {
+    int32_t tile0[kMaxCopySegs];
+    int32_t nseg;
+    int32_t pad;
+    CopySeg seg[kMaxCopySegs];
+};
+
+// Work per tile (one workgroup), matching the kernels' tiling.
+int64_t red_tile_elems(bool vec, bool bf16);
+int64_t copy_tile_bytes(int32_t mode);
+
+// Enqueue one launch; the batch's tile0/nseg must be filled and the total
+// tile count must not exceed kMaxTilesPerLaunch.  Returns the HIP status.
+hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, hipStream_t stream);
+// A copy batch holds either only kCopyShifted segments (shifted = true) or
+// none of them.
+hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hipStream_t stream);
+
+}  // namespace rr

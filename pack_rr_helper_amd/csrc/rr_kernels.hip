@@ -1,0 +1,346 @@
+// rr_kernels.hip -- gfx950 (MI355X) streaming kernels for the sharded relay
+// hot path: the K-input reduction (helper reduce-at-helper, active add+scale
+// epilogue, the reduce-scatter multi-input passes) and the chunk copy engine
+// (all-to-all strided gather/scatter).
+//
+// Both are HBM-bound element-wise operations (at most 0.4 flop per byte), so
+// the design is about moving bytes: 16-byte global loads per lane, several of
+// them in flight per input before any arithmetic, non-temporal hints on data
+// that is touched exactly once, fp32 accumulation in registers, and one
+// packed bf16 conversion (v_cvt_pk_bf16_f32, round-to-nearest-even) per pair
+// of outputs.  No LDS: nothing is reused, and the copy engine realigns
+// strided sources in registers with v_alignbyte instead of staging them.
+//
+// Tiling: one workgroup of 256 threads processes one tile of one segment; a
+// launch's segment table lives in the kernel arguments and a workgroup finds
+// its segment with a branch-free count over the table's tile offsets.
+#include "rr_internal.h"
+
+namespace rr {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+
+__device__ __forceinline__ u32x4 ld16(const u32x4 *p)
+{
+#if RR_LOAD_NT
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+__device__ __forceinline__ void st16(u32x4 *p, u32x4 v)
+{
+#if RR_STORE_NT
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+// bf16 is the upper half of a binary32: widening is a shift or a mask.
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 values to a packed bf16 pair, round-to-nearest-even, lo in bits 0..15.
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi)
+{
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void *p, int64_t i)
+{
+    if constexpr (BF16)
+        return __uint_as_float((unsigned)static_cast<const unsigned short *>(p)[i] << 16);
+    else
+        return static_cast<const float *>(p)[i];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_elem(void *p, int64_t i, float v)
+{
+    if constexpr (BF16)
+        static_cast<__bf16 *>(p)[i] = (__bf16)v;
+    else
+        static_cast<float *>(p)[i] = v;
+}
+
+// Index of the segment that owns tile t: the number of later segment starts
+// at or before t.  Unrolled over the table so the scalar loads issue together.
+template <int MAXS>
+__device__ __forceinline__ int find_seg(const int32_t (&tile0)[MAXS], int nseg, int32_t t)
+{
+    int s = 0;
+#pragma unroll
+    for (int i = 1; i < MAXS; ++i)
+        s += (i < nseg && t >= tile0[i]) ? 1 : 0;
+    return s;
+}
+
+// ---------------------------------------------------------------------------
+// Reduction
+// ---------------------------------------------------------------------------
+
+// One 16-byte output vector from the K inputs' vectors at the same index.
+template <bool BF16, int K>
+__device__ __forceinline__ u32x4 fold_vec(const u32x4 (&x)[K], float scale)
+{
+    u32x4 r;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        if constexpr (BF16) {
+            float lo = bf16_lo(x[0][w]);
+            float hi = bf16_hi(x[0][w]);
+#pragma unroll
+            for (int k = 1; k < K; ++k) {
+                lo = lo + bf16_lo(x[k][w]);
+                hi = hi + bf16_hi(x[k][w]);
+            }
+            r[w] = pack_bf16x2(lo * scale, hi * scale);
+        } else {
+            float a = __uint_as_float(x[0][w]);
+#pragma unroll
+            for (int k = 1; k < K; ++k)
+                a = a + __uint_as_float(x[k][w]);
+            r[w] = __float_as_uint(a * scale);
+        }
+    }
+    return r;
+}
+
+template <bool BF16, int K>
+__device__ __forceinline__ void reduce_vec(const RedSeg &sg, int64_t lt)
+{
+    constexpr int kVecElems = BF16 ? 8 : 4;
+    constexpr int64_t kTileVecs = int64_t(kBlock) * kUnroll;
+    const int64_t nv = sg.n / kVecElems;
+    const int64_t vbase = lt * kTileVecs + threadIdx.x;
+    const float scale = sg.scale;
+
+    const u32x4 *in[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        in[k] = static_cast<const u32x4 *>(sg.in[k]);
+    u32x4 *out = static_cast<u32x4 *>(sg.out);
+
+    if ((lt + 1) * kTileVecs <= nv) {
+        // Full tile: issue every load before any arithmetic.
+        u32x4 x[kUnroll][K];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                x[u][k] = ld16(in[k] + vbase + u * kBlock);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            st16(out + vbase + u * kBlock, fold_vec<BF16, K>(x[u], scale));
+    } else {
+        // The segment's last, partial tile.
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t v = vbase + (int64_t)u * kBlock;
+            if (v >= nv)
+                break;
+            u32x4 x[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                x[k] = ld16(in[k] + v);
+            st16(out + v, fold_vec<BF16, K>(x, scale));
+        }
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void reduce_scalar(const RedSeg &sg, int64_t lt)
+{
+    const int64_t base = lt * (int64_t)(kBlock * kScalarPerThread) + threadIdx.x;
+    for (int j = 0; j < kScalarPerThread; ++j) {
+        const int64_t i = base + (int64_t)j * kBlock;
+        if (i >= sg.n)
+            return;
+        float acc = load_elem<BF16>(sg.in[0], i);
+        for (int k = 1; k < sg.k; ++k)
+            acc = acc + load_elem<BF16>(sg.in[k], i);
+        store_elem<BF16>(sg.out, i, acc * sg.scale);
+    }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kBlock) void reduce_kernel(RedBatch b)
+{
+    const int32_t t = (int32_t)blockIdx.x;
+    const int s = find_seg(b.tile0, b.nseg, t);
+    const RedSeg &sg = b.seg[s];
+    const int64_t lt = (int64_t)(t - b.tile0[s]);
+    if (sg.vec) {
+        switch (sg.k) {
+        case 1: reduce_vec<BF16, 1>(sg, lt); break;
+        case 2: reduce_vec<BF16, 2>(sg, lt); break;
+        case 3: reduce_vec<BF16, 3>(sg, lt); break;
+        case 4: reduce_vec<BF16, 4>(sg, lt); break;
+        default: break;
+        }
+    } else {
+        reduce_scalar<BF16>(sg, lt);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Copy
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void copy_aligned(const CopySeg &sg, int64_t lt)
+{
+    constexpr int64_t kTileVecs = int64_t(kBlock) * kCopyUnroll;
+    const int64_t nv = sg.nbytes / 16;
+    const int64_t vbase = lt * kTileVecs + threadIdx.x;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(sg.src);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(sg.dst);
+    if ((lt + 1) * kTileVecs <= nv) {
+        u32x4 x[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u)
+            x[u] = ld16(src + vbase + u * kBlock);
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u)
+            st16(dst + vbase + u * kBlock, x[u]);
+    } else {
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const int64_t v = vbase + (int64_t)u * kBlock;
+            if (v >= nv)
+                break;
+            st16(dst + v, ld16(src + v));
+        }
+    }
+}
+
+// Destination aligned, source `shift` bytes past the aligned address sg.src.
+// Output vector v is bytes [16v + shift, 16v + shift + 16) of the aligned
+// source, i.e. dwords Q.. of the pair (word v, word v+1) shifted right by
+// R = shift % 4 bytes, with Q = shift / 4.  The second word of the last
+// vector is the aligned 16-byte block holding the segment's last source
+// bytes, so it never leaves the page those bytes live in.
+template <int Q>
+__device__ __forceinline__ u32x4 realign(u32x4 a, u32x4 b, unsigned r)
+{
+    const unsigned w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = __builtin_amdgcn_alignbyte(w[j + Q + 1], w[j + Q], r);
+    return o;
+}
+
+template <int Q>
+__device__ __forceinline__ void copy_shifted(const CopySeg &sg, int64_t lt)
+{
+    constexpr int64_t kTileVecs = int64_t(kBlock) * kShiftUnroll;
+    const int64_t nv = sg.nbytes / 16;
+    const int64_t vbase = lt * kTileVecs + threadIdx.x;
+    const unsigned r = (unsigned)(sg.shift & 3);
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(sg.src);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(sg.dst);
+    if ((lt + 1) * kTileVecs <= nv) {
+        u32x4 a[kShiftUnroll], b[kShiftUnroll];
+#pragma unroll
+        for (int u = 0; u < kShiftUnroll; ++u) {
+            a[u] = src[vbase + u * kBlock];
+            b[u] = src[vbase + u * kBlock + 1];
+        }
+#pragma unroll
+        for (int u = 0; u < kShiftUnroll; ++u)
+            st16(dst + vbase + u * kBlock, realign<Q>(a[u], b[u], r));
+    } else {
+        for (int u = 0; u < kShiftUnroll; ++u) {
+            const int64_t v = vbase + (int64_t)u * kBlock;
+            if (v >= nv)
+                break;
+            st16(dst + v, realign<Q>(src[v], src[v + 1], r));
+        }
+    }
+}
+
+__device__ __forceinline__ void copy_bytes(const CopySeg &sg, int64_t lt)
+{
+    const int64_t base = lt * (int64_t)(kBlock * kCopyBytesPerThread) + threadIdx.x;
+    for (int j = 0; j < kCopyBytesPerThread; ++j) {
+        const int64_t i = base + (int64_t)j * kBlock;
+        if (i >= sg.nbytes)
+            return;
+        sg.dst[i] = sg.src[i];
+    }
+}
+
+// Aligned bodies and byte heads/tails.
+__global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch b)
+{
+    const int32_t t = (int32_t)blockIdx.x;
+    const int s = find_seg(b.tile0, b.nseg, t);
+    const CopySeg &sg = b.seg[s];
+    const int64_t lt = (int64_t)(t - b.tile0[s]);
+    if (sg.mode == kCopyAligned)
+        copy_aligned(sg, lt);
+    else
+        copy_bytes(sg, lt);
+}
+
+// Realigned bodies (source and destination disagree modulo 16 bytes); a
+// kernel of its own so its register budget does not limit the aligned path.
+__global__ __launch_bounds__(kBlock) void copy_shifted_kernel(CopyBatch b)
+{
+    const int32_t t = (int32_t)blockIdx.x;
+    const int s = find_seg(b.tile0, b.nseg, t);
+    const CopySeg &sg = b.seg[s];
+    const int64_t lt = (int64_t)(t - b.tile0[s]);
+    switch (sg.shift >> 2) {
+    case 0: copy_shifted<0>(sg, lt); break;
+    case 1: copy_shifted<1>(sg, lt); break;
+    case 2: copy_shifted<2>(sg, lt); break;
+    default: copy_shifted<3>(sg, lt); break;
+    }
+}
+
+}  // namespace
+
+int64_t red_tile_elems(bool vec, bool bf16)
+{
+    return vec ? int64_t(kBlock) * kUnroll * (bf16 ? 8 : 4) : int64_t(kBlock) * kScalarPerThread;
+}
+
+int64_t copy_tile_bytes(int32_t mode)
+{
+    if (mode == kCopyBytes)
+        return int64_t(kBlock) * kCopyBytesPerThread;
+    return int64_t(kBlock) * (mode == kCopyShifted ? kShiftUnroll : kCopyUnroll) * 16;
+}
+
+hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, hipStream_t stream)
+{
+    if (total_tiles <= 0)
+        return hipSuccess;
+    (void)hipGetLastError();  // report this launch's status only
+    if (b.bf16)
+        reduce_kernel<true><<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
+    else
+        reduce_kernel<false><<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hipStream_t stream)
+{
+    if (total_tiles <= 0)
+        return hipSuccess;
+    (void)hipGetLastError();  // report this launch's status only
+    if (shifted)
+        copy_shifted_kernel<<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
+    else
+        copy_kernel<<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
+    return hipGetLastError();
+}
+
+}  // namespace rr

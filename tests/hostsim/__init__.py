@@ -1,0 +1,63 @@
+"""TEST INFRASTRUCTURE: build and load libhostsim.so, the product's C-ABI
+layer (pack_rr_helper_amd/csrc/rr_api.cpp) linked with a host-memory replay
+of the kernels' index arithmetic (sim_launch.cpp)."""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+LIB = os.path.join(HERE, "libhostsim.so")
+SOURCES = [os.path.join(HERE, "sim_launch.cpp"),
+           os.path.join(ROOT, "pack_rr_helper_amd", "csrc", "rr_api.cpp")]
+
+
+def build():
+    tmp = LIB + ".tmp"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-D__HIP_PLATFORM_AMD__",
+                    "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
+                    "-I", os.path.join(ROOT, "pack_rr_helper_amd", "csrc"),
+                    "-o", tmp, *SOURCES, "-L/opt/rocm/lib", "-lamdhip64"], check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+class Sim:
+    def __init__(self):
+        if not os.path.exists(LIB) or any(os.path.getmtime(s) > os.path.getmtime(LIB) for s in SOURCES):
+            build()
+        self.L = ctypes.CDLL(LIB)
+        self.L.sim_message.restype = ctypes.c_char_p
+        self.L.sim_register.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
+        self.L.rr_last_error.restype = ctypes.c_char_p
+        self.keep = []
+
+    def reset(self):
+        self.L.sim_reset()
+        self.keep = []
+
+    def buf(self, a, writable=True):
+        """Register a numpy array (its whole byte range) as a buffer."""
+        assert a.flags.c_contiguous
+        self.L.sim_register(ctypes.c_void_p(a.ctypes.data), a.nbytes, int(writable))
+        self.keep.append(a)
+        return a
+
+    def check(self):
+        assert self.L.sim_violations() == 0, self.L.sim_message().decode()
+
+    def call(self, name, *args):
+        st = getattr(self.L, name)(*args)
+        if st != 0:
+            raise RuntimeError(f"{name} -> {st}: {self.L.rr_last_error().decode()}")
+        self.check()
+
+
+def ptr(a, off_elems=0):
+    return ctypes.c_void_p(a.ctypes.data + off_elems * a.itemsize)
+
+
+def parr(*ps):
+    return (ctypes.c_void_p * len(ps))(*[p.value if isinstance(p, ctypes.c_void_p) else p for p in ps])

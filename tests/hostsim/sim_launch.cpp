@@ -1,0 +1,232 @@
+// sim_launch.cpp -- TEST INFRASTRUCTURE: a host-memory stand-in for the two
+// kernel launch functions of rr_kernels.hip, linked with the product's
+// rr_api.cpp into tests/hostsim/libhostsim.so.  It replays, workgroup by
+// workgroup and lane by lane, the tile and index arithmetic the kernels use,
+// checks every access against the buffers the test registered, and performs
+// the access on host memory.  It exercises the C ABI's validation, geometry,
+// segment tables, head/body/tail splits and launch batching on the CPU, so an
+// addressing mistake shows up here as a recorded violation rather than as a
+// fault on the GPU.  It is never part of the product library.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "rr_internal.h"
+
+namespace {
+
+struct Buf {
+    uintptr_t lo, hi;
+    bool writable;
+};
+std::vector<Buf> g_bufs;
+long g_violations = 0;
+char g_msg[256];
+long g_launches = 0;
+
+bool inside(uintptr_t a, int64_t n, bool write)
+{
+    for (const Buf &b : g_bufs)
+        if (a >= b.lo && a + uintptr_t(n) <= b.hi && (!write || b.writable))
+            return true;
+    return false;
+}
+
+// The realigned copy reads whole aligned 16-byte words; one that holds at
+// least one byte of a registered buffer stays inside that buffer's page.
+bool touches(uintptr_t a, int64_t n)
+{
+    for (const Buf &b : g_bufs)
+        if (a < b.hi && b.lo < a + uintptr_t(n))
+            return true;
+    return false;
+}
+
+void violation(const char *what, uintptr_t a, int64_t n)
+{
+    if (g_violations++ == 0)
+        snprintf(g_msg, sizeof g_msg, "%s at %#lx (+%lld)", what, (unsigned long)a, (long long)n);
+}
+
+float ld(const void *p, int64_t i, bool bf16)
+{
+    const uintptr_t a = uintptr_t(p) + uintptr_t(i * (bf16 ? 2 : 4));
+    if (!inside(a, bf16 ? 2 : 4, false)) {
+        violation("read", a, bf16 ? 2 : 4);
+        return 0.0f;
+    }
+    if (bf16) {
+        uint32_t u = uint32_t(*reinterpret_cast<const uint16_t *>(a)) << 16;
+        float f;
+        memcpy(&f, &u, 4);
+        return f;
+    }
+    return *reinterpret_cast<const float *>(a);
+}
+
+void st(void *p, int64_t i, float v, bool bf16)
+{
+    const uintptr_t a = uintptr_t(p) + uintptr_t(i * (bf16 ? 2 : 4));
+    if (!inside(a, bf16 ? 2 : 4, true)) {
+        violation("write", a, bf16 ? 2 : 4);
+        return;
+    }
+    if (bf16) {
+        uint32_t u;
+        memcpy(&u, &v, 4);
+        if ((u & 0x7fffffffu) > 0x7f800000u)
+            u = (u | 0x00400000u);
+        else
+            u += 0x7fffu + ((u >> 16) & 1u);
+        *reinterpret_cast<uint16_t *>(a) = uint16_t(u >> 16);
+    } else {
+        *reinterpret_cast<float *>(a) = v;
+    }
+}
+
+void fold(const rr::RedSeg &s, int64_t i, bool bf16)
+{
+    float acc = ld(s.in[0], i, bf16);
+    for (int k = 1; k < s.k; ++k)
+        acc = acc + ld(s.in[k], i, bf16);
+    st(s.out, i, acc * s.scale, bf16);
+}
+
+void copy_byte(const unsigned char *src, unsigned char *dst, int64_t i)
+{
+    if (!inside(uintptr_t(src + i), 1, false))
+        violation("copy read", uintptr_t(src + i), 1);
+    else if (!inside(uintptr_t(dst + i), 1, true))
+        violation("copy write", uintptr_t(dst + i), 1);
+    else
+        dst[i] = src[i];
+}
+
+template <int MAXS>
+int find_seg(const int32_t (&tile0)[MAXS], int nseg, int32_t t)
+{
+    int s = 0;
+    for (int i = 1; i < MAXS; ++i)
+        s += (i < nseg && t >= tile0[i]) ? 1 : 0;
+    return s;
+}
+
+}  // namespace
+
+namespace rr {
+
+int64_t red_tile_elems(bool vec, bool bf16)
+{
+    return vec ? int64_t(kBlock) * kUnroll * (bf16 ? 8 : 4) : int64_t(kBlock) * kScalarPerThread;
+}
+
+int64_t copy_tile_bytes(int32_t mode)
+{
+    if (mode == kCopyBytes)
+        return int64_t(kBlock) * kCopyBytesPerThread;
+    return int64_t(kBlock) * (mode == kCopyShifted ? kShiftUnroll : kCopyUnroll) * 16;
+}
+
+hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, hipStream_t)
+{
+    ++g_launches;
+    const bool bf16 = b.bf16;
+    const int ve = bf16 ? 8 : 4;
+    for (int64_t t = 0; t < total_tiles; ++t) {
+        const int s = find_seg(b.tile0, b.nseg, int32_t(t));
+        const RedSeg &sg = b.seg[s];
+        const int64_t lt = t - b.tile0[s];
+        if (sg.vec) {
+            for (int k = 0; k < sg.k; ++k)
+                if (uintptr_t(sg.in[k]) % 16)
+                    violation("unaligned vector input", uintptr_t(sg.in[k]), 16);
+            if (uintptr_t(sg.out) % 16 || sg.n % ve)
+                violation("unaligned vector output", uintptr_t(sg.out), sg.n);
+            const int64_t nv = sg.n / ve, tv = int64_t(kBlock) * kUnroll;
+            const bool full = (lt + 1) * tv <= nv;
+            for (int x = 0; x < kBlock; ++x)
+                for (int u = 0; u < kUnroll; ++u) {
+                    const int64_t v = lt * tv + x + int64_t(u) * kBlock;
+                    if (!full && v >= nv)
+                        break;
+                    for (int e = 0; e < ve; ++e)
+                        fold(sg, v * ve + e, bf16);
+                }
+        } else {
+            for (int x = 0; x < kBlock; ++x)
+                for (int j = 0; j < kScalarPerThread; ++j) {
+                    const int64_t i = lt * (int64_t(kBlock) * kScalarPerThread) + x + int64_t(j) * kBlock;
+                    if (i >= sg.n)
+                        break;
+                    fold(sg, i, bf16);
+                }
+        }
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hipStream_t)
+{
+    ++g_launches;
+    for (int64_t t = 0; t < total_tiles; ++t) {
+        const int s = find_seg(b.tile0, b.nseg, int32_t(t));
+        const CopySeg &sg = b.seg[s];
+        const int64_t lt = t - b.tile0[s];
+        if ((sg.mode == kCopyShifted) != shifted)
+            violation("copy mode in the wrong kernel", uintptr_t(sg.dst), sg.mode);
+        if (sg.mode == kCopyBytes) {
+            for (int x = 0; x < kBlock; ++x)
+                for (int j = 0; j < kCopyBytesPerThread; ++j) {
+                    const int64_t i = lt * (int64_t(kBlock) * kCopyBytesPerThread) + x + int64_t(j) * kBlock;
+                    if (i >= sg.nbytes)
+                        break;
+                    copy_byte(sg.src, sg.dst, i);
+                }
+            continue;
+        }
+        const int unroll = sg.mode == kCopyShifted ? kShiftUnroll : kCopyUnroll;
+        const int64_t nv = sg.nbytes / 16, tv = int64_t(kBlock) * unroll;
+        if (uintptr_t(sg.dst) % 16 || uintptr_t(sg.src) % 16 || sg.nbytes % 16)
+            violation("unaligned copy body", uintptr_t(sg.dst), sg.nbytes);
+        const bool full = (lt + 1) * tv <= nv;
+        for (int x = 0; x < kBlock; ++x)
+            for (int u = 0; u < unroll; ++u) {
+                const int64_t v = lt * tv + x + int64_t(u) * kBlock;
+                if (!full && v >= nv)
+                    break;
+                if (sg.mode == kCopyAligned) {
+                    for (int e = 0; e < 16; ++e)
+                        copy_byte(sg.src, sg.dst, v * 16 + e);
+                } else {
+                    // words v and v+1 of the aligned source are loaded whole
+                    if (!touches(uintptr_t(sg.src) + uintptr_t(v * 16), 16) ||
+                        !touches(uintptr_t(sg.src) + uintptr_t((v + 1) * 16), 16))
+                        violation("realigned word outside every buffer", uintptr_t(sg.src) + v * 16, 32);
+                    for (int e = 0; e < 16; ++e)
+                        copy_byte(sg.src + sg.shift, sg.dst, v * 16 + e);
+                }
+            }
+    }
+    return hipSuccess;
+}
+
+}  // namespace rr
+
+extern "C" {
+void sim_reset(void)
+{
+    g_bufs.clear();
+    g_violations = 0;
+    g_launches = 0;
+    g_msg[0] = '\0';
+}
+void sim_register(const void *p, int64_t bytes, int writable)
+{
+    g_bufs.push_back(Buf{uintptr_t(p), uintptr_t(p) + uintptr_t(bytes), writable != 0});
+}
+long sim_violations(void) { return g_violations; }
+long sim_launches(void) { return g_launches; }
+const char *sim_message(void) { return g_msg; }
+}

@@ -1,0 +1,314 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle
+on the same seeded bytes.
+
+Tolerances (written here, checked per element):
+* pack/unpack: bit-exact;
+* fp32 reductions: |gpu - ref| <= 1e-6 * max(|ref|, sum_i |x_i|);
+* bf16 reductions: at most 1 unit in the last place (monotone bit order).
+Both sides add in fp32 in the same order and round once (round-to-nearest-
+even), so the expected outcome is bit-exact; the tests also count and assert
+the exactly-equal elements, so a silent drift shows up.  NaN results compare
+as NaN (their payload is unspecified).
+
+Full-size cases use the workload classes bench.py times (same entry points,
+same arguments).
+"""
+import numpy as np
+import pytest
+import torch
+
+import pack_rr_helper_amd as rr
+from pack_rr_helper_amd import synth
+from pack_rr_helper_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = 0, 1
+SUM, AVG = 0, 1
+AR, RS, A2A = 0, 1, 2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rr.load()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+def dev(a, dt=BF16):
+    return synth.to_device(a, dt)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return synth.to_host(t)
+
+
+def ords(b):
+    b = b.astype(np.int32)
+    return np.where(b & 0x8000, 0x8000 - (b & 0x7FFF) - 1, b + 0x8000)
+
+
+def check_bf16(got, ref, what):
+    assert got.shape == ref.shape, what
+    gnan = ((got & 0x7F80) == 0x7F80) & (got & 0x7F != 0)
+    rnan = ((ref & 0x7F80) == 0x7F80) & (ref & 0x7F != 0)
+    assert np.array_equal(gnan, rnan), f"{what}: NaN positions differ"
+    d = np.abs(ords(got[~gnan]) - ords(ref[~rnan]))
+    assert d.size == 0 or d.max() <= 1, f"{what}: {int(d.max())} ulp at {int(np.argmax(d))}"
+    exact = int(np.sum(d == 0))
+    say(what, f"{exact}/{d.size} bit-exact")
+    assert exact == d.size, f"{what}: {d.size - exact} elements within 1 ulp but not bit-exact"
+
+
+def check_f32(got, ref, inputs, what):
+    absum = sum(np.abs(x.astype(np.float64)) for x in inputs)
+    tol = 1e-6 * np.maximum(np.abs(ref.astype(np.float64)), absum)
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= tol), what
+    exact = int(np.sum(got.view(np.uint32) == ref.view(np.uint32)))
+    say(what, f"{exact}/{got.size} bit-exact")
+    assert exact == got.size
+
+
+# --------------------------------------------------------------------------
+# A=2 allreduce helper, fp32, count 2^20, U[-1,1) seed 0, every k
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("op", [SUM, AVG])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_ar2_helper_fp32_every_k(orc, op, in_place):
+    count, H, nc = 2 ** 20, 6, 8
+    say("ar2 helper fp32", count, op, in_place)
+    xs = [synth.uniform(count, -1, 1, 0, a) for a in range(2)]
+    dx = [dev(x, F32) for x in xs]
+    relay = rr.Relay(2, H, nc, 0, count)
+    c = rr.rr_geometry(relay, AR, F32)["chunk"]
+    assert c == 131072
+    for k in range(H):
+        sl = slice(k * c, (k + 1) * c)
+        slots = [dx[0][sl].clone(), dx[1][sl].clone()]
+        out = slots[0] if in_place else torch.empty(c, dtype=torch.float32, device="cuda")
+        rr.rr_helper_reduce(relay, AR, F32, op, k, slots, out)
+        ref = orc.ar2_helper(F32, op, xs[0][sl].copy(), xs[1][sl].copy())
+        check_f32(host(out), ref, [xs[0][sl], xs[1][sl]], f"k={k}")
+
+
+# --------------------------------------------------------------------------
+# A=2 allreduce group and reduce-scatter, bf16, count 2^25, N(0,1) seed 1
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("count", [2 ** 25, 8 * 128 * 37 + 1001, 1000])
+def test_ar2_group_bf16(orc, count):
+    say("ar2 group bf16", count)
+    xs = [synth.as_bf16_bits(synth.normal(count, 1, a)) for a in range(2)]
+    wl = W.AR2([dev(x) for x in xs], BF16, AVG)
+    wl.run()
+    c = wl.g["chunk"]
+    for k in range(6):
+        if c:
+            ref = orc.ar2_helper(BF16, AVG, xs[0][k * c:(k + 1) * c].copy(), xs[1][k * c:(k + 1) * c].copy())
+            check_bf16(host(wl.red[k])[:c], ref, f"helper k={k}")
+    wl.deliver_returns()
+    o0, o1 = orc.ar2_group(BF16, AVG, 6, 8, count, xs[0], xs[1])
+    check_bf16(host(wl.out[0]), o0, "active 0 output")
+    check_bf16(host(wl.out[1]), o1, "active 1 output")
+
+
+@pytest.mark.parametrize("R,in_place", [(2 ** 24, False), (2 ** 24, True), (8 * 128 * 9 + 77, False)])
+def test_rs2_passthrough_and_owner_bf16(orc, R, in_place):
+    say("rs2 bf16", R, in_place)
+    xs = [synth.as_bf16_bits(synth.normal(2 * R, 1, a)) for a in range(2)]
+    dx = [dev(x) for x in xs]
+    relay = rr.Relay(2, 6, 8, 0, R)
+    g = rr.rr_geometry(relay, RS, BF16)
+    c = g["chunk"]
+    # passthrough: the helpers forward slot 0 (a0's block 1) to a1 and slot 1
+    # (a1's block 0) to a0 unsummed; the direct exchange completes the blocks
+    recv = [torch.empty(R, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    for k in range(6):
+        sl = slice(k * c, (k + 1) * c)
+        slot0, slot1 = dx[0][R:][sl].clone(), dx[1][:R][sl].clone()
+        recv[1][sl].copy_(slot0)
+        recv[0][sl].copy_(slot1)
+    recv[1][6 * c:].copy_(dx[0][R + 6 * c:])
+    recv[0][6 * c:].copy_(dx[1][6 * c:R])
+    assert np.array_equal(host(recv[0]), xs[1][:R]) and np.array_equal(host(recv[1]), xs[0][R:])
+    with pytest.raises(rr.RRError, match="passthrough"):
+        rr.rr_helper_reduce(relay, RS, BF16, AVG, 0, [slot0, slot1], slot0)
+    own = [dx[0][:R].clone(), dx[1][R:].clone()]
+    outs = own if in_place else [torch.empty(R, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    rr.rr_active_add_scale(relay, RS, BF16, AVG, 0, [own[0], recv[0]], outs[0])
+    rr.rr_active_add_scale(relay, RS, BF16, AVG, 1, [recv[1], own[1]], outs[1])
+    p0, p1 = orc.rs2_group(BF16, AVG, 6, 8, R, xs[0], xs[1])
+    check_bf16(host(outs[0]), p0, "owner 0")
+    check_bf16(host(outs[1]), p1, "owner 1")
+    # the timed workload reads the peer block in place of the delivered copy
+    wl = W.RS2(dx, BF16, AVG)
+    wl.run()
+    check_bf16(host(wl.out[0]), p0, "workload owner 0")
+    check_bf16(host(wl.out[1]), p1, "workload owner 1")
+
+
+# --------------------------------------------------------------------------
+# A=4 reduce-scatter, recvCount 2^22, N(0,1) seed 2
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("R", [2 ** 22, 8 * 128 * 11 + 24, 3000])
+@pytest.mark.parametrize("op", [SUM, AVG])
+def test_rs4_two_passes(orc, R, op):
+    say("rs4", R, op)
+    A, H = 4, 4
+    xs = [synth.as_bf16_bits(synth.normal(A * R, 2, s)) for s in range(A)]
+    wl = W.RS4([dev(x) for x in xs], BF16, op)
+    c = wl.g["chunk"]
+    wl.run()
+    for h in range(H):
+        if not c:
+            break
+        scratch = host(wl.scratch[h])
+        ref = orc.rs4_pass1(BF16, A, c, np.ascontiguousarray(scratch[:A * (A - 1) * c]))
+        check_bf16(scratch[A * (A - 1) * c:A * A * c], ref, f"pass1 helper {h}")
+    outs = orc.rs4_group(BF16, op, H, 500, R, xs)
+    for o in range(A):
+        check_bf16(host(wl.out[o]), outs[o], f"pass2 owner {o}")
+
+
+def test_rs4_pass2_in_place(orc):
+    A, H, R = 4, 4, 8 * 128 * 5 + 8
+    say("rs4 in-place", R)
+    blk = [synth.as_bf16_bits(synth.normal(R, 5, s)) for s in range(A)]
+    relay = rr.Relay(A, H, 0, 500, R)
+    c = rr.rr_geometry(relay, RS, BF16)["chunk"]
+    reds = [synth.as_bf16_bits(synth.normal(c, 6, h)) for h in range(H)]
+    db, dr = [dev(b) for b in blk], [dev(r) for r in reds]
+    rr.rr_rs_multi_reduce(relay, BF16, AVG, 2, 1, db + dr, db[1])
+    check_bf16(host(db[1]), orc.rs4_pass2(BF16, AVG, A, H, 500, R, 1, blk, reds), "owner 1 in place")
+
+
+# --------------------------------------------------------------------------
+# A=4 allreduce, count 2^27, U[-2,2) seed 3, 500 permille, 2 MiB floor
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("count", [2 ** 27, 2 ** 20, 2 ** 20 - 8, 2 ** 21 + 4 * 128 + 36])
+def test_ar4_group(orc, count):
+    say("ar4", count)
+    xs = [synth.as_bf16_bits(synth.uniform(count, -2, 2, 3, a)) for a in range(4)]
+    wl = W.AR4([dev(x) for x in xs], BF16, AVG)
+    assert wl.g["pure_direct"] == (count * 2 < 2 * 2 ** 20)
+    wl.run()
+    c = wl.g["chunk"]
+    for h in range(4):
+        if c:
+            ref = orc.ar4_helper(BF16, AVG, [x[h * c:(h + 1) * c].copy() for x in xs])
+            check_bf16(host(wl.red[h])[:c], ref, f"helper {h}")
+    wl.deliver()
+    outs = orc.ar4_group(BF16, AVG, 4, 500, count, xs)
+    for a in range(4):
+        check_bf16(host(wl.out[a]), outs[a], f"active {a}")
+
+
+# --------------------------------------------------------------------------
+# A=4 all-to-all pack/unpack, random bits seed 4, 13.5 MiB .. 1 GiB
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", [1 << 30, int(13.5 * 2 ** 20), 64 * 2 ** 20, 4 * (5 * 128 * 7 + 3) * 2])
+def test_a2a_pack_unpack(orc, M):
+    A, H, nc = 4, 4, 5
+    seg = M // (A * 2)
+    say("a2a", M, seg)
+    src = [synth.bits16(A * seg, 4, s) for s in range(A)]
+    wl = W.A2A([dev(s, None) for s in src], BF16)
+    c = wl.g["chunk"]
+    wl.run()
+    for h in range(H):
+        ref = orc.a2a_pack(2, A, seg, c, h, src)
+        for d in range(A):
+            got = host(wl.packed[h][d])[:(A - 1) * c]
+            assert np.array_equal(got.view(np.uint8), ref[d]), f"pack h={h} d={d}"
+        del ref
+    expect = [np.zeros(A * seg, np.uint16) for _ in range(A)]
+    for h in range(H):
+        orc.a2a_unpack(2, A, seg, c, h, orc.a2a_pack(2, A, seg, c, h, src), expect)
+    for d in range(A):
+        assert np.array_equal(host(wl.out[d]), expect[d]), f"unpack d={d}"
+    say("a2a bit-exact", M)
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+
+def test_misaligned_views_take_the_scalar_and_realigned_paths(orc):
+    say("misaligned")
+    count = 8 * 128 * 20 + 13
+    xs = [synth.as_bf16_bits(synth.normal(count, 7, a)) for a in range(2)]
+    big = [dev(np.concatenate([np.zeros(lead, np.uint16), x, np.zeros(8, np.uint16)]))
+           for lead, x in zip((1, 3), xs)]
+    views = [big[0][1:1 + count], big[1][3:3 + count]]
+    relay = rr.Relay(2, 6, 8, 0, count)
+    out = torch.zeros(count + 5, dtype=torch.bfloat16, device="cuda")[5:]
+    for a in range(2):
+        rr.rr_active_add_scale(relay, AR, BF16, SUM, a, views, out)
+        ref = orc.ar_active(BF16, SUM, 2, 6, 8, 0, count, a, xs, np.zeros(count, np.uint16))
+        g = rr.rr_geometry(relay, AR, BF16)
+        check_bf16(host(out)[g["direct_off"]:], ref[g["direct_off"]:], f"misaligned active {a}")
+    # odd segmentCount: source chunks sit at 2-byte offsets from the packed buffers
+    A, seg = 4, 5 * 128 * 9 + 5
+    src = [synth.bits16(A * seg, 8, s) for s in range(A)]
+    wl = W.A2A([dev(s, None) for s in src], BF16)
+    wl.run()
+    c = wl.g["chunk"]
+    for h in range(4):
+        ref = orc.a2a_pack(2, A, seg, c, h, src)
+        for d in range(A):
+            assert np.array_equal(host(wl.packed[h][d])[:(A - 1) * c].view(np.uint8), ref[d])
+    expect = [np.zeros(A * seg, np.uint16) for _ in range(A)]
+    for h in range(4):
+        orc.a2a_unpack(2, A, seg, c, h, orc.a2a_pack(2, A, seg, c, h, src), expect)
+    for d in range(A):
+        assert np.array_equal(host(wl.out[d]), expect[d])
+
+
+def test_special_values_subnormals_and_infinities(orc):
+    say("special values")
+    n = 8 * 128 * 8
+    rng = np.random.default_rng(9)
+    a = rng.integers(0, 1 << 16, n, dtype=np.uint16)
+    b = rng.integers(0, 1 << 16, n, dtype=np.uint16)
+    a[:512] = rng.integers(0, 0x80, 512)            # positive subnormals
+    b[:512] = rng.integers(0x8000, 0x8080, 512)     # negative subnormals
+    a[512:520] = 0x7F80                             # +inf
+    b[512:520] = 0xFF80                             # -inf -> NaN
+    relay = rr.Relay(2, 6, 8, 0, n)
+    c = rr.rr_geometry(relay, AR, BF16)["chunk"]
+    for op in (SUM, AVG):
+        out = torch.empty(c, dtype=torch.bfloat16, device="cuda")
+        rr.rr_helper_reduce(relay, AR, BF16, op, 0, [dev(a[:c]), dev(b[:c])], out)
+        check_bf16(host(out), orc.ar2_helper(BF16, op, a[:c].copy(), b[:c].copy()), f"special op={op}")
+
+
+def test_empty_and_zero_chunk_calls_are_no_ops(orc):
+    say("empty")
+    x = torch.full((64,), 3.0, dtype=torch.bfloat16, device="cuda")
+    relay = rr.Relay(2, 6, 8, 0, 0)
+    rr.rr_active_add_scale(relay, AR, BF16, SUM, 0, [x, x], x)
+    rr.rr_helper_reduce(rr.Relay(2, 6, 8, 0, 1000), AR, BF16, SUM, 0, [x, x], x)
+    torch.cuda.synchronize()
+    assert torch.all(x == 3.0)
+
+
+def test_partial_overlap_is_rejected_on_device_tensors():
+    say("alias")
+    x = torch.zeros(2 ** 16, dtype=torch.bfloat16, device="cuda")
+    relay = rr.Relay(2, 6, 8, 0, 2 ** 14)
+    c = rr.rr_geometry(relay, AR, BF16)["chunk"]
+    with pytest.raises(rr.RRError, match="RR_EALIAS"):
+        rr.rr_helper_reduce(relay, AR, BF16, SUM, 0, [x[:c], x[c:2 * c]], x[8:8 + c])
+    with pytest.raises(rr.RRError, match="dtype"):   # bf16 tensors passed as fp32 buffers
+        rr.rr_helper_reduce(relay, AR, F32, SUM, 0, [x[:c], x[c:2 * c]], x[:c])

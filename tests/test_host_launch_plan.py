@@ -1,0 +1,165 @@
+"""Host-logic tests: every entry point of the C ABI, driven through
+libhostsim.so on host buffers, must (a) touch only the registered buffers when
+its segment tables are replayed with the kernels' index arithmetic and
+(b) produce the oracle's bytes.  Covers ragged tails, zero chunks, views at
+every 2-byte misalignment (scalar reduction path, realigned copies), in-place
+aliases and segment tables large enough to split a call into several
+launches."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from pack_rr_helper_amd import synth
+from pack_rr_helper_amd import _Relay
+from tests.hostsim import Sim, parr, ptr
+
+AR, RS, A2A = 0, 1, 2
+F32, BF16 = 0, 1
+SUM, AVG = 0, 1
+
+
+@pytest.fixture(scope="module")
+def sim():
+    return Sim()
+
+
+def rel(A, H, nc=0, pm=500, count=0):
+    return ctypes.byref(_Relay(A, H, nc, pm, count))
+
+
+def bits(n, seed, rank):
+    return synth.as_bf16_bits(synth.normal(n, seed, rank))
+
+
+def padded(a, lead):
+    """a copy of a placed `lead` elements into a larger buffer (misaligned view)."""
+    big = np.zeros(a.size + lead + 16, a.dtype)
+    big[lead:lead + a.size] = a
+    return big
+
+
+@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("count", [8 * 128 * 6 + 8, 2 ** 16 + 8 * 37 + 5, 900])
+@pytest.mark.parametrize("lead", [0, 3])
+def test_ar2_helper_and_active(sim, orc, dt, count, lead):
+    sim.reset()
+    A, H, nc = 2, 6, 8
+    g = orc.geometry(A, H, nc, 0, count, AR, dt)
+    c = g["chunk"]
+    xs = [synth.uniform(count, -1, 1, 0, r) for r in range(A)]
+    if dt == BF16:
+        xs = [synth.as_bf16_bits(x) for x in xs]
+    bx = [sim.buf(padded(x, lead), writable=False) for x in xs]
+    for k in range(H):
+        out = sim.buf(np.zeros(max(c, 1) + 8, xs[0].dtype))
+        sim.call("rr_helper_reduce", rel(A, H, nc, 0, count), AR, dt, AVG, k,
+                 parr(ptr(bx[0], lead + k * c), ptr(bx[1], lead + k * c)), 2, ptr(out, 1 if lead else 0), None)
+        if c:
+            ref = orc.ar2_helper(dt, AVG, xs[0][k * c:(k + 1) * c].copy(), xs[1][k * c:(k + 1) * c].copy())
+            o = 1 if lead else 0
+            assert np.array_equal(out[o:o + c], ref)
+    for a in range(A):
+        out = sim.buf(np.full(count + lead + 8, 7, xs[0].dtype))
+        sim.call("rr_active_add_scale", rel(A, H, nc, 0, count), AR, dt, SUM, a,
+                 parr(ptr(bx[0], lead), ptr(bx[1], lead)), 2, ptr(out, lead), None)
+        ref = orc.ar_active(dt, SUM, A, H, nc, 0, count, a, xs, np.full(count, 7, xs[0].dtype))
+        assert np.array_equal(out[lead:lead + count], ref)
+        assert np.all(out[:lead] == 7) and np.all(out[lead + count:] == 7)
+
+
+@pytest.mark.parametrize("R", [8 * 128 * 3 + 40, 100])
+def test_rs2_active_in_place(sim, orc, R):
+    sim.reset()
+    x0, x1 = bits(2 * R, 1, 0), bits(2 * R, 1, 1)
+    own = sim.buf(x0.copy())
+    peer = sim.buf(x1[:R].copy(), writable=False)
+    sim.call("rr_active_add_scale", rel(2, 6, 8, 0, R), RS, BF16, AVG, 0,
+             parr(ptr(own), ptr(peer)), 2, ptr(own), None)
+    assert np.array_equal(own[:R], orc.rs2_active(BF16, AVG, x0[:R].copy(), x1[:R].copy()))
+    assert np.array_equal(own[R:], x0[R:])
+
+
+@pytest.mark.parametrize("count", [2 ** 20 + 4 * 128 + 12, 2 ** 19 + 3])
+def test_ar4_helper_and_active(sim, orc, count):
+    sim.reset()
+    A, H = 4, 4
+    xs = [synth.as_bf16_bits(synth.uniform(count, -2, 2, 3, r)) for r in range(A)]
+    bx = [sim.buf(x.copy(), writable=False) for x in xs]
+    g = orc.geometry(A, H, 0, 500, count, AR, BF16)
+    c = g["chunk"]
+    for h in range(H):
+        out = sim.buf(np.zeros(max(c, 1), np.uint16))
+        sim.call("rr_helper_reduce", rel(A, H, 0, 500, count), AR, BF16, AVG, h,
+                 parr(*[ptr(b, h * c) for b in bx]), 4, ptr(out), None)
+        if c:
+            ref = orc.ar4_helper(BF16, AVG, [x[h * c:(h + 1) * c].copy() for x in xs])
+            assert np.array_equal(out[:c], ref)
+    for a in range(A):
+        out = sim.buf(np.zeros(count, np.uint16))
+        sim.call("rr_active_add_scale", rel(A, H, 0, 500, count), AR, BF16, AVG, a,
+                 parr(*[ptr(b) for b in bx]), 4, ptr(out), None)
+        ref = orc.ar_active(BF16, AVG, A, H, 0, 500, count, a, xs, np.zeros(count, np.uint16))
+        assert np.array_equal(out, ref)
+
+
+@pytest.mark.parametrize("H,R,lead", [(4, 8 * 128 * 4 + 24, 0), (4, 8 * 128 * 2 + 5, 1), (12, 24 * 128 * 2 + 40, 3)])
+def test_rs4_passes(sim, orc, H, R, lead):
+    """H=12 with misaligned views makes pass 2 exceed one segment table."""
+    sim.reset()
+    A = 4
+    g = orc.geometry(A, H, 0, 500, R, RS, BF16)
+    c = g["chunk"]
+    scratch = bits(A * (A - 1) * c, 2, 9)
+    sbuf = sim.buf(padded(scratch, lead), writable=False)
+    red = sim.buf(np.zeros(A * c + lead + 8, np.uint16))
+    sim.call("rr_rs_multi_reduce", rel(A, H, 0, 500, R), BF16, SUM, 1, 0, parr(ptr(sbuf, lead)), 1,
+             ptr(red, lead), None)
+    assert np.array_equal(red[lead:lead + A * c], orc.rs4_pass1(BF16, A, c, scratch))
+    blk = [bits(R, 2, s) for s in range(A)]
+    reds = [bits(c, 3, h) for h in range(H)]
+    # H=12: every view shares one misalignment, so each item splits into a
+    # head, a vector body and a tail (39 segments, more than one table);
+    # otherwise the views disagree modulo 16 bytes and take the scalar path.
+    bl = [lead if (H == 12 or s % 2) else 0 for s in range(A)]
+    ol = lead if H == 12 else 0
+    bb = [sim.buf(padded(b, bl[s]), writable=False) for s, b in enumerate(blk)]
+    rb = [sim.buf(padded(r, lead), writable=False) for r in reds]
+    for o in range(A):
+        out = sim.buf(np.zeros(R + 16, np.uint16))
+        launches0 = sim.L.sim_launches()
+        sim.call("rr_rs_multi_reduce", rel(A, H, 0, 500, R), BF16, AVG, 2, o,
+                 parr(*[ptr(b, bl[s]) for s, b in enumerate(bb)], *[ptr(r, lead) for r in rb]),
+                 A + H, ptr(out, ol), None)
+        assert np.array_equal(out[ol:ol + R], orc.rs4_pass2(BF16, AVG, A, H, 500, R, o, blk, reds))
+        if H == 12 and lead:
+            assert sim.L.sim_launches() - launches0 >= 2
+
+
+@pytest.mark.parametrize("seg,lead", [(5 * 128 * 4 + 8, 0), (5 * 128 * 2 + 3, 0), (5 * 128 * 3, 5), (400, 0)])
+@pytest.mark.parametrize("es", [2, 4])
+def test_a2a_pack_unpack(sim, orc, seg, lead, es):
+    sim.reset()
+    A, H, nc = 4, 4, 5
+    dt = BF16 if es == 2 else F32
+    c = orc.geometry(A, H, nc, 0, seg, A2A, dt)["chunk"]
+    npdt = np.uint16 if es == 2 else np.uint32
+    src = [synth.rng(4, s).integers(0, 2 ** (8 * es), A * seg, dtype=npdt) for s in range(A)]
+    sb = [sim.buf(padded(s, lead), writable=False) for s in src]
+    outs = [sim.buf(np.full(A * seg + 16, 0x5A, npdt)) for _ in range(A)]
+    for h in range(H):
+        dst = [sim.buf(np.zeros(max((A - 1) * c, 1) + 8, npdt)) for _ in range(A)]
+        sim.call("rr_a2a_pack", rel(A, H, nc, 0, seg), dt, h, parr(*[ptr(b, lead) for b in sb]),
+                 parr(*[ptr(d) for d in dst]), None)
+        ref = orc.a2a_pack(es, A, seg, c, h, src)
+        for d in range(A):
+            assert np.array_equal(dst[d][:(A - 1) * c].view(np.uint8), ref[d])
+        recv = [sim.buf(d.copy(), writable=False) for d in dst]
+        sim.call("rr_a2a_unpack", rel(A, H, nc, 0, seg), dt, h, parr(*[ptr(r) for r in recv]),
+                 parr(*[ptr(o, 1) for o in outs]), None)
+    expect = [np.full(A * seg, 0x5A, npdt) for _ in range(A)]
+    for h in range(H):
+        orc.a2a_unpack(es, A, seg, c, h, orc.a2a_pack(es, A, seg, c, h, src), expect)
+    for d in range(A):
+        assert np.array_equal(outs[d][1:1 + A * seg], expect[d])
+        assert outs[d][0] == 0x5A and np.all(outs[d][1 + A * seg:] == 0x5A)
