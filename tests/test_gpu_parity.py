@@ -171,9 +171,13 @@ def test_rs4_two_passes(orc, R, op):
     for h in range(H):
         if not c:
             break
-        scratch = host(wl.scratch[h])
-        ref = orc.rs4_pass1(BF16, A, c, np.ascontiguousarray(scratch[:A * (A - 1) * c]))
-        check_bf16(scratch[A * (A - 1) * c:A * A * c], ref, f"pass1 helper {h}")
+        # the helper scratch as the scatter fills it, built on the host
+        hs = np.concatenate([xs[s][o * R + h * c:o * R + (h + 1) * c]
+                             for o in range(A) for s in range(A) if s != o])
+        ref = orc.rs4_pass1(BF16, A, c, hs)
+        got = host(wl.scratch[h])
+        assert np.array_equal(got[:A * (A - 1) * c], hs), "staging"
+        check_bf16(got[A * (A - 1) * c:A * A * c], ref, f"pass1 helper {h}")
     outs = orc.rs4_group(BF16, op, H, 500, R, xs)
     for o in range(A):
         check_bf16(host(wl.out[o]), outs[o], f"pass2 owner {o}")
