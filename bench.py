@@ -10,6 +10,10 @@ synthetic input at one message size M (per-active-rank input bytes, bf16):
   A=4 reduce-scatter (H=4):           4 helper pass-1 + 4 owner pass-2 launches
   A=4 all-to-all (H=4, numChunks=5):  4 packs + 4 unpacks (segmentCount = M/8)
 
+Each role is one batched call over all of its jobs (rr_*_many: one kernel
+launch per role, 10 launches per step); --unbatched issues one call per job
+(34 launches per step) instead.
+
 Inputs are resident in HBM before timing starts.  ``value`` is the step's
 algorithmic bytes (every input element read once, every output element
 written once) divided by the measured step time, in GB/s (10^9 bytes/s).
@@ -45,6 +49,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--message-mib", type=float, default=64.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--unbatched", action="store_true",
+                   help="one launch per job instead of one batched launch per role")
     p.add_argument("--sweep", action="store_true", help="per-row sweep instead of the step benchmark")
     p.add_argument("--sweep-sizes", default="2,4,8,16,32,64,128,256,512,1024")
     p.add_argument("--sweep-reps", type=int, default=20)
@@ -69,22 +75,22 @@ def host_inputs(M):
     }
 
 
-def build_rows(inp, rows=("ar2", "rs2", "ar4", "rs4", "a2a")):
+def build_rows(inp, rows=("ar2", "rs2", "ar4", "rs4", "a2a"), batched=True):
     import pack_rr_helper_amd as rr
     from pack_rr_helper_amd import synth
     from pack_rr_helper_amd import workloads as W
     dev = lambda arrs, code=rr.BF16: [synth.to_device(a, code) for a in arrs]
     out = {}
     if "ar2" in rows:
-        out["ar2"] = W.AR2(dev(inp["ar2"]), rr.BF16, rr.AVG)
+        out["ar2"] = W.AR2(dev(inp["ar2"]), rr.BF16, rr.AVG, batched=batched)
     if "rs2" in rows:
-        out["rs2"] = W.RS2(dev(inp["rs2"]), rr.BF16, rr.AVG)
+        out["rs2"] = W.RS2(dev(inp["rs2"]), rr.BF16, rr.AVG, batched=batched)
     if "ar4" in rows:
-        out["ar4"] = W.AR4(dev(inp["ar4"]), rr.BF16, rr.AVG)
+        out["ar4"] = W.AR4(dev(inp["ar4"]), rr.BF16, rr.AVG, batched=batched)
     if "rs4" in rows:
-        out["rs4"] = W.RS4(dev(inp["rs4"]), rr.BF16, rr.SUM)
+        out["rs4"] = W.RS4(dev(inp["rs4"]), rr.BF16, rr.SUM, batched=batched)
     if "a2a" in rows:
-        out["a2a"] = W.A2A(dev(inp["a2a"], None), rr.BF16)
+        out["a2a"] = W.A2A(dev(inp["a2a"], None), rr.BF16, batched=batched)
     return out
 
 
@@ -190,7 +196,7 @@ def step_bench(args):
     M = int(args.message_mib * MIB)
     print(f"[bench] generating inputs, M={args.message_mib} MiB", file=sys.stderr, flush=True)
     inp = host_inputs(M)
-    wls = build_rows(inp)
+    wls = build_rows(inp, batched=not args.unbatched)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     calls = [c for wl in wls.values() for c in wl.calls(stream)]
@@ -258,6 +264,7 @@ def step_bench(args):
                          "reduce-scatter + A=4 all-to-all pack/unpack, one GPU"),
             "message_bytes": M,
             "launches_per_step": len(calls),
+            "batched": not args.unbatched,
             "algorithmic_bytes_per_step": step_bytes,
             "rows_gbs": {row: round(b / (ms * 1e-3) / 1e9, 1) for row, (ms, b, n) in per_row.items()},
             "rows_us_per_launch": {row: round(1e3 * ms / n, 2) for row, (ms, b, n) in per_row.items()},

@@ -164,8 +164,8 @@ rr_status rr_helper_reduce(const rr_relay *relay, int coll, int dtype, int op,
  *     which is written.  This fuses the add + scale of the relayed chunks and
  *     the final reduction of the direct chunks (reduce-scatter core commit,
  *     phases 3 and 5) into one pass.  A=4 uses rr_rs_multi_reduce (RR_EINVAL).
- *   Aliasing: out may equal in[activeIdx] exactly (in-place); any other overlap
- *   is RR_EALIAS.
+ *   Aliasing: out's region may equal the same region of one input exactly
+ *   (in-place, normally in[activeIdx]); any other overlap is RR_EALIAS.
  */
 rr_status rr_active_add_scale(const rr_relay *relay, int coll, int dtype, int op,
                               int activeIdx, const void *const *in, int nIn,
@@ -222,6 +222,66 @@ rr_status rr_a2a_pack(const rr_relay *relay, int dtype, int helper,
  */
 rr_status rr_a2a_unpack(const rr_relay *relay, int dtype, int helper,
                         const void *const *recv, void *const *out, void *stream);
+
+/*
+ * Batched forms -- one fused call for all the groups a GPU serves in one
+ * phase (the fused multi-group call of the reduce-scatter distributed-layer
+ * commit: "ONE fused phase-synchronized call across all sparse groups"), with
+ * a per-group geometry: each job carries its own rr_relay, so groups of
+ * different sizes mix freely and a job whose chunk aligns down to zero is a
+ * no-op (zero-chunk direct-fallback commit: every group picks its schedule
+ * independently).
+ *
+ * Each job means exactly what the single-job call with the same fields means.
+ * All jobs are validated before anything is enqueued; an invalid job fails
+ * the whole call with its status and a message naming the job index.  The
+ * jobs of one call run concurrently, typically in a single kernel launch, so
+ * no job may write memory another job of the call reads or writes
+ * (RR_EALIAS); the exact in-place aliases of the single-job calls stay
+ * allowed within a job.  Pointer arrays inside the job structs are host
+ * memory, read during the call only.
+ */
+typedef struct {
+    rr_relay relay;
+    int32_t helper;
+    int32_t nSlots;
+    const void *slots[4];
+    void *out;
+} rr_helper_job;
+
+typedef struct {
+    rr_relay relay;
+    int32_t activeIdx;
+    int32_t nIn;
+    const void *in[4];
+    void *out;
+} rr_active_job;
+
+typedef struct {
+    rr_relay relay;
+    int32_t pass;            /* 1 helper, 2 owner */
+    int32_t idx;
+    int32_t nIn;
+    int32_t reserved;
+    const void *const *in;   /* nIn device pointers (host array) */
+    void *out;
+} rr_rs_job;
+
+typedef struct {
+    rr_relay relay;
+    int32_t helper;
+    int32_t reserved;
+    const void *const *in;   /* pack: src[A]; unpack: recv[A] (host arrays) */
+    void *const *out;        /* pack: dst[A]; unpack: out[A] */
+} rr_a2a_job;
+
+rr_status rr_helper_reduce_many(int coll, int dtype, int op, const rr_helper_job *jobs, int nJobs,
+                                void *stream);
+rr_status rr_active_add_scale_many(int coll, int dtype, int op, const rr_active_job *jobs, int nJobs,
+                                   void *stream);
+rr_status rr_rs_multi_reduce_many(int dtype, int op, const rr_rs_job *jobs, int nJobs, void *stream);
+rr_status rr_a2a_pack_many(int dtype, const rr_a2a_job *jobs, int nJobs, void *stream);
+rr_status rr_a2a_unpack_many(int dtype, const rr_a2a_job *jobs, int nJobs, void *stream);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,12 @@ contiguous, has the buffer dtype and is large enough -- and raises
 ``ValueError`` for a rejected argument and ``RuntimeError`` for a HIP failure
 or a missing library.  There is no CPU fallback.
 
+Every entry point also accepts ``prepare=True``: the checks and the ctypes
+marshalling then run once and a zero-argument callable is returned that only
+re-issues the C call (on the stream chosen at preparation; the tensors are
+kept alive by the callable).  The ``*_many`` forms take lists of per-group jobs
+and enqueue them together, typically as one kernel launch.
+
 Pointer/layout semantics of each call are documented in include/rr.h.
 """
 import ctypes
@@ -22,7 +28,8 @@ __all__ = [
     "Relay", "RRError", "F32", "BF16", "SUM", "AVG", "ALLREDUCE", "REDUCE_SCATTER", "ALLTOALL",
     "library_path", "load", "rr_abi_version", "rr_geometry", "rr_passthrough_helper_size",
     "rr_helper_reduce", "rr_active_add_scale", "rr_rs_multi_reduce", "rr_a2a_pack",
-    "rr_a2a_unpack",
+    "rr_a2a_unpack", "rr_helper_reduce_many", "rr_active_add_scale_many",
+    "rr_rs_multi_reduce_many", "rr_a2a_pack_many", "rr_a2a_unpack_many",
 ]
 
 F32, BF16 = 0, 1
@@ -68,6 +75,27 @@ class Relay:
         return _Relay(self.A, self.H, self.numChunks, self.permille, self.count)
 
 
+class _HelperJob(ctypes.Structure):
+    _fields_ = [("relay", _Relay), ("helper", ctypes.c_int32), ("nSlots", ctypes.c_int32),
+                ("slots", ctypes.c_void_p * 4), ("out", ctypes.c_void_p)]
+
+
+class _ActiveJob(ctypes.Structure):
+    _fields_ = [("relay", _Relay), ("activeIdx", ctypes.c_int32), ("nIn", ctypes.c_int32),
+                ("inp", ctypes.c_void_p * 4), ("out", ctypes.c_void_p)]
+
+
+class _RsJob(ctypes.Structure):
+    _fields_ = [("relay", _Relay), ("pass_", ctypes.c_int32), ("idx", ctypes.c_int32),
+                ("nIn", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("inp", ctypes.POINTER(ctypes.c_void_p)), ("out", ctypes.c_void_p)]
+
+
+class _A2AJob(ctypes.Structure):
+    _fields_ = [("relay", _Relay), ("helper", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("inp", ctypes.POINTER(ctypes.c_void_p)), ("out", ctypes.POINTER(ctypes.c_void_p))]
+
+
 _lib = None
 
 
@@ -94,6 +122,11 @@ def load():
         ("rr_rs_multi_reduce", ci, [rp, ci, ci, ci, ci, pp, ci, vp, vp]),
         ("rr_a2a_pack", ci, [rp, ci, ci, pp, pp, vp]),
         ("rr_a2a_unpack", ci, [rp, ci, ci, pp, pp, vp]),
+        ("rr_helper_reduce_many", ci, [ci, ci, ci, ctypes.POINTER(_HelperJob), ci, vp]),
+        ("rr_active_add_scale_many", ci, [ci, ci, ci, ctypes.POINTER(_ActiveJob), ci, vp]),
+        ("rr_rs_multi_reduce_many", ci, [ci, ci, ctypes.POINTER(_RsJob), ci, vp]),
+        ("rr_a2a_pack_many", ci, [ci, ctypes.POINTER(_A2AJob), ci, vp]),
+        ("rr_a2a_unpack_many", ci, [ci, ctypes.POINTER(_A2AJob), ci, vp]),
     ]:
         f = getattr(L, name)
         f.restype, f.argtypes = res, args
@@ -183,38 +216,58 @@ def rr_passthrough_helper_size(count_g, A, num_chunks):
     return v
 
 
-def rr_helper_reduce(relay, coll, dtype, op, helper, slots, out, stream=None):
-    g = rr_geometry(relay, coll, dtype) if coll == ALLREDUCE else {"chunk": 0}
-    n = g["chunk"]
+def _issue(fn, args, keep, prepare):
+    """Call the C entry point now, or return a callable that re-issues it."""
+    if not prepare:
+        _raise(fn(*args))
+        return None
+
+    def call():
+        _raise(fn(*args))
+    call.keep = keep
+    return call
+
+
+def _helper_need(relay, coll, dtype):
+    return rr_geometry(relay, coll, dtype)["chunk"] if coll == ALLREDUCE else 0
+
+
+def rr_helper_reduce(relay, coll, dtype, op, helper, slots, out, stream=None, prepare=False):
+    n = _helper_need(relay, coll, dtype)
     arr, k = _ptrs(slots, "slots", dtype, n)
     o = _dev(out, "out", dtype, n)
     r = relay._c()
-    _raise(load().rr_helper_reduce(ctypes.byref(r), coll, dtype, op, helper, arr, k,
-                                   ctypes.c_void_p(o), _stream(stream)))
+    return _issue(load().rr_helper_reduce,
+                  (ctypes.byref(r), coll, dtype, op, helper, arr, k, ctypes.c_void_p(o), _stream(stream)),
+                  (r, arr, slots, out), prepare)
 
 
-def rr_active_add_scale(relay, coll, dtype, op, active_idx, inputs, out, stream=None):
+def rr_active_add_scale(relay, coll, dtype, op, active_idx, inputs, out, stream=None, prepare=False):
     arr, k = _ptrs(inputs, "in", dtype, relay.count)
     o = _dev(out, "out", dtype, relay.count)
     r = relay._c()
-    _raise(load().rr_active_add_scale(ctypes.byref(r), coll, dtype, op, active_idx, arr, k,
-                                      ctypes.c_void_p(o), _stream(stream)))
+    return _issue(load().rr_active_add_scale,
+                  (ctypes.byref(r), coll, dtype, op, active_idx, arr, k, ctypes.c_void_p(o), _stream(stream)),
+                  (r, arr, inputs, out), prepare)
 
 
-def rr_rs_multi_reduce(relay, dtype, op, pass_, idx, inputs, out, stream=None):
+def _rs_need(relay, dtype, pass_, n_inputs):
     g = rr_geometry(relay, REDUCE_SCATTER, dtype)
-    A, H, c, R = relay.A, relay.H, g["chunk"], relay.count
-    inputs = list(inputs) if not isinstance(inputs, torch.Tensor) else [inputs]
+    A, c, R = relay.A, g["chunk"], relay.count
     if pass_ == 1:
-        need, out_need = [A * (A - 1) * c] * len(inputs), A * c
-    else:
-        need = [R if i < A else c for i in range(len(inputs))]
-        out_need = R
+        return [A * (A - 1) * c] * n_inputs, A * c
+    return [R if i < A else c for i in range(n_inputs)], R
+
+
+def rr_rs_multi_reduce(relay, dtype, op, pass_, idx, inputs, out, stream=None, prepare=False):
+    inputs = list(inputs) if not isinstance(inputs, torch.Tensor) else [inputs]
+    need, out_need = _rs_need(relay, dtype, pass_, len(inputs))
     arr, k = _ptrs(inputs, "in", dtype, need)
     o = _dev(out, "out", dtype, out_need)
     r = relay._c()
-    _raise(load().rr_rs_multi_reduce(ctypes.byref(r), dtype, op, pass_, idx, arr, k,
-                                     ctypes.c_void_p(o), _stream(stream)))
+    return _issue(load().rr_rs_multi_reduce,
+                  (ctypes.byref(r), dtype, op, pass_, idx, arr, k, ctypes.c_void_p(o), _stream(stream)),
+                  (r, arr, inputs, out), prepare)
 
 
 def _a2a_sizes(relay, dtype):
@@ -222,21 +275,94 @@ def _a2a_sizes(relay, dtype):
     return relay.A * relay.count, (relay.A - 1) * g["chunk"]
 
 
-def rr_a2a_pack(relay, dtype, helper, src, dst, stream=None):
+def _a2a_arrays(relay, dtype, ins, outs, unpack):
     full, packed = _a2a_sizes(relay, dtype)
-    if len(src) != relay.A or len(dst) != relay.A:
-        raise RRError(RR_EINVAL, f"pack takes A={relay.A} sources and A destinations")
-    s, _ = _ptrs(src, "src", dtype, full, bits=True)
-    d, _ = _ptrs(dst, "dst", dtype, packed, bits=True)
-    r = relay._c()
-    _raise(load().rr_a2a_pack(ctypes.byref(r), dtype, helper, s, d, _stream(stream)))
+    if len(ins) != relay.A or len(outs) != relay.A:
+        raise RRError(RR_EINVAL, f"all-to-all takes A={relay.A} input and A output buffers")
+    names = ("recv", "out") if unpack else ("src", "dst")
+    a, _ = _ptrs(ins, names[0], dtype, packed if unpack else full, bits=True)
+    b, _ = _ptrs(outs, names[1], dtype, full if unpack else packed, bits=True)
+    return a, b
 
 
-def rr_a2a_unpack(relay, dtype, helper, recv, out, stream=None):
-    full, packed = _a2a_sizes(relay, dtype)
-    if len(recv) != relay.A or len(out) != relay.A:
-        raise RRError(RR_EINVAL, f"unpack takes A={relay.A} receive buffers and A outputs")
-    s, _ = _ptrs(recv, "recv", dtype, packed, bits=True)
-    d, _ = _ptrs(out, "out", dtype, full, bits=True)
+def rr_a2a_pack(relay, dtype, helper, src, dst, stream=None, prepare=False):
+    s, d = _a2a_arrays(relay, dtype, src, dst, False)
     r = relay._c()
-    _raise(load().rr_a2a_unpack(ctypes.byref(r), dtype, helper, s, d, _stream(stream)))
+    return _issue(load().rr_a2a_pack, (ctypes.byref(r), dtype, helper, s, d, _stream(stream)),
+                  (r, s, d, src, dst), prepare)
+
+
+def rr_a2a_unpack(relay, dtype, helper, recv, out, stream=None, prepare=False):
+    s, d = _a2a_arrays(relay, dtype, recv, out, True)
+    r = relay._c()
+    return _issue(load().rr_a2a_unpack, (ctypes.byref(r), dtype, helper, s, d, _stream(stream)),
+                  (r, s, d, recv, out), prepare)
+
+
+# --------------------------------------------------------------------------
+# batched forms: jobs are tuples in the single-job argument order
+# --------------------------------------------------------------------------
+
+def rr_helper_reduce_many(coll, dtype, op, jobs, stream=None, prepare=False):
+    """jobs: [(relay, helper, slots, out), ...]"""
+    arr = (_HelperJob * max(len(jobs), 1))()
+    for j, (relay, helper, slots, out) in enumerate(jobs):
+        n = _helper_need(relay, coll, dtype)
+        p, k = _ptrs(slots, f"job {j} slots", dtype, n)
+        arr[j].relay, arr[j].helper, arr[j].nSlots = relay._c(), helper, k
+        for i in range(min(k, 4)):
+            arr[j].slots[i] = p[i]
+        arr[j].out = _dev(out, f"job {j} out", dtype, n)
+    return _issue(load().rr_helper_reduce_many, (coll, dtype, op, arr, len(jobs), _stream(stream)),
+                  (arr, jobs), prepare)
+
+
+def rr_active_add_scale_many(coll, dtype, op, jobs, stream=None, prepare=False):
+    """jobs: [(relay, active_idx, inputs, out), ...]"""
+    arr = (_ActiveJob * max(len(jobs), 1))()
+    for j, (relay, idx, inputs, out) in enumerate(jobs):
+        p, k = _ptrs(inputs, f"job {j} in", dtype, relay.count)
+        arr[j].relay, arr[j].activeIdx, arr[j].nIn = relay._c(), idx, k
+        for i in range(min(k, 4)):
+            arr[j].inp[i] = p[i]
+        arr[j].out = _dev(out, f"job {j} out", dtype, relay.count)
+    return _issue(load().rr_active_add_scale_many, (coll, dtype, op, arr, len(jobs), _stream(stream)),
+                  (arr, jobs), prepare)
+
+
+def rr_rs_multi_reduce_many(dtype, op, jobs, stream=None, prepare=False):
+    """jobs: [(relay, pass_, idx, inputs, out), ...]"""
+    arr = (_RsJob * max(len(jobs), 1))()
+    keep = [arr, jobs]
+    for j, (relay, pass_, idx, inputs, out) in enumerate(jobs):
+        inputs = list(inputs)
+        need, out_need = _rs_need(relay, dtype, pass_, len(inputs))
+        p, k = _ptrs(inputs, f"job {j} in", dtype, need)
+        keep.append(p)
+        arr[j].relay, arr[j].pass_, arr[j].idx, arr[j].nIn = relay._c(), pass_, idx, k
+        arr[j].inp = ctypes.cast(p, ctypes.POINTER(ctypes.c_void_p))
+        arr[j].out = _dev(out, f"job {j} out", dtype, out_need)
+    return _issue(load().rr_rs_multi_reduce_many, (dtype, op, arr, len(jobs), _stream(stream)),
+                  keep, prepare)
+
+
+def _a2a_many(fn, dtype, jobs, unpack, stream, prepare):
+    arr = (_A2AJob * max(len(jobs), 1))()
+    keep = [arr, jobs]
+    for j, (relay, helper, ins, outs) in enumerate(jobs):
+        a, b = _a2a_arrays(relay, dtype, list(ins), list(outs), unpack)
+        keep += [a, b]
+        arr[j].relay, arr[j].helper = relay._c(), helper
+        arr[j].inp = ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
+        arr[j].out = ctypes.cast(b, ctypes.POINTER(ctypes.c_void_p))
+    return _issue(fn, (dtype, arr, len(jobs), _stream(stream)), keep, prepare)
+
+
+def rr_a2a_pack_many(dtype, jobs, stream=None, prepare=False):
+    """jobs: [(relay, helper, src, dst), ...]"""
+    return _a2a_many(load().rr_a2a_pack_many, dtype, jobs, False, stream, prepare)
+
+
+def rr_a2a_unpack_many(dtype, jobs, stream=None, prepare=False):
+    """jobs: [(relay, helper, recv, out), ...]"""
+    return _a2a_many(load().rr_a2a_unpack_many, dtype, jobs, True, stream, prepare)

@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "rr_internal.h"
 
@@ -146,7 +147,7 @@ rr_status check_ptr(const void *p, int64_t es, const char *what, int idx)
 }
 
 // ---------------------------------------------------------------------------
-// Reduction segments
+// Reduction items: one element-wise K-input sum with its own scale
 // ---------------------------------------------------------------------------
 
 struct RedItem {
@@ -154,17 +155,20 @@ struct RedItem {
     int k;
     void *out;
     int64_t n;
+    float scale;
 };
 
 // An element-wise output is safe when its range equals an input's range
 // exactly (each lane reads its inputs before writing the same elements) or is
 // disjoint from it; everything else is a forbidden alias.  Outputs must also
-// be disjoint from every other item's inputs and outputs.
-rr_status check_items(const RedItem *items, int nitems, int64_t es)
+// be disjoint from every other item's inputs and outputs, since all items of
+// one call run concurrently.
+rr_status check_items(const std::vector<RedItem> &items, int64_t es)
 {
-    for (int i = 0; i < nitems; ++i) {
+    const int n = int(items.size());
+    for (int i = 0; i < n; ++i) {
         const Range o = range_of(items[i].out, 0, items[i].n, es);
-        for (int j = 0; j < nitems; ++j) {
+        for (int j = 0; j < n; ++j) {
             for (int k = 0; k < items[j].k; ++k) {
                 const Range x = range_of(items[j].in[k], 0, items[j].n, es);
                 if (!overlap(o, x))
@@ -172,7 +176,7 @@ rr_status check_items(const RedItem *items, int nitems, int64_t es)
                 if (i == j && same(o, x))
                     continue;
                 return fail(RR_EALIAS,
-                            "output range overlaps an input range other than an exact in-place alias");
+                            "an output range overlaps an input range other than an exact in-place alias");
             }
             if (j != i && overlap(o, range_of(items[j].out, 0, items[j].n, es)))
                 return fail(RR_EALIAS, "two output ranges overlap");
@@ -189,10 +193,10 @@ public:
         b_.bf16 = bf16;
     }
 
-    // Splits one element-wise item into an unaligned head, a 16-byte
-    // vector body and a tail when every pointer agrees modulo 16 bytes;
-    // otherwise the whole item takes the element-wise path.
-    void add(const RedItem &it, float scale, int64_t es)
+    // Splits one item into an unaligned head, a 16-byte vector body and a
+    // tail when every pointer agrees modulo 16 bytes; otherwise the whole
+    // item takes the element-wise path.
+    void add(const RedItem &it, int64_t es)
     {
         if (it.n <= 0)
             return;
@@ -201,15 +205,15 @@ public:
         for (int k = 0; k < it.k; ++k)
             agree = agree && (addr(it.in[k]) % 16 == m);
         if (!agree) {
-            piece(it, 0, it.n, false, scale, es);
+            piece(it, 0, it.n, false, es);
             return;
         }
         const int64_t ve = 16 / es;
         const int64_t head = std::min<int64_t>(it.n, int64_t((16 - m) % 16) / es);
         const int64_t body = ((it.n - head) / ve) * ve;
-        piece(it, 0, head, false, scale, es);
-        piece(it, head, body, true, scale, es);
-        piece(it, head + body, it.n - head - body, false, scale, es);
+        piece(it, 0, head, false, es);
+        piece(it, head, body, true, es);
+        piece(it, head + body, it.n - head - body, false, es);
     }
 
     hipError_t finish()
@@ -219,7 +223,7 @@ public:
     }
 
 private:
-    void piece(const RedItem &it, int64_t off, int64_t n, bool vec, float scale, int64_t es)
+    void piece(const RedItem &it, int64_t off, int64_t n, bool vec, int64_t es)
     {
         while (n > 0) {
             rr::RedSeg s{};
@@ -228,7 +232,7 @@ private:
             s.out = static_cast<char *>(it.out) + off * es;
             s.k = it.k;
             s.vec = vec;
-            s.scale = scale;
+            s.scale = it.scale;
             s.n = n;
             if (b_.nseg == rr::kMaxRedSegs || tiles_ >= rr::kMaxTilesPerLaunch)
                 flush();
@@ -263,15 +267,15 @@ private:
     hipError_t err_ = hipSuccess;
 };
 
-rr_status run_reduce(const RedItem *items, int nitems, int dtype, float scale, void *stream)
+rr_status run_reduce(const std::vector<RedItem> &items, int dtype, void *stream)
 {
     const int64_t es = elem_size(dtype);
-    rr_status st = check_items(items, nitems, es);
+    rr_status st = check_items(items, es);
     if (st != RR_OK)
         return st;
     RedLauncher L(dtype == RR_BF16, static_cast<hipStream_t>(stream));
-    for (int i = 0; i < nitems; ++i)
-        L.add(items[i], scale, es);
+    for (const RedItem &it : items)
+        L.add(it, es);
     const hipError_t e = L.finish();
     if (e != hipSuccess)
         return fail(RR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -303,8 +307,195 @@ rr_status check_array(const void *const *arr, int n, int64_t es, const char *wha
 }
 
 // ---------------------------------------------------------------------------
-// Copy segments (all-to-all pack / unpack)
+// Per-job collectors: validate one job and append its reduction items
 // ---------------------------------------------------------------------------
+
+rr_status collect_helper(const rr_relay *relay, int coll, int dtype, int op, int helper,
+                         const void *const *slots, int nSlots, void *out, std::vector<RedItem> &items)
+{
+    rr_geom g;
+    rr_status st = check_common(relay, coll, dtype, op, &g);
+    if (st != RR_OK)
+        return st;
+    if (coll == RR_REDUCE_SCATTER)
+        return fail(RR_EINVAL,
+                    relay->A == 2
+                        ? "A=2 reduce-scatter helpers are passthrough: slot 0 and slot 1 feed "
+                          "different outputs and are not summable"
+                        : "the A=4 reduce-scatter helper reduces with rr_rs_multi_reduce pass 1");
+    if (coll == RR_ALLTOALL)
+        return fail(RR_EINVAL, "all-to-all performs no reduction");
+    const int A = relay->A;
+    if (nSlots != A)
+        return fail(RR_EINVAL, "nSlots=%d: the allreduce helper sums exactly A=%d slots", nSlots, A);
+    if (helper < 0 || helper >= relay->H)
+        return fail(RR_EINVAL, "helper=%d outside [0, H=%d)", helper, relay->H);
+    if (g.chunk == 0)
+        return RR_OK;  // pure direct: the helper has nothing to reduce
+    const int64_t es = elem_size(dtype);
+    if ((st = check_array(slots, nSlots, es, "slots")) != RR_OK)
+        return st;
+    if ((st = check_ptr(out, es, "out", 0)) != RR_OK)
+        return st;
+    RedItem it{};
+    for (int a = 0; a < A; ++a)
+        it.in[a] = slots[a];
+    it.k = A;
+    it.out = out;
+    it.n = g.chunk;
+    it.scale = op_scale(op, A);
+    items.push_back(it);
+    return RR_OK;
+}
+
+rr_status collect_active(const rr_relay *relay, int coll, int dtype, int op, int activeIdx,
+                         const void *const *in, int nIn, void *out, std::vector<RedItem> &items)
+{
+    rr_geom g;
+    rr_status st = check_common(relay, coll, dtype, op, &g);
+    if (st != RR_OK)
+        return st;
+    const int A = relay->A;
+    if (coll == RR_ALLTOALL)
+        return fail(RR_EINVAL, "all-to-all performs no reduction");
+    if (coll == RR_REDUCE_SCATTER && A != 2)
+        return fail(RR_EINVAL, "the A=4 reduce-scatter owner reduces with rr_rs_multi_reduce pass 2");
+    if (nIn != A)
+        return fail(RR_EINVAL, "nIn=%d: the active epilogue sums one input per active (A=%d)", nIn, A);
+    if (activeIdx < 0 || activeIdx >= A)
+        return fail(RR_EINVAL, "activeIdx=%d outside [0, A=%d)", activeIdx, A);
+    const int64_t es = elem_size(dtype);
+    if ((st = check_array(in, nIn, es, "in")) != RR_OK)
+        return st;
+    if ((st = check_ptr(out, es, "out", 0)) != RR_OK)
+        return st;
+
+    int64_t lo = 0, n = relay->count;  // reduce-scatter: the whole block
+    if (coll == RR_ALLREDUCE) {
+        lo = g.direct_off;
+        n = g.direct_len;
+        if (A > 2) {
+            lo = g.direct_off + int64_t(activeIdx) * g.dslice;
+            n = activeIdx == A - 1 ? g.direct_off + g.direct_len - lo : g.dslice;
+        }
+    }
+    if (n == 0)
+        return RR_OK;
+    RedItem it{};
+    for (int s = 0; s < A; ++s)
+        it.in[s] = static_cast<const char *>(in[s]) + lo * es;
+    it.k = A;
+    it.out = static_cast<char *>(out) + lo * es;
+    it.n = n;
+    it.scale = op_scale(op, A);
+    items.push_back(it);
+    return RR_OK;
+}
+
+rr_status collect_rs(const rr_relay *relay, int dtype, int op, int pass, int idx,
+                     const void *const *in, int nIn, void *out, std::vector<RedItem> &items)
+{
+    rr_geom g;
+    rr_status st = check_common(relay, RR_REDUCE_SCATTER, dtype, op, &g);
+    if (st != RR_OK)
+        return st;
+    const int A = relay->A, H = relay->H;
+    if (A != 4)
+        return fail(RR_EINVAL,
+                    "the two multi-input passes belong to the A=4 reduce-scatter; A=2 helpers "
+                    "are passthrough and the owner uses rr_active_add_scale");
+    const int64_t es = elem_size(dtype);
+    const int64_t c = g.chunk;
+    if (pass == 1) {
+        if (idx < 0 || idx >= H)
+            return fail(RR_EINVAL, "pass 1: helper idx=%d outside [0, H=%d)", idx, H);
+        if (nIn != 1)
+            return fail(RR_EINVAL, "pass 1 takes the helper scratch as its single input (nIn=%d)", nIn);
+        if (c == 0)
+            return RR_OK;
+        if ((st = check_array(in, 1, es, "in")) != RR_OK)
+            return st;
+        if ((st = check_ptr(out, es, "out", 0)) != RR_OK)
+            return st;
+        if (overlap(range_of(out, 0, A * c, es), range_of(in[0], 0, int64_t(A) * (A - 1) * c, es)))
+            return fail(RR_EALIAS, "pass 1 output overlaps the A*(A-1) input chunks of the scratch");
+        for (int o = 0; o < A; ++o) {
+            RedItem it{};
+            for (int j = 0; j < A - 1; ++j)
+                it.in[j] = static_cast<const char *>(in[0]) + (int64_t(o) * (A - 1) + j) * c * es;
+            it.k = A - 1;
+            it.out = static_cast<char *>(out) + int64_t(o) * c * es;
+            it.n = c;
+            it.scale = 1.0f;  // a partial sum: the owner applies the op scale once
+            items.push_back(it);
+        }
+        return RR_OK;
+    }
+    if (pass != 2)
+        return fail(RR_EINVAL, "pass=%d: the reduction has two passes (1 helper, 2 owner)", pass);
+    if (idx < 0 || idx >= A)
+        return fail(RR_EINVAL, "pass 2: owner idx=%d outside [0, A=%d)", idx, A);
+    if (nIn != A + H)
+        return fail(RR_EINVAL, "pass 2 takes A blocks and H reduced chunks (nIn=%d, expected %d)",
+                    nIn, A + H);
+    if ((st = check_array(in, A, es, "in")) != RR_OK)
+        return st;
+    if (c > 0 && (st = check_array(in + A, H, es, "in[A+h]")) != RR_OK)
+        return st;
+    if ((st = check_ptr(out, es, "out", 0)) != RR_OK)
+        return st;
+    for (int h = 0; h < H && c > 0; ++h) {
+        RedItem it{};
+        it.in[0] = static_cast<const char *>(in[idx]) + int64_t(h) * c * es;
+        it.in[1] = in[A + h];
+        it.k = 2;
+        it.out = static_cast<char *>(out) + int64_t(h) * c * es;
+        it.n = c;
+        it.scale = op_scale(op, A);
+        items.push_back(it);
+    }
+    if (g.direct_len > 0) {
+        RedItem it{};
+        for (int s = 0; s < A; ++s)
+            it.in[s] = static_cast<const char *>(in[s]) + g.direct_off * es;
+        it.k = A;
+        it.out = static_cast<char *>(out) + g.direct_off * es;
+        it.n = g.direct_len;
+        it.scale = op_scale(op, A);
+        items.push_back(it);
+    }
+    return RR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Copy moves (all-to-all pack / unpack)
+// ---------------------------------------------------------------------------
+
+struct Move {
+    const void *src;
+    void *dst;
+    int64_t nbytes;
+};
+
+// Every destination range is written by one move only and is read by none.
+rr_status check_moves(const std::vector<Move> &mv)
+{
+    const size_t n = mv.size();
+    for (size_t i = 0; i < n; ++i) {
+        const Range d{addr(mv[i].dst), addr(mv[i].dst) + uintptr_t(mv[i].nbytes)};
+        for (size_t j = 0; j < n; ++j) {
+            const Range s{addr(mv[j].src), addr(mv[j].src) + uintptr_t(mv[j].nbytes)};
+            if (overlap(d, s))
+                return fail(RR_EALIAS, "a destination chunk overlaps a source chunk");
+            if (j != i) {
+                const Range d2{addr(mv[j].dst), addr(mv[j].dst) + uintptr_t(mv[j].nbytes)};
+                if (overlap(d, d2))
+                    return fail(RR_EALIAS, "two destination chunks overlap");
+            }
+        }
+    }
+    return RR_OK;
+}
 
 class CopyLauncher {
 public:
@@ -393,35 +584,83 @@ private:
     hipError_t err_ = hipSuccess;
 };
 
-// All-to-all chunk moves of helper slice h: for destination d and the j-th
-// source s_j != d, (source segment d of s_j at slice h) <-> (chunk j of the
-// per-destination buffer of d).
-struct A2AMove {
-    int d, s, j;
-};
-
-int a2a_moves(int A, A2AMove *mv)
+rr_status run_copy(const std::vector<Move> &mv, void *stream)
 {
-    int n = 0;
+    rr_status st = check_moves(mv);
+    if (st != RR_OK)
+        return st;
+    CopyLauncher L(static_cast<hipStream_t>(stream));
+    for (const Move &m : mv)
+        L.add(m.src, m.dst, m.nbytes);
+    const hipError_t e = L.finish();
+    if (e != hipSuccess)
+        return fail(RR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+// Validates one pack (unpack == false) or unpack job of helper slice `helper`
+// and appends its A*(A-1) chunk moves: for destination d and the j-th source
+// s_j != d, (segment d of source s_j at slice helper) <-> (chunk j of the
+// per-destination buffer of d).  `ins` are the job's read buffers (sources or
+// per-destination receive buffers), `outs` its written buffers.
+rr_status collect_a2a(const rr_relay *relay, int dtype, int helper, const void *const *ins,
+                      void *const *outs, bool unpack, std::vector<Move> &mv)
+{
+    rr_geom g;
+    rr_status st = compute_geometry(relay, RR_ALLTOALL, dtype, &g);
+    if (st != RR_OK)
+        return st;
+    if (helper < 0 || helper >= relay->H)
+        return fail(RR_EINVAL, "helper=%d outside [0, H=%d)", helper, relay->H);
+    if (g.chunk == 0)
+        return RR_OK;
+    const int A = relay->A;
+    const int64_t es = elem_size(dtype), seg = relay->count, c = g.chunk;
+    const int64_t full = int64_t(A) * seg, packed = int64_t(A - 1) * c;
+    const char *in_name = unpack ? "recv" : "src";
+    const char *out_name = unpack ? "out" : "dst";
+    if ((st = check_array(ins, A, es, in_name)) != RR_OK)
+        return st;
+    if ((st = check_array(const_cast<const void *const *>(outs), A, es, out_name)) != RR_OK)
+        return st;
+    const int64_t in_len = unpack ? packed : full, out_len = unpack ? full : packed;
+    // out-of-place only: no written buffer may overlap a read buffer
+    for (int d = 0; d < A; ++d) {
+        const Range ro = range_of(outs[d], 0, out_len, es);
+        for (int s = 0; s < A; ++s)
+            if (overlap(ro, range_of(ins[s], 0, in_len, es)))
+                return fail(RR_EALIAS, "all-to-all is out-of-place: %s[%d] overlaps %s[%d]", out_name,
+                            d, in_name, s);
+        for (int e = 0; e < d; ++e)
+            if (overlap(ro, range_of(outs[e], 0, out_len, es)))
+                return fail(RR_EALIAS, "%s[%d] overlaps %s[%d]", out_name, d, out_name, e);
+    }
     for (int d = 0; d < A; ++d) {
         int j = 0;
         for (int s = 0; s < A; ++s) {
             if (s == d)
                 continue;
-            mv[n++] = A2AMove{d, s, j++};
+            const int64_t strided = (int64_t(d) * seg + int64_t(helper) * c) * es;
+            const int64_t strided_out = (int64_t(s) * seg + int64_t(helper) * c) * es;
+            const int64_t contiguous = int64_t(j) * c * es;
+            if (!unpack)
+                mv.push_back(Move{static_cast<const char *>(ins[s]) + strided,
+                                  static_cast<char *>(outs[d]) + contiguous, c * es});
+            else
+                mv.push_back(Move{static_cast<const char *>(ins[d]) + contiguous,
+                                  static_cast<char *>(outs[d]) + strided_out, c * es});
+            ++j;
         }
     }
-    return n;
+    return RR_OK;
 }
 
-rr_status check_a2a(const rr_relay *r, int dtype, int helper, rr_geom *g)
+rr_status job_error(int j, rr_status st)
 {
-    rr_status st = compute_geometry(r, RR_ALLTOALL, dtype, g);
-    if (st != RR_OK)
-        return st;
-    if (helper < 0 || helper >= r->H)
-        return fail(RR_EINVAL, "helper=%d outside [0, H=%d)", helper, r->H);
-    return RR_OK;
+    char tmp[sizeof g_err];
+    snprintf(tmp, sizeof tmp, "job %d: %.480s", j, g_err);
+    memcpy(g_err, tmp, sizeof g_err);
+    return st;
 }
 
 }  // namespace
@@ -455,220 +694,109 @@ int64_t rr_passthrough_helper_size(int64_t count_g, int32_t A, int32_t num_chunk
 rr_status rr_helper_reduce(const rr_relay *relay, int coll, int dtype, int op, int helper,
                            const void *const *slots, int nSlots, void *out, void *stream)
 {
-    rr_geom g;
-    rr_status st = check_common(relay, coll, dtype, op, &g);
-    if (st != RR_OK)
-        return st;
-    if (coll == RR_REDUCE_SCATTER)
-        return fail(RR_EINVAL,
-                    relay->A == 2
-                        ? "A=2 reduce-scatter helpers are passthrough: slot 0 and slot 1 feed "
-                          "different outputs and are not summable"
-                        : "the A=4 reduce-scatter helper reduces with rr_rs_multi_reduce pass 1");
-    if (coll == RR_ALLTOALL)
-        return fail(RR_EINVAL, "all-to-all performs no reduction");
-    const int A = relay->A;
-    if (nSlots != A)
-        return fail(RR_EINVAL, "nSlots=%d: the allreduce helper sums exactly A=%d slots", nSlots, A);
-    if (helper < 0 || helper >= relay->H)
-        return fail(RR_EINVAL, "helper=%d outside [0, H=%d)", helper, relay->H);
-    if (g.chunk == 0)
-        return ok();  // pure direct: the helper has nothing to reduce
-    const int64_t es = elem_size(dtype);
-    if ((st = check_array(slots, nSlots, es, "slots")) != RR_OK)
-        return st;
-    if ((st = check_ptr(out, es, "out", 0)) != RR_OK)
-        return st;
-    RedItem it{};
-    for (int a = 0; a < A; ++a)
-        it.in[a] = slots[a];
-    it.k = A;
-    it.out = out;
-    it.n = g.chunk;
-    return run_reduce(&it, 1, dtype, op_scale(op, A), stream);
+    std::vector<RedItem> items;
+    rr_status st = collect_helper(relay, coll, dtype, op, helper, slots, nSlots, out, items);
+    return st != RR_OK ? st : run_reduce(items, dtype, stream);
 }
 
 rr_status rr_active_add_scale(const rr_relay *relay, int coll, int dtype, int op, int activeIdx,
                               const void *const *in, int nIn, void *out, void *stream)
 {
-    rr_geom g;
-    rr_status st = check_common(relay, coll, dtype, op, &g);
-    if (st != RR_OK)
-        return st;
-    const int A = relay->A;
-    if (coll == RR_ALLTOALL)
-        return fail(RR_EINVAL, "all-to-all performs no reduction");
-    if (coll == RR_REDUCE_SCATTER && A != 2)
-        return fail(RR_EINVAL, "the A=4 reduce-scatter owner reduces with rr_rs_multi_reduce pass 2");
-    if (nIn != A)
-        return fail(RR_EINVAL, "nIn=%d: the active epilogue sums one input per active (A=%d)", nIn, A);
-    if (activeIdx < 0 || activeIdx >= A)
-        return fail(RR_EINVAL, "activeIdx=%d outside [0, A=%d)", activeIdx, A);
-    const int64_t es = elem_size(dtype);
-    if ((st = check_array(in, nIn, es, "in")) != RR_OK)
-        return st;
-    if ((st = check_ptr(out, es, "out", 0)) != RR_OK)
-        return st;
-
-    int64_t lo = 0, n = relay->count;  // reduce-scatter: the whole block
-    if (coll == RR_ALLREDUCE) {
-        lo = g.direct_off;
-        n = g.direct_len;
-        if (A > 2) {
-            lo = g.direct_off + int64_t(activeIdx) * g.dslice;
-            n = activeIdx == A - 1 ? g.direct_off + g.direct_len - lo : g.dslice;
-        }
-    }
-    RedItem it{};
-    for (int s = 0; s < A; ++s)
-        it.in[s] = static_cast<const char *>(in[s]) + lo * es;
-    it.k = A;
-    it.out = static_cast<char *>(out) + lo * es;
-    it.n = n;
-    return run_reduce(&it, 1, dtype, op_scale(op, A), stream);
+    std::vector<RedItem> items;
+    rr_status st = collect_active(relay, coll, dtype, op, activeIdx, in, nIn, out, items);
+    return st != RR_OK ? st : run_reduce(items, dtype, stream);
 }
 
 rr_status rr_rs_multi_reduce(const rr_relay *relay, int dtype, int op, int pass, int idx,
                              const void *const *in, int nIn, void *out, void *stream)
 {
-    rr_geom g;
-    rr_status st = check_common(relay, RR_REDUCE_SCATTER, dtype, op, &g);
-    if (st != RR_OK)
-        return st;
-    const int A = relay->A, H = relay->H;
-    if (A != 4)
-        return fail(RR_EINVAL,
-                    "the two multi-input passes belong to the A=4 reduce-scatter; A=2 helpers "
-                    "are passthrough and the owner uses rr_active_add_scale");
-    const int64_t es = elem_size(dtype);
-    const int64_t c = g.chunk;
-    if (pass == 1) {
-        if (idx < 0 || idx >= H)
-            return fail(RR_EINVAL, "pass 1: helper idx=%d outside [0, H=%d)", idx, H);
-        if (nIn != 1)
-            return fail(RR_EINVAL, "pass 1 takes the helper scratch as its single input (nIn=%d)", nIn);
-        if (c == 0)
-            return ok();
-        if ((st = check_array(in, 1, es, "in")) != RR_OK)
-            return st;
-        if ((st = check_ptr(out, es, "out", 0)) != RR_OK)
-            return st;
-        if (overlap(range_of(out, 0, A * c, es), range_of(in[0], 0, int64_t(A) * (A - 1) * c, es)))
-            return fail(RR_EALIAS, "pass 1 output overlaps the A*(A-1) input chunks of the scratch");
-        RedItem items[4]{};
-        for (int o = 0; o < A; ++o) {
-            for (int j = 0; j < A - 1; ++j)
-                items[o].in[j] = static_cast<const char *>(in[0]) + (int64_t(o) * (A - 1) + j) * c * es;
-            items[o].k = A - 1;
-            items[o].out = static_cast<char *>(out) + int64_t(o) * c * es;
-            items[o].n = c;
-        }
-        return run_reduce(items, A, dtype, 1.0f, stream);
-    }
-    if (pass != 2)
-        return fail(RR_EINVAL, "pass=%d: the reduction has two passes (1 helper, 2 owner)", pass);
-    if (idx < 0 || idx >= A)
-        return fail(RR_EINVAL, "pass 2: owner idx=%d outside [0, A=%d)", idx, A);
-    if (nIn != A + H)
-        return fail(RR_EINVAL, "pass 2 takes A blocks and H reduced chunks (nIn=%d, expected %d)",
-                    nIn, A + H);
-    if ((st = check_array(in, A, es, "in")) != RR_OK)
-        return st;
-    if (c > 0 && (st = check_array(in + A, H, es, "in[A+h]")) != RR_OK)
-        return st;
-    if ((st = check_ptr(out, es, "out", 0)) != RR_OK)
-        return st;
-    if (H + 1 > 24)
-        return fail(RR_EUNSUPPORTED, "H=%d exceeds this library's segment table", H);
-    RedItem items[25]{};
-    int n = 0;
-    for (int h = 0; h < H && c > 0; ++h, ++n) {
-        items[n].in[0] = static_cast<const char *>(in[idx]) + int64_t(h) * c * es;
-        items[n].in[1] = in[A + h];
-        items[n].k = 2;
-        items[n].out = static_cast<char *>(out) + int64_t(h) * c * es;
-        items[n].n = c;
-    }
-    for (int s = 0; s < A; ++s)
-        items[n].in[s] = static_cast<const char *>(in[s]) + g.direct_off * es;
-    items[n].k = A;
-    items[n].out = static_cast<char *>(out) + g.direct_off * es;
-    items[n].n = g.direct_len;
-    ++n;
-    return run_reduce(items, n, dtype, op_scale(op, A), stream);
+    std::vector<RedItem> items;
+    rr_status st = collect_rs(relay, dtype, op, pass, idx, in, nIn, out, items);
+    return st != RR_OK ? st : run_reduce(items, dtype, stream);
 }
 
 rr_status rr_a2a_pack(const rr_relay *relay, int dtype, int helper, const void *const *src,
                       void *const *dst, void *stream)
 {
-    rr_geom g;
-    rr_status st = check_a2a(relay, dtype, helper, &g);
-    if (st != RR_OK)
-        return st;
-    if (g.chunk == 0)
-        return ok();
-    const int A = relay->A;
-    const int64_t es = elem_size(dtype), seg = relay->count, c = g.chunk;
-    if ((st = check_array(src, A, es, "src")) != RR_OK)
-        return st;
-    if ((st = check_array(const_cast<const void *const *>(dst), A, es, "dst")) != RR_OK)
-        return st;
-    for (int d = 0; d < A; ++d) {
-        const Range rd = range_of(dst[d], 0, int64_t(A - 1) * c, es);
-        for (int s = 0; s < A; ++s)
-            if (overlap(rd, range_of(src[s], 0, int64_t(A) * seg, es)))
-                return fail(RR_EALIAS, "all-to-all is out-of-place: dst[%d] overlaps src[%d]", d, s);
-        for (int e = 0; e < d; ++e)
-            if (overlap(rd, range_of(dst[e], 0, int64_t(A - 1) * c, es)))
-                return fail(RR_EALIAS, "dst[%d] overlaps dst[%d]", d, e);
-    }
-    A2AMove mv[16];
-    const int nm = a2a_moves(A, mv);
-    CopyLauncher L(static_cast<hipStream_t>(stream));
-    for (int m = 0; m < nm; ++m)
-        L.add(static_cast<const char *>(src[mv[m].s]) + (int64_t(mv[m].d) * seg + int64_t(helper) * c) * es,
-              static_cast<char *>(dst[mv[m].d]) + int64_t(mv[m].j) * c * es, c * es);
-    const hipError_t e = L.finish();
-    if (e != hipSuccess)
-        return fail(RR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
+    std::vector<Move> mv;
+    rr_status st = collect_a2a(relay, dtype, helper, src, dst, false, mv);
+    return st != RR_OK ? st : run_copy(mv, stream);
 }
 
 rr_status rr_a2a_unpack(const rr_relay *relay, int dtype, int helper, const void *const *recv,
                         void *const *out, void *stream)
 {
-    rr_geom g;
-    rr_status st = check_a2a(relay, dtype, helper, &g);
-    if (st != RR_OK)
-        return st;
-    if (g.chunk == 0)
-        return ok();
-    const int A = relay->A;
-    const int64_t es = elem_size(dtype), seg = relay->count, c = g.chunk;
-    if ((st = check_array(recv, A, es, "recv")) != RR_OK)
-        return st;
-    if ((st = check_array(const_cast<const void *const *>(out), A, es, "out")) != RR_OK)
-        return st;
-    for (int d = 0; d < A; ++d) {
-        const Range ro = range_of(out[d], 0, int64_t(A) * seg, es);
-        for (int s = 0; s < A; ++s)
-            if (overlap(ro, range_of(recv[s], 0, int64_t(A - 1) * c, es)))
-                return fail(RR_EALIAS, "all-to-all is out-of-place: out[%d] overlaps recv[%d]", d, s);
-        for (int e = 0; e < d; ++e)
-            if (overlap(ro, range_of(out[e], 0, int64_t(A) * seg, es)))
-                return fail(RR_EALIAS, "out[%d] overlaps out[%d]", d, e);
+    std::vector<Move> mv;
+    rr_status st = collect_a2a(relay, dtype, helper, recv, out, true, mv);
+    return st != RR_OK ? st : run_copy(mv, stream);
+}
+
+rr_status rr_helper_reduce_many(int coll, int dtype, int op, const rr_helper_job *jobs, int nJobs,
+                                void *stream)
+{
+    if (nJobs < 0 || (nJobs > 0 && !jobs))
+        return fail(RR_EINVAL, "job array is null or nJobs=%d is negative", nJobs);
+    std::vector<RedItem> items;
+    for (int j = 0; j < nJobs; ++j) {
+        const rr_helper_job &b = jobs[j];
+        rr_status st = collect_helper(&b.relay, coll, dtype, op, b.helper, b.slots, b.nSlots, b.out, items);
+        if (st != RR_OK)
+            return job_error(j, st);
     }
-    A2AMove mv[16];
-    const int nm = a2a_moves(A, mv);
-    CopyLauncher L(static_cast<hipStream_t>(stream));
-    for (int m = 0; m < nm; ++m)
-        L.add(static_cast<const char *>(recv[mv[m].d]) + int64_t(mv[m].j) * c * es,
-              static_cast<char *>(out[mv[m].d]) + (int64_t(mv[m].s) * seg + int64_t(helper) * c) * es,
-              c * es);
-    const hipError_t e = L.finish();
-    if (e != hipSuccess)
-        return fail(RR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
+    return run_reduce(items, dtype, stream);
+}
+
+rr_status rr_active_add_scale_many(int coll, int dtype, int op, const rr_active_job *jobs, int nJobs,
+                                   void *stream)
+{
+    if (nJobs < 0 || (nJobs > 0 && !jobs))
+        return fail(RR_EINVAL, "job array is null or nJobs=%d is negative", nJobs);
+    std::vector<RedItem> items;
+    for (int j = 0; j < nJobs; ++j) {
+        const rr_active_job &b = jobs[j];
+        rr_status st = collect_active(&b.relay, coll, dtype, op, b.activeIdx, b.in, b.nIn, b.out, items);
+        if (st != RR_OK)
+            return job_error(j, st);
+    }
+    return run_reduce(items, dtype, stream);
+}
+
+rr_status rr_rs_multi_reduce_many(int dtype, int op, const rr_rs_job *jobs, int nJobs, void *stream)
+{
+    if (nJobs < 0 || (nJobs > 0 && !jobs))
+        return fail(RR_EINVAL, "job array is null or nJobs=%d is negative", nJobs);
+    std::vector<RedItem> items;
+    for (int j = 0; j < nJobs; ++j) {
+        const rr_rs_job &b = jobs[j];
+        rr_status st = collect_rs(&b.relay, dtype, op, b.pass, b.idx, b.in, b.nIn, b.out, items);
+        if (st != RR_OK)
+            return job_error(j, st);
+    }
+    return run_reduce(items, dtype, stream);
+}
+
+static rr_status a2a_many(int dtype, const rr_a2a_job *jobs, int nJobs, bool unpack, void *stream)
+{
+    if (nJobs < 0 || (nJobs > 0 && !jobs))
+        return fail(RR_EINVAL, "job array is null or nJobs=%d is negative", nJobs);
+    std::vector<Move> mv;
+    for (int j = 0; j < nJobs; ++j) {
+        const rr_a2a_job &b = jobs[j];
+        rr_status st = collect_a2a(&b.relay, dtype, b.helper, b.in, b.out, unpack, mv);
+        if (st != RR_OK)
+            return job_error(j, st);
+    }
+    return run_copy(mv, stream);
+}
+
+rr_status rr_a2a_pack_many(int dtype, const rr_a2a_job *jobs, int nJobs, void *stream)
+{
+    return a2a_many(dtype, jobs, nJobs, false, stream);
+}
+
+rr_status rr_a2a_unpack_many(int dtype, const rr_a2a_job *jobs, int nJobs, void *stream)
+{
+    return a2a_many(dtype, jobs, nJobs, true, stream);
 }
 
 }  // extern "C"

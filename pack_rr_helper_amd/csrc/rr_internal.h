@@ -16,7 +16,7 @@ namespace rr {
 
 constexpr int kBlock = 256;          // threads per workgroup (4 wave64)
 constexpr int kMaxIn = 4;            // inputs per reduction segment (A <= 4)
-constexpr int kMaxRedSegs = 24;      // segments per reduction launch
+constexpr int kMaxRedSegs = 40;      // segments per reduction launch
 constexpr int kMaxCopySegs = 64;     // segments per copy launch
 constexpr int64_t kMaxTilesPerLaunch = int64_t(1) << 22;
 

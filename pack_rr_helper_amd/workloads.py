@@ -16,20 +16,23 @@ rank would receive is represented by the bytes it would receive:
 
 Message size M is the per-active-rank input in bytes (the pull request's sweep
 axis), bf16 unless stated.  Workload classes expose ``calls(stream)``: one
-entry per kernel launch, ``(row, kernel, algorithmic_bytes, fn)`` with ``fn()``
-issuing exactly that launch; ``run(stream)`` issues them all, and the buffers
-the parity tests compare are attributes.  Algorithmic bytes count every input
-element read once and every output element written once.
+entry per role, ``(row, kernel, algorithmic_bytes, fn)`` with ``fn()``
+issuing that role's work.  With ``batched=True`` (the default) a role is one
+``*_many`` call over all of its jobs -- one kernel launch, as in the fused
+multi-group call; with ``batched=False`` every job is its own call and entry.
+Calls are prepared once (checks and marshalling), so issuing one costs a single
+C call.  ``run(stream)`` issues every entry.  Algorithmic bytes count every
+input element read once and every output element written once.
 """
 import torch
 
-from . import (ALLREDUCE, AVG, BF16, F32, REDUCE_SCATTER, SUM, Relay, rr_a2a_pack, rr_a2a_unpack,
-               rr_active_add_scale, rr_geometry, rr_helper_reduce, rr_rs_multi_reduce)
+from . import (ALLREDUCE, ALLTOALL, AVG, BF16, F32, REDUCE_SCATTER, SUM, Relay, rr_a2a_pack,
+               rr_a2a_pack_many, rr_a2a_unpack, rr_a2a_unpack_many, rr_active_add_scale,
+               rr_active_add_scale_many, rr_geometry, rr_helper_reduce, rr_helper_reduce_many,
+               rr_rs_multi_reduce, rr_rs_multi_reduce_many)
 
 TORCH = {F32: torch.float32, BF16: torch.bfloat16}
 ESIZE = {F32: 4, BF16: 2}
-
-
 COPY = "copy_kernel"
 
 
@@ -38,6 +41,16 @@ def reduce_kernel(dtype):
 
 
 class _Row:
+    batched = True
+
+    def calls(self, stream=None):
+        key = id(stream) if stream is not None else None
+        if getattr(self, "_calls_key", object()) != key:
+            self._calls = self._build(stream)
+            self._calls_key = key
+            self._stream_ref = stream
+        return self._calls
+
     def run(self, stream=None):
         for _, _, _, fn in self.calls(stream):
             fn()
@@ -45,39 +58,43 @@ class _Row:
     def bytes_per_step(self):
         return sum(b for _, _, b, _ in self.calls())
 
+    def _roles(self, stream, row, kernel, per_job_bytes, jobs, many, single):
+        """One entry for all jobs (batched) or one entry per job."""
+        if not jobs:
+            return []
+        if self.batched:
+            return [(row, kernel, sum(per_job_bytes),
+                     many(jobs, stream=stream, prepare=True))]
+        return [(row, kernel, b, single(job, stream=stream, prepare=True))
+                for b, job in zip(per_job_bytes, jobs)]
+
 
 class AR2(_Row):
     """A=2 allreduce: reduce-at-helper (summary section 2) over the H relay
     chunks and the active epilogue over the direct region (section 1)."""
 
-    def __init__(self, xs, dtype, op=AVG, H=6, numChunks=8, helpers=True, actives=True):
-        self.dtype, self.op = dtype, op
+    def __init__(self, xs, dtype, op=AVG, H=6, numChunks=8, batched=True):
+        self.dtype, self.op, self.batched = dtype, op, batched
         self.count = xs[0].numel()
         self.relay = Relay(2, H, numChunks, 0, self.count)
-        g = rr_geometry(self.relay, ALLREDUCE, dtype)
-        self.g, c, es = g, g["chunk"], ESIZE[dtype]
+        self.g = rr_geometry(self.relay, ALLREDUCE, dtype)
+        c, self.es = self.g["chunk"], ESIZE[dtype]
         self.x = xs
         self.red = [torch.empty(max(c, 1), dtype=TORCH[dtype], device=xs[0].device) for _ in range(H)]
         self.out = [torch.empty_like(xs[0]) for _ in range(2)]
-        self.do_helpers, self.do_actives = helpers, actives
-        self.es = es
 
-    def calls(self, stream=None):
-        c, es, out = self.g["chunk"], self.es, []
-        if self.do_helpers and c:
-            for k in range(self.relay.H):
-                sl = slice(k * c, (k + 1) * c)
-                out.append(("ar2_helper", reduce_kernel(self.dtype), 3 * c * es,
-                            lambda sl=sl, k=k: rr_helper_reduce(
-                                self.relay, ALLREDUCE, self.dtype, self.op, k,
-                                [self.x[0][sl], self.x[1][sl]], self.red[k], stream)))
-        if self.do_actives and self.g["direct_len"]:
-            for a in range(2):
-                out.append(("ar2_active", reduce_kernel(self.dtype), 3 * self.g["direct_len"] * es,
-                            lambda a=a: rr_active_add_scale(
-                                self.relay, ALLREDUCE, self.dtype, self.op, a, self.x,
-                                self.out[a], stream)))
-        return out
+    def _build(self, stream):
+        c, es, r, k = self.g["chunk"], self.es, self.relay, reduce_kernel(self.dtype)
+        hjobs = [(r, h, [self.x[0][h * c:(h + 1) * c], self.x[1][h * c:(h + 1) * c]], self.red[h])
+                 for h in range(r.H)] if c else []
+        ajobs = [(r, a, self.x, self.out[a]) for a in range(2)] if self.g["direct_len"] else []
+        op, dt = self.op, self.dtype
+        return (self._roles(stream, "ar2_helper", k, [3 * c * es] * len(hjobs), hjobs,
+                            lambda j, **kw: rr_helper_reduce_many(ALLREDUCE, dt, op, j, **kw),
+                            lambda j, **kw: rr_helper_reduce(j[0], ALLREDUCE, dt, op, *j[1:], **kw))
+                + self._roles(stream, "ar2_active", k, [3 * self.g["direct_len"] * es] * len(ajobs), ajobs,
+                              lambda j, **kw: rr_active_add_scale_many(ALLREDUCE, dt, op, j, **kw),
+                              lambda j, **kw: rr_active_add_scale(j[0], ALLREDUCE, dt, op, *j[1:], **kw)))
 
     def deliver_returns(self):
         """The helpers' return hop (a copy per active), for whole-group checks."""
@@ -92,12 +109,11 @@ class RS2(_Row):
     and direct chunks over the whole recvCount block (reduce-scatter core
     commit, phases 3 and 5).  xs[a] holds 2 blocks of R."""
 
-    def __init__(self, xs, dtype, op=AVG, H=6, numChunks=8, in_place=False):
-        self.dtype, self.op = dtype, op
-        self.R = xs[0].numel() // 2
-        self.relay = Relay(2, H, numChunks, 0, self.R)
+    def __init__(self, xs, dtype, op=AVG, H=6, numChunks=8, in_place=False, batched=True):
+        self.dtype, self.op, self.batched = dtype, op, batched
+        self.R = R = xs[0].numel() // 2
+        self.relay = Relay(2, H, numChunks, 0, R)
         self.x = xs
-        R = self.R
         if in_place:
             self.own = [xs[0][:R].clone(), xs[1][R:].clone()]
             self.out = self.own
@@ -107,15 +123,13 @@ class RS2(_Row):
         # the peer block as delivered: the other active's contribution, unsummed
         self.peer = [xs[1][:R], xs[0][R:]]
 
-    def calls(self, stream=None):
-        out = []
-        for o in range(2 if self.R else 0):
-            ins = [self.own[0], self.peer[0]] if o == 0 else [self.peer[1], self.own[1]]
-            out.append(("rs2_owner", reduce_kernel(self.dtype), 3 * self.R * ESIZE[self.dtype],
-                        lambda o=o, ins=ins: rr_active_add_scale(
-                            self.relay, REDUCE_SCATTER, self.dtype, self.op, o, ins, self.out[o],
-                            stream)))
-        return out
+    def _build(self, stream):
+        r, dt, op = self.relay, self.dtype, self.op
+        jobs = [(r, 0, [self.own[0], self.peer[0]], self.out[0]),
+                (r, 1, [self.peer[1], self.own[1]], self.out[1])] if self.R else []
+        return self._roles(stream, "rs2_owner", reduce_kernel(dt), [3 * self.R * ESIZE[dt]] * len(jobs), jobs,
+                           lambda j, **kw: rr_active_add_scale_many(REDUCE_SCATTER, dt, op, j, **kw),
+                           lambda j, **kw: rr_active_add_scale(j[0], REDUCE_SCATTER, dt, op, *j[1:], **kw))
 
 
 class AR4(_Row):
@@ -123,33 +137,28 @@ class AR4(_Row):
     reduce their position slices 4->1, the A actives reduce their direct
     slices."""
 
-    def __init__(self, xs, dtype, op=AVG, H=4, permille=500):
-        self.dtype, self.op = dtype, op
+    def __init__(self, xs, dtype, op=AVG, H=4, permille=500, batched=True):
+        self.dtype, self.op, self.batched = dtype, op, batched
         self.count = xs[0].numel()
         self.relay = Relay(4, H, 0, permille, self.count)
-        g = rr_geometry(self.relay, ALLREDUCE, dtype)
-        self.g, c, es = g, g["chunk"], ESIZE[dtype]
+        self.g = rr_geometry(self.relay, ALLREDUCE, dtype)
+        c, self.es = self.g["chunk"], ESIZE[dtype]
         self.x = xs
         self.red = [torch.empty(max(c, 1), dtype=TORCH[dtype], device=xs[0].device) for _ in range(H)]
         self.out = [torch.empty_like(xs[0]) for _ in range(4)]
-        self.es = es
 
-    def calls(self, stream=None):
-        c, g, es, out = self.g["chunk"], self.g, self.es, []
-        for h in range(self.relay.H if c else 0):
-            sl = slice(h * c, (h + 1) * c)
-            out.append(("ar4_helper", reduce_kernel(self.dtype), 5 * c * es,
-                        lambda sl=sl, h=h: rr_helper_reduce(
-                            self.relay, ALLREDUCE, self.dtype, self.op, h,
-                            [x[sl] for x in self.x], self.red[h], stream)))
-        for a in range(4):
-            n = g["dslice"] if a < 3 else g["direct_len"] - 3 * g["dslice"]
-            if n:
-                out.append(("ar4_active", reduce_kernel(self.dtype), 5 * n * es,
-                            lambda a=a: rr_active_add_scale(
-                                self.relay, ALLREDUCE, self.dtype, self.op, a, self.x,
-                                self.out[a], stream)))
-        return out
+    def _build(self, stream):
+        c, g, es, r, dt, op = self.g["chunk"], self.g, self.es, self.relay, self.dtype, self.op
+        k = reduce_kernel(dt)
+        hjobs = [(r, h, [x[h * c:(h + 1) * c] for x in self.x], self.red[h]) for h in range(r.H)] if c else []
+        sizes = [g["dslice"] if a < 3 else g["direct_len"] - 3 * g["dslice"] for a in range(4)]
+        ajobs = [(r, a, self.x, self.out[a]) for a in range(4) if sizes[a]]
+        return (self._roles(stream, "ar4_helper", k, [5 * c * es] * len(hjobs), hjobs,
+                            lambda j, **kw: rr_helper_reduce_many(ALLREDUCE, dt, op, j, **kw),
+                            lambda j, **kw: rr_helper_reduce(j[0], ALLREDUCE, dt, op, *j[1:], **kw))
+                + self._roles(stream, "ar4_active", k, [5 * sizes[j[1]] * es for j in ajobs], ajobs,
+                              lambda j, **kw: rr_active_add_scale_many(ALLREDUCE, dt, op, j, **kw),
+                              lambda j, **kw: rr_active_add_scale(j[0], ALLREDUCE, dt, op, *j[1:], **kw)))
 
     def deliver(self):
         """Broadcast of the helpers' chunks and the all-gather of the direct
@@ -171,13 +180,13 @@ class RS4(_Row):
     each helper over its (owner, source) scratch, pass 2 at each owner.
     xs[s] holds A blocks of R."""
 
-    def __init__(self, xs, dtype, op=SUM, H=4, permille=500):
+    def __init__(self, xs, dtype, op=SUM, H=4, permille=500, batched=True):
         A = 4
-        self.dtype, self.op = dtype, op
+        self.dtype, self.op, self.batched = dtype, op, batched
         self.R = R = xs[0].numel() // A
         self.relay = Relay(A, H, 0, permille, R)
-        g = rr_geometry(self.relay, REDUCE_SCATTER, dtype)
-        self.g, c, es = g, g["chunk"], ESIZE[dtype]
+        self.g = rr_geometry(self.relay, REDUCE_SCATTER, dtype)
+        c, self.es = self.g["chunk"], ESIZE[dtype]
         self.x = xs
         dev = xs[0].device
         # helper scratch, 2R each: A*(A-1) chunks owner-major, then A reduced chunks
@@ -188,59 +197,57 @@ class RS4(_Row):
                     dst = (o * (A - 1) + j) * c
                     self.scratch[h][dst:dst + c].copy_(xs[s][o * R + h * c:o * R + (h + 1) * c])
         self.out = [torch.empty(R, dtype=TORCH[dtype], device=dev) for _ in range(A)]
-        self.es = es
 
     def reduced(self, h, o):
         c, A = self.g["chunk"], 4
         base = A * (A - 1) * c
         return self.scratch[h][base + o * c:base + (o + 1) * c]
 
-    def calls(self, stream=None):
-        A, c, R, H, es, out = 4, self.g["chunk"], self.R, self.relay.H, self.es, []
-        for h in range(H if c else 0):
-            out.append(("rs4_pass1", reduce_kernel(self.dtype), (A * (A - 1) + A) * c * es,
-                        lambda h=h: rr_rs_multi_reduce(
-                            self.relay, self.dtype, self.op, 1, h, [self.scratch[h]],
-                            self.scratch[h][A * (A - 1) * c:], stream)))
+    def _build(self, stream):
+        A, c, R, H, es, r = 4, self.g["chunk"], self.R, self.relay.H, self.es, self.relay
+        dt, op, k = self.dtype, self.op, reduce_kernel(self.dtype)
+        p1 = [(r, 1, h, [self.scratch[h]], self.scratch[h][A * (A - 1) * c:]) for h in range(H)] if c else []
+        p2 = []
         for o in range(A if R else 0):
             blocks = [x[o * R:(o + 1) * R] for x in self.x]
             reds = [self.reduced(h, o) if c else blocks[0] for h in range(H)]
-            out.append(("rs4_pass2", reduce_kernel(self.dtype), (3 * H * c + (A + 1) * (R - H * c)) * es,
-                        lambda o=o, ins=blocks + reds: rr_rs_multi_reduce(
-                            self.relay, self.dtype, self.op, 2, o, ins, self.out[o], stream)))
-        return out
+            p2.append((r, 2, o, blocks + reds, self.out[o]))
+        many = lambda j, **kw: rr_rs_multi_reduce_many(dt, op, j, **kw)
+        single = lambda j, **kw: rr_rs_multi_reduce(j[0], dt, op, *j[1:], **kw)
+        return (self._roles(stream, "rs4_pass1", k, [(A * (A - 1) + A) * c * es] * len(p1), p1, many, single)
+                + self._roles(stream, "rs4_pass2", k, [(3 * H * c + (A + 1) * (R - H * c)) * es] * len(p2),
+                              p2, many, single))
 
 
 class A2A(_Row):
     """A=4 all-to-all helper coalescing (reverted all-to-all paragraph): one
     pack and one unpack per helper slice.  src[s] holds A segments of seg."""
 
-    def __init__(self, src, dtype=BF16, H=4, numChunks=5):
+    def __init__(self, src, dtype=BF16, H=4, numChunks=5, batched=True):
         A = 4
-        self.dtype = dtype
-        self.seg = seg = src[0].numel() // A
-        self.relay = Relay(A, H, numChunks, 0, seg)
-        g = rr_geometry(self.relay, 2, dtype)
-        self.g, c, es = g, g["chunk"], ESIZE[dtype]
+        self.dtype, self.batched = dtype, batched
+        self.seg = src[0].numel() // A
+        self.relay = Relay(A, H, numChunks, 0, self.seg)
+        self.g = rr_geometry(self.relay, ALLTOALL, dtype)
+        c, self.es = self.g["chunk"], ESIZE[dtype]
         self.src = src
         dev = src[0].device
         self.packed = [[torch.empty(max((A - 1) * c, 1), dtype=src[0].dtype, device=dev) for _ in range(A)]
                        for _ in range(H)]
         self.out = [torch.zeros_like(s) for s in src]
-        self.es = es
 
-    def calls(self, stream=None):
-        A, c, es, out = 4, self.g["chunk"], self.es, []
+    def _build(self, stream):
+        A, c, es, r, dt = 4, self.g["chunk"], self.es, self.relay, self.dtype
         kern = COPY if (self.seg * es) % 16 == 0 else "copy_kernel+copy_shifted_kernel"
-        for h in range(self.relay.H if c else 0):
-            out.append(("a2a_pack", kern, 2 * A * (A - 1) * c * es,
-                        lambda h=h: rr_a2a_pack(self.relay, self.dtype, h, self.src, self.packed[h],
-                                                stream)))
-        for h in range(self.relay.H if c else 0):
-            out.append(("a2a_unpack", kern, 2 * A * (A - 1) * c * es,
-                        lambda h=h: rr_a2a_unpack(self.relay, self.dtype, h, self.packed[h],
-                                                  self.out, stream)))
-        return out
+        pj = [(r, h, self.src, self.packed[h]) for h in range(r.H)] if c else []
+        uj = [(r, h, self.packed[h], self.out) for h in range(r.H)] if c else []
+        b = 2 * A * (A - 1) * c * es
+        return (self._roles(stream, "a2a_pack", kern, [b] * len(pj), pj,
+                            lambda j, **kw: rr_a2a_pack_many(dt, j, **kw),
+                            lambda j, **kw: rr_a2a_pack(j[0], dt, *j[1:], **kw))
+                + self._roles(stream, "a2a_unpack", kern, [b] * len(uj), uj,
+                              lambda j, **kw: rr_a2a_unpack_many(dt, j, **kw),
+                              lambda j, **kw: rr_a2a_unpack(j[0], dt, *j[1:], **kw)))
 
 
 def message_shapes(M, es=2):

@@ -316,3 +316,61 @@ def test_partial_overlap_is_rejected_on_device_tensors():
         rr.rr_helper_reduce(relay, AR, BF16, SUM, 0, [x[:c], x[c:2 * c]], x[8:8 + c])
     with pytest.raises(rr.RRError, match="dtype"):   # bf16 tensors passed as fp32 buffers
         rr.rr_helper_reduce(relay, AR, F32, SUM, 0, [x[:c], x[c:2 * c]], x[:c])
+
+
+# --------------------------------------------------------------------------
+# fused multi-group calls: heterogeneous groups, zero-chunk groups skipped
+# --------------------------------------------------------------------------
+
+def test_many_calls_over_heterogeneous_groups(orc):
+    """One GPU helping three A=2 groups of different sizes (one of them too
+    small to relay) and running the active epilogue of an A=2 and an A=4
+    group, each role as one batched call."""
+    say("many heterogeneous")
+    counts = [2 ** 22 + 8 * 128 * 3 + 11, 8 * 128 * 40, 700]
+    xs = [[synth.as_bf16_bits(synth.normal(n, 60 + g, a)) for a in range(2)] for g, n in enumerate(counts)]
+    dx = [[dev(x) for x in pair] for pair in xs]
+    jobs, outs = [], []
+    for g, n in enumerate(counts):
+        relay = rr.Relay(2, 6, 8, 0, n)
+        c = rr.rr_geometry(relay, AR, BF16)["chunk"]
+        h = (2 * g + 1) % 6
+        o = torch.zeros(max(c, 1), dtype=torch.bfloat16, device="cuda")
+        jobs.append((relay, h, [dx[g][0][h * c:(h + 1) * c], dx[g][1][h * c:(h + 1) * c]], o))
+        outs.append((o, c, h))
+    rr.rr_helper_reduce_many(AR, BF16, AVG, jobs)
+    for g, (o, c, h) in enumerate(outs):
+        if c:
+            ref = orc.ar2_helper(BF16, AVG, xs[g][0][h * c:(h + 1) * c].copy(), xs[g][1][h * c:(h + 1) * c].copy())
+            check_bf16(host(o)[:c], ref, f"group {g} helper {h}")
+        else:
+            assert torch.all(o == 0)
+    n4 = 2 ** 21 + 4 * 128 * 5 + 6
+    x4 = [synth.as_bf16_bits(synth.uniform(n4, -2, 2, 61, a)) for a in range(4)]
+    d4 = [dev(x) for x in x4]
+    o2 = [torch.zeros(counts[0], dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    o4 = [torch.zeros(n4, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    ajobs = [(rr.Relay(2, 6, 8, 0, counts[0]), a, dx[0], o2[a]) for a in range(2)] + \
+            [(rr.Relay(4, 4, 0, 500, n4), a, d4, o4[a]) for a in range(4)]
+    rr.rr_active_add_scale_many(AR, BF16, AVG, ajobs)
+    for a in range(2):
+        ref = orc.ar_active(BF16, AVG, 2, 6, 8, 0, counts[0], a, xs[0], np.zeros(counts[0], np.uint16))
+        check_bf16(host(o2[a]), ref, f"A=2 active {a}")
+    for a in range(4):
+        ref = orc.ar_active(BF16, AVG, 4, 4, 0, 500, n4, a, x4, np.zeros(n4, np.uint16))
+        check_bf16(host(o4[a]), ref, f"A=4 active {a}")
+
+
+def test_unbatched_and_batched_workloads_agree(orc):
+    """The per-job calls and the batched calls of the timed workload write the
+    same bytes (both checked against the oracle)."""
+    say("batched vs unbatched")
+    M = 8 * 2 ** 20
+    xs = [synth.as_bf16_bits(synth.normal(M // 2, 2, s)) for s in range(4)]
+    ref = orc.rs4_group(BF16, SUM, 4, 500, M // 8, xs)
+    for batched in (False, True):
+        wl = W.RS4([dev(x) for x in xs], BF16, SUM, batched=batched)
+        assert len(wl.calls()) == (8 if not batched else 2)
+        wl.run()
+        for o in range(4):
+            check_bf16(host(wl.out[o]), ref[o], f"batched={batched} owner {o}")

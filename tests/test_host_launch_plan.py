@@ -103,9 +103,9 @@ def test_ar4_helper_and_active(sim, orc, count):
         assert np.array_equal(out, ref)
 
 
-@pytest.mark.parametrize("H,R,lead", [(4, 8 * 128 * 4 + 24, 0), (4, 8 * 128 * 2 + 5, 1), (12, 24 * 128 * 2 + 40, 3)])
+@pytest.mark.parametrize("H,R,lead", [(4, 8 * 128 * 4 + 24, 0), (4, 8 * 128 * 2 + 5, 1), (16, 32 * 128 * 2 + 40, 3)])
 def test_rs4_passes(sim, orc, H, R, lead):
-    """H=12 with misaligned views makes pass 2 exceed one segment table."""
+    """H=16 with misaligned views makes pass 2 exceed one segment table."""
     sim.reset()
     A = 4
     g = orc.geometry(A, H, 0, 500, R, RS, BF16)
@@ -118,11 +118,11 @@ def test_rs4_passes(sim, orc, H, R, lead):
     assert np.array_equal(red[lead:lead + A * c], orc.rs4_pass1(BF16, A, c, scratch))
     blk = [bits(R, 2, s) for s in range(A)]
     reds = [bits(c, 3, h) for h in range(H)]
-    # H=12: every view shares one misalignment, so each item splits into a
-    # head, a vector body and a tail (39 segments, more than one table);
+    # H=16: every view shares one misalignment, so each item splits into a
+    # head, a vector body and a tail (51 segments, more than one table);
     # otherwise the views disagree modulo 16 bytes and take the scalar path.
-    bl = [lead if (H == 12 or s % 2) else 0 for s in range(A)]
-    ol = lead if H == 12 else 0
+    bl = [lead if (H == 16 or s % 2) else 0 for s in range(A)]
+    ol = lead if H == 16 else 0
     bb = [sim.buf(padded(b, bl[s]), writable=False) for s, b in enumerate(blk)]
     rb = [sim.buf(padded(r, lead), writable=False) for r in reds]
     for o in range(A):
@@ -132,7 +132,7 @@ def test_rs4_passes(sim, orc, H, R, lead):
                  parr(*[ptr(b, bl[s]) for s, b in enumerate(bb)], *[ptr(r, lead) for r in rb]),
                  A + H, ptr(out, ol), None)
         assert np.array_equal(out[ol:ol + R], orc.rs4_pass2(BF16, AVG, A, H, 500, R, o, blk, reds))
-        if H == 12 and lead:
+        if H == 16 and lead:
             assert sim.L.sim_launches() - launches0 >= 2
 
 
@@ -163,3 +163,139 @@ def test_a2a_pack_unpack(sim, orc, seg, lead, es):
     for d in range(A):
         assert np.array_equal(outs[d][1:1 + A * seg], expect[d])
         assert outs[d][0] == 0x5A and np.all(outs[d][1 + A * seg:] == 0x5A)
+
+
+# --------------------------------------------------------------------------
+# batched multi-group calls
+# --------------------------------------------------------------------------
+
+import pack_rr_helper_amd as _rr  # noqa: E402  (ctypes job layouts only)
+
+
+def _relay(A, H, nc, pm, count):
+    return _Relay(A, H, nc, pm, count)
+
+
+def test_helper_many_heterogeneous_groups_one_launch(sim, orc):
+    """Three A=2 groups of different sizes and one zero-chunk group in one
+    call: one launch, each group's helper output equal to the oracle's."""
+    sim.reset()
+    counts = [8 * 128 * 12 + 5, 8 * 128 * 3, 900, 8 * 128 * 7 + 3]
+    jobs = (_rr._HelperJob * len(counts))()
+    refs, outs = [], []
+    for j, n in enumerate(counts):
+        x = [sim.buf(bits(n, 20 + j, a), writable=False) for a in range(2)]
+        c = orc.geometry(2, 6, 8, 0, n, AR, BF16)["chunk"]
+        h = j % 6
+        out = sim.buf(np.zeros(max(c, 1), np.uint16))
+        jobs[j].relay, jobs[j].helper, jobs[j].nSlots = _relay(2, 6, 8, 0, n), h, 2
+        jobs[j].slots[0], jobs[j].slots[1] = ptr(x[0], h * c).value, ptr(x[1], h * c).value
+        jobs[j].out = ptr(out).value
+        outs.append((out, c))
+        refs.append(orc.ar2_helper(BF16, AVG, x[0][h * c:(h + 1) * c].copy(), x[1][h * c:(h + 1) * c].copy())
+                    if c else None)
+    L0 = sim.L.sim_launches()
+    sim.call("rr_helper_reduce_many", AR, BF16, AVG, jobs, len(counts), None)
+    assert sim.L.sim_launches() - L0 == 1
+    for (out, c), ref in zip(outs, refs):
+        if c:
+            assert np.array_equal(out[:c], ref)
+        else:
+            assert np.all(out == 0)
+
+
+def test_active_many_mixes_a2_and_a4_groups(sim, orc):
+    sim.reset()
+    n2, n4 = 8 * 128 * 5 + 17, 2 ** 20 + 4 * 128 * 3
+    x2 = [sim.buf(bits(n2, 30, a), writable=False) for a in range(2)]
+    x4 = [sim.buf(bits(n4, 31, a), writable=False) for a in range(4)]
+    o2 = [sim.buf(np.zeros(n2, np.uint16)) for _ in range(2)]
+    o4 = [sim.buf(np.zeros(n4, np.uint16)) for _ in range(4)]
+    specs = [(_relay(2, 6, 8, 0, n2), a, x2, o2[a]) for a in range(2)] + \
+            [(_relay(4, 4, 0, 500, n4), a, x4, o4[a]) for a in range(4)]
+    jobs = (_rr._ActiveJob * len(specs))()
+    for j, (r, a, xs, o) in enumerate(specs):
+        jobs[j].relay, jobs[j].activeIdx, jobs[j].nIn = r, a, len(xs)
+        for i, x in enumerate(xs):
+            jobs[j].inp[i] = ptr(x).value
+        jobs[j].out = ptr(o).value
+    sim.call("rr_active_add_scale_many", AR, BF16, AVG, jobs, len(specs), None)
+    for a in range(2):
+        assert np.array_equal(o2[a], orc.ar_active(BF16, AVG, 2, 6, 8, 0, n2, a, x2, np.zeros(n2, np.uint16)))
+    for a in range(4):
+        assert np.array_equal(o4[a], orc.ar_active(BF16, AVG, 4, 4, 0, 500, n4, a, x4, np.zeros(n4, np.uint16)))
+
+
+def test_many_rejects_cross_job_overlap_and_names_the_job(sim):
+    sim.reset()
+    n = 8 * 128 * 4
+    x = [sim.buf(bits(n, 40, a), writable=False) for a in range(2)]
+    out = sim.buf(np.zeros(2 * n, np.uint16))
+    jobs = (_rr._HelperJob * 2)()
+    c = n // 8
+    for j in range(2):
+        jobs[j].relay, jobs[j].helper, jobs[j].nSlots = _relay(2, 6, 8, 0, n), j, 2
+        jobs[j].slots[0], jobs[j].slots[1] = ptr(x[0], j * c).value, ptr(x[1], j * c).value
+        jobs[j].out = ptr(out, j * 64).value           # job 1's output overlaps job 0's
+    L = sim.L
+    L0 = L.sim_launches()
+    assert L.rr_helper_reduce_many(AR, BF16, AVG, jobs, 2, None) == 2    # RR_EALIAS
+    jobs[1].helper = 9
+    assert L.rr_helper_reduce_many(AR, BF16, AVG, jobs, 2, None) == 1    # RR_EINVAL
+    assert L.rr_last_error().decode().startswith("job 1:")
+    assert L.sim_launches() == L0
+
+
+def test_rs_and_a2a_many_match_single_calls(sim, orc):
+    sim.reset()
+    A, H, R = 4, 4, 8 * 128 * 3 + 16
+    c = orc.geometry(A, H, 0, 500, R, RS, BF16)["chunk"]
+    xs = [bits(A * R, 50, s) for s in range(A)]
+    bx = [sim.buf(x, writable=False) for x in xs]
+    scratch = [sim.buf(np.concatenate([xs[s][o * R + h * c:o * R + (h + 1) * c] for o in range(A)
+                                       for s in range(A) if s != o] + [np.zeros(4 * c + 16, np.uint16)]))
+               for h in range(H)]
+    jobs = (_rr._RsJob * H)()
+    keep = []
+    for h in range(H):
+        p = parr(ptr(scratch[h]))
+        keep.append(p)
+        jobs[h].relay, jobs[h].pass_, jobs[h].idx, jobs[h].nIn = _relay(A, H, 0, 500, R), 1, h, 1
+        jobs[h].inp = ctypes.cast(p, ctypes.POINTER(ctypes.c_void_p))
+        jobs[h].out = ptr(scratch[h], 12 * c).value
+    sim.call("rr_rs_multi_reduce_many", BF16, SUM, jobs, H, None)
+    outs = [sim.buf(np.zeros(R, np.uint16)) for _ in range(A)]
+    jobs2 = (_rr._RsJob * A)()
+    for o in range(A):
+        p = parr(*[ptr(b, o * R) for b in bx], *[ptr(scratch[h], 12 * c + o * c) for h in range(H)])
+        keep.append(p)
+        jobs2[o].relay, jobs2[o].pass_, jobs2[o].idx, jobs2[o].nIn = _relay(A, H, 0, 500, R), 2, o, A + H
+        jobs2[o].inp = ctypes.cast(p, ctypes.POINTER(ctypes.c_void_p))
+        jobs2[o].out = ptr(outs[o]).value
+    L0 = sim.L.sim_launches()
+    sim.call("rr_rs_multi_reduce_many", BF16, SUM, jobs2, A, None)
+    assert sim.L.sim_launches() - L0 == 1
+    ref = orc.rs4_group(BF16, SUM, H, 500, R, xs)
+    for o in range(A):
+        assert np.array_equal(outs[o], ref[o])
+    # all-to-all: the four helper slices' packs and unpacks as two calls
+    seg = 5 * 128 * 3 + 8
+    cc = orc.geometry(A, H, 5, 0, seg, A2A, BF16)["chunk"]
+    src = [sim.buf(synth.bits16(A * seg, 51, s), writable=False) for s in range(A)]
+    packed = [[sim.buf(np.zeros(3 * cc, np.uint16)) for _ in range(A)] for _ in range(H)]
+    out = [sim.buf(np.zeros(A * seg, np.uint16)) for _ in range(A)]
+    for name, ins, outs_ in (("rr_a2a_pack_many", lambda h: src, lambda h: packed[h]),
+                             ("rr_a2a_unpack_many", lambda h: packed[h], lambda h: out)):
+        aj = (_rr._A2AJob * H)()
+        for h in range(H):
+            pi, po = parr(*[ptr(b) for b in ins(h)]), parr(*[ptr(b) for b in outs_(h)])
+            keep += [pi, po]
+            aj[h].relay, aj[h].helper = _relay(A, H, 5, 0, seg), h
+            aj[h].inp = ctypes.cast(pi, ctypes.POINTER(ctypes.c_void_p))
+            aj[h].out = ctypes.cast(po, ctypes.POINTER(ctypes.c_void_p))
+        sim.call(name, BF16, aj, H, None)
+    expect = [np.zeros(A * seg, np.uint16) for _ in range(A)]
+    for h in range(H):
+        orc.a2a_unpack(2, A, seg, cc, h, orc.a2a_pack(2, A, seg, cc, h, src), expect)
+    for d in range(A):
+        assert np.array_equal(out[d], expect[d])
