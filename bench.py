@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--message-mib", type=float, default=64.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy-mib", type=float, default=0.0,
+                   help="run a plain device copy of this size first (HBM counter calibration)")
     p.add_argument("--unbatched", action="store_true",
                    help="one launch per job instead of one batched launch per role")
     p.add_argument("--sweep", action="store_true", help="per-row sweep instead of the step benchmark")
@@ -168,9 +170,10 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel, message_mib):
-    """HBM bytes per launch of `kernel` from profiles/traffic.json, or None if
-    absent or taken on other kernel sources."""
+def traffic_for(kernel, message_mib, unbatched):
+    """HBM bytes per launch of `kernel` (counter-measured, scaled by a plain
+    copy of known size) from profiles/traffic.json, or None if absent, taken
+    on another workload, or taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -178,17 +181,39 @@ def traffic_for(kernel, message_mib):
         t = json.load(fh)
     if t.get("kernel_source_digest") != kernel_source_digest():
         return None
-    k = t.get("kernels", {}).get(kernel)
-    if not k or k.get("message_mib") != message_mib:
+    if t.get("message_mib") != message_mib or bool(t.get("unbatched")) != bool(unbatched):
         return None
-    return k.get("hbm_bytes_per_launch")
+    k = t.get("kernels", {}).get(kernel)
+    return None if not k else k.get("hbm_bytes_per_launch")
 
 
 # --------------------------------------------------------------------------
 # main benchmark
 # --------------------------------------------------------------------------
 
+def hip_runtime():
+    """The HIP runtime library this process already uses (torch's), for
+    fence-free timing events; loading the same file returns the same handle."""
+    import ctypes
+    path = "libamdhip64.so"
+    with open("/proc/self/maps") as fh:
+        for line in fh:
+            if "libamdhip64" in line:
+                path = line.split()[-1]
+                break
+    L = ctypes.CDLL(path)
+    L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return L
+
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hip_runtime_api.h: timing-only events
+
+
 def step_bench(args):
+    import ctypes
     import torch
     import pack_rr_helper_amd as rr
     rr.load()
@@ -202,23 +227,30 @@ def step_bench(args):
     calls = [c for wl in wls.values() for c in wl.calls(stream)]
     step_bytes = sum(b for _, _, b, _ in calls)
 
+    if args.calibrate_copy_mib:
+        # a plain device copy of known size, for scaling the HBM byte counters
+        n = int(args.calibrate_copy_mib * MIB)
+        a = torch.ones(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
     print(f"[bench] warmup {args.warmup} steps, {len(calls)} launches per step", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         for _, _, _, fn in calls:
             fn()
     torch.cuda.synchronize()
 
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
-          for _ in range(args.steps)]
+    # Timed region 1 -- the value: K whole steps, nothing between launches.
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
-    for s in range(args.steps):
-        for (e0, e1), (_, _, _, fn) in zip(ev[s], calls):
-            e0.record(stream)
+    for _ in range(args.steps):
+        for _, _, _, fn in calls:
             fn()
-            e1.record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -226,22 +258,45 @@ def step_bench(args):
     print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)", file=sys.stderr,
           flush=True)
 
+    # Timed region 2 -- per launch: K more steps with one timing-only HIP event
+    # (no system-scope fence) between consecutive launches on the stream the
+    # kernels run on; launch i lasts from event i to event i+1.
+    hip = hip_runtime()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    nev = args.steps * len(calls) + 1
+    evs = []
+    for _ in range(nev):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        evs.append(e)
+    i = 0
+    hip.hipEventRecord(evs[0], sp)
+    for _ in range(args.steps):
+        for _, _, _, fn in calls:
+            fn()
+            i += 1
+            hip.hipEventRecord(evs[i], sp)
+    torch.cuda.synchronize()
     per_row, per_kernel = {}, {}
-    for s in range(args.steps):
-        for (e0, e1), (row, kern, b, _) in zip(ev[s], calls):
-            ms = e0.elapsed_time(e1)
-            r = per_row.setdefault(row, [0.0, 0, 0])
-            r[0] += ms
-            r[1] += b
-            r[2] += 1
-            k = per_kernel.setdefault(kern, [0.0, 0, 0])
-            k[0] += ms
-            k[1] += b
-            k[2] += 1
+    f = ctypes.c_float()
+    i = 0
+    for _ in range(args.steps):
+        for row, kern, b, _ in calls:
+            hip.hipEventElapsedTime(ctypes.byref(f), evs[i], evs[i + 1])
+            ms = f.value
+            i += 1
+            for key, table in ((row, per_row), (kern, per_kernel)):
+                r = table.setdefault(key, [0.0, 0, 0])
+                r[0] += ms
+                r[1] += b
+                r[2] += 1
+    for e in evs:
+        hip.hipEventDestroy(e)
     dom = max(per_kernel, key=lambda k: per_kernel[k][0])
     d_ms, d_b, d_n = per_kernel[dom]
     achieved = (d_b / d_n) / (d_ms / d_n * 1e-3) / 1e9
-    traffic = traffic_for(dom, args.message_mib)
+    traffic = traffic_for(dom, args.message_mib, args.unbatched)
 
     value = step_bytes / (ms_step * 1e-3) / 1e9
     result = {
@@ -266,11 +321,15 @@ def step_bench(args):
             "launches_per_step": len(calls),
             "batched": not args.unbatched,
             "algorithmic_bytes_per_step": step_bytes,
+            "timed_region_1": "K steps, no events between launches (value, ms_per_step)",
             "rows_gbs": {row: round(b / (ms * 1e-3) / 1e9, 1) for row, (ms, b, n) in per_row.items()},
             "rows_us_per_launch": {row: round(1e3 * ms / n, 2) for row, (ms, b, n) in per_row.items()},
+            "rows_bytes_per_launch": {row: b // n for row, (ms, b, n) in per_row.items()},
+            "launch_order": [row for row, _, _, _ in calls],
         },
         "roofline": {
             "kernel": dom,
+            "timing": "timing-only HIP events between consecutive launches (second timed region)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_GBS,

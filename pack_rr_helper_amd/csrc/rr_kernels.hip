@@ -171,9 +171,8 @@ __device__ __forceinline__ void reduce_scalar(const RedSeg &sg, int64_t lt)
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(kBlock) void reduce_kernel(RedBatch b)
+__device__ __forceinline__ void reduce_tile(const RedBatch &b, int32_t t)
 {
-    const int32_t t = (int32_t)blockIdx.x;
     const int s = find_seg(b.tile0, b.nseg, t);
     const RedSeg &sg = b.seg[s];
     const int64_t lt = (int64_t)(t - b.tile0[s]);
@@ -187,6 +186,19 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(RedBatch b)
         }
     } else {
         reduce_scalar<BF16>(sg, lt);
+    }
+}
+
+// Tiles [0, ntiles): one per workgroup, or a grid stride when the grid is
+// capped below the tile count.
+template <bool BF16>
+__global__ __launch_bounds__(kBlock) void reduce_kernel(RedBatch b, int32_t ntiles)
+{
+    if constexpr (kGridCap == 0) {
+        reduce_tile<BF16>(b, (int32_t)blockIdx.x);
+    } else {
+        for (int32_t t = (int32_t)blockIdx.x; t < ntiles; t += (int32_t)gridDim.x)
+            reduce_tile<BF16>(b, t);
     }
 }
 
@@ -277,9 +289,8 @@ __device__ __forceinline__ void copy_bytes(const CopySeg &sg, int64_t lt)
 }
 
 // Aligned bodies and byte heads/tails.
-__global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch b)
+__device__ __forceinline__ void copy_tile(const CopyBatch &b, int32_t t)
 {
-    const int32_t t = (int32_t)blockIdx.x;
     const int s = find_seg(b.tile0, b.nseg, t);
     const CopySeg &sg = b.seg[s];
     const int64_t lt = (int64_t)(t - b.tile0[s]);
@@ -289,11 +300,20 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch b)
         copy_bytes(sg, lt);
 }
 
+__global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch b, int32_t ntiles)
+{
+    if constexpr (kGridCap == 0) {
+        copy_tile(b, (int32_t)blockIdx.x);
+    } else {
+        for (int32_t t = (int32_t)blockIdx.x; t < ntiles; t += (int32_t)gridDim.x)
+            copy_tile(b, t);
+    }
+}
+
 // Realigned bodies (source and destination disagree modulo 16 bytes); a
 // kernel of its own so its register budget does not limit the aligned path.
-__global__ __launch_bounds__(kBlock) void copy_shifted_kernel(CopyBatch b)
+__device__ __forceinline__ void copy_shifted_tile(const CopyBatch &b, int32_t t)
 {
-    const int32_t t = (int32_t)blockIdx.x;
     const int s = find_seg(b.tile0, b.nseg, t);
     const CopySeg &sg = b.seg[s];
     const int64_t lt = (int64_t)(t - b.tile0[s]);
@@ -303,6 +323,21 @@ __global__ __launch_bounds__(kBlock) void copy_shifted_kernel(CopyBatch b)
     case 2: copy_shifted<2>(sg, lt); break;
     default: copy_shifted<3>(sg, lt); break;
     }
+}
+
+__global__ __launch_bounds__(kBlock) void copy_shifted_kernel(CopyBatch b, int32_t ntiles)
+{
+    if constexpr (kGridCap == 0) {
+        copy_shifted_tile(b, (int32_t)blockIdx.x);
+    } else {
+        for (int32_t t = (int32_t)blockIdx.x; t < ntiles; t += (int32_t)gridDim.x)
+            copy_shifted_tile(b, t);
+    }
+}
+
+unsigned grid_for(int64_t total_tiles)
+{
+    return (unsigned)(kGridCap > 0 && total_tiles > kGridCap ? kGridCap : total_tiles);
 }
 
 }  // namespace
@@ -325,9 +360,9 @@ hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, hipStream_t str
         return hipSuccess;
     (void)hipGetLastError();  // report this launch's status only
     if (b.bf16)
-        reduce_kernel<true><<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
+        reduce_kernel<true><<<dim3(grid_for(total_tiles)), dim3(kBlock), 0, stream>>>(b, (int32_t)total_tiles);
     else
-        reduce_kernel<false><<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
+        reduce_kernel<false><<<dim3(grid_for(total_tiles)), dim3(kBlock), 0, stream>>>(b, (int32_t)total_tiles);
     return hipGetLastError();
 }
 
@@ -337,9 +372,9 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
         return hipSuccess;
     (void)hipGetLastError();  // report this launch's status only
     if (shifted)
-        copy_shifted_kernel<<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
+        copy_shifted_kernel<<<dim3(grid_for(total_tiles)), dim3(kBlock), 0, stream>>>(b, (int32_t)total_tiles);
     else
-        copy_kernel<<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
+        copy_kernel<<<dim3(grid_for(total_tiles)), dim3(kBlock), 0, stream>>>(b, (int32_t)total_tiles);
     return hipGetLastError();
 }
 

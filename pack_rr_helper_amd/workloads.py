@@ -7,6 +7,9 @@ rank would receive is represented by the bytes it would receive:
 
 * a helper's slots are views of the active ranks' buffers (the scatter would
   copy exactly those bytes into the helper's scratch);
+* an A=2 allreduce active reads the peer's direct region from its own receive
+  buffer, filled once, untimed, as the direct exchange would fill it (so the
+  two actives never share an input, as on two GPUs);
 * the A=2 reduce-scatter peer block is the other active's block (the
   passthrough forwards and the direct exchange deliver it unchanged);
 * the A=4 reduce-scatter helper scratch is filled once, untimed, with the
@@ -82,12 +85,18 @@ class AR2(_Row):
         self.x = xs
         self.red = [torch.empty(max(c, 1), dtype=TORCH[dtype], device=xs[0].device) for _ in range(H)]
         self.out = [torch.empty_like(xs[0]) for _ in range(2)]
+        # each active's copy of the other active's direct region, as received
+        lo = self.g["direct_off"]
+        self.recv = [torch.zeros_like(xs[0]) for _ in range(2)]
+        self.recv[0][lo:].copy_(xs[1][lo:])
+        self.recv[1][lo:].copy_(xs[0][lo:])
 
     def _build(self, stream):
         c, es, r, k = self.g["chunk"], self.es, self.relay, reduce_kernel(self.dtype)
         hjobs = [(r, h, [self.x[0][h * c:(h + 1) * c], self.x[1][h * c:(h + 1) * c]], self.red[h])
                  for h in range(r.H)] if c else []
-        ajobs = [(r, a, self.x, self.out[a]) for a in range(2)] if self.g["direct_len"] else []
+        ins = [[self.x[0], self.recv[0]], [self.recv[1], self.x[1]]]   # source-rank order
+        ajobs = [(r, a, ins[a], self.out[a]) for a in range(2)] if self.g["direct_len"] else []
         op, dt = self.op, self.dtype
         return (self._roles(stream, "ar2_helper", k, [3 * c * es] * len(hjobs), hjobs,
                             lambda j, **kw: rr_helper_reduce_many(ALLREDUCE, dt, op, j, **kw),
