@@ -198,8 +198,9 @@ rr_status rr_rs_multi_reduce(const rr_relay *relay, int dtype, int op, int pass,
 
 /*
  * rr_a2a_pack -- strided gather that coalesces helper slice h's all-to-all
- * traffic per destination (the reverted all-to-all paragraph of the summary:
- * "both ends are strided by segmentCount").  Out-of-place only.
+ * traffic per destination (the reverted all-to-all paragraph of the summary: the
+ * open lead needs gather/scatter kernels because sources and destinations are
+ * both laid out with a segmentCount stride).  Out-of-place only.
  *   src[s] (A pointers): source s's input, A segments of count elements,
  *     segment d destined for rank d.
  *   dst[d] (A pointers): (A-1)*chunk elements; chunk j holds the slice
@@ -226,7 +227,7 @@ rr_status rr_a2a_unpack(const rr_relay *relay, int dtype, int helper,
 /*
  * Batched forms -- one fused call for all the groups a GPU serves in one
  * phase (the fused multi-group call of the reduce-scatter distributed-layer
- * commit: "ONE fused phase-synchronized call across all sparse groups"), with
+ * commit: one fused call covers every sparse group at once), with
  * a per-group geometry: each job carries its own rr_relay, so groups of
  * different sizes mix freely and a job whose chunk aligns down to zero is a
  * no-op (zero-chunk direct-fallback commit: every group picks its schedule

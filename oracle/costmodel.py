@@ -11,10 +11,11 @@ forms the pull request prints can be compared exactly.
 
 Schedules built here (ranks 0..7; sparse group g of A actives = ranks
 [g*A, (g+1)*A); the helpers of a group are the other ranks in ascending order):
-  * ``a2_three_group``: the A=2 schedule before the pull request -- scatter,
-    forward, then a separate direct exchange, numChunks = H+1 (section 1).
-  * ``a2_two_group``: the link-balanced A=2 schedule -- two groups, one direct
-    piece riding along with each relay group; ``d`` is the direct size
+  * ``a2_three_group``: the A=2 schedule before the pull request: three
+    serialized groups (scatter to the helpers, helper forwarding, and the
+    direct active-to-active swap on its own), numChunks = H+1 (section 1).
+  * ``a2_two_group``: the link-balanced A=2 schedule -- two groups, half of the
+    direct region travelling inside each relay group; ``d`` is the direct size
     (section 1; numChunks = H+2 gives d = 2*count/8).
   * ``a4_allreduce``: A=4 allreduce with offload fraction p (section 4).
   * ``a4_all_to_all``: A=4 all-to-all helper offload with fraction p (the
@@ -68,7 +69,7 @@ def a2_three_group(count=Fraction(1), fused=True):
 
 def a2_two_group(count=Fraction(1), d=None, fused=True):
     """Two groups; relay region count - d over H helpers; the direct region d
-    is split in two halves, one riding along with each group."""
+    is split in two halves, sent with group 1 and group 2 respectively."""
     sparse = _groups(2) if fused else _groups(2)[:1]
     H = NODE - 2
     count = Fraction(count)

@@ -331,8 +331,8 @@ void orc_rs4_pass2(int dt, int op, int A, int H, int permille, int64_t R, int o,
     fold(dt, A, blk, off, g.direct_len, scale, out, g.direct_off);
 }
 
-/* All-to-all coalescing at helper slice h (reverted section: "both ends are
- * strided by segmentCount").  src[s] holds A segments of seg elements, segment
+/* All-to-all coalescing at helper slice h (reverted section: sources and destinations are both
+ * laid out with a segmentCount stride).  src[s] holds A segments of seg elements, segment
  * d destined for rank d.  The per-destination buffer dst[d] receives the slice
  * h of every source other than d, in ascending source order. */
 void orc_a2a_pack(int es, int A, int64_t seg, int64_t chunk, int h,
@@ -426,8 +426,9 @@ int orc_rs2_group(int dt, int op, int H, int numChunks, int64_t R,
     void *slot0 = (char *)scratch + 2 * R * es;
     void *slot1 = (char *)scratch + 3 * R * es;
     for (int k = 0; k < H && g.chunk > 0; k++) {
-        /* slot 0 = a0's contribution to a1's output, slot 1 = a1's to a0's:
-         * different outputs, so the helper forwards them unsummed */
+        /* slot 0 carries what a0 adds into a1's block and slot 1 what a1 adds
+         * into a0's block: they belong to different outputs, so the helper
+         * forwards them unsummed */
         copy_elems(slot0, 0, x0, R + (int64_t)k * g.chunk, g.chunk, es);
         copy_elems(slot1, 0, x1, 0 + (int64_t)k * g.chunk, g.chunk, es);
         copy_elems(recv1, (int64_t)k * g.chunk, slot0, 0, g.chunk, es);

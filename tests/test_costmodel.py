@@ -31,7 +31,7 @@ def test_a2_two_groups_cost_a_quarter_and_the_optimum_is_count_over_4():
     best = min(costs, key=costs.get)
     assert best == F(GOLD["a2_optimal_direct"])
     assert costs[best] == F(1, 4)
-    # every link carries exactly one chunk per direction per group at the optimum
+    # at the optimum each (link, direction) moves one chunk in each of the two groups
     for group in cm.a2_two_group(fused=True):
         loads = {}
         for s, d, n in group:

@@ -100,7 +100,7 @@ def test_a4_allreduce_balanced_split_and_scratch_cover(orc):
     g = orc.geometry(4, 4, 0, 500, 2 ** 27, AR, BF16)
     assert g["chunk"] == 2 ** 24 and g["relay_total"] == 2 ** 26
     assert g["direct_len"] == 2 ** 26 and g["dslice"] == 2 ** 24
-    # the 2*total_g helper buffer covers (A+1)*oChunk for any offload fraction
+    # a 2*total_g helper buffer holds the (A+1) offload chunks at every permille
     for count in (2 ** 20, 3 * 2 ** 20 + 5, 2 ** 27):
         for p in (1, 250, 500, 780, 999, 1000):
             gg = orc.geometry(4, 4, 0, p, count, AR, BF16)
