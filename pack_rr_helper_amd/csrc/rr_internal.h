@@ -17,11 +17,7 @@ namespace rr {
 #ifndef RR_BLOCK
 #define RR_BLOCK 256                 // threads per workgroup (4 wave64)
 #endif
-#ifndef RR_GRID_CAP
-#define RR_GRID_CAP 0                // 0: one workgroup per tile; else at most this many,
-#endif                               // each looping over tiles with a grid stride
 constexpr int kBlock = RR_BLOCK;
-constexpr int kGridCap = RR_GRID_CAP;
 constexpr int kMaxIn = 4;            // inputs per reduction segment (A <= 4)
 constexpr int kMaxRedSegs = 40;      // segments per reduction launch
 constexpr int kMaxCopySegs = 64;     // segments per copy launch

@@ -71,6 +71,15 @@ __device__ __forceinline__ void store_elem(void *p, int64_t i, float v)
         static_cast<float *>(p)[i] = v;
 }
 
+// Vector index of unroll step u of this thread within tile lt (a tile is
+// kBlock*U vectors): step u of thread t is t + u*kBlock, so each wave
+// instruction covers 1 KiB and the workgroup's four waves fill each 4 KiB.
+template <int U>
+__device__ __forceinline__ int64_t vec_index(int64_t lt, int u)
+{
+    return lt * (int64_t)(kBlock * U) + (int64_t)threadIdx.x + (int64_t)u * kBlock;
+}
+
 // Index of the segment that owns tile t: the number of later segment starts
 // at or before t.  Unrolled over the table so the scalar loads issue together.
 template <int MAXS>
@@ -120,7 +129,6 @@ __device__ __forceinline__ void reduce_vec(const RedSeg &sg, int64_t lt)
     constexpr int kVecElems = BF16 ? 8 : 4;
     constexpr int64_t kTileVecs = int64_t(kBlock) * kUnroll;
     const int64_t nv = sg.n / kVecElems;
-    const int64_t vbase = lt * kTileVecs + threadIdx.x;
     const float scale = sg.scale;
 
     const u32x4 *in[K];
@@ -136,14 +144,14 @@ __device__ __forceinline__ void reduce_vec(const RedSeg &sg, int64_t lt)
         for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
             for (int k = 0; k < K; ++k)
-                x[u][k] = ld16(in[k] + vbase + u * kBlock);
+                x[u][k] = ld16(in[k] + vec_index<kUnroll>(lt, u));
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            st16(out + vbase + u * kBlock, fold_vec<BF16, K>(x[u], scale));
+            st16(out + vec_index<kUnroll>(lt, u), fold_vec<BF16, K>(x[u], scale));
     } else {
-        // The segment's last, partial tile.
+        // The segment's last, partial tile (indices grow with u).
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t v = vbase + (int64_t)u * kBlock;
+            const int64_t v = vec_index<kUnroll>(lt, u);
             if (v >= nv)
                 break;
             u32x4 x[K];
@@ -189,17 +197,13 @@ __device__ __forceinline__ void reduce_tile(const RedBatch &b, int32_t t)
     }
 }
 
-// Tiles [0, ntiles): one per workgroup, or a grid stride when the grid is
-// capped below the tile count.
+// One workgroup per tile.  Workgroups reach the eight XCDs round-robin, so
+// neighbouring tiles stream through different XCDs; this interleave measured
+// faster than giving each XCD a contiguous range of tiles.
 template <bool BF16>
-__global__ __launch_bounds__(kBlock) void reduce_kernel(RedBatch b, int32_t ntiles)
+__global__ __launch_bounds__(kBlock) void reduce_kernel(RedBatch b)
 {
-    if constexpr (kGridCap == 0) {
-        reduce_tile<BF16>(b, (int32_t)blockIdx.x);
-    } else {
-        for (int32_t t = (int32_t)blockIdx.x; t < ntiles; t += (int32_t)gridDim.x)
-            reduce_tile<BF16>(b, t);
-    }
+    reduce_tile<BF16>(b, (int32_t)blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -210,20 +214,19 @@ __device__ __forceinline__ void copy_aligned(const CopySeg &sg, int64_t lt)
 {
     constexpr int64_t kTileVecs = int64_t(kBlock) * kCopyUnroll;
     const int64_t nv = sg.nbytes / 16;
-    const int64_t vbase = lt * kTileVecs + threadIdx.x;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(sg.src);
     u32x4 *dst = reinterpret_cast<u32x4 *>(sg.dst);
     if ((lt + 1) * kTileVecs <= nv) {
         u32x4 x[kCopyUnroll];
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u)
-            x[u] = ld16(src + vbase + u * kBlock);
+            x[u] = ld16(src + vec_index<kCopyUnroll>(lt, u));
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u)
-            st16(dst + vbase + u * kBlock, x[u]);
+            st16(dst + vec_index<kCopyUnroll>(lt, u), x[u]);
     } else {
         for (int u = 0; u < kCopyUnroll; ++u) {
-            const int64_t v = vbase + (int64_t)u * kBlock;
+            const int64_t v = vec_index<kCopyUnroll>(lt, u);
             if (v >= nv)
                 break;
             st16(dst + v, ld16(src + v));
@@ -231,12 +234,6 @@ __device__ __forceinline__ void copy_aligned(const CopySeg &sg, int64_t lt)
     }
 }
 
-// Destination aligned, source `shift` bytes past the aligned address sg.src.
-// Output vector v is bytes [16v + shift, 16v + shift + 16) of the aligned
-// source, i.e. dwords Q.. of the pair (word v, word v+1) shifted right by
-// R = shift % 4 bytes, with Q = shift / 4.  The second word of the last
-// vector is the aligned 16-byte block holding the segment's last source
-// bytes, so it never leaves the page those bytes live in.
 template <int Q>
 __device__ __forceinline__ u32x4 realign(u32x4 a, u32x4 b, unsigned r)
 {
@@ -300,14 +297,9 @@ __device__ __forceinline__ void copy_tile(const CopyBatch &b, int32_t t)
         copy_bytes(sg, lt);
 }
 
-__global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch b, int32_t ntiles)
+__global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch b)
 {
-    if constexpr (kGridCap == 0) {
-        copy_tile(b, (int32_t)blockIdx.x);
-    } else {
-        for (int32_t t = (int32_t)blockIdx.x; t < ntiles; t += (int32_t)gridDim.x)
-            copy_tile(b, t);
-    }
+    copy_tile(b, (int32_t)blockIdx.x);
 }
 
 // Realigned bodies (source and destination disagree modulo 16 bytes); a
@@ -325,19 +317,9 @@ __device__ __forceinline__ void copy_shifted_tile(const CopyBatch &b, int32_t t)
     }
 }
 
-__global__ __launch_bounds__(kBlock) void copy_shifted_kernel(CopyBatch b, int32_t ntiles)
+__global__ __launch_bounds__(kBlock) void copy_shifted_kernel(CopyBatch b)
 {
-    if constexpr (kGridCap == 0) {
-        copy_shifted_tile(b, (int32_t)blockIdx.x);
-    } else {
-        for (int32_t t = (int32_t)blockIdx.x; t < ntiles; t += (int32_t)gridDim.x)
-            copy_shifted_tile(b, t);
-    }
-}
-
-unsigned grid_for(int64_t total_tiles)
-{
-    return (unsigned)(kGridCap > 0 && total_tiles > kGridCap ? kGridCap : total_tiles);
+    copy_shifted_tile(b, (int32_t)blockIdx.x);
 }
 
 }  // namespace
@@ -360,9 +342,9 @@ hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, hipStream_t str
         return hipSuccess;
     (void)hipGetLastError();  // report this launch's status only
     if (b.bf16)
-        reduce_kernel<true><<<dim3(grid_for(total_tiles)), dim3(kBlock), 0, stream>>>(b, (int32_t)total_tiles);
+        reduce_kernel<true><<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
     else
-        reduce_kernel<false><<<dim3(grid_for(total_tiles)), dim3(kBlock), 0, stream>>>(b, (int32_t)total_tiles);
+        reduce_kernel<false><<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
     return hipGetLastError();
 }
 
@@ -372,9 +354,9 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
         return hipSuccess;
     (void)hipGetLastError();  // report this launch's status only
     if (shifted)
-        copy_shifted_kernel<<<dim3(grid_for(total_tiles)), dim3(kBlock), 0, stream>>>(b, (int32_t)total_tiles);
+        copy_shifted_kernel<<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
     else
-        copy_kernel<<<dim3(grid_for(total_tiles)), dim3(kBlock), 0, stream>>>(b, (int32_t)total_tiles);
+        copy_kernel<<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
     return hipGetLastError();
 }
 
