@@ -30,10 +30,13 @@ from fractions import Fraction
 NODE = 8
 
 
-def link_cost(schedule):
-    """Sum over groups of the max over (src, dst) of the elements carried."""
+def link_cost(schedule, per_group=0):
+    """Sum over groups of the max over (src, dst) of the elements carried,
+    plus ``per_group`` for every serialized group boundary (the fixed cost
+    that makes a latency-bound schedule prefer fewer groups, summary section 3)."""
     total = Fraction(0)
     for group in schedule:
+        total += Fraction(per_group)
         load = defaultdict(Fraction)
         for src, dst, n in group:
             if src == dst:

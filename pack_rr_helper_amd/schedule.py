@@ -25,6 +25,13 @@ paragraph; layouts as in include/rr.h):
 * ``a4_reduce_scatter``: flat reduce-at-helper; the helper scratch holds one
   chunk per (owner, source) pair; the direct region is split over the two
   groups.
+* ``a2_allreduce_small``: the small-message path of summary section 3 -- one
+  full exchange of the buffer (or, for comparison, a reduce-scatter swap then
+  an all-gather swap), then the add + scale over the whole buffer.
+* ``a4_all_gather``: summary section 5 -- two balanced groups: offload chunks
+  go to the helpers in group 1 and are forwarded to the other actives in
+  group 2, whose cross links therefore carry A-1 times group 1's; the direct
+  region is split 1:(A-1) over the two groups to balance them.
 * ``a4_all_to_all``: helper offload with per-destination coalescing; the
   gather (pack) and scatter (unpack) kernels stand in for the source->helper
   and helper->destination hops (the one-GPU collapse: the pack reads the
@@ -199,8 +206,89 @@ def a2_all_gather(S, dtype=BF16, H=6, numChunks=8):
     return _a2("all_gather", S, dtype, 0, H, numChunks)
 
 
+def a2_allreduce_small(count, dtype=BF16, op=1, H=6, numChunks=8, exchange="full"):
+    """exchange = "full": one group, each active sends its whole buffer to the
+    other and both reduce all of it; "rs_ag": a reduce-scatter swap of halves,
+    the half reduced by its owner, then an all-gather swap (two groups)."""
+    relay = Relay(2, H, numChunks, 0, count)
+    bufs = {}
+    for r in range(NODE):
+        bufs[(r, "in")] = bufs[(r, "out")] = bufs[(r, "recv")] = count
+    groups = []
+    if exchange == "full":
+        g1 = Group()
+        for act in sparse_groups(2):
+            for i, a in enumerate(act):
+                _hop(g1.hops, Ref(a, "in", 0, count), Ref(act[1 - i], "recv", 0, count))
+            for i, a in enumerate(act):
+                # the whole buffer as one block: the reduce-scatter form of the
+                # two-input add + scale (it covers every element)
+                ins = [Ref(a, "in", 0, count), Ref(a, "recv", 0, count)]
+                g1.after.append(Step(a, "active", relay, REDUCE_SCATTER, i, ins if i == 0 else ins[::-1],
+                                     [Ref(a, "out", 0, count)]))
+        groups = [g1]
+    elif exchange == "rs_ag":
+        half = count // 2
+        part = [(0, half), (half, count - half)]          # active i owns part i
+        g1, g2 = Group(), Group()
+        for act in sparse_groups(2):
+            for i, a in enumerate(act):
+                lo, n = part[1 - i]
+                _hop(g1.hops, Ref(a, "in", lo, n), Ref(act[1 - i], "recv", lo, n))
+                _hop(g2.hops, Ref(a, "out", part[i][0], part[i][1]), Ref(act[1 - i], "out", part[i][0], part[i][1]))
+            for i, a in enumerate(act):
+                lo, n = part[i]
+                rel = Relay(2, H, numChunks, 0, n)
+                ins = [Ref(a, "in", lo, n), Ref(a, "recv", lo, n)]
+                g1.after.append(Step(a, "active", rel, REDUCE_SCATTER, i, ins if i == 0 else ins[::-1],
+                                     [Ref(a, "out", lo, n)]))
+        groups = [g1, g2]
+    else:
+        raise ValueError(exchange)
+    return Schedule(f"a2_allreduce_small_{exchange}", 2, dtype, op, bufs, groups, count, count)
+
+
 # --------------------------------------------------------------------------
 # A = 4
+# --------------------------------------------------------------------------
+
+def a4_all_gather(S, dtype=BF16, H=4, numChunks=8):
+    """Offload chunk = align_down(S/numChunks, 128) per helper; active a's
+    slice k goes to helper k in group 1 and from there to the other actives in
+    group 2.  The direct remainder is sent a quarter in group 1 and three
+    quarters in group 2.  Output slot a of every active holds active a's
+    input."""
+    A = 4
+    c = (S // numChunks) // 128 * 128
+    if H * c > S:
+        raise ValueError("offload chunks exceed the send count")
+    d0 = H * c
+    d1 = (S - d0) // A                  # the 1 : (A-1) split of the direct region
+    bufs = {}
+    for r in range(NODE):
+        bufs[(r, "in")] = S
+        bufs[(r, "out")] = A * S
+    g1, g2 = Group(), Group()
+    for gi, act in enumerate(sparse_groups(A)):
+        hs = f"hs{gi}"
+        for k, h in enumerate(helpers_of(act)):
+            if not c:
+                break
+            bufs[(h, hs)] = A * c       # one chunk per source: the A-slot helper buffer
+            for ai, a in enumerate(act):
+                _hop(g1.hops, Ref(a, "in", k * c, c), Ref(h, hs, ai * c, c))
+                for b in act:
+                    if b != a:
+                        _hop(g2.hops, Ref(h, hs, ai * c, c), Ref(b, "out", ai * S + k * c, c))
+        for ai, a in enumerate(act):
+            g1.after.append(Step(a, "copy", ins=[Ref(a, "in", 0, S)], outs=[Ref(a, "out", ai * S, S)]))
+            for b in act:
+                if b != a:
+                    _hop(g1.hops, Ref(a, "in", d0, d1), Ref(b, "out", ai * S + d0, d1))
+                    _hop(g2.hops, Ref(a, "in", d0 + d1, S - d0 - d1), Ref(b, "out", ai * S + d0 + d1, S - d0 - d1))
+    return Schedule("a4_all_gather", A, dtype, 0, bufs, [g1, g2], S, A * S)
+
+
 # --------------------------------------------------------------------------
 
 def a4_allreduce(count, dtype=BF16, op=1, H=4, permille=500):

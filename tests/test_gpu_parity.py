@@ -374,3 +374,74 @@ def test_unbatched_and_batched_workloads_agree(orc):
         wl.run()
         for o in range(4):
             check_bf16(host(wl.out[o]), ref[o], f"batched={batched} owner {o}")
+
+
+# --------------------------------------------------------------------------
+# maximum sizes and fp32 coverage
+# --------------------------------------------------------------------------
+
+def _pattern(n, mult, device="cuda", step=1 << 26):
+    """bf16 small integers ((i*mult) % 61 - 30), built on the device in pieces."""
+    out = torch.empty(n, dtype=torch.bfloat16, device=device)
+    for lo in range(0, n, step):
+        hi = min(n, lo + step)
+        i = torch.arange(lo, hi, dtype=torch.int64, device=device)
+        out[lo:hi] = ((i * mult) % 61 - 30).to(torch.bfloat16)
+    return out
+
+
+def _pattern_host(idx, mult):
+    return synth.as_bf16_bits((((idx.astype(np.int64) * mult) % 61) - 30).astype(np.float32))
+
+
+def test_reduction_beyond_2_31_elements(orc):
+    """A reduce-scatter owner epilogue over recvCount > 2^31 elements (over
+    4 GiB per input): 64-bit offsets and tile counts across one launch."""
+    R = 2 ** 31 + 8 * 128 * 3 + 5
+    say("beyond 2^31", R)
+    a, b = _pattern(R, 3), _pattern(R, 7)
+    out = torch.empty(R, dtype=torch.bfloat16, device="cuda")
+    rr.rr_active_add_scale(rr.Relay(2, 6, 8, 0, R), RS, BF16, AVG, 0, [a, b], out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    idx = np.unique(np.concatenate([rng.integers(0, R, 1 << 20), np.arange(R - 4096, R),
+                                    np.arange(2 ** 31 - 4096, 2 ** 31 + 4096), np.arange(0, 4096)]))
+    ti = torch.from_numpy(idx).cuda()
+    got = synth.to_host(out[ti])
+    ref = orc.rs2_active(BF16, AVG, _pattern_host(idx, 3), _pattern_host(idx, 7))
+    check_bf16(got, ref, "sampled outputs past 2^31")
+    del a, b, out
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("R", [8 * 128 * 6 + 40, 2 ** 20 + 8])
+def test_fp32_a4_reduce_scatter_and_allreduce(orc, R):
+    say("fp32 A=4", R)
+    xs = [synth.normal(4 * R, 80, s) for s in range(4)]
+    wl = W.RS4([dev(x, F32) for x in xs], F32, AVG)
+    wl.run()
+    ref = orc.rs4_group(F32, AVG, 4, 500, R, xs)
+    for o in range(4):
+        check_f32(host(wl.out[o]), ref[o], [x[o * R:(o + 1) * R] for x in xs], f"fp32 RS owner {o}")
+    count = 4 * R
+    ar = W.AR4([dev(x, F32) for x in xs], F32, AVG)
+    ar.run()
+    ar.deliver()
+    ref = orc.ar4_group(F32, AVG, 4, 500, count, xs)
+    for a in range(4):
+        check_f32(host(ar.out[a]), ref[a], xs, f"fp32 AR active {a}")
+
+
+def test_fp32_all_to_all_bits(orc):
+    say("fp32 a2a")
+    A, seg = 4, 5 * 128 * 7 + 3
+    src = [synth.rng(81, s).integers(0, 2 ** 32, A * seg, dtype=np.uint32) for s in range(A)]
+    wl = W.A2A([torch.from_numpy(s.view(np.int32)).cuda() for s in src], F32)
+    wl.run()
+    torch.cuda.synchronize()
+    c = wl.g["chunk"]
+    expect = [np.zeros(A * seg, np.uint32) for _ in range(A)]
+    for h in range(4):
+        orc.a2a_unpack(4, A, seg, c, h, orc.a2a_pack(4, A, seg, c, h, src), expect)
+    for d in range(A):
+        assert np.array_equal(wl.out[d].cpu().numpy().view(np.uint32), expect[d])

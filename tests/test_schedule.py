@@ -61,6 +61,8 @@ def expected(s, xs):
             outs.append(orc.plain_sum(BF16, s.op, peers, 0, s.in_elems))
         elif s.name.endswith("reduce_scatter"):
             outs.append(orc.plain_sum(BF16, s.op, peers, i * s.out_elems, s.out_elems))
+        elif s.name.startswith("a2_allreduce_small"):
+            outs.append(orc.plain_sum(BF16, s.op, peers, 0, s.in_elems))
         elif s.name.endswith("all_to_all"):
             outs.append(orc.plain_all_to_all(2, s.A, s.in_elems // s.A, i, peers).view(np.uint16))
         else:
@@ -78,6 +80,9 @@ CASES = [
     ("a4_allreduce_floor", lambda n: S.a4_allreduce(n), 5000),
     ("a4_reduce_scatter", lambda n: S.a4_reduce_scatter(n // 4, op=SUM), 4 * (8 * 128 * 4 + 24)),
     ("a4_all_to_all", lambda n: S.a4_all_to_all(n // 4), 4 * (5 * 128 * 6 + 3)),
+    ("a2_allreduce_small_full", lambda n: S.a2_allreduce_small(n), 3000),
+    ("a2_allreduce_small_rs_ag", lambda n: S.a2_allreduce_small(n, exchange="rs_ag"), 3001),
+    ("a4_all_gather", lambda n: S.a4_all_gather(n), 8 * 128 * 5 + 19),
 ]
 
 
@@ -89,7 +94,7 @@ def test_schedule_on_cpu_is_the_plain_collective(name, mk, n):
         got = run_on_cpu(s, xs)
         exp = expected(s, xs)
         for r in range(8):
-            if ints or not s.name.endswith(("allreduce", "reduce_scatter")):
+            if ints or not ("allreduce" in s.name or s.name.endswith("reduce_scatter")):
                 assert np.array_equal(got[r], exp[r]), (name, r)
             elif s.name == "a4_reduce_scatter":
                 assert_rs4_bound(s, xs, r, got[r])
@@ -148,3 +153,33 @@ def test_schedule_on_gpu_matches_the_host_execution(name, mk, n):
     ref = run_on_cpu(s, xs)
     for r in range(8):
         assert np.array_equal(synth.to_host(outs[r]), ref[r]), (name, r)
+
+
+def test_small_message_single_exchange_beats_rs_plus_ag():
+    """Summary section 3: both move the whole buffer per link direction, but
+    the reduce-scatter + all-gather form pays two group boundaries."""
+    n = 4096
+    full, rsag = S.a2_allreduce_small(n), S.a2_allreduce_small(n, exchange="rs_ag")
+    assert len(full.groups) == 1 and len(rsag.groups) == 2
+    assert cost(full) == cost(rsag) == n
+    lat = Fraction(1)
+    assert cm.link_cost([[(a, b, Fraction(m)) for a, b, m in g] for g in full.link_groups()], lat) < \
+        cm.link_cost([[(a, b, Fraction(m)) for a, b, m in g] for g in rsag.link_groups()], lat)
+
+
+def test_a4_all_gather_two_balanced_groups():
+    """Summary section 5: group 2's cross links carry A-1 times group 1's; the
+    1:(A-1) direct split balances both groups, halving the pure-direct time."""
+    S_ = 8 * 128 * 400
+    s = S.a4_all_gather(S_)
+    g1, g2 = s.link_groups()
+    def peak(g, intra):
+        load = {}
+        for a, b, m in g:
+            if (a // 4 == b // 4) == intra:
+                load[(a, b)] = load.get((a, b), 0) + m
+        return max(load.values())
+    assert peak(g2, False) == 3 * peak(g1, False)          # cross: forwarding carries 3 sources
+    assert peak(g1, True) == peak(g1, False) and peak(g2, True) == peak(g2, False)
+    direct = Fraction(S_)                                    # pure direct: one group of S per link
+    assert cost(s) == direct / 2
