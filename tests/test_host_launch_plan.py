@@ -299,3 +299,107 @@ def test_rs_and_a2a_many_match_single_calls(sim, orc):
         orc.a2a_unpack(2, A, seg, cc, h, orc.a2a_pack(2, A, seg, cc, h, src), expect)
     for d in range(A):
         assert np.array_equal(out[d], expect[d])
+
+
+# --------------------------------------------------------------------------
+# randomized: geometry, sizes, ops, dtypes, misalignment, batching
+# --------------------------------------------------------------------------
+
+def _rand_case(rng):
+    A = int(rng.choice([2, 4]))
+    H = int(rng.integers(1, 7)) if A == 2 else int(rng.integers(1, 5))
+    dt = int(rng.choice([F32, BF16]))
+    op = int(rng.choice([SUM, AVG]))
+    return A, H, dt, op
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_active_and_helper_calls_match_the_oracle(sim, orc, seed):
+    rng = np.random.default_rng(1000 + seed)
+    sim.reset()
+    A, H, dt, op = _rand_case(rng)
+    npdt = np.float32 if dt == F32 else np.uint16
+    es = 4 if dt == F32 else 2
+    nc = H + 2 + int(rng.integers(0, 3)) if A == 2 else 0
+    pm = int(rng.choice([250, 500, 780, 1000])) if A == 4 else 0
+    count = int(rng.integers(0, 3 * 2 ** 20 // es)) if A == 4 else int(rng.integers(0, 40000))
+    g = orc.geometry(A, H, nc, pm, count, AR, dt)
+    assert g is not None
+    lead = int(rng.integers(0, 8))
+    def mk(r):
+        x = synth.normal(count, 2000 + seed, r)
+        return x if dt == F32 else synth.as_bf16_bits(x)
+    xs = [mk(r) for r in range(A)]
+    bx = [sim.buf(padded(x, lead if rng.random() < 0.5 else 0), writable=False) for x in xs]
+    leads = [(b.size - 16 - x.size) for b, x in zip(bx, xs)]
+    rel = _Relay(A, H, nc, pm, count)
+    # actives, batched
+    jobs = (_rr._ActiveJob * A)()
+    outs = []
+    for a in range(A):
+        o = sim.buf(np.zeros(count + 8, npdt))
+        outs.append(o)
+        jobs[a].relay, jobs[a].activeIdx, jobs[a].nIn = rel, a, A
+        for s in range(A):
+            jobs[a].inp[s] = ptr(bx[s], leads[s]).value
+        jobs[a].out = ptr(o).value
+    sim.call("rr_active_add_scale_many", AR, dt, op, jobs, A, None)
+    for a in range(A):
+        ref = orc.ar_active(dt, op, A, H, nc, pm, count, a, xs, np.zeros(count, npdt))
+        assert np.array_equal(outs[a][:count].view(np.uint8), ref.view(np.uint8)), (A, H, dt, count, a)
+    # helpers, one batched call over every helper
+    c = g["chunk"]
+    hj = (_rr._HelperJob * H)()
+    houts = []
+    for h in range(H):
+        o = sim.buf(np.zeros(max(c, 1) + 8, npdt))
+        houts.append(o)
+        hj[h].relay, hj[h].helper, hj[h].nSlots = rel, h, A
+        for s in range(A):
+            hj[h].slots[s] = ptr(bx[s], leads[s] + h * c).value
+        hj[h].out = ptr(o, 1 if rng.random() < 0.3 else 0).value
+    sim.call("rr_helper_reduce_many", AR, dt, op, hj, H, None)
+    for h in range(H):
+        if not c:
+            continue
+        sl = [x[h * c:(h + 1) * c].copy() for x in xs]
+        ref = orc.ar2_helper(dt, op, *sl) if A == 2 else orc.ar4_helper(dt, op, sl)
+        o = houts[h]
+        start = (hj[h].out - o.ctypes.data) // es
+        assert np.array_equal(o[start:start + c].view(np.uint8), ref.view(np.uint8)), (A, H, dt, count, h)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_all_to_all_round_trip(sim, orc, seed):
+    rng = np.random.default_rng(3000 + seed)
+    sim.reset()
+    A = int(rng.choice([2, 4]))
+    H = int(rng.integers(1, 7)) if A == 2 else int(rng.integers(1, 5))
+    nc = (H + 2 if A == 2 else H + 1) + int(rng.integers(0, 4))
+    es = int(rng.choice([2, 4]))
+    dt = BF16 if es == 2 else F32
+    npdt = np.uint16 if es == 2 else np.uint32
+    seg = int(rng.integers(0, 20000))
+    c = orc.geometry(A, H, nc, 0, seg, A2A, dt)["chunk"]
+    src = [rng.integers(0, 2 ** (8 * es), A * seg, dtype=npdt) for _ in range(A)]
+    lead = int(rng.integers(0, 8))
+    sb = [sim.buf(padded(s, lead), writable=False) for s in src]
+    packed = [[sim.buf(np.zeros(max((A - 1) * c, 1) + 8, npdt)) for _ in range(A)] for _ in range(H)]
+    out = [sim.buf(np.full(A * seg + 16, 7, npdt)) for _ in range(A)]
+    keep = []
+    for name, ins, outs_ in (("rr_a2a_pack_many", lambda h: [ptr(b, lead) for b in sb], lambda h: [ptr(p) for p in packed[h]]),
+                             ("rr_a2a_unpack_many", lambda h: [ptr(p) for p in packed[h]], lambda h: [ptr(o, 3) for o in out])):
+        aj = (_rr._A2AJob * H)()
+        for h in range(H):
+            pi, po = parr(*ins(h)), parr(*outs_(h))
+            keep += [pi, po]
+            aj[h].relay, aj[h].helper = _relay(A, H, nc, 0, seg), h
+            aj[h].inp = ctypes.cast(pi, ctypes.POINTER(ctypes.c_void_p))
+            aj[h].out = ctypes.cast(po, ctypes.POINTER(ctypes.c_void_p))
+        sim.call(name, dt, aj, H, None)
+    expect = [np.full(A * seg, 7, npdt) for _ in range(A)]
+    for h in range(H):
+        if c:
+            orc.a2a_unpack(es, A, seg, c, h, orc.a2a_pack(es, A, seg, c, h, src), expect)
+    for d in range(A):
+        assert np.array_equal(out[d][3:3 + A * seg], expect[d]), (A, H, nc, es, seg, d)
