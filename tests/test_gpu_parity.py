@@ -449,3 +449,43 @@ def test_fp32_all_to_all_bits(orc):
         orc.a2a_unpack(4, A, seg, c, h, orc.a2a_pack(4, A, seg, c, h, src), expect)
     for d in range(A):
         assert np.array_equal(wl.out[d].cpu().numpy().view(np.uint32), expect[d])
+
+
+def test_step_captured_in_a_hip_graph_replays_like_eager():
+    """The library enqueues kernels only (no allocation, no memset), so a whole
+    step can be captured in a HIP graph.  Each replay -- with eager work and
+    synchronisations between replays -- must write what the eager step wrote."""
+    say("graph replay")
+    M = 8 * 2 ** 20
+    n = M // 2
+    xs2 = [dev(synth.as_bf16_bits(synth.normal(n, 90, a))) for a in range(2)]
+    xs4 = [dev(synth.as_bf16_bits(synth.normal(n, 91, a))) for a in range(4)]
+    src = [dev(synth.bits16(n, 92, a), None) for a in range(4)]
+    rows = [W.AR2(xs2, BF16, AVG), W.RS4(xs4, BF16, SUM), W.A2A(src, BF16)]
+    outs = lambda: [o for w in rows for o in w.out]
+    main = torch.cuda.current_stream()
+    for o in outs():
+        o.zero_()                          # parts no kernel writes stay zero throughout
+    for w in rows:
+        w.run(main)
+    torch.cuda.synchronize()
+    eager = [synth.to_host(o).copy() for o in outs()]
+    cs = torch.cuda.Stream()
+    cs.wait_stream(main)
+    with torch.cuda.stream(cs):
+        for w in rows:
+            w.run(cs)                      # prepare and warm on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        for w in rows:
+            w.run(cs)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs():
+            o.zero_()                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, o in enumerate(outs()):
+            assert np.array_equal(synth.to_host(o), eager[i]), f"replay {rep} output {i}"
