@@ -489,3 +489,76 @@ def test_step_captured_in_a_hip_graph_replays_like_eager():
         torch.cuda.synchronize()
         for i, o in enumerate(outs()):
             assert np.array_equal(synth.to_host(o), eager[i]), f"replay {rep} output {i}"
+
+
+GUARD = 4096
+SENTINEL = 0x7FA5
+
+
+def _guarded(n, lead):
+    """A bf16 buffer of n elements at offset GUARD+lead inside a sentinel-filled
+    allocation; returns (whole buffer, view)."""
+    big = torch.full((n + 2 * GUARD + 8,), 0, dtype=torch.int16, device="cuda")
+    big.fill_(SENTINEL)
+    v = big[GUARD + lead:GUARD + lead + n]
+    return big, v.view(torch.bfloat16)
+
+
+def _guards_intact(big, n, lead):
+    h = synth.to_host(big)
+    assert np.all(h[:GUARD + lead] == SENTINEL), "write before the output"
+    assert np.all(h[GUARD + lead + n:] == SENTINEL), "write past the output"
+
+
+@pytest.mark.parametrize("lead", [0, 1, 3, 7])
+def test_every_entry_point_writes_only_its_output(orc, lead):
+    say("canaries", lead)
+    # helper reduce (A=4) and active epilogue (A=2)
+    count = 2 ** 20 + 4 * 128 * 7 + 6
+    xs = [synth.as_bf16_bits(synth.normal(count, 95, a)) for a in range(4)]
+    dx = [dev(x) for x in xs]
+    r4 = rr.Relay(4, 4, 0, 500, count)
+    c = rr.rr_geometry(r4, AR, BF16)["chunk"]
+    big, out = _guarded(c, lead)
+    rr.rr_helper_reduce(r4, AR, BF16, AVG, 2, [x[2 * c:3 * c] for x in dx], out)
+    _guards_intact(big, c, lead)
+    check_bf16(synth.to_host(out), orc.ar4_helper(BF16, AVG, [x[2 * c:3 * c].copy() for x in xs]), "guarded helper")
+    r2 = rr.Relay(2, 6, 8, 0, count)
+    g2 = rr.rr_geometry(r2, AR, BF16)
+    big, out = _guarded(count, lead)
+    rr.rr_active_add_scale(r2, AR, BF16, SUM, 1, dx[:2], out)
+    _guards_intact(big, count, lead)
+    ref = orc.ar_active(BF16, SUM, 2, 6, 8, 0, count, 1, xs[:2], np.full(count, SENTINEL, np.uint16))
+    got = synth.to_host(out)
+    assert np.all(got[:g2["direct_off"]] == SENTINEL)
+    check_bf16(got[g2["direct_off"]:], ref[g2["direct_off"]:], "guarded active")
+    # reduce-scatter pass 2 (A=4)
+    R = 8 * 128 * 9 + 40
+    blk = [synth.as_bf16_bits(synth.normal(R, 96, s)) for s in range(4)]
+    rs = rr.Relay(4, 4, 0, 500, R)
+    cr = rr.rr_geometry(rs, RS, BF16)["chunk"]
+    reds = [synth.as_bf16_bits(synth.normal(cr, 97, h)) for h in range(4)]
+    big, out = _guarded(R, lead)
+    rr.rr_rs_multi_reduce(rs, BF16, AVG, 2, 3, [dev(b) for b in blk] + [dev(r) for r in reds], out)
+    _guards_intact(big, R, lead)
+    check_bf16(synth.to_host(out), orc.rs4_pass2(BF16, AVG, 4, 4, 500, R, 3, blk, reds), "guarded pass 2")
+    # all-to-all pack and unpack
+    A, seg = 4, 5 * 128 * 5 + 3
+    ra = rr.Relay(A, 4, 5, 0, seg)
+    ca = rr.rr_geometry(ra, A2A, BF16)["chunk"]
+    src = [synth.bits16(A * seg, 98, s) for s in range(A)]
+    dsts = [_guarded((A - 1) * ca, lead) for _ in range(A)]
+    rr.rr_a2a_pack(ra, BF16, 1, [dev(s, None) for s in src], [d[1] for d in dsts])
+    ref = orc.a2a_pack(2, A, seg, ca, 1, src)
+    for (big, v), r in zip(dsts, ref):
+        _guards_intact(big, (A - 1) * ca, lead)
+        assert np.array_equal(synth.to_host(v).view(np.uint8), r)
+    outs = [_guarded(A * seg, lead) for _ in range(A)]
+    for _, v in outs:
+        v.view(torch.int16).fill_(0)
+    rr.rr_a2a_unpack(ra, BF16, 1, [d[1] for d in dsts], [o[1] for o in outs])
+    expect = [np.zeros(A * seg, np.uint16) for _ in range(A)]
+    orc.a2a_unpack(2, A, seg, ca, 1, ref, expect)
+    for (big, v), e in zip(outs, expect):
+        _guards_intact(big, A * seg, lead)
+        assert np.array_equal(synth.to_host(v), e)
