@@ -345,7 +345,7 @@ def step_bench(args):
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one step of the same workload", file=sys.stderr, flush=True)
         t, b, reps = 0.0, 0, 0
-        while t < 10.0 and reps < 10:
+        while t < 12.0 and reps < 30:
             dt, db = cpu_baseline(inp)
             t, b, reps = t + dt, b + db, reps + 1
         result["cpu_baseline"] = {
