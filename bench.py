@@ -56,6 +56,7 @@ def parse():
     p.add_argument("--sweep", action="store_true", help="per-row sweep instead of the step benchmark")
     p.add_argument("--sweep-sizes", default="2,4,8,16,32,64,128,256,512,1024")
     p.add_argument("--sweep-reps", type=int, default=20)
+    p.add_argument("--sweep-dtypes", default="bf16,f32")
     p.add_argument("--sweep-out", default=None)
     return p.parse_args()
 
@@ -362,67 +363,86 @@ def step_bench(args):
 # --------------------------------------------------------------------------
 
 def sweep(args):
+    """Per-role GB/s over message sizes and dtypes: one batched launch of each
+    role, timed alone with a fence-free HIP event pair, after a 1 GiB overwrite
+    that evicts the inputs from the 256 MB Infinity Cache; best and median of
+    the reps after 3 warm-ups."""
+    import ctypes
+    import zlib
     import torch
     import pack_rr_helper_amd as rr
     from pack_rr_helper_amd import workloads as W
     rr.load()
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    hip = hip_runtime()
+    evs = []
+    for _ in range(2):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        evs.append(e)
+    f = ctypes.c_float()
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")  # > the 256 MB MALL
-    out = open(args.sweep_out, "w") if args.sweep_out else sys.stdout
-    gen = torch.Generator(device="cuda")
-    for mib in [float(v) for v in args.sweep_sizes.split(",")]:
-        M = int(mib * MIB)
-        n = M // 2
-        for row in ("ar2", "rs2", "ar4", "rs4", "a2a"):
-            gen.manual_seed(hash((row, M)) & 0xFFFFFFFF)
-            ranks = 2 if row in ("ar2", "rs2") else 4
-            if row == "a2a":
-                xs = [torch.randint(-32768, 32767, (n,), dtype=torch.int16, device="cuda", generator=gen)
-                      for _ in range(ranks)]
-            else:
-                xs = [torch.randn(n, device="cuda", generator=gen).to(torch.bfloat16) for _ in range(ranks)]
-            wl = {"ar2": lambda: W.AR2(xs, rr.BF16, rr.AVG), "rs2": lambda: W.RS2(xs, rr.BF16, rr.AVG),
-                  "ar4": lambda: W.AR4(xs, rr.BF16, rr.AVG), "rs4": lambda: W.RS4(xs, rr.BF16, rr.SUM),
-                  "a2a": lambda: W.A2A(xs, rr.BF16)}[row]()
-            for role in sorted({c[0] for c in wl.calls(stream)}):
-                cs = [c for c in wl.calls(stream) if c[0] == role]
-                times = []
-                for rep in range(args.sweep_reps + 3):
-                    flush.zero_()
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    cs[0][3]()
-                    e1.record(stream)
-                    torch.cuda.synchronize()
-                    if rep >= 3:
-                        times.append(e0.elapsed_time(e1) * 1e-3)
-                b = cs[0][2]
-                rec = {"message_mib": mib, "row": role, "kernel": cs[0][1], "bytes_per_launch": b,
-                       "us_min": round(min(times) * 1e6, 2), "us_median": round(statistics.median(times) * 1e6, 2),
-                       "gbs_best": round(b / min(times) / 1e9, 1),
-                       "gbs_median": round(b / statistics.median(times) / 1e9, 1),
-                       "pct_peak_median": round(100 * b / statistics.median(times) / 1e9 / PEAK_GBS, 1)}
-                print(json.dumps(rec), file=out, flush=True)
-            del wl, xs
-            torch.cuda.empty_cache()
-        # calibration: a plain device-to-device copy of M bytes through torch
-        a = torch.empty(M, dtype=torch.uint8, device="cuda")
-        bb = torch.empty_like(a)
-        times = []
+
+    def times_of(fn):
+        ts = []
         for rep in range(args.sweep_reps + 3):
             flush.zero_()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            bb.copy_(a)
-            e1.record(stream)
+            hip.hipEventRecord(evs[0], sp)
+            fn()
+            hip.hipEventRecord(evs[1], sp)
             torch.cuda.synchronize()
+            hip.hipEventElapsedTime(ctypes.byref(f), evs[0], evs[1])
             if rep >= 3:
-                times.append(e0.elapsed_time(e1) * 1e-3)
-        print(json.dumps({"message_mib": mib, "row": "torch_copy_calibration", "bytes_per_launch": 2 * M,
-                          "gbs_median": round(2 * M / statistics.median(times) / 1e9, 1)}), file=out, flush=True)
+                ts.append(f.value * 1e-3)
+        return ts
+
+    def record(mib, dt_name, role, kernel, b, ts):
+        return {"message_mib": mib, "dtype": dt_name, "row": role, "kernel": kernel, "bytes_per_launch": b,
+                "reps": len(ts), "us_min": round(min(ts) * 1e6, 2),
+                "us_median": round(statistics.median(ts) * 1e6, 2),
+                "gbs_best": round(b / min(ts) / 1e9, 1),
+                "gbs_median": round(b / statistics.median(ts) / 1e9, 1),
+                "pct_peak_median": round(100 * b / statistics.median(ts) / 1e9 / PEAK_GBS, 1)}
+
+    out = open(args.sweep_out, "w") if args.sweep_out else sys.stdout
+    gen = torch.Generator(device="cuda")
+    dtypes = {"bf16": (rr.BF16, torch.bfloat16, torch.int16), "f32": (rr.F32, torch.float32, torch.int32)}
+    for mib in [float(v) for v in args.sweep_sizes.split(",")]:
+        M = int(mib * MIB)
+        for dt_name in args.sweep_dtypes.split(","):
+            dt, tdt, bits_dt = dtypes[dt_name]
+            n = M // W.ESIZE[dt]
+            for row in ("ar2", "rs2", "ar4", "rs4", "a2a"):
+                gen.manual_seed(zlib.crc32(f"{row}/{dt_name}/{M}".encode()))
+                ranks = 2 if row in ("ar2", "rs2") else 4
+                if row == "a2a":
+                    lim = 1 << (8 * W.ESIZE[dt] - 1)
+                    xs = [torch.randint(-lim, lim - 1, (n,), dtype=bits_dt, device="cuda", generator=gen)
+                          for _ in range(ranks)]
+                else:
+                    xs = [torch.randn(n, device="cuda", generator=gen).to(tdt) for _ in range(ranks)]
+                wl = {"ar2": lambda: W.AR2(xs, dt, rr.AVG), "rs2": lambda: W.RS2(xs, dt, rr.AVG),
+                      "ar4": lambda: W.AR4(xs, dt, rr.AVG), "rs4": lambda: W.RS4(xs, dt, rr.SUM),
+                      "a2a": lambda: W.A2A(xs, dt)}[row]()
+                calls = wl.calls(stream)
+                for role in sorted({c[0] for c in calls}):
+                    role_call = next(c for c in calls if c[0] == role)
+                    rec = record(mib, dt_name, role, role_call[1], role_call[2], times_of(role_call[3]))
+                    print(json.dumps(rec), file=out, flush=True)
+                del wl, xs, calls
+                torch.cuda.empty_cache()
+        # calibration: the runtime's own device-to-device copy of M bytes
+        a = torch.empty(M, dtype=torch.uint8, device="cuda")
+        bb = torch.empty_like(a)
+        rec = record(mib, "u8", "torch_copy_calibration", "hipMemcpyAsync D2D", 2 * M, times_of(lambda: bb.copy_(a)))
+        print(json.dumps(rec), file=out, flush=True)
         del a, bb
         torch.cuda.empty_cache()
+    for e in evs:
+        hip.hipEventDestroy(e)
 
 
 def main():
