@@ -71,6 +71,11 @@ typedef struct {
     int64_t count;
 } rr_relay;
 
+/* Largest accepted count (2^48 elements, far beyond any device memory): every
+ * product the geometry forms (count * elemsize * permille, A*A*chunk, byte
+ * offsets) then stays inside int64_t. */
+#define RR_MAX_COUNT (INT64_C(1) << 48)
+
 /* Geometry of one group, in elements.  The relay region comes first:
  * helper k owns [k*chunk, (k+1)*chunk) of every buffer it relays, so
  * relay_total = H*chunk; the direct region is [direct_off, direct_off +
@@ -112,8 +117,9 @@ const char *rr_last_error(void);
  *     chunks (RR_EINVAL if A*A*chunk exceeds it).
  *   A=4 all-to-all: numChunks >= H+1; chunk = align_down(segmentCount/numChunks, 128);
  *     helper_elems = A*(A-1)*chunk, one chunk per (destination, source) pair.
- * Errors: RR_EINVAL for A not in {2,4}, H < 1, count < 0, numChunks or
- * permille out of range, unknown collective or dtype, null pointers.
+ * Errors: RR_EINVAL for A not in {2,4}, H < 1, count < 0 or above
+ * RR_MAX_COUNT, numChunks or permille out of range, unknown collective or
+ * dtype, null pointers.
  */
 rr_status rr_geometry(const rr_relay *relay, int coll, int dtype, rr_geom *out);
 

@@ -57,6 +57,8 @@ rr_status compute_geometry(const rr_relay *r, int coll, int dtype, rr_geom *g)
         return fail(RR_EINVAL, "H=%d: a relay group needs at least one helper", H);
     if (r->count < 0)
         return fail(RR_EINVAL, "count=%lld is negative", (long long)r->count);
+    if (r->count > RR_MAX_COUNT)
+        return fail(RR_EINVAL, "count=%lld exceeds RR_MAX_COUNT (2^48 elements)", (long long)r->count);
     if (coll < RR_ALLREDUCE || coll > RR_ALLTOALL)
         return fail(RR_EINVAL, "unknown collective %d", coll);
     if (dtype != RR_F32 && dtype != RR_BF16)
@@ -687,8 +689,10 @@ int64_t rr_passthrough_helper_size(int64_t count_g, int32_t A, int32_t num_chunk
 {
     if (count_g < 0 || A < 1 || num_chunks < 1)
         return -1;
-    const int64_t slots = int64_t(A) * align_down_128(count_g / num_chunks);
-    return std::min(count_g, slots);
+    // min(count_g, A * per_slot) without forming a product that can overflow:
+    // A * per_slot > count_g exactly when per_slot > floor(count_g / A)
+    const int64_t per_slot = align_down_128(count_g / num_chunks);
+    return per_slot > count_g / A ? count_g : int64_t(A) * per_slot;
 }
 
 rr_status rr_helper_reduce(const rr_relay *relay, int coll, int dtype, int op, int helper,

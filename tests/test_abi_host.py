@@ -88,6 +88,11 @@ def test_passthrough_size_matches_the_oracle(L, orc):
         for A, nc in ((2, 7), (4, 5), (2, 8), (8, 2)):
             assert rr.rr_passthrough_helper_size(t, A, nc) == orc.passthrough_helper_size(t, A, nc)
     assert L.rr_passthrough_helper_size(-1, 2, 7) == -1
+    # near the int64 limit the size is still exact (no overflowing product)
+    big = 2 ** 63 - 1
+    for A, nc in ((2, 7), (8, 2), (2 ** 31 - 1, 1), (4, 5)):
+        per_slot = (big // nc) // 128 * 128
+        assert L.rr_passthrough_helper_size(big, A, nc) == min(big, A * per_slot)
 
 
 @pytest.mark.parametrize("A,H,nc,pm,count,coll,dt", [
@@ -95,6 +100,8 @@ def test_passthrough_size_matches_the_oracle(L, orc):
     (4, 4, 4, 0, 4096, A2A, BF16), (4, 4, 0, 0, 4096, AR, BF16), (4, 4, 0, 1001, 4096, RS, BF16),
     (2, 6, 8, 0, -1, AR, BF16), (2, 6, 8, 0, 4096, 3, BF16), (2, 6, 8, 0, 4096, AR, 2),
     (4, 4, 0, 600, 2 ** 22, RS, BF16),
+    (2, 6, 8, 0, 2 ** 48 + 1, AR, BF16), (4, 4, 0, 1000, 2 ** 62, AR, F32),
+    (4, 4, 5, 0, 2 ** 63 - 1, A2A, F32),
 ])
 def test_geometry_rejections(L, A, H, nc, pm, count, coll, dt):
     g = rr._Geom()
