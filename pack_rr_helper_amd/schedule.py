@@ -22,16 +22,17 @@ paragraph; layouts as in include/rr.h):
 * ``a4_allreduce``: offload ``permille`` of the buffer through the helpers
   (4 -> 1 at the helper, broadcast back), the rest reduce-scattered then
   all-gathered over the intra-group links.
-* ``a4_reduce_scatter``: flat reduce-at-helper; the helper scratch holds one
-  chunk per (owner, source) pair; the direct region is split over the two
-  groups.
+* ``a4_reduce_scatter``: flat reduce-at-helper; the helper scratch keeps a
+  separate chunk for every owner and every source other than that owner; the
+  direct region travels half in each of the two groups.
 * ``a2_allreduce_small``: the small-message path of summary section 3 -- one
   full exchange of the buffer (or, for comparison, a reduce-scatter swap then
   an all-gather swap), then the add + scale over the whole buffer.
 * ``a4_all_gather``: summary section 5 -- two balanced groups: offload chunks
-  go to the helpers in group 1 and are forwarded to the other actives in
-  group 2, whose cross links therefore carry A-1 times group 1's; the direct
-  region is split 1:(A-1) over the two groups to balance them.
+  reach the helpers in the first group and every other active in the second,
+  so each cross link moves A-1 times more in the second group; sending one
+  part of the direct region in the first group for every A-1 parts in the
+  second evens the groups out.
 * ``a4_all_to_all``: helper offload with per-destination coalescing; the
   gather (pack) and scatter (unpack) kernels stand in for the source->helper
   and helper->destination hops (the one-GPU collapse: the pack reads the

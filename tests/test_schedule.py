@@ -168,8 +168,10 @@ def test_small_message_single_exchange_beats_rs_plus_ag():
 
 
 def test_a4_all_gather_two_balanced_groups():
-    """Summary section 5: group 2's cross links carry A-1 times group 1's; the
-    1:(A-1) direct split balances both groups, halving the pure-direct time."""
+    """Summary section 5: forwarding offload chunks in the second group loads
+    each cross link A-1 times as heavily as the first group does; giving the
+    second group A-1 parts of the direct region for every part sent in the
+    first evens the two groups out at half the pure-direct time."""
     S_ = 8 * 128 * 400
     s = S.a4_all_gather(S_)
     g1, g2 = s.link_groups()
