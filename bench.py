@@ -30,6 +30,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import statistics
 import sys
 import time
@@ -164,10 +165,16 @@ def cpu_baseline(inp):
 # --------------------------------------------------------------------------
 
 def kernel_source_digest():
+    """Digest of the kernel code the counters were taken on: the kernel source
+    and its tiling header with comments and white space removed, so that only
+    a change to the code itself invalidates the stored traffic."""
     h = hashlib.sha256()
     for f in ("rr_kernels.hip", "rr_internal.h"):
-        with open(os.path.join(ROOT, "pack_rr_helper_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "pack_rr_helper_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -415,22 +422,26 @@ def sweep(args):
         for dt_name in args.sweep_dtypes.split(","):
             dt, tdt, bits_dt = dtypes[dt_name]
             n = M // W.ESIZE[dt]
-            for row in ("ar2", "rs2", "ar4", "rs4", "a2a"):
+            for row in ("ar2", "rs2", "ar4", "rs4", "a2a", "a2a_ragged"):
                 gen.manual_seed(zlib.crc32(f"{row}/{dt_name}/{M}".encode()))
                 ranks = 2 if row in ("ar2", "rs2") else 4
-                if row == "a2a":
+                if row.startswith("a2a"):
+                    # ragged: segmentCount = 5 mod 8, so odd destinations' chunks sit at
+                    # byte offsets that disagree with the packed buffer modulo 16
+                    nr = n if row == "a2a" else 4 * (n // 4 - 3)
                     lim = 1 << (8 * W.ESIZE[dt] - 1)
-                    xs = [torch.randint(-lim, lim - 1, (n,), dtype=bits_dt, device="cuda", generator=gen)
+                    xs = [torch.randint(-lim, lim - 1, (nr,), dtype=bits_dt, device="cuda", generator=gen)
                           for _ in range(ranks)]
                 else:
                     xs = [torch.randn(n, device="cuda", generator=gen).to(tdt) for _ in range(ranks)]
                 wl = {"ar2": lambda: W.AR2(xs, dt, rr.AVG), "rs2": lambda: W.RS2(xs, dt, rr.AVG),
                       "ar4": lambda: W.AR4(xs, dt, rr.AVG), "rs4": lambda: W.RS4(xs, dt, rr.SUM),
-                      "a2a": lambda: W.A2A(xs, dt)}[row]()
+                      "a2a": lambda: W.A2A(xs, dt), "a2a_ragged": lambda: W.A2A(xs, dt)}[row]()
                 calls = wl.calls(stream)
                 for role in sorted({c[0] for c in calls}):
                     role_call = next(c for c in calls if c[0] == role)
-                    rec = record(mib, dt_name, role, role_call[1], role_call[2], times_of(role_call[3]))
+                    name = role + ("_ragged" if row == "a2a_ragged" else "")
+                    rec = record(mib, dt_name, name, role_call[1], role_call[2], times_of(role_call[3]))
                     print(json.dumps(rec), file=out, flush=True)
                 del wl, xs, calls
                 torch.cuda.empty_cache()

@@ -245,6 +245,11 @@ __device__ __forceinline__ u32x4 realign(u32x4 a, u32x4 b, unsigned r)
     return o;
 }
 
+// Output vector v is bytes [shift + 16v, shift + 16v + 16) of the aligned
+// source, i.e. the tail of source word v and the head of word v+1.  Word v+1
+// of the last vector always holds at least one byte of this move (shift > 0),
+// and an aligned 16-byte word never straddles a page, so the read stays in
+// mapped memory even where the source buffer ends inside that word.
 template <int Q>
 __device__ __forceinline__ void copy_shifted(const CopySeg &sg, int64_t lt)
 {
