@@ -43,7 +43,11 @@ constexpr int64_t kMaxTilesPerLaunch = int64_t(1) << 22;
 constexpr int kUnroll = RR_UNROLL;
 constexpr int kScalarPerThread = 4;  // elements per thread in a scalar tile
 constexpr int kCopyUnroll = RR_COPY_UNROLL;
-constexpr int kShiftUnroll = 4;      // realigned copies hold two words per vector
+#ifndef RR_SHIFT_UNROLL
+#define RR_SHIFT_UNROLL 2            // 16-byte vectors per thread in a realigning copy tile
+                                     // (8 KiB tiles; measured faster than 16 and 32 KiB)
+#endif
+constexpr int kShiftUnroll = RR_SHIFT_UNROLL;
 constexpr int kCopyBytesPerThread = 16;
 
 // One reduction segment: out[i] = RND(scale * fold_k in[k][i]) for i < n.

@@ -8,8 +8,10 @@
 // them in flight per input before any arithmetic, non-temporal hints on data
 // that is touched exactly once, fp32 accumulation in registers, and one
 // packed bf16 conversion (v_cvt_pk_bf16_f32, round-to-nearest-even) per pair
-// of outputs.  No LDS: nothing is reused, and the copy engine realigns
-// strided sources in registers with v_alignbyte instead of staging them.
+// of outputs.  No LDS allocation: nothing is reused, and the copy engine
+// realigns strided sources in registers (v_alignbyte), taking each lane's
+// neighbouring source word from the next lane (ds_bpermute) instead of
+// loading it a second time or staging the tile.
 //
 // Tiling: one workgroup of 256 threads processes one tile of one segment; a
 // launch's segment table lives in the kernel arguments and a workgroup finds
@@ -234,6 +236,20 @@ __device__ __forceinline__ void copy_aligned(const CopySeg &sg, int64_t lt)
     }
 }
 
+constexpr int kWave = 64;  // gfx950 runs wave64
+
+// The 16-byte vector held by the next lane of this wave (ds_bpermute).  Call
+// it outside any lane-dependent branch: a lane reading from a lane that is
+// switched off gets no data.  The last lane receives its own value.
+__device__ __forceinline__ u32x4 next_lane(u32x4 x)
+{
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = (unsigned)__shfl_down((int)x[j], 1, kWave);
+    return o;
+}
+
 template <int Q>
 __device__ __forceinline__ u32x4 realign(u32x4 a, u32x4 b, unsigned r)
 {
@@ -246,35 +262,53 @@ __device__ __forceinline__ u32x4 realign(u32x4 a, u32x4 b, unsigned r)
 }
 
 // Output vector v is bytes [shift + 16v, shift + 16v + 16) of the aligned
-// source, i.e. the tail of source word v and the head of word v+1.  Word v+1
-// of the last vector always holds at least one byte of this move (shift > 0),
-// and an aligned 16-byte word never straddles a page, so the read stays in
-// mapped memory even where the source buffer ends inside that word.
+// source: the tail of source word v and the head of word v+1.  Each lane
+// loads its own word once (non-temporal) and takes word v+1 from the next
+// lane of its wave; the wave's last lane, whose neighbour word belongs to
+// another wave or tile, loads word v+1 itself, issued with the other loads.
+// In a partial tile a lane also loads word nv, which its left neighbour
+// needs, and stores nothing.  Word nv always holds at least one byte of this
+// move (shift > 0), and an aligned 16-byte word never straddles a page, so
+// that read stays in mapped memory even where the source buffer ends inside
+// the word.
 template <int Q>
 __device__ __forceinline__ void copy_shifted(const CopySeg &sg, int64_t lt)
 {
     constexpr int64_t kTileVecs = int64_t(kBlock) * kShiftUnroll;
     const int64_t nv = sg.nbytes / 16;
-    const int64_t vbase = lt * kTileVecs + threadIdx.x;
     const unsigned r = (unsigned)(sg.shift & 3);
     const u32x4 *src = reinterpret_cast<const u32x4 *>(sg.src);
     u32x4 *dst = reinterpret_cast<u32x4 *>(sg.dst);
+    const bool wave_end = (threadIdx.x & (kWave - 1)) == kWave - 1;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    u32x4 a[kShiftUnroll], c[kShiftUnroll];
     if ((lt + 1) * kTileVecs <= nv) {
-        u32x4 a[kShiftUnroll], b[kShiftUnroll];
 #pragma unroll
         for (int u = 0; u < kShiftUnroll; ++u) {
-            a[u] = src[vbase + u * kBlock];
-            b[u] = src[vbase + u * kBlock + 1];
+            const int64_t v = vec_index<kShiftUnroll>(lt, u);
+            a[u] = ld16(src + v);
+            c[u] = wave_end ? ld16(src + v + 1) : zero;
         }
 #pragma unroll
-        for (int u = 0; u < kShiftUnroll; ++u)
-            st16(dst + vbase + u * kBlock, realign<Q>(a[u], b[u], r));
-    } else {
         for (int u = 0; u < kShiftUnroll; ++u) {
-            const int64_t v = vbase + (int64_t)u * kBlock;
-            if (v >= nv)
-                break;
-            st16(dst + v, realign<Q>(src[v], src[v + 1], r));
+            const u32x4 nb = next_lane(a[u]);  // on every lane: the source lane must be active
+            const u32x4 b = wave_end ? c[u] : nb;
+            st16(dst + vec_index<kShiftUnroll>(lt, u), realign<Q>(a[u], b, r));
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kShiftUnroll; ++u) {
+            const int64_t v = vec_index<kShiftUnroll>(lt, u);
+            a[u] = v <= nv ? ld16(src + v) : zero;
+            c[u] = wave_end && v < nv ? ld16(src + v + 1) : zero;
+        }
+#pragma unroll
+        for (int u = 0; u < kShiftUnroll; ++u) {
+            const int64_t v = vec_index<kShiftUnroll>(lt, u);
+            const u32x4 nb = next_lane(a[u]);
+            const u32x4 b = wave_end ? c[u] : nb;
+            if (v < nv)
+                st16(dst + v, realign<Q>(a[u], b, r));
         }
     }
 }

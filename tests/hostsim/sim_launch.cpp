@@ -200,14 +200,24 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
                     for (int e = 0; e < 16; ++e)
                         copy_byte(sg.src, sg.dst, v * 16 + e);
                 } else {
-                    // words v and v+1 of the aligned source are loaded whole
+                    // each lane loads aligned word v whole; the wave's last lane
+                    // also loads word v+1 (the others take it from the next lane)
+                    const bool wave_end = x % 64 == 63;
                     if (!touches(uintptr_t(sg.src) + uintptr_t(v * 16), 16) ||
-                        !touches(uintptr_t(sg.src) + uintptr_t((v + 1) * 16), 16))
+                        (wave_end && !touches(uintptr_t(sg.src) + uintptr_t((v + 1) * 16), 16)))
                         violation("realigned word outside every buffer", uintptr_t(sg.src) + v * 16, 32);
                     for (int e = 0; e < 16; ++e)
                         copy_byte(sg.src + sg.shift, sg.dst, v * 16 + e);
                 }
             }
+        if (sg.mode == kCopyShifted && !full)
+            // a partial tile's lanes also load word nv for their left neighbour
+            for (int x = 0; x < kBlock; ++x)
+                for (int u = 0; u < unroll; ++u) {
+                    const int64_t v = lt * tv + x + int64_t(u) * kBlock;
+                    if (v == nv && !touches(uintptr_t(sg.src) + uintptr_t(v * 16), 16))
+                        violation("realigned word outside every buffer", uintptr_t(sg.src) + v * 16, 16);
+                }
     }
     return hipSuccess;
 }

@@ -451,6 +451,47 @@ def test_fp32_all_to_all_bits(orc):
         assert np.array_equal(wl.out[d].cpu().numpy().view(np.uint32), expect[d])
 
 
+def _ragged_a2a_case(orc, es, seg, seed):
+    """Pack and unpack of every helper slice for a segmentCount off the 16-byte
+    grid, compared bit for bit with the oracle; returns the chunk size."""
+    A = 4
+    npdt, sdt = (np.uint16, np.int16) if es == 2 else (np.uint32, np.int32)
+    src = [synth.rng(seed, s).integers(0, 1 << (8 * es), A * seg, dtype=npdt) for s in range(A)]
+    wl = W.A2A([torch.from_numpy(s.view(sdt)).cuda() for s in src], BF16 if es == 2 else F32)
+    c = wl.g["chunk"]
+    wl.run()
+    torch.cuda.synchronize()
+    expect = [np.zeros(A * seg, npdt) for _ in range(A)]
+    for h in range(4):
+        ref = orc.a2a_pack(es, A, seg, c, h, src)
+        for d in range(A):
+            got = wl.packed[h][d].cpu().numpy()[:(A - 1) * c].view(np.uint8)
+            assert np.array_equal(got, ref[d]), ("pack", es, seg, h, d)
+        orc.a2a_unpack(es, A, seg, c, h, ref, expect)
+    for d in range(A):
+        assert np.array_equal(wl.out[d].cpu().numpy().view(npdt), expect[d]), ("unpack", es, seg, d)
+    return c
+
+
+@pytest.mark.parametrize("es,seg", [(2, 5 * 128 * 400 + r) for r in (1, 3, 5, 7)]
+                         + [(4, 5 * 128 * 300 + r) for r in (1, 2, 3)])
+def test_ragged_all_to_all_spans_full_realign_tiles(orc, es, seg):
+    """Every shift residue of the source against the packed buffer, with chunks
+    long enough for several full realigning tiles (each lane's neighbour
+    exchange and the wave-end lanes' own loads) and a partial tail tile."""
+    say("ragged a2a", es, seg)
+    c = _ragged_a2a_case(orc, es, seg, 120 + seg % 8)
+    assert c * es // 16 > 4 * 1024   # more than four realigning tiles of 1024 vectors or fewer
+
+
+def test_ragged_all_to_all_at_64MiB(orc):
+    """The 64 MiB per-rank message with segmentCount = 5 (mod 8): 9 of every
+    helper's 12 chunk moves are realigned."""
+    seg = (64 << 20) // 2 // 4 - 3
+    say("ragged a2a 64 MiB", seg)
+    _ragged_a2a_case(orc, 2, seg, 131)
+
+
 def test_step_captured_in_a_hip_graph_replays_like_eager():
     """The library enqueues kernels only (no allocation, no memset), so a whole
     step can be captured in a HIP graph.  Each replay -- with eager work and
