@@ -2,8 +2,8 @@
 
 The library links only the HIP runtime: no torch, no Python.  Device code is
 compiled for gfx950 with FMA contraction off (the reductions add and then
-scale, each rounded once, in a fixed order), fp32 denormals kept, and packed
-fp32 instructions disabled.
+scale, each rounded once, in a fixed order), fp32 denormals kept, packed fp32
+instructions disabled, and scalar kernel arguments preloaded into registers.
 """
 import os
 import subprocess
@@ -23,6 +23,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # scalar kernel arguments (the single-segment reduction's pointers, length
+    # and scale) arrive preloaded in SGPRs instead of through scalar loads
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]

@@ -667,6 +667,44 @@ rr_status job_error(int j, rr_status st)
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Launch forms (declared in rr_internal.h)
+// ---------------------------------------------------------------------------
+
+namespace rr {
+
+namespace {
+
+// Uniform when every segment of the batch spans the same number of tiles.
+template <typename Batch>
+LaunchShape uniform_or_table(const Batch &b, int64_t total_tiles)
+{
+    const int n = b.nseg;
+    const int64_t first = n > 1 ? int64_t(b.tile0[1]) - b.tile0[0] : total_tiles;
+    for (int s = 1; s < n; ++s) {
+        const int64_t end = s + 1 < n ? int64_t(b.tile0[s + 1]) : total_tiles;
+        if (end - b.tile0[s] != first)
+            return LaunchShape{kFormTable, total_tiles, 1};
+    }
+    return LaunchShape{kFormUniform, first, n};
+}
+
+}  // namespace
+
+LaunchShape reduce_shape(const RedBatch &b, int64_t total_tiles)
+{
+    if (b.nseg == 1 && b.seg[0].vec && b.seg[0].k >= 1 && b.seg[0].k <= kMaxIn)
+        return LaunchShape{kFormOne, total_tiles, 1};
+    return uniform_or_table(b, total_tiles);
+}
+
+LaunchShape copy_shape(const CopyBatch &b, int64_t total_tiles)
+{
+    return uniform_or_table(b, total_tiles);
+}
+
+}  // namespace rr
+
 // ===========================================================================
 // Exported entry points
 // ===========================================================================

@@ -64,6 +64,8 @@ struct RedSeg {
     int32_t pad;
 };
 
+static_assert(sizeof(RedSeg) == 64, "a reduction descriptor is one 64-byte scalar load");
+
 struct RedBatch {
     int32_t tile0[kMaxRedSegs];  // first tile of each segment within this launch
     int32_t nseg;
@@ -86,6 +88,8 @@ struct CopySeg {
     int32_t shift;
 };
 
+static_assert(sizeof(CopySeg) == 32, "a copy descriptor is one 32-byte scalar load");
+
 struct CopyBatch {
     int32_t tile0[kMaxCopySegs];
     int32_t nseg;
@@ -96,6 +100,25 @@ struct CopyBatch {
 // Work per tile (one workgroup), matching the kernels' tiling.
 int64_t red_tile_elems(bool vec, bool bf16);
 int64_t copy_tile_bytes(int32_t mode);
+
+// How a batch is launched.  Every form runs the same work per tile; they
+// differ in how a workgroup learns its segment before its first load:
+//   kFormTable:   1-D grid of all tiles; a count over tile0 finds the
+//                 segment, then its descriptor is loaded (dependent scalar
+//                 loads from the kernel arguments);
+//   kFormUniform: every segment has gx tiles: 2-D grid (gx, nseg), the
+//                 segment is blockIdx.y and the tile blockIdx.x;
+//   kFormOne:     one 16-byte aligned reduction segment: 1-D grid of gx
+//                 tiles, the descriptor passed as scalar kernel arguments
+//                 that the hardware preloads into registers.
+enum LaunchForm : int32_t { kFormTable = 0, kFormUniform = 1, kFormOne = 2 };
+struct LaunchShape {
+    int32_t form;
+    int64_t gx, gy;
+};
+// Host-side choice of the form for a filled batch (rr_api.cpp).
+LaunchShape reduce_shape(const RedBatch &b, int64_t total_tiles);
+LaunchShape copy_shape(const CopyBatch &b, int64_t total_tiles);
 
 // Enqueue one launch; the batch's tile0/nseg must be filled and the total
 // tile count must not exceed kMaxTilesPerLaunch.  Returns the HIP status.

@@ -94,6 +94,17 @@ __device__ __forceinline__ int find_seg(const int32_t (&tile0)[MAXS], int nseg, 
     return s;
 }
 
+// A segment descriptor read as one vector, so it arrives in a single scalar
+// load (s_load_dwordx16 / x8) before the workgroup branches on its fields;
+// read field by field, the loads are issued one dependent round at a time.
+template <typename Seg>
+__device__ __forceinline__ Seg load_seg(const Seg &p)
+{
+    constexpr int kWords = (int)(sizeof(Seg) / 4);
+    typedef int32_t words __attribute__((ext_vector_type(kWords), aligned(4)));
+    return __builtin_bit_cast(Seg, *reinterpret_cast<const words *>(&p));
+}
+
 // ---------------------------------------------------------------------------
 // Reduction
 // ---------------------------------------------------------------------------
@@ -174,18 +185,18 @@ __device__ __forceinline__ void reduce_scalar(const RedSeg &sg, int64_t lt)
         if (i >= sg.n)
             return;
         float acc = load_elem<BF16>(sg.in[0], i);
-        for (int k = 1; k < sg.k; ++k)
-            acc = acc + load_elem<BF16>(sg.in[k], i);
+#pragma unroll
+        for (int k = 1; k < kMaxIn; ++k)  // static indices keep the descriptor in registers
+            if (k < sg.k)
+                acc = acc + load_elem<BF16>(sg.in[k], i);
         store_elem<BF16>(sg.out, i, acc * sg.scale);
     }
 }
 
+// Tile lt of one segment.
 template <bool BF16>
-__device__ __forceinline__ void reduce_tile(const RedBatch &b, int32_t t)
+__device__ __forceinline__ void reduce_seg(const RedSeg &sg, int64_t lt)
 {
-    const int s = find_seg(b.tile0, b.nseg, t);
-    const RedSeg &sg = b.seg[s];
-    const int64_t lt = (int64_t)(t - b.tile0[s]);
     if (sg.vec) {
         switch (sg.k) {
         case 1: reduce_vec<BF16, 1>(sg, lt); break;
@@ -199,13 +210,47 @@ __device__ __forceinline__ void reduce_tile(const RedBatch &b, int32_t t)
     }
 }
 
-// One workgroup per tile.  Workgroups reach the eight XCDs round-robin, so
-// neighbouring tiles stream through different XCDs; this interleave measured
-// faster than giving each XCD a contiguous range of tiles.
+// One workgroup per tile in every launch form.  Workgroups reach the eight
+// XCDs round-robin, so neighbouring tiles stream through different XCDs; this
+// interleave measured faster than giving each XCD a contiguous range of tiles.
+
+// Table form: tile t of the whole batch.
 template <bool BF16>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(RedBatch b)
 {
-    reduce_tile<BF16>(b, (int32_t)blockIdx.x);
+    const int32_t t = (int32_t)blockIdx.x;
+    const int s = find_seg(b.tile0, b.nseg, t);
+    reduce_seg<BF16>(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
+}
+
+// Uniform form: segment blockIdx.y, tile blockIdx.x (every segment has
+// gridDim.x tiles), so no table is searched.
+template <bool BF16>
+__global__ __launch_bounds__(kBlock) void reduce_uniform_kernel(RedBatch b)
+{
+    reduce_seg<BF16>(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
+}
+
+// Single-segment form: the aligned segment's pointers, length and scale are
+// plain arguments, preloaded into scalar registers at wave launch, and K is
+// a template parameter, so the first vector load issues at once.
+template <bool BF16, int K>
+__global__ __launch_bounds__(kBlock) void reduce_one_kernel(const void *in0, const void *in1,
+                                                            const void *in2, const void *in3,
+                                                            void *out, int64_t n, float scale)
+{
+    RedSeg sg;
+    sg.in[0] = in0;
+    sg.in[1] = in1;
+    sg.in[2] = in2;
+    sg.in[3] = in3;
+    sg.out = out;
+    sg.n = n;
+    sg.k = K;
+    sg.vec = 1;
+    sg.scale = scale;
+    sg.pad = 0;
+    reduce_vec<BF16, K>(sg, (int64_t)blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -325,11 +370,8 @@ __device__ __forceinline__ void copy_bytes(const CopySeg &sg, int64_t lt)
 }
 
 // Aligned bodies and byte heads/tails.
-__device__ __forceinline__ void copy_tile(const CopyBatch &b, int32_t t)
+__device__ __forceinline__ void copy_seg(const CopySeg &sg, int64_t lt)
 {
-    const int s = find_seg(b.tile0, b.nseg, t);
-    const CopySeg &sg = b.seg[s];
-    const int64_t lt = (int64_t)(t - b.tile0[s]);
     if (sg.mode == kCopyAligned)
         copy_aligned(sg, lt);
     else
@@ -338,16 +380,20 @@ __device__ __forceinline__ void copy_tile(const CopyBatch &b, int32_t t)
 
 __global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch b)
 {
-    copy_tile(b, (int32_t)blockIdx.x);
+    const int32_t t = (int32_t)blockIdx.x;
+    const int s = find_seg(b.tile0, b.nseg, t);
+    copy_seg(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
+}
+
+__global__ __launch_bounds__(kBlock) void copy_uniform_kernel(CopyBatch b)
+{
+    copy_seg(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
 }
 
 // Realigned bodies (source and destination disagree modulo 16 bytes); a
 // kernel of its own so its register budget does not limit the aligned path.
-__device__ __forceinline__ void copy_shifted_tile(const CopyBatch &b, int32_t t)
+__device__ __forceinline__ void copy_shifted_seg(const CopySeg &sg, int64_t lt)
 {
-    const int s = find_seg(b.tile0, b.nseg, t);
-    const CopySeg &sg = b.seg[s];
-    const int64_t lt = (int64_t)(t - b.tile0[s]);
     switch (sg.shift >> 2) {
     case 0: copy_shifted<0>(sg, lt); break;
     case 1: copy_shifted<1>(sg, lt); break;
@@ -358,7 +404,14 @@ __device__ __forceinline__ void copy_shifted_tile(const CopyBatch &b, int32_t t)
 
 __global__ __launch_bounds__(kBlock) void copy_shifted_kernel(CopyBatch b)
 {
-    copy_shifted_tile(b, (int32_t)blockIdx.x);
+    const int32_t t = (int32_t)blockIdx.x;
+    const int s = find_seg(b.tile0, b.nseg, t);
+    copy_shifted_seg(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
+}
+
+__global__ __launch_bounds__(kBlock) void copy_shifted_uniform_kernel(CopyBatch b)
+{
+    copy_shifted_seg(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
 }
 
 }  // namespace
@@ -375,15 +428,59 @@ int64_t copy_tile_bytes(int32_t mode)
     return int64_t(kBlock) * (mode == kCopyShifted ? kShiftUnroll : kCopyUnroll) * 16;
 }
 
+namespace {
+
+template <bool BF16>
+void launch_one(const RedSeg &sg, int64_t tiles, hipStream_t stream)
+{
+    const dim3 grid((unsigned)tiles), block(kBlock);
+    switch (sg.k) {
+    case 1:
+        reduce_one_kernel<BF16, 1><<<grid, block, 0, stream>>>(sg.in[0], sg.in[1], sg.in[2], sg.in[3],
+                                                               sg.out, sg.n, sg.scale);
+        break;
+    case 2:
+        reduce_one_kernel<BF16, 2><<<grid, block, 0, stream>>>(sg.in[0], sg.in[1], sg.in[2], sg.in[3],
+                                                               sg.out, sg.n, sg.scale);
+        break;
+    case 3:
+        reduce_one_kernel<BF16, 3><<<grid, block, 0, stream>>>(sg.in[0], sg.in[1], sg.in[2], sg.in[3],
+                                                               sg.out, sg.n, sg.scale);
+        break;
+    default:
+        reduce_one_kernel<BF16, 4><<<grid, block, 0, stream>>>(sg.in[0], sg.in[1], sg.in[2], sg.in[3],
+                                                               sg.out, sg.n, sg.scale);
+        break;
+    }
+}
+
+}  // namespace
+
 hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, hipStream_t stream)
 {
     if (total_tiles <= 0)
         return hipSuccess;
     (void)hipGetLastError();  // report this launch's status only
-    if (b.bf16)
-        reduce_kernel<true><<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
-    else
-        reduce_kernel<false><<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
+    const LaunchShape sh = reduce_shape(b, total_tiles);
+    const dim3 block(kBlock);
+    if (sh.form == kFormOne) {
+        if (b.bf16)
+            launch_one<true>(b.seg[0], sh.gx, stream);
+        else
+            launch_one<false>(b.seg[0], sh.gx, stream);
+    } else if (sh.form == kFormUniform) {
+        const dim3 grid((unsigned)sh.gx, (unsigned)sh.gy);
+        if (b.bf16)
+            reduce_uniform_kernel<true><<<grid, block, 0, stream>>>(b);
+        else
+            reduce_uniform_kernel<false><<<grid, block, 0, stream>>>(b);
+    } else {
+        const dim3 grid((unsigned)total_tiles);
+        if (b.bf16)
+            reduce_kernel<true><<<grid, block, 0, stream>>>(b);
+        else
+            reduce_kernel<false><<<grid, block, 0, stream>>>(b);
+    }
     return hipGetLastError();
 }
 
@@ -392,10 +489,21 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
     if (total_tiles <= 0)
         return hipSuccess;
     (void)hipGetLastError();  // report this launch's status only
-    if (shifted)
-        copy_shifted_kernel<<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
-    else
-        copy_kernel<<<dim3((unsigned)total_tiles), dim3(kBlock), 0, stream>>>(b);
+    const LaunchShape sh = copy_shape(b, total_tiles);
+    const dim3 block(kBlock);
+    if (sh.form == kFormUniform) {
+        const dim3 grid((unsigned)sh.gx, (unsigned)sh.gy);
+        if (shifted)
+            copy_shifted_uniform_kernel<<<grid, block, 0, stream>>>(b);
+        else
+            copy_uniform_kernel<<<grid, block, 0, stream>>>(b);
+    } else {
+        const dim3 grid((unsigned)total_tiles);
+        if (shifted)
+            copy_shifted_kernel<<<grid, block, 0, stream>>>(b);
+        else
+            copy_kernel<<<grid, block, 0, stream>>>(b);
+    }
     return hipGetLastError();
 }
 

@@ -12,6 +12,8 @@ ROOT = os.path.dirname(os.path.dirname(HERE))
 LIB = os.path.join(HERE, "libhostsim.so")
 SOURCES = [os.path.join(HERE, "sim_launch.cpp"),
            os.path.join(ROOT, "pack_rr_helper_amd", "csrc", "rr_api.cpp")]
+HEADERS = [os.path.join(ROOT, "pack_rr_helper_amd", "csrc", "rr_internal.h"),
+           os.path.join(ROOT, "include", "rr.h")]
 
 
 def build():
@@ -26,7 +28,8 @@ def build():
 
 class Sim:
     def __init__(self):
-        if not os.path.exists(LIB) or any(os.path.getmtime(s) > os.path.getmtime(LIB) for s in SOURCES):
+        if not os.path.exists(LIB) or any(os.path.getmtime(s) > os.path.getmtime(LIB)
+                                          for s in SOURCES + HEADERS):
             build()
         self.L = ctypes.CDLL(LIB)
         self.L.sim_message.restype = ctypes.c_char_p

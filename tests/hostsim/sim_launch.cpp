@@ -11,6 +11,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <utility>
 #include <vector>
 
 #include "rr_internal.h"
@@ -43,6 +44,8 @@ bool touches(uintptr_t a, int64_t n)
             return true;
     return false;
 }
+
+long g_forms[2][3];  // launches per (copy?, launch form)
 
 void violation(const char *what, uintptr_t a, int64_t n)
 {
@@ -113,6 +116,40 @@ int find_seg(const int32_t (&tile0)[MAXS], int nseg, int32_t t)
     return s;
 }
 
+// The (segment, tile) pairs that the workgroups of a launch process, in the
+// launch form the library chose: the table form walks the batch's tiles, the
+// uniform form its (tile, segment) grid, the single-segment form segment 0.
+// Flags a form whose grid would not cover every tile of the batch exactly once.
+template <typename Batch>
+std::vector<std::pair<int, int64_t>> tiles_of(const Batch &b, int64_t total, const rr::LaunchShape &sh)
+{
+    std::vector<std::pair<int, int64_t>> out;
+    auto tiles = [&](int s) { return (s + 1 < b.nseg ? int64_t(b.tile0[s + 1]) : total) - b.tile0[s]; };
+    if (sh.form == rr::kFormUniform) {
+        if (sh.gy != b.nseg)
+            violation("uniform grid height differs from the segment count", 0, sh.gy);
+        for (int y = 0; y < sh.gy && y < b.nseg; ++y) {
+            if (tiles(y) != sh.gx)
+                violation("uniform grid width differs from a segment's tile count", 0, tiles(y));
+            for (int64_t x = 0; x < sh.gx; ++x)
+                out.emplace_back(y, x);
+        }
+    } else if (sh.form == rr::kFormOne) {
+        if (b.nseg != 1 || sh.gx != total || sh.gy != 1)
+            violation("single-segment grid for a batch it does not cover", 0, b.nseg);
+        for (int64_t x = 0; x < sh.gx; ++x)
+            out.emplace_back(0, x);
+    } else {
+        if (sh.gx != total || sh.gy != 1)
+            violation("table grid differs from the tile count", 0, sh.gx);
+        for (int64_t t = 0; t < total; ++t) {
+            const int s = find_seg(b.tile0, b.nseg, int32_t(t));
+            out.emplace_back(s, t - b.tile0[s]);
+        }
+    }
+    return out;
+}
+
 }  // namespace
 
 namespace rr {
@@ -134,10 +171,13 @@ hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, hipStream_t)
     ++g_launches;
     const bool bf16 = b.bf16;
     const int ve = bf16 ? 8 : 4;
-    for (int64_t t = 0; t < total_tiles; ++t) {
-        const int s = find_seg(b.tile0, b.nseg, int32_t(t));
-        const RedSeg &sg = b.seg[s];
-        const int64_t lt = t - b.tile0[s];
+    const LaunchShape sh = reduce_shape(b, total_tiles);
+    ++g_forms[0][sh.form];
+    if (sh.form == kFormOne && (!b.seg[0].vec || b.seg[0].k < 1 || b.seg[0].k > kMaxIn))
+        violation("single-segment form for a segment it cannot run", uintptr_t(b.seg[0].out), b.seg[0].k);
+    for (const auto &st : tiles_of(b, total_tiles, sh)) {
+        const RedSeg &sg = b.seg[st.first];
+        const int64_t lt = st.second;
         if (sg.vec) {
             for (int k = 0; k < sg.k; ++k)
                 if (uintptr_t(sg.in[k]) % 16)
@@ -170,10 +210,13 @@ hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, hipStream_t)
 hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hipStream_t)
 {
     ++g_launches;
-    for (int64_t t = 0; t < total_tiles; ++t) {
-        const int s = find_seg(b.tile0, b.nseg, int32_t(t));
-        const CopySeg &sg = b.seg[s];
-        const int64_t lt = t - b.tile0[s];
+    const LaunchShape sh = copy_shape(b, total_tiles);
+    ++g_forms[1][sh.form];
+    if (sh.form == kFormOne)
+        violation("single-segment form for a copy", 0, 0);
+    for (const auto &st : tiles_of(b, total_tiles, sh)) {
+        const CopySeg &sg = b.seg[st.first];
+        const int64_t lt = st.second;
         if ((sg.mode == kCopyShifted) != shifted)
             violation("copy mode in the wrong kernel", uintptr_t(sg.dst), sg.mode);
         if (sg.mode == kCopyBytes) {
@@ -230,6 +273,7 @@ void sim_reset(void)
     g_bufs.clear();
     g_violations = 0;
     g_launches = 0;
+    memset(g_forms, 0, sizeof g_forms);
     g_msg[0] = '\0';
 }
 void sim_register(const void *p, int64_t bytes, int writable)
@@ -238,5 +282,8 @@ void sim_register(const void *p, int64_t bytes, int writable)
 }
 long sim_violations(void) { return g_violations; }
 long sim_launches(void) { return g_launches; }
+// launches since the last reset in launch form `form` (0 table, 1 uniform,
+// 2 single segment) of the reduction (copy == 0) or copy (copy == 1) kernels
+long sim_form_launches(int copy, int form) { return g_forms[copy != 0][form]; }
 const char *sim_message(void) { return g_msg; }
 }

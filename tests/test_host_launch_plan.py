@@ -403,3 +403,79 @@ def test_random_all_to_all_round_trip(sim, orc, seed):
             orc.a2a_unpack(es, A, seg, c, h, orc.a2a_pack(es, A, seg, c, h, src), expect)
     for d in range(A):
         assert np.array_equal(out[d][3:3 + A * seg], expect[d]), (A, H, nc, es, seg, d)
+
+
+# --------------------------------------------------------------------------
+# launch forms
+# --------------------------------------------------------------------------
+
+def test_every_launch_form_is_replayed(sim, orc):
+    """The library launches a batch in one of three forms (one aligned
+    segment with preloaded arguments, a uniform (tile, segment) grid, the
+    tile table).  Each form, replayed here, writes the oracle's values and
+    touches only the registered buffers."""
+    def forms(copy):
+        return [sim.L.sim_form_launches(copy, f) for f in range(3)]   # table, uniform, one
+
+    sim.reset()
+    # one aligned segment: an A=2 reduce-scatter owner over its whole block
+    R = 8 * 128 * 20
+    x0, x1 = bits(R, 41, 0), bits(R, 41, 1)
+    a, b = sim.buf(x0.copy(), writable=False), sim.buf(x1.copy(), writable=False)
+    out = sim.buf(np.zeros(R, np.uint16))
+    sim.call("rr_active_add_scale", rel(2, 6, 8, 0, R), RS, BF16, AVG, 0, parr(ptr(a), ptr(b)), 2,
+             ptr(out), None)
+    assert np.array_equal(out, orc.rs2_active(BF16, AVG, x0.copy(), x1.copy()))
+    assert forms(0) == [0, 0, 1]
+
+    # equal segments: all six helpers of an A=2 group, three tiles each
+    n = 8 * 8192 * 3
+    xs = [sim.buf(bits(n, 42, s), writable=False) for s in range(2)]
+    c = orc.geometry(2, 6, 8, 0, n, AR, BF16)["chunk"]
+    jobs = (_rr._HelperJob * 6)()
+    outs = [sim.buf(np.zeros(c, np.uint16)) for _ in range(6)]
+    for h in range(6):
+        jobs[h].relay, jobs[h].helper, jobs[h].nSlots = _relay(2, 6, 8, 0, n), h, 2
+        jobs[h].slots[0], jobs[h].slots[1] = ptr(xs[0], h * c).value, ptr(xs[1], h * c).value
+        jobs[h].out = ptr(outs[h]).value
+    sim.call("rr_helper_reduce_many", AR, BF16, AVG, jobs, 6, None)
+    for h in range(6):
+        ref = orc.ar2_helper(BF16, AVG, xs[0][h * c:(h + 1) * c].copy(), xs[1][h * c:(h + 1) * c].copy())
+        assert np.array_equal(outs[h], ref)
+    assert forms(0) == [0, 1, 1]
+
+    # unequal segments: every buffer 6 bytes past a 16-byte boundary, so the
+    # item splits into an element-wise head, a vector body and a tail
+    lead = 3
+    xb = [sim.buf(padded(bits(R, 43, s), lead), writable=False) for s in range(2)]
+    ob = sim.buf(np.zeros(R + lead + 16, np.uint16))
+    sim.call("rr_active_add_scale", rel(2, 6, 8, 0, R), RS, BF16, SUM, 1,
+             parr(ptr(xb[0], lead), ptr(xb[1], lead)), 2, ptr(ob, lead), None)
+    ref = orc.rs2_active(BF16, SUM, xb[0][lead:lead + R].copy(), xb[1][lead:lead + R].copy())
+    assert np.array_equal(ob[lead:lead + R], ref)
+    assert forms(0) == [1, 1, 1]
+
+    # copies: an aligned all-to-all pack (twelve equal moves) runs on the
+    # uniform grid; a ragged unpack's byte heads and tails do not
+    A, H, nc = 4, 4, 5
+    for seg, want in ((5 * 128 * 40, 1), (5 * 128 * 40 + 3, 0)):   # chunks of several tiles
+        before = forms(1)
+        c = orc.geometry(A, H, nc, 0, seg, A2A, BF16)["chunk"]
+        src = [sim.buf(bits(A * seg, 44, s), writable=False) for s in range(A)]
+        dst = [sim.buf(np.zeros((A - 1) * c, np.uint16)) for _ in range(A)]
+        sim.call("rr_a2a_pack", rel(A, H, nc, 0, seg), BF16, 2, parr(*[ptr(s) for s in src]),
+                 parr(*[ptr(d) for d in dst]), None)
+        ref = orc.a2a_pack(2, A, seg, c, 2, src)
+        for d in range(A):
+            assert np.array_equal(dst[d].view(np.uint8), ref[d])
+        outs = [sim.buf(np.zeros(A * seg, np.uint16)) for _ in range(A)]
+        recv = [sim.buf(d.copy(), writable=False) for d in dst]
+        sim.call("rr_a2a_unpack", rel(A, H, nc, 0, seg), BF16, 2, parr(*[ptr(r) for r in recv]),
+                 parr(*[ptr(o) for o in outs]), None)
+        expect = [np.zeros(A * seg, np.uint16) for _ in range(A)]
+        orc.a2a_unpack(2, A, seg, c, 2, ref, expect)
+        for d in range(A):
+            assert np.array_equal(outs[d], expect[d])
+        after = forms(1)
+        assert after[1] > before[1]                      # uniform grid used
+        assert (after[0] > before[0]) == (want == 0)     # table only for the ragged case
