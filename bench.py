@@ -2,17 +2,21 @@
 """Benchmark of the sharded relay hot path on one MI355X.
 
 One step is one pass of every relay kernel of the method over one batch of
-synthetic input at one message size M (per-active-rank input bytes, bf16):
+synthetic input at one message size M (per-active-rank input bytes, bf16),
+in the fused 8-GPU collectives' layout (A=2: four sparse groups; A=4: two):
 
-  A=2 allreduce  (H=6, numChunks=8):  6 helper reductions + 2 active epilogues
-  A=2 reduce-scatter:                 2 owner epilogues (recvCount = M/4 elems)
-  A=4 allreduce  (H=4, 500 permille): 4 helper reductions + 4 active slices
-  A=4 reduce-scatter (H=4):           4 helper pass-1 + 4 owner pass-2 launches
-  A=4 all-to-all (H=4, numChunks=5):  4 packs + 4 unpacks (segmentCount = M/8)
+  A=2 allreduce  (H=6, numChunks=8):  helper reduce-at-helper, active epilogue
+  A=2 reduce-scatter:                 owner epilogue (recvCount = M/4 elems)
+  A=4 allreduce  (H=4, 500 permille): helper 4->1 slice, active direct slice
+  A=4 reduce-scatter (H=4):           helper pass 1, owner pass 2
+  A=4 all-to-all (H=4, numChunks=5):  helper-slice pack and unpack (segmentCount = M/8)
 
-Each role is one batched call over all of its jobs (rr_*_many: one kernel
-launch per role, 10 launches per step); --unbatched issues one call per job
-(34 launches per step) instead.
+--variant chooses the jobs each role's launch covers (one launch per role):
+  share  (default) one GPU's share of the fused call: a GPU is a helper for
+         the three other A=2 groups (3 helper jobs) and runs one job in
+         every other role; 9 launches per step;
+  group  every job of one simulated group in one launch (2-4x a GPU's share);
+  job    one launch per job of the group (34 launches per step).
 
 Inputs are resident in HBM before timing starts.  ``value`` is the step's
 algorithmic bytes (every input element read once, every output element
@@ -39,6 +43,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0  # MI355X HBM3E, published
+KERNEL_FORMS = {
+    "reduce<bf16>": "reduce_one_kernel<bf16,K> (one aligned segment), reduce_uniform_kernel<bf16> "
+                    "(equal segments), reduce_kernel<bf16> (tile table): one per-tile code, three "
+                    "launch forms",
+    "reduce<f32>": "reduce_one_kernel<f32,K>, reduce_uniform_kernel<f32>, reduce_kernel<f32>",
+    "copy": "copy_uniform_kernel, copy_kernel, copy_shifted_uniform_kernel, copy_shifted_kernel",
+}
+VARIANTS = {
+    "share": "each role's launch covers one GPU's share of the fused 8-GPU call (3 A=2 helper "
+             "jobs, one job in every other role)",
+    "group": "each role's launch covers every job of one simulated group (2-4x one GPU's share)",
+    "job": "one launch per job",
+}
 METRIC = "achieved HBM GB/s (and % of peak) of relay reduce/pack kernels, 2MB-1GB msgs"
 MIB = 1 << 20
 
@@ -52,8 +69,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy-mib", type=float, default=0.0,
                    help="run a plain device copy of this size first (HBM counter calibration)")
-    p.add_argument("--unbatched", action="store_true",
-                   help="one launch per job instead of one batched launch per role")
+    p.add_argument("--variant", choices=("share", "group", "job"), default="share",
+                   help="jobs per launch: one GPU's share of the fused call (default), the "
+                        "whole simulated group, or one job")
     p.add_argument("--sweep", action="store_true", help="per-row sweep instead of the step benchmark")
     p.add_argument("--sweep-sizes", default="2,4,8,16,32,64,128,256,512,1024")
     p.add_argument("--sweep-reps", type=int, default=20)
@@ -79,22 +97,22 @@ def host_inputs(M):
     }
 
 
-def build_rows(inp, rows=("ar2", "rs2", "ar4", "rs4", "a2a"), batched=True):
+def build_rows(inp, rows=("ar2", "rs2", "ar4", "rs4", "a2a"), mode="share"):
     import pack_rr_helper_amd as rr
     from pack_rr_helper_amd import synth
     from pack_rr_helper_amd import workloads as W
     dev = lambda arrs, code=rr.BF16: [synth.to_device(a, code) for a in arrs]
     out = {}
     if "ar2" in rows:
-        out["ar2"] = W.AR2(dev(inp["ar2"]), rr.BF16, rr.AVG, batched=batched)
+        out["ar2"] = W.AR2(dev(inp["ar2"]), rr.BF16, rr.AVG, mode=mode)
     if "rs2" in rows:
-        out["rs2"] = W.RS2(dev(inp["rs2"]), rr.BF16, rr.AVG, batched=batched)
+        out["rs2"] = W.RS2(dev(inp["rs2"]), rr.BF16, rr.AVG, mode=mode)
     if "ar4" in rows:
-        out["ar4"] = W.AR4(dev(inp["ar4"]), rr.BF16, rr.AVG, batched=batched)
+        out["ar4"] = W.AR4(dev(inp["ar4"]), rr.BF16, rr.AVG, mode=mode)
     if "rs4" in rows:
-        out["rs4"] = W.RS4(dev(inp["rs4"]), rr.BF16, rr.SUM, batched=batched)
+        out["rs4"] = W.RS4(dev(inp["rs4"]), rr.BF16, rr.SUM, mode=mode)
     if "a2a" in rows:
-        out["a2a"] = W.A2A(dev(inp["a2a"], None), rr.BF16, batched=batched)
+        out["a2a"] = W.A2A(dev(inp["a2a"], None), rr.BF16, mode=mode)
     return out
 
 
@@ -102,8 +120,9 @@ def build_rows(inp, rows=("ar2", "rs2", "ar4", "rs4", "a2a"), batched=True):
 # CPU baseline: the oracle, single thread, one step of the same workload
 # --------------------------------------------------------------------------
 
-def cpu_baseline(inp):
-    """Seconds and algorithmic bytes of one step through the oracle."""
+def cpu_baseline(inp, variant="share"):
+    """Seconds and algorithmic bytes of one step through the oracle: the jobs
+    the GPU step runs (one GPU's share, or every job of the group)."""
     import numpy as np
     import oracle as orc
 
@@ -116,44 +135,47 @@ def cpu_baseline(inp):
         t_total += time.perf_counter() - t
         nbytes += b
 
+    share = variant == "share"
+    n_ar2_helpers, n_a2_actives, n_a4 = (3, 1, 1) if share else (6, 2, 4)
     BF, AVG, SUM, AR, RS, A2A = orc.BF16, orc.AVG, orc.SUM, orc.ALLREDUCE, orc.REDUCE_SCATTER, orc.ALLTOALL
     x = inp["ar2"]
     g = orc.geometry(2, 6, 8, 0, x[0].size, AR, BF)
     c = g["chunk"]
-    for k in range(6):
+    for k in range(n_ar2_helpers):
         timed(lambda: orc.ar2_helper(BF, AVG, x[0][k * c:(k + 1) * c], x[1][k * c:(k + 1) * c]), 3 * c * 2)
     out = np.zeros_like(x[0])
-    for a in range(2):
+    for a in range(n_a2_actives):
         timed(lambda: orc.ar_active(BF, AVG, 2, 6, 8, 0, x[0].size, a, x, out), 3 * g["direct_len"] * 2)
     x = inp["rs2"]
     R = x[0].size // 2
     timed(lambda: orc.rs2_active(BF, AVG, x[0][:R], x[1][:R]), 3 * R * 2)
-    timed(lambda: orc.rs2_active(BF, AVG, x[0][R:], x[1][R:]), 3 * R * 2)
+    if not share:
+        timed(lambda: orc.rs2_active(BF, AVG, x[0][R:], x[1][R:]), 3 * R * 2)
     x = inp["ar4"]
     g = orc.geometry(4, 4, 0, 500, x[0].size, AR, BF)
     c = g["chunk"]
-    for h in range(4):
+    for h in range(n_a4):
         timed(lambda: orc.ar4_helper(BF, AVG, [v[h * c:(h + 1) * c] for v in x]), 5 * c * 2)
     out = np.zeros_like(x[0])
-    for a in range(4):
+    for a in range(n_a4):
         n = g["dslice"] if a < 3 else g["direct_len"] - 3 * g["dslice"]
         timed(lambda: orc.ar_active(BF, AVG, 4, 4, 0, 500, x[0].size, a, x, out), 5 * n * 2)
     x = inp["rs4"]
     R = x[0].size // 4
     c = orc.geometry(4, 4, 0, 500, R, RS, BF)["chunk"]
-    for h in range(4):
+    for h in range(n_a4):
         scratch = np.concatenate([x[s][o * R + h * c:o * R + (h + 1) * c]
                                   for o in range(4) for s in range(4) if s != o])
         timed(lambda: orc.rs4_pass1(BF, 4, c, scratch), 16 * c * 2)
     reds = [np.ascontiguousarray(x[0][:c]) for _ in range(4)]
-    for o in range(4):
+    for o in range(n_a4):
         blk = [v[o * R:(o + 1) * R] for v in x]
         timed(lambda: orc.rs4_pass2(BF, SUM, 4, 4, 500, R, o, blk, reds), (3 * 4 * c + 5 * (R - 4 * c)) * 2)
     x = inp["a2a"]
     seg = x[0].size // 4
     c = orc.geometry(4, 4, 5, 0, seg, A2A, BF)["chunk"]
     outs = [np.zeros(4 * seg, np.uint16) for _ in range(4)]
-    for h in range(4):
+    for h in range(n_a4):
         packed = []
         timed(lambda: packed.extend(orc.a2a_pack(2, 4, seg, c, h, x)), 24 * c * 2)
         timed(lambda: orc.a2a_unpack(2, 4, seg, c, h, packed, outs), 24 * c * 2)
@@ -178,7 +200,7 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel, message_mib, unbatched):
+def traffic_for(kernel, message_mib, variant):
     """HBM bytes per launch of `kernel` (counter-measured, scaled by a plain
     copy of known size) from profiles/traffic.json, or None if absent, taken
     on another workload, or taken on other kernel sources."""
@@ -189,7 +211,7 @@ def traffic_for(kernel, message_mib, unbatched):
         t = json.load(fh)
     if t.get("kernel_source_digest") != kernel_source_digest():
         return None
-    if t.get("message_mib") != message_mib or bool(t.get("unbatched")) != bool(unbatched):
+    if t.get("message_mib") != message_mib or t.get("variant") != variant:
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if not k else k.get("hbm_bytes_per_launch")
@@ -229,7 +251,7 @@ def step_bench(args):
     M = int(args.message_mib * MIB)
     print(f"[bench] generating inputs, M={args.message_mib} MiB", file=sys.stderr, flush=True)
     inp = host_inputs(M)
-    wls = build_rows(inp, batched=not args.unbatched)
+    wls = build_rows(inp, mode=args.variant)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     calls = [c for wl in wls.values() for c in wl.calls(stream)]
@@ -301,10 +323,19 @@ def step_bench(args):
                 r[2] += 1
     for e in evs:
         hip.hipEventDestroy(e)
+    # An event between two launches delays the second one (the event is
+    # processed after the first kernel ends, the next dispatch after it), so
+    # an interval is a launch plus the events' own cost.  That cost per launch
+    # is the second region's step time minus the event-free first region's,
+    # spread over the step's launches; it is subtracted from every interval.
+    events_ms_step = sum(r[0] for r in per_row.values()) / args.steps
+    event_cost_ms = max(0.0, events_ms_step - ms_step) / len(calls)
+    def launch_ms(ms, n):
+        return ms / n - event_cost_ms
     dom = max(per_kernel, key=lambda k: per_kernel[k][0])
     d_ms, d_b, d_n = per_kernel[dom]
-    achieved = (d_b / d_n) / (d_ms / d_n * 1e-3) / 1e9
-    traffic = traffic_for(dom, args.message_mib, args.unbatched)
+    achieved = (d_b / d_n) / (launch_ms(d_ms, d_n) * 1e-3) / 1e9
+    traffic = traffic_for(dom, args.message_mib, args.variant)
 
     value = step_bytes / (ms_step * 1e-3) / 1e9
     result = {
@@ -325,19 +356,24 @@ def step_bench(args):
             "workload": (f"relay hot path, {args.message_mib:g} MiB per-rank bf16 message: A=2 allreduce "
                          "(H=6) + A=2 reduce-scatter + A=4 allreduce (H=4, 500 permille) + A=4 "
                          "reduce-scatter + A=4 all-to-all pack/unpack, one GPU"),
+            "variant": args.variant,
+            "variant_means": VARIANTS[args.variant],
             "message_bytes": M,
             "launches_per_step": len(calls),
-            "batched": not args.unbatched,
             "algorithmic_bytes_per_step": step_bytes,
             "timed_region_1": "K steps, no events between launches (value, ms_per_step)",
-            "rows_gbs": {row: round(b / (ms * 1e-3) / 1e9, 1) for row, (ms, b, n) in per_row.items()},
-            "rows_us_per_launch": {row: round(1e3 * ms / n, 2) for row, (ms, b, n) in per_row.items()},
+            "rows_gbs": {row: round(b / n / (launch_ms(ms, n) * 1e-3) / 1e9, 1)
+                         for row, (ms, b, n) in per_row.items()},
+            "rows_us_per_launch": {row: round(1e3 * launch_ms(ms, n), 2) for row, (ms, b, n) in per_row.items()},
             "rows_bytes_per_launch": {row: b // n for row, (ms, b, n) in per_row.items()},
             "launch_order": [row for row, _, _, _ in calls],
         },
         "roofline": {
             "kernel": dom,
-            "timing": "timing-only HIP events between consecutive launches (second timed region)",
+            "kernel_symbols": KERNEL_FORMS.get(dom, dom),
+            "timing": ("timing-only HIP events between consecutive launches on the kernels' stream "
+                       "(second timed region), less the events' own cost per launch: (second region's "
+                       "step time - event-free first region's) / launches per step"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_GBS,
@@ -345,7 +381,9 @@ def step_bench(args):
             "frac": round(achieved / PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": d_b // d_n,
-            "avg_launch_us": round(1e3 * d_ms / d_n, 3),
+            "avg_launch_us": round(1e3 * launch_ms(d_ms, d_n), 3),
+            "avg_event_interval_us": round(1e3 * d_ms / d_n, 3),
+            "event_cost_us_per_launch": round(1e3 * event_cost_ms, 3),
             "launches": d_n,
         },
         "cpu_baseline": None,
@@ -353,13 +391,14 @@ def step_bench(args):
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one step of the same workload", file=sys.stderr, flush=True)
         t, b, reps = 0.0, 0, 0
-        while t < 12.0 and reps < 30:
-            dt, db = cpu_baseline(inp)
+        while t < 12.0 and reps < 100:
+            dt, db = cpu_baseline(inp, args.variant)
             t, b, reps = t + dt, b + db, reps + 1
         result["cpu_baseline"] = {
             "value": round(b / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{reps} full step(s) (every row, {args.message_mib:g} MiB message, {b} algorithmic "
-                       f"bytes) through the scalar C oracle, single thread, {t:.1f} s; host "
+            "sample": (f"{reps} full step(s) (every row, {args.message_mib:g} MiB message, {args.variant} "
+                       f"variant, {b} algorithmic bytes) through the scalar C oracle, single thread, "
+                       f"{t:.1f} s; host "
                        f"{platform.processor() or platform.machine()}"),
         }
     print(json.dumps(result), flush=True)
@@ -370,8 +409,8 @@ def step_bench(args):
 # --------------------------------------------------------------------------
 
 def sweep(args):
-    """Per-role GB/s over message sizes and dtypes: one batched launch of each
-    role, timed alone with a fence-free HIP event pair, after a 1 GiB overwrite
+    """Per-role GB/s over message sizes and dtypes: one launch of each role
+    (covering the jobs --variant selects), timed alone with a fence-free HIP event pair, after a 1 GiB overwrite
     that evicts the inputs from the 256 MB Infinity Cache; best and median of
     the reps after 3 warm-ups."""
     import ctypes
@@ -407,7 +446,8 @@ def sweep(args):
         return ts
 
     def record(mib, dt_name, role, kernel, b, ts):
-        return {"message_mib": mib, "dtype": dt_name, "row": role, "kernel": kernel, "bytes_per_launch": b,
+        return {"message_mib": mib, "dtype": dt_name, "variant": args.variant if args.variant != "job" else "share",
+                "row": role, "kernel": kernel, "bytes_per_launch": b,
                 "reps": len(ts), "us_min": round(min(ts) * 1e6, 2),
                 "us_median": round(statistics.median(ts) * 1e6, 2),
                 "gbs_best": round(b / min(ts) / 1e9, 1),
@@ -434,9 +474,10 @@ def sweep(args):
                           for _ in range(ranks)]
                 else:
                     xs = [torch.randn(n, device="cuda", generator=gen).to(tdt) for _ in range(ranks)]
-                wl = {"ar2": lambda: W.AR2(xs, dt, rr.AVG), "rs2": lambda: W.RS2(xs, dt, rr.AVG),
-                      "ar4": lambda: W.AR4(xs, dt, rr.AVG), "rs4": lambda: W.RS4(xs, dt, rr.SUM),
-                      "a2a": lambda: W.A2A(xs, dt), "a2a_ragged": lambda: W.A2A(xs, dt)}[row]()
+                mode = args.variant if args.variant != "job" else "share"
+                wl = {"ar2": lambda: W.AR2(xs, dt, rr.AVG, mode=mode), "rs2": lambda: W.RS2(xs, dt, rr.AVG, mode=mode),
+                      "ar4": lambda: W.AR4(xs, dt, rr.AVG, mode=mode), "rs4": lambda: W.RS4(xs, dt, rr.SUM, mode=mode),
+                      "a2a": lambda: W.A2A(xs, dt, mode=mode), "a2a_ragged": lambda: W.A2A(xs, dt, mode=mode)}[row]()
                 calls = wl.calls(stream)
                 for role in sorted({c[0] for c in calls}):
                     role_call = next(c for c in calls if c[0] == role)

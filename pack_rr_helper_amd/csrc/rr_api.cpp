@@ -456,13 +456,18 @@ rr_status collect_rs(const rr_relay *relay, int dtype, int op, int pass, int idx
         it.scale = op_scale(op, A);
         items.push_back(it);
     }
-    if (g.direct_len > 0) {
+    // The direct region goes out in pieces of one offload chunk, so that with
+    // the offload slices every segment of the owner's pass spans the same
+    // tiles and the pass launches on the uniform grid (500 permille: the
+    // direct region is exactly H chunks).
+    const int64_t piece = c > 0 ? c : g.direct_len;
+    for (int64_t lo = 0; lo < g.direct_len; lo += piece) {
         RedItem it{};
         for (int s = 0; s < A; ++s)
-            it.in[s] = static_cast<const char *>(in[s]) + g.direct_off * es;
+            it.in[s] = static_cast<const char *>(in[s]) + (g.direct_off + lo) * es;
         it.k = A;
-        it.out = static_cast<char *>(out) + g.direct_off * es;
-        it.n = g.direct_len;
+        it.out = static_cast<char *>(out) + (g.direct_off + lo) * es;
+        it.n = std::min(piece, g.direct_len - lo);
         it.scale = op_scale(op, A);
         items.push_back(it);
     }

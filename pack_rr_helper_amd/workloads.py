@@ -20,9 +20,18 @@ rank would receive is represented by the bytes it would receive:
 Message size M is the per-active-rank input in bytes (the pull request's sweep
 axis), bf16 unless stated.  Workload classes expose ``calls(stream)``: one
 entry per role, ``(row, kernel, algorithmic_bytes, fn)`` with ``fn()``
-issuing that role's work.  With ``batched=True`` (the default) a role is one
-``*_many`` call over all of its jobs -- one kernel launch, as in the fused
-multi-group call; with ``batched=False`` every job is its own call and entry.
+issuing that role's work.  ``mode`` chooses which jobs a role's call covers:
+
+* ``"share"``: the jobs one GPU runs for that role in the fused 8-GPU call,
+  as one ``*_many`` call (one launch).  A GPU is a helper for the three other
+  A=2 sparse groups (three helper jobs; chunks 0-2 of the simulated group
+  stand in for the other groups' chunks) and runs one job in every other
+  role (its own active epilogue, owner pass, A=4 helper slice, all-to-all
+  helper slice);
+* ``"group"`` (the default): every job of the simulated group in one call,
+  2-4x one GPU's share -- the whole group's work in one launch;
+* ``"job"``: one call (one launch) per job.
+
 Calls are prepared once (checks and marshalling), so issuing one costs a single
 C call.  ``run(stream)`` issues every entry.  Algorithmic bytes count every
 input element read once and every output element written once.
@@ -36,15 +45,28 @@ from . import (ALLREDUCE, ALLTOALL, AVG, BF16, F32, REDUCE_SCATTER, SUM, Relay, 
 
 TORCH = {F32: torch.float32, BF16: torch.bfloat16}
 ESIZE = {F32: 4, BF16: 2}
-COPY = "copy_kernel"
+# Kernel families.  The library launches a batch in one of three forms (one
+# aligned segment, a uniform grid of equal segments, a tile table), each its
+# own kernel symbol running the same per-tile code; timings are reported per
+# family: the reduction kernels of one element type, and the copy kernels
+# (aligned and realigning).
+COPY = "copy"
 
 
 def reduce_kernel(dtype):
-    return "reduce_kernel<bf16>" if dtype == BF16 else "reduce_kernel<f32>"
+    return "reduce<bf16>" if dtype == BF16 else "reduce<f32>"
+
+
+MODES = ("share", "group", "job")
 
 
 class _Row:
-    batched = True
+    mode = "group"
+
+    def _set_mode(self, mode):
+        if mode not in MODES:
+            raise ValueError(f"mode {mode!r}: one of {MODES}")
+        self.mode = mode
 
     def calls(self, stream=None):
         key = id(stream) if stream is not None else None
@@ -61,23 +83,25 @@ class _Row:
     def bytes_per_step(self):
         return sum(b for _, _, b, _ in self.calls())
 
-    def _roles(self, stream, row, kernel, per_job_bytes, jobs, many, single):
-        """One entry for all jobs (batched) or one entry per job."""
+    def _roles(self, stream, row, kernel, per_job_bytes, jobs, many, single, share=1):
+        """Entries for one role: one call over every job ("group"), over the
+        first ``share`` jobs -- one GPU's share ("share"), or one per job."""
         if not jobs:
             return []
-        if self.batched:
-            return [(row, kernel, sum(per_job_bytes),
-                     many(jobs, stream=stream, prepare=True))]
-        return [(row, kernel, b, single(job, stream=stream, prepare=True))
-                for b, job in zip(per_job_bytes, jobs)]
+        if self.mode == "job":
+            return [(row, kernel, b, single(job, stream=stream, prepare=True))
+                    for b, job in zip(per_job_bytes, jobs)]
+        n = len(jobs) if self.mode == "group" else min(share, len(jobs))
+        return [(row, kernel, sum(per_job_bytes[:n]), many(jobs[:n], stream=stream, prepare=True))]
 
 
 class AR2(_Row):
     """A=2 allreduce: reduce-at-helper (summary section 2) over the H relay
     chunks and the active epilogue over the direct region (section 1)."""
 
-    def __init__(self, xs, dtype, op=AVG, H=6, numChunks=8, batched=True):
-        self.dtype, self.op, self.batched = dtype, op, batched
+    def __init__(self, xs, dtype, op=AVG, H=6, numChunks=8, mode="group"):
+        self.dtype, self.op = dtype, op
+        self._set_mode(mode)
         self.count = xs[0].numel()
         self.relay = Relay(2, H, numChunks, 0, self.count)
         self.g = rr_geometry(self.relay, ALLREDUCE, dtype)
@@ -100,7 +124,8 @@ class AR2(_Row):
         op, dt = self.op, self.dtype
         return (self._roles(stream, "ar2_helper", k, [3 * c * es] * len(hjobs), hjobs,
                             lambda j, **kw: rr_helper_reduce_many(ALLREDUCE, dt, op, j, **kw),
-                            lambda j, **kw: rr_helper_reduce(j[0], ALLREDUCE, dt, op, *j[1:], **kw))
+                            lambda j, **kw: rr_helper_reduce(j[0], ALLREDUCE, dt, op, *j[1:], **kw),
+                            share=3)
                 + self._roles(stream, "ar2_active", k, [3 * self.g["direct_len"] * es] * len(ajobs), ajobs,
                               lambda j, **kw: rr_active_add_scale_many(ALLREDUCE, dt, op, j, **kw),
                               lambda j, **kw: rr_active_add_scale(j[0], ALLREDUCE, dt, op, *j[1:], **kw)))
@@ -118,8 +143,9 @@ class RS2(_Row):
     and direct chunks over the whole recvCount block (reduce-scatter core
     commit, phases 3 and 5).  xs[a] holds 2 blocks of R."""
 
-    def __init__(self, xs, dtype, op=AVG, H=6, numChunks=8, in_place=False, batched=True):
-        self.dtype, self.op, self.batched = dtype, op, batched
+    def __init__(self, xs, dtype, op=AVG, H=6, numChunks=8, in_place=False, mode="group"):
+        self.dtype, self.op = dtype, op
+        self._set_mode(mode)
         self.R = R = xs[0].numel() // 2
         self.relay = Relay(2, H, numChunks, 0, R)
         self.x = xs
@@ -146,8 +172,9 @@ class AR4(_Row):
     reduce their position slices 4->1, the A actives reduce their direct
     slices."""
 
-    def __init__(self, xs, dtype, op=AVG, H=4, permille=500, batched=True):
-        self.dtype, self.op, self.batched = dtype, op, batched
+    def __init__(self, xs, dtype, op=AVG, H=4, permille=500, mode="group"):
+        self.dtype, self.op = dtype, op
+        self._set_mode(mode)
         self.count = xs[0].numel()
         self.relay = Relay(4, H, 0, permille, self.count)
         self.g = rr_geometry(self.relay, ALLREDUCE, dtype)
@@ -189,9 +216,10 @@ class RS4(_Row):
     each helper over its (owner, source) scratch, pass 2 at each owner.
     xs[s] holds A blocks of R."""
 
-    def __init__(self, xs, dtype, op=SUM, H=4, permille=500, batched=True):
+    def __init__(self, xs, dtype, op=SUM, H=4, permille=500, mode="group"):
         A = 4
-        self.dtype, self.op, self.batched = dtype, op, batched
+        self.dtype, self.op = dtype, op
+        self._set_mode(mode)
         self.R = R = xs[0].numel() // A
         self.relay = Relay(A, H, 0, permille, R)
         self.g = rr_geometry(self.relay, REDUCE_SCATTER, dtype)
@@ -206,6 +234,12 @@ class RS4(_Row):
                     dst = (o * (A - 1) + j) * c
                     self.scratch[h][dst:dst + c].copy_(xs[s][o * R + h * c:o * R + (h + 1) * c])
         self.out = [torch.empty(R, dtype=TORCH[dtype], device=dev) for _ in range(A)]
+        # every helper's reduced chunks as its pass 1 returns them, staged once:
+        # an owner's pass 2 reads all H of them, while one GPU's share of the
+        # step runs a single helper's pass 1
+        if c:
+            rr_rs_multi_reduce_many(dtype, op, [(self.relay, 1, h, [self.scratch[h]],
+                                                 self.scratch[h][A * (A - 1) * c:]) for h in range(H)])
 
     def reduced(self, h, o):
         c, A = self.g["chunk"], 4
@@ -232,9 +266,10 @@ class A2A(_Row):
     """A=4 all-to-all helper coalescing (reverted all-to-all paragraph): one
     pack and one unpack per helper slice.  src[s] holds A segments of seg."""
 
-    def __init__(self, src, dtype=BF16, H=4, numChunks=5, batched=True):
+    def __init__(self, src, dtype=BF16, H=4, numChunks=5, mode="group"):
         A = 4
-        self.dtype, self.batched = dtype, batched
+        self.dtype = dtype
+        self._set_mode(mode)
         self.seg = src[0].numel() // A
         self.relay = Relay(A, H, numChunks, 0, self.seg)
         self.g = rr_geometry(self.relay, ALLTOALL, dtype)
@@ -247,7 +282,7 @@ class A2A(_Row):
 
     def _build(self, stream):
         A, c, es, r, dt = 4, self.g["chunk"], self.es, self.relay, self.dtype
-        kern = COPY if (self.seg * es) % 16 == 0 else "copy_kernel+copy_shifted_kernel"
+        kern = COPY
         pj = [(r, h, self.src, self.packed[h]) for h in range(r.H)] if c else []
         uj = [(r, h, self.packed[h], self.out) for h in range(r.H)] if c else []
         b = 2 * A * (A - 1) * c * es

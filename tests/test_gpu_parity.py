@@ -361,19 +361,23 @@ def test_many_calls_over_heterogeneous_groups(orc):
         check_bf16(host(o4[a]), ref, f"A=4 active {a}")
 
 
-def test_unbatched_and_batched_workloads_agree(orc):
-    """The per-job calls and the batched calls of the timed workload write the
-    same bytes (both checked against the oracle)."""
-    say("batched vs unbatched")
+def test_workload_modes_agree(orc):
+    """One call per job, one call over the whole group's jobs and one call
+    over one GPU's share write the same bytes where they overlap, each checked
+    against the oracle (one GPU's share of the A=4 reduce-scatter: helper 0's
+    pass 1 and owner 0's pass 2)."""
+    say("workload modes")
     M = 8 * 2 ** 20
     xs = [synth.as_bf16_bits(synth.normal(M // 2, 2, s)) for s in range(4)]
     ref = orc.rs4_group(BF16, SUM, 4, 500, M // 8, xs)
-    for batched in (False, True):
-        wl = W.RS4([dev(x) for x in xs], BF16, SUM, batched=batched)
-        assert len(wl.calls()) == (8 if not batched else 2)
+    for mode, ncalls, owners in (("job", 8, 4), ("group", 2, 4), ("share", 2, 1)):
+        wl = W.RS4([dev(x) for x in xs], BF16, SUM, mode=mode)
+        assert len(wl.calls()) == ncalls
         wl.run()
-        for o in range(4):
-            check_bf16(host(wl.out[o]), ref[o], f"batched={batched} owner {o}")
+        for o in range(owners):
+            check_bf16(host(wl.out[o]), ref[o], f"mode={mode} owner {o}")
+    with pytest.raises(ValueError):
+        W.RS4([dev(x) for x in xs], BF16, SUM, mode="batched")
 
 
 # --------------------------------------------------------------------------
