@@ -20,14 +20,16 @@ in the fused 8-GPU collectives' layout (A=2: four sparse groups; A=4: two):
 
 Inputs are resident in HBM before timing starts.  ``value`` is the step's
 algorithmic bytes (every input element read once, every output element
-written once) divided by the measured step time, in GB/s (10^9 bytes/s).
-Each launch is bracketed by HIP events on the stream it runs on; the kernel
-with the largest share of the step's time is reported against the 8 TB/s HBM
-peak in ``roofline``.  ``cpu_baseline`` times the CPU oracle (single thread)
-on one step of the same workload.
+written once) divided by the step time of a first timed region with nothing
+between the launches, in GB/s (10^9 bytes/s).  A second timed region puts a
+timing-only HIP event between consecutive launches on their stream; less the
+events' own cost per launch, it gives each launch's duration, and the kernel
+family with the largest share of the step's time is reported against the
+8 TB/s HBM peak in ``roofline``.  ``cpu_baseline`` times the CPU oracle
+(single thread) on steps of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--message-mib M]
-  python bench.py --sweep [--sweep-out FILE]   # per-row GB/s, 2 MiB .. 1 GiB
+  python bench.py [--steps K] [--warmup W] [--message-mib M] [--variant share|group|job]
+  python bench.py --sweep [--sweep-out FILE]   # per-role GB/s, 2 MiB .. 1 GiB, bf16 and fp32
 """
 import argparse
 import hashlib
