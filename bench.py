@@ -188,18 +188,25 @@ def cpu_baseline(inp, variant="share"):
 # traffic from the committed rocprofv3 counter summary
 # --------------------------------------------------------------------------
 
-def kernel_source_digest():
-    """Digest of the kernel code the counters were taken on: the kernel source
-    and its tiling header with comments and white space removed, so that only
-    a change to the code itself invalidates the stored traffic."""
+def code_digest(texts):
+    """Digest of C/C++ sources with comments and white space removed."""
     h = hashlib.sha256()
-    for f in ("rr_kernels.hip", "rr_internal.h"):
-        with open(os.path.join(ROOT, "pack_rr_helper_amd", "csrc", f)) as fh:
-            text = fh.read()
+    for text in texts:
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def kernel_source_digest():
+    """Digest of the kernel code the counters were taken on: the kernel source
+    and its tiling header, so that only a change to the code itself (not to
+    its comments) invalidates the stored traffic."""
+    texts = []
+    for f in ("rr_kernels.hip", "rr_internal.h"):
+        with open(os.path.join(ROOT, "pack_rr_helper_amd", "csrc", f)) as fh:
+            texts.append(fh.read())
+    return code_digest(texts)
 
 
 def traffic_for(kernel, message_mib, variant):
