@@ -75,6 +75,10 @@ def parse():
                    help="jobs per launch: one GPU's share of the fused call (default), the "
                         "whole simulated group, or one job")
     p.add_argument("--sweep", action="store_true", help="per-row sweep instead of the step benchmark")
+    p.add_argument("--calibrate", action="store_true",
+                   help="time plain read/write stream mixes (bench_calib.so) instead of the step")
+    p.add_argument("--calibrate-sizes", default="256,1024", help="MiB per stream")
+    p.add_argument("--calibrate-out", default=None)
     p.add_argument("--sweep-sizes", default="2,4,8,16,32,64,128,256,512,1024")
     p.add_argument("--sweep-reps", type=int, default=20)
     p.add_argument("--sweep-dtypes", default="bf16,f32")
@@ -506,6 +510,70 @@ def sweep(args):
         hip.hipEventDestroy(e)
 
 
+# --------------------------------------------------------------------------
+# calibration: what plain streams of each read/write mix reach on this GPU
+# --------------------------------------------------------------------------
+
+CALIB_MIXES = [(1, 0), (2, 0), (4, 0), (0, 1), (1, 1), (2, 1), (3, 1), (4, 1), (2, 2)]
+
+
+def calibrate(args):
+    """R reads + W writes per element with the relay kernels' access pattern
+    (bench_calib.hip), each mix timed alone after a 1 GiB overwrite with a
+    fence-free HIP event pair; best and median of the reps."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "bench_calib.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run __graft_entry__.build()")
+    torch.cuda.set_device(0)
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    lib.calib_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), vp,
+                                 ctypes.c_int64, vp]
+    stream = torch.cuda.current_stream()
+    sp = vp(stream.cuda_stream)
+    hip = hip_runtime()
+    evs = []
+    for _ in range(2):
+        e = vp()
+        if hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        evs.append(e)
+    f = ctypes.c_float()
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    out = open(args.calibrate_out, "w") if args.calibrate_out else sys.stdout
+    for mib in [int(v) for v in args.calibrate_sizes.split(",")]:
+        vectors = (mib * MIB // 16) // 1024 * 1024
+        bufs = [torch.ones(vectors * 16, dtype=torch.uint8, device="cuda") for _ in range(6)]
+        for R, W in CALIB_MIXES:
+            ins = (vp * 4)(*[b.data_ptr() for b in bufs[:4]])
+            outs = (vp * 4)(*[b.data_ptr() for b in bufs[4:]] + [0, 0])
+            ts = []
+            for rep in range(args.sweep_reps + 3):
+                flush.zero_()
+                hip.hipEventRecord(evs[0], sp)
+                rc = lib.calib_stream(R, W, ins, outs, vp(sink.data_ptr()), vectors, sp)
+                hip.hipEventRecord(evs[1], sp)
+                if rc != 0:
+                    raise RuntimeError(f"calib_stream({R}, {W}) failed: {rc}")
+                torch.cuda.synchronize()
+                hip.hipEventElapsedTime(ctypes.byref(f), evs[0], evs[1])
+                if rep >= 3:
+                    ts.append(f.value * 1e-3)
+            b = (R + W) * vectors * 16
+            print(json.dumps({"mib_per_stream": mib, "reads": R, "writes": W, "bytes": b, "reps": len(ts),
+                              "gbs_best": round(b / min(ts) / 1e9, 1),
+                              "gbs_median": round(b / statistics.median(ts) / 1e9, 1),
+                              "pct_peak_median": round(100 * b / statistics.median(ts) / 1e9 / PEAK_GBS, 1)}),
+                  file=out, flush=True)
+        del bufs
+        torch.cuda.empty_cache()
+    for e in evs:
+        hip.hipEventDestroy(e)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -514,6 +582,8 @@ def main():
         sys.exit(2)
     if args.sweep:
         sweep(args)
+    elif args.calibrate:
+        calibrate(args)
     else:
         step_bench(args)
 
