@@ -82,6 +82,8 @@ def parse():
     p.add_argument("--sweep-sizes", default="2,4,8,16,32,64,128,256,512,1024")
     p.add_argument("--sweep-reps", type=int, default=20)
     p.add_argument("--sweep-dtypes", default="bf16,f32")
+    p.add_argument("--flush", choices=("read", "write", "none"), default="read",
+                   help="how the sweep and calibration evict inputs from the caches before each rep")
     p.add_argument("--sweep-out", default=None)
     return p.parse_args()
 
@@ -421,11 +423,26 @@ def step_bench(args):
 # sweep: per-row GB/s at 2 MiB .. 1 GiB
 # --------------------------------------------------------------------------
 
+def cache_evictor(torch, mode):
+    """A function that pushes a launch's inputs out of the L2 caches and the
+    256 MB Infinity Cache before a timed rep: "read" sums a 1 GiB buffer (the
+    caches end up holding clean lines), "write" overwrites it (they end up
+    holding dirty lines that the timed launch then writes back), "none"
+    leaves the caches as the previous rep left them."""
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    if mode == "read":
+        words = buf.view(torch.int32)
+        return lambda: torch.sum(words, dtype=torch.int64)
+    if mode == "write":
+        return buf.zero_
+    return lambda: None
+
+
 def sweep(args):
     """Per-role GB/s over message sizes and dtypes: one launch of each role
-    (covering the jobs --variant selects), timed alone with a fence-free HIP event pair, after a 1 GiB overwrite
-    that evicts the inputs from the 256 MB Infinity Cache; best and median of
-    the reps after 3 warm-ups."""
+    (covering the jobs --variant selects), timed alone with a fence-free HIP
+    event pair after the caches are cleared of its inputs (--flush); best and
+    median of the reps after 3 warm-ups."""
     import ctypes
     import zlib
     import torch
@@ -443,12 +460,12 @@ def sweep(args):
             raise RuntimeError("hipEventCreateWithFlags failed")
         evs.append(e)
     f = ctypes.c_float()
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")  # > the 256 MB MALL
+    evict = cache_evictor(torch, args.flush)
 
     def times_of(fn):
         ts = []
         for rep in range(args.sweep_reps + 3):
-            flush.zero_()
+            evict()
             hip.hipEventRecord(evs[0], sp)
             fn()
             hip.hipEventRecord(evs[1], sp)
@@ -460,6 +477,7 @@ def sweep(args):
 
     def record(mib, dt_name, role, kernel, b, ts):
         return {"message_mib": mib, "dtype": dt_name, "variant": args.variant if args.variant != "job" else "share",
+                "flush": args.flush,
                 "row": role, "kernel": kernel, "bytes_per_launch": b,
                 "reps": len(ts), "us_min": round(min(ts) * 1e6, 2),
                 "us_median": round(statistics.median(ts) * 1e6, 2),
@@ -519,8 +537,9 @@ CALIB_MIXES = [(1, 0), (2, 0), (4, 0), (0, 1), (1, 1), (2, 1), (3, 1), (4, 1), (
 
 def calibrate(args):
     """R reads + W writes per element with the relay kernels' access pattern
-    (bench_calib.hip), each mix timed alone after a 1 GiB overwrite with a
-    fence-free HIP event pair; best and median of the reps."""
+    (bench_calib.hip), each mix timed alone with a fence-free HIP event pair
+    after the caches are cleared of its inputs (--flush); best and median of
+    the reps."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "bench_calib.so")
@@ -541,7 +560,7 @@ def calibrate(args):
             raise RuntimeError("hipEventCreateWithFlags failed")
         evs.append(e)
     f = ctypes.c_float()
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    evict = cache_evictor(torch, args.flush)
     sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
     out = open(args.calibrate_out, "w") if args.calibrate_out else sys.stdout
     for mib in [int(v) for v in args.calibrate_sizes.split(",")]:
@@ -552,7 +571,7 @@ def calibrate(args):
             outs = (vp * 4)(*[b.data_ptr() for b in bufs[4:]] + [0, 0])
             ts = []
             for rep in range(args.sweep_reps + 3):
-                flush.zero_()
+                evict()
                 hip.hipEventRecord(evs[0], sp)
                 rc = lib.calib_stream(R, W, ins, outs, vp(sink.data_ptr()), vectors, sp)
                 hip.hipEventRecord(evs[1], sp)
@@ -563,7 +582,8 @@ def calibrate(args):
                 if rep >= 3:
                     ts.append(f.value * 1e-3)
             b = (R + W) * vectors * 16
-            print(json.dumps({"mib_per_stream": mib, "reads": R, "writes": W, "bytes": b, "reps": len(ts),
+            print(json.dumps({"mib_per_stream": mib, "reads": R, "writes": W, "flush": args.flush,
+                              "bytes": b, "reps": len(ts),
                               "gbs_best": round(b / min(ts) / 1e9, 1),
                               "gbs_median": round(b / statistics.median(ts) / 1e9, 1),
                               "pct_peak_median": round(100 * b / statistics.median(ts) / 1e9 / PEAK_GBS, 1)}),
