@@ -496,17 +496,22 @@ def test_ragged_all_to_all_at_64MiB(orc):
     _ragged_a2a_case(orc, 2, seg, 131)
 
 
-def test_step_captured_in_a_hip_graph_replays_like_eager():
+@pytest.mark.parametrize("mode", ["group", "share"])
+def test_step_captured_in_a_hip_graph_replays_like_eager(mode):
     """The library enqueues kernels only (no allocation, no memset), so a whole
-    step can be captured in a HIP graph.  Each replay -- with eager work and
+    step can be captured in a HIP graph, in every launch form (one GPU's share
+    runs its single-segment launches with arguments preloaded into registers,
+    the whole group mostly uniform grids).  Each replay -- with eager work and
     synchronisations between replays -- must write what the eager step wrote."""
-    say("graph replay")
+    say("graph replay", mode)
     M = 8 * 2 ** 20
     n = M // 2
     xs2 = [dev(synth.as_bf16_bits(synth.normal(n, 90, a))) for a in range(2)]
     xs4 = [dev(synth.as_bf16_bits(synth.normal(n, 91, a))) for a in range(4)]
+    xa4 = [dev(synth.as_bf16_bits(synth.normal(n, 93, a))) for a in range(4)]
     src = [dev(synth.bits16(n, 92, a), None) for a in range(4)]
-    rows = [W.AR2(xs2, BF16, AVG), W.RS4(xs4, BF16, SUM), W.A2A(src, BF16)]
+    rows = [W.AR2(xs2, BF16, AVG, mode=mode), W.AR4(xa4, BF16, AVG, mode=mode),
+            W.RS4(xs4, BF16, SUM, mode=mode), W.A2A(src, BF16, mode=mode)]
     outs = lambda: [o for w in rows for o in w.out]
     main = torch.cuda.current_stream()
     for o in outs():
