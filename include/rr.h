@@ -22,7 +22,10 @@
  *   - Pointer arguments of the form `const void* const* p` are HOST arrays of
  *     DEVICE pointers.
  *   - Kernels are enqueued on `stream` (a hipStream_t passed as void*; NULL =
- *     the null stream) and run asynchronously.
+ *     the null stream) and run asynchronously.  A call enqueues kernel
+ *     launches only -- no allocation, memset, copy or synchronisation -- so
+ *     calls can be captured in a HIP graph and replayed.  Calls that overlap
+ *     on different streams must not write the same buffers.
  *   - Buffer sizes are the caller's contract (they are stated per entry
  *     point); the library cannot check them.
  *   - Every call validates its arguments before any HIP call and returns an
