@@ -496,10 +496,12 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
     const dim3 block(kBlock);
     if (sh.form == kFormUniform) {
         const dim3 grid((unsigned)sh.gx, (unsigned)sh.gy);
-        if (shifted)
+        if (shifted) {
             copy_shifted_uniform_kernel<<<grid, block, 0, stream>>>(b);
-        else
-            copy_uniform_kernel<<<grid, block, 0, stream>>>(b);
+        } else {
+            const unsigned lds = total_tiles >= kCopyThrottleTiles ? kCopyThrottleLds : 0u;
+            copy_uniform_kernel<<<grid, block, lds, stream>>>(b);
+        }
     } else {
         const dim3 grid((unsigned)total_tiles);
         if (shifted)
