@@ -211,3 +211,30 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(rr, "library_path", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         rr.load()
+
+
+def test_error_messages_are_per_thread(L):
+    """rr_last_error() is thread-local: threads failing at the same time with
+    different arguments each read back the message of their own call."""
+    import threading
+    bad = {t: relay(3 + 2 * t, 5, 8, 0, 4096) for t in range(8)}   # A = 3, 5, 7, ... all rejected
+    got, start = {}, threading.Barrier(8)
+
+    def work(t):
+        start.wait()
+        for _ in range(200):
+            g = rr._Geom()
+            assert L.rr_geometry(bad[t], 0, 1, ctypes.byref(g)) == EINVAL
+            msg = L.rr_last_error().decode()
+            if f"A={3 + 2 * t}:" not in msg:
+                got[t] = msg
+                return
+        got[t] = "ok"
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert all(v == "ok" for v in got.values()), got
+    assert len(got) == 8
