@@ -25,8 +25,9 @@ between the launches, in GB/s (10^9 bytes/s).  A second timed region puts a
 timing-only HIP event between consecutive launches on their stream; less the
 events' own cost per launch, it gives each launch's duration, and the kernel
 family with the largest share of the step's time is reported against the
-8 TB/s HBM peak in ``roofline``.  ``cpu_baseline`` times the CPU oracle
-(single thread) on steps of the same workload.
+8 TB/s HBM peak in ``roofline``.  ``cpu_baseline`` times the CPU oracle on
+the same jobs, on the host's cores (up to 16 threads, the value) and on one
+thread; the sweep records both oracle rates beside every row.
 
   python bench.py [--steps K] [--warmup W] [--message-mib M] [--variant share|group|job]
   python bench.py --sweep [--sweep-out FILE]   # per-role GB/s, 2 MiB .. 1 GiB, bf16 and fp32
@@ -60,6 +61,7 @@ VARIANTS = {
 }
 METRIC = "achieved HBM GB/s (and % of peak) of relay reduce/pack kernels, 2MB-1GB msgs"
 MIB = 1 << 20
+BF16_CODE, F32_CODE = 1, 0  # dtype codes of the C ABI and the oracle
 
 
 def parse():
@@ -68,7 +70,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--message-mib", type=float, default=64.0)
-    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the CPU oracle timings (the step's cpu_baseline, the sweep rows' oracle)")
     p.add_argument("--calibrate-copy-mib", type=float, default=0.0,
                    help="run a plain device copy of this size first (HBM counter calibration)")
     p.add_argument("--variant", choices=("share", "group", "job"), default="share",
@@ -92,17 +95,25 @@ def parse():
 # workload
 # --------------------------------------------------------------------------
 
-def host_inputs(M):
-    """Seeded host inputs of every row at message M (pack_rr_helper_amd.synth)."""
+def host_inputs(M, dtype="bf16", rows=("ar2", "rs2", "ar4", "rs4", "a2a")):
+    """Seeded host inputs of the rows at message M (pack_rr_helper_amd.synth):
+    bf16 bit patterns (uint16) or float32 values; the all-to-all rows carry raw
+    bits, and ``a2a_ragged`` has segmentCount = 5 mod 8 (the sweep's
+    realigning shape)."""
     from pack_rr_helper_amd import synth
-    n = M // 2
-    return {
-        "ar2": [synth.as_bf16_bits(synth.normal(n, 1, a)) for a in range(2)],
-        "rs2": [synth.as_bf16_bits(synth.normal(n, 1, 10 + a)) for a in range(2)],
-        "ar4": [synth.as_bf16_bits(synth.uniform(n, -2, 2, 3, a)) for a in range(4)],
-        "rs4": [synth.as_bf16_bits(synth.normal(n, 2, s)) for s in range(4)],
-        "a2a": [synth.bits16(n, 4, s) for s in range(4)],
+    f32 = dtype == "f32"
+    n = M // (4 if f32 else 2)
+    fp = (lambda v: v) if f32 else synth.as_bf16_bits
+    bits = synth.bits32 if f32 else synth.bits16
+    make = {
+        "ar2": lambda: [fp(synth.normal(n, 1, a)) for a in range(2)],
+        "rs2": lambda: [fp(synth.normal(n, 1, 10 + a)) for a in range(2)],
+        "ar4": lambda: [fp(synth.uniform(n, -2, 2, 3, a)) for a in range(4)],
+        "rs4": lambda: [fp(synth.normal(n, 2, s)) for s in range(4)],
+        "a2a": lambda: [bits(n, 4, s) for s in range(4)],
+        "a2a_ragged": lambda: [bits(4 * (n // 4 - 3), 5, s) for s in range(4)],
     }
+    return {r: make[r]() for r in rows}
 
 
 def build_rows(inp, rows=("ar2", "rs2", "ar4", "rs4", "a2a"), mode="share"):
@@ -125,69 +136,206 @@ def build_rows(inp, rows=("ar2", "rs2", "ar4", "rs4", "a2a"), mode="share"):
 
 
 # --------------------------------------------------------------------------
-# CPU baseline: the oracle, single thread, one step of the same workload
+# CPU baseline: the oracle beside the GPU, on one thread and on the host's cores
 # --------------------------------------------------------------------------
 
-def cpu_baseline(inp, variant="share"):
-    """Seconds and algorithmic bytes of one step through the oracle: the jobs
-    the GPU step runs (one GPU's share, or every job of the group)."""
+def host_threads():
+    """Threads for the oracle's multi-thread figure: the CPUs this process may
+    run on, at most 16 (one GPU's share of an 8-GPU host's cores)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def oracle_prep(inp, dt):
+    """Read-only oracle inputs derived from the rows' inputs, built once and
+    untimed: each A=4 reduce-scatter helper's scratch of twelve (owner, source)
+    chunks, stand-ins for the reduced chunks an owner receives, and each
+    all-to-all helper slice's packed buffers (the unpack's input)."""
     import numpy as np
     import oracle as orc
+    prep = {}
+    if "rs4" in inp:
+        x = inp["rs4"]
+        R = x[0].size // 4
+        c = orc.geometry(4, 4, 0, 500, R, orc.REDUCE_SCATTER, dt)["chunk"]
+        prep["rs4_scratch"] = [np.concatenate([x[s][o * R + h * c:o * R + (h + 1) * c]
+                                               for o in range(4) for s in range(4) if s != o])
+                               for h in range(4)]
+        prep["rs4_reds"] = [np.ascontiguousarray(x[0][:c]) for _ in range(4)]
+    es = orc.esize(dt)
+    for row in ("a2a", "a2a_ragged"):
+        if row in inp:
+            x = inp[row]
+            seg = x[0].size // 4
+            c = orc.geometry(4, 4, 5, 0, seg, orc.ALLTOALL, dt)["chunk"]
+            prep[row + "_packed"] = [orc.a2a_pack(es, 4, seg, c, h, x) for h in range(4)]
+    return prep
 
-    t_total, nbytes = 0.0, 0
 
-    def timed(fn, b):
-        nonlocal t_total, nbytes
-        t = time.perf_counter()
-        fn()
-        t_total += time.perf_counter() - t
-        nbytes += b
-
+def oracle_jobs(inp, prep, dt, variant="share"):
+    """The GPU step's jobs through the oracle, as (role, algorithmic bytes,
+    callable) in launch order: one GPU's share (3 A=2 helper jobs, one job in
+    every other role) or, for the other variants, every job of the group.
+    Outputs are private to the returned list; inputs are only read.  Every
+    callable binds its arguments when it is made."""
+    import functools
+    import numpy as np
+    import oracle as orc
+    P = functools.partial
     share = variant == "share"
-    n_ar2_helpers, n_a2_actives, n_a4 = (3, 1, 1) if share else (6, 2, 4)
-    BF, AVG, SUM, AR, RS, A2A = orc.BF16, orc.AVG, orc.SUM, orc.ALLREDUCE, orc.REDUCE_SCATTER, orc.ALLTOALL
-    x = inp["ar2"]
-    g = orc.geometry(2, 6, 8, 0, x[0].size, AR, BF)
-    c = g["chunk"]
-    for k in range(n_ar2_helpers):
-        timed(lambda: orc.ar2_helper(BF, AVG, x[0][k * c:(k + 1) * c], x[1][k * c:(k + 1) * c]), 3 * c * 2)
-    out = np.zeros_like(x[0])
-    for a in range(n_a2_actives):
-        timed(lambda: orc.ar_active(BF, AVG, 2, 6, 8, 0, x[0].size, a, x, out), 3 * g["direct_len"] * 2)
-    x = inp["rs2"]
-    R = x[0].size // 2
-    timed(lambda: orc.rs2_active(BF, AVG, x[0][:R], x[1][:R]), 3 * R * 2)
-    if not share:
-        timed(lambda: orc.rs2_active(BF, AVG, x[0][R:], x[1][R:]), 3 * R * 2)
-    x = inp["ar4"]
-    g = orc.geometry(4, 4, 0, 500, x[0].size, AR, BF)
-    c = g["chunk"]
-    for h in range(n_a4):
-        timed(lambda: orc.ar4_helper(BF, AVG, [v[h * c:(h + 1) * c] for v in x]), 5 * c * 2)
-    out = np.zeros_like(x[0])
-    for a in range(n_a4):
-        n = g["dslice"] if a < 3 else g["direct_len"] - 3 * g["dslice"]
-        timed(lambda: orc.ar_active(BF, AVG, 4, 4, 0, 500, x[0].size, a, x, out), 5 * n * 2)
-    x = inp["rs4"]
-    R = x[0].size // 4
-    c = orc.geometry(4, 4, 0, 500, R, RS, BF)["chunk"]
-    for h in range(n_a4):
-        scratch = np.concatenate([x[s][o * R + h * c:o * R + (h + 1) * c]
-                                  for o in range(4) for s in range(4) if s != o])
-        timed(lambda: orc.rs4_pass1(BF, 4, c, scratch), 16 * c * 2)
-    reds = [np.ascontiguousarray(x[0][:c]) for _ in range(4)]
-    for o in range(n_a4):
-        blk = [v[o * R:(o + 1) * R] for v in x]
-        timed(lambda: orc.rs4_pass2(BF, SUM, 4, 4, 500, R, o, blk, reds), (3 * 4 * c + 5 * (R - 4 * c)) * 2)
-    x = inp["a2a"]
-    seg = x[0].size // 4
-    c = orc.geometry(4, 4, 5, 0, seg, A2A, BF)["chunk"]
-    outs = [np.zeros(4 * seg, np.uint16) for _ in range(4)]
-    for h in range(n_a4):
-        packed = []
-        timed(lambda: packed.extend(orc.a2a_pack(2, 4, seg, c, h, x)), 24 * c * 2)
-        timed(lambda: orc.a2a_unpack(2, 4, seg, c, h, packed, outs), 24 * c * 2)
-    return t_total, nbytes
+    n_ar2, n_a2, n_a4 = (3, 1, 1) if share else (6, 2, 4)
+    AVG, SUM = orc.AVG, orc.SUM
+    es = orc.esize(dt)
+    jobs = []
+    if "ar2" in inp:
+        x = inp["ar2"]
+        count = x[0].size
+        g = orc.geometry(2, 6, 8, 0, count, orc.ALLREDUCE, dt)
+        c = g["chunk"]
+        for k in range(n_ar2):
+            jobs.append(("ar2_helper", 3 * c * es,
+                         P(orc.ar2_helper, dt, AVG, x[0][k * c:(k + 1) * c], x[1][k * c:(k + 1) * c])))
+        out = np.zeros_like(x[0])
+        for a in range(n_a2):
+            jobs.append(("ar2_active", 3 * g["direct_len"] * es,
+                         P(orc.ar_active, dt, AVG, 2, 6, 8, 0, count, a, x, out)))
+    if "rs2" in inp:
+        x = inp["rs2"]
+        R = x[0].size // 2
+        for o in range(1 if share else 2):
+            jobs.append(("rs2_owner", 3 * R * es,
+                         P(orc.rs2_active, dt, AVG, x[0][o * R:(o + 1) * R], x[1][o * R:(o + 1) * R])))
+    if "ar4" in inp:
+        x = inp["ar4"]
+        count = x[0].size
+        g = orc.geometry(4, 4, 0, 500, count, orc.ALLREDUCE, dt)
+        c = g["chunk"]
+        for h in range(n_a4):
+            jobs.append(("ar4_helper", 5 * c * es, P(orc.ar4_helper, dt, AVG, [v[h * c:(h + 1) * c] for v in x])))
+        out = np.zeros_like(x[0])
+        for a in range(n_a4):
+            n = g["dslice"] if a < 3 else g["direct_len"] - 3 * g["dslice"]
+            jobs.append(("ar4_active", 5 * n * es, P(orc.ar_active, dt, AVG, 4, 4, 0, 500, count, a, x, out)))
+    if "rs4" in inp:
+        x = inp["rs4"]
+        R = x[0].size // 4
+        c = orc.geometry(4, 4, 0, 500, R, orc.REDUCE_SCATTER, dt)["chunk"]
+        for h in range(n_a4):
+            jobs.append(("rs4_pass1", 16 * c * es, P(orc.rs4_pass1, dt, 4, c, prep["rs4_scratch"][h])))
+        for o in range(n_a4):
+            blk = [v[o * R:(o + 1) * R] for v in x]
+            jobs.append(("rs4_pass2", (3 * 4 * c + 5 * (R - 4 * c)) * es,
+                         P(orc.rs4_pass2, dt, SUM, 4, 4, 500, R, o, blk, prep["rs4_reds"])))
+    for row, tag in (("a2a", ""), ("a2a_ragged", "_ragged")):
+        if row not in inp:
+            continue
+        x = inp[row]
+        seg = x[0].size // 4
+        c = orc.geometry(4, 4, 5, 0, seg, orc.ALLTOALL, dt)["chunk"]
+        outs = [np.zeros_like(v) for v in x]
+        for h in range(n_a4):
+            jobs.append(("a2a_pack" + tag, 24 * c * es, P(orc.a2a_pack, es, 4, seg, c, h, x)))
+            jobs.append(("a2a_unpack" + tag, 24 * c * es,
+                         P(orc.a2a_unpack, es, 4, seg, c, h, prep[row + "_packed"][h], outs)))
+    return jobs
+
+
+def oracle_one_thread(jobs, budget_s, max_reps=100):
+    """Runs the job list in order until `budget_s` seconds of job time (at
+    least once); returns (seconds, bytes, passes)."""
+    t, b, reps = 0.0, 0, 0
+    while (t < budget_s and reps < max_reps) or reps == 0:
+        for _, nb, fn in jobs:
+            t0 = time.perf_counter()
+            fn()
+            t += time.perf_counter() - t0
+            b += nb
+        reps += 1
+    return t, b, reps
+
+
+def oracle_threads(make_jobs, threads, budget_s):
+    """`threads` host threads, each running its own job list (make_jobs())
+    over and over until `budget_s` seconds of wall time have passed (every
+    thread completes at least one pass).  The oracle's C routines run without
+    the interpreter lock, so the threads compute in parallel.  Returns (wall
+    seconds from the common start to the last thread's end, bytes, passes)."""
+    import threading
+    lists = [make_jobs() for _ in range(threads)]
+    done, passes, ends = [0] * threads, [0] * threads, [0.0] * threads
+    gate = threading.Barrier(threads + 1)
+    deadline = [0.0]
+
+    def work(i):
+        gate.wait()
+        while True:
+            for _, nb, fn in lists[i]:
+                fn()
+                done[i] += nb
+            passes[i] += 1
+            if time.perf_counter() >= deadline[0]:
+                break
+        ends[i] = time.perf_counter()
+
+    ts = [threading.Thread(target=work, args=(i,)) for i in range(threads)]
+    for t in ts:
+        t.start()
+    deadline[0] = time.perf_counter() + budget_s
+    gate.wait()
+    start = time.perf_counter()
+    for t in ts:
+        t.join()
+    return max(ends) - start, sum(done), sum(passes)
+
+
+def cpu_baseline(inp, dt, variant, budget_s=(10.0, 8.0), label=""):
+    """The bench line's cpu_baseline object: the oracle on the step's jobs,
+    on `host_threads()` threads (the value) and on one thread."""
+    prep = oracle_prep(inp, dt)
+    t1, b1, r1 = oracle_one_thread(oracle_jobs(inp, prep, dt, variant), budget_s[0])
+    T = host_threads()
+    tT, bT, rT = oracle_threads(lambda: oracle_jobs(inp, prep, dt, variant), T, budget_s[1])
+    return {
+        "value": round(bT / tT / 1e9, 3), "unit": "GB/s", "cores": T, "kind": "oracle",
+        "sample": (f"{label}{variant} variant, one step = {b1 // r1} algorithmic bytes: {rT} step(s) over "
+                   f"{T} threads in {tT:.1f} s wall (each thread its own outputs, same inputs); "
+                   f"host {cpu_model()}"),
+        "single_thread": {"value": round(b1 / t1 / 1e9, 3), "cores": 1,
+                          "sample": f"{r1} step(s), {t1:.1f} s of oracle time"},
+    }
+
+
+def oracle_role_rates(M, dt_name, variant, budget_s=0.3):
+    """The oracle's GB/s per role at message M, on one thread and on
+    host_threads() threads, over the jobs the GPU launch of that role covers
+    (same shapes, host inputs from the same recipe).  Roles are named as the
+    sweep names them."""
+    dt = F32_CODE if dt_name == "f32" else BF16_CODE
+    rows = ("ar2", "rs2", "ar4", "rs4", "a2a", "a2a_ragged")
+    inp = host_inputs(M, dt_name, rows)
+    T, cpu = host_threads(), cpu_model()
+    rates = {}
+    for row in rows:
+        sub = {row: inp[row]}
+        prep = oracle_prep(sub, dt)
+        for role in sorted({j[0] for j in oracle_jobs(sub, prep, dt, variant)}):
+            def make(role=role, sub=sub, prep=prep):
+                return [j for j in oracle_jobs(sub, prep, dt, variant) if j[0] == role]
+            t1, b1, _ = oracle_one_thread(make(), budget_s)
+            tT, bT, _ = oracle_threads(make, T, budget_s)
+            rates[role] = {"threads": T, "gbs": round(bT / tT / 1e9, 3), "gbs_1t": round(b1 / t1 / 1e9, 3),
+                           "sample_mib": M / MIB, "cpu": cpu}
+    return rates
 
 
 # --------------------------------------------------------------------------
@@ -404,18 +552,10 @@ def step_bench(args):
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on one step of the same workload", file=sys.stderr, flush=True)
-        t, b, reps = 0.0, 0, 0
-        while t < 12.0 and reps < 100:
-            dt, db = cpu_baseline(inp, args.variant)
-            t, b, reps = t + dt, b + db, reps + 1
-        result["cpu_baseline"] = {
-            "value": round(b / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{reps} full step(s) (every row, {args.message_mib:g} MiB message, {args.variant} "
-                       f"variant, {b} algorithmic bytes) through the scalar C oracle, single thread, "
-                       f"{t:.1f} s; host "
-                       f"{platform.processor() or platform.machine()}"),
-        }
+        print(f"[bench] timing the CPU oracle on the step's jobs: one thread, then {host_threads()} threads",
+              file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(inp, BF16_CODE, args.variant,
+                                              label=f"{args.message_mib:g} MiB message, every row, ")
     print(json.dumps(result), flush=True)
 
 
@@ -436,6 +576,11 @@ def cache_evictor(torch, mode):
     if mode == "write":
         return buf.zero_
     return lambda: None
+
+
+def mode_of(args):
+    """The sweep times one launch per role: the job variant sweeps as share."""
+    return args.variant if args.variant != "job" else "share"
 
 
 def sweep(args):
@@ -476,7 +621,7 @@ def sweep(args):
         return ts
 
     def record(mib, dt_name, role, kernel, b, ts):
-        return {"message_mib": mib, "dtype": dt_name, "variant": args.variant if args.variant != "job" else "share",
+        return {"message_mib": mib, "dtype": dt_name, "variant": mode_of(args),
                 "flush": args.flush,
                 "row": role, "kernel": kernel, "bytes_per_launch": b,
                 "reps": len(ts), "us_min": round(min(ts) * 1e6, 2),
@@ -487,12 +632,24 @@ def sweep(args):
 
     out = open(args.sweep_out, "w") if args.sweep_out else sys.stdout
     gen = torch.Generator(device="cuda")
+    oracle_cache = {}
     dtypes = {"bf16": (rr.BF16, torch.bfloat16, torch.int16), "f32": (rr.F32, torch.float32, torch.int32)}
     for mib in [float(v) for v in args.sweep_sizes.split(",")]:
         M = int(mib * MIB)
         for dt_name in args.sweep_dtypes.split(","):
             dt, tdt, bits_dt = dtypes[dt_name]
             n = M // W.ESIZE[dt]
+            orates = {}
+            if not args.no_cpu_baseline:
+                # the oracle beside every row, on a sample of at most 64 MiB (its
+                # rate does not depend on the message size past the host caches)
+                sample = min(M, 64 * MIB)
+                key = (dt_name, sample)
+                if key not in oracle_cache:
+                    print(f"[sweep] timing the CPU oracle per role, {dt_name}, {sample / MIB:g} MiB",
+                          file=sys.stderr, flush=True)
+                    oracle_cache[key] = oracle_role_rates(sample, dt_name, mode_of(args))
+                orates = oracle_cache[key]
             for row in ("ar2", "rs2", "ar4", "rs4", "a2a", "a2a_ragged"):
                 gen.manual_seed(zlib.crc32(f"{row}/{dt_name}/{M}".encode()))
                 ranks = 2 if row in ("ar2", "rs2") else 4
@@ -505,7 +662,7 @@ def sweep(args):
                           for _ in range(ranks)]
                 else:
                     xs = [torch.randn(n, device="cuda", generator=gen).to(tdt) for _ in range(ranks)]
-                mode = args.variant if args.variant != "job" else "share"
+                mode = mode_of(args)
                 wl = {"ar2": lambda: W.AR2(xs, dt, rr.AVG, mode=mode), "rs2": lambda: W.RS2(xs, dt, rr.AVG, mode=mode),
                       "ar4": lambda: W.AR4(xs, dt, rr.AVG, mode=mode), "rs4": lambda: W.RS4(xs, dt, rr.SUM, mode=mode),
                       "a2a": lambda: W.A2A(xs, dt, mode=mode), "a2a_ragged": lambda: W.A2A(xs, dt, mode=mode)}[row]()
@@ -514,6 +671,10 @@ def sweep(args):
                     role_call = next(c for c in calls if c[0] == role)
                     name = role + ("_ragged" if row == "a2a_ragged" else "")
                     rec = record(mib, dt_name, name, role_call[1], role_call[2], times_of(role_call[3]))
+                    if name in orates:
+                        o = dict(orates[name])
+                        o["gpu_over_oracle"] = round(rec["gbs_median"] / o["gbs"], 1)
+                        rec["oracle"] = o
                     print(json.dumps(rec), file=out, flush=True)
                 del wl, xs, calls
                 torch.cuda.empty_cache()

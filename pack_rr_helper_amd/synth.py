@@ -9,8 +9,8 @@ stream ``numpy.random.default_rng([seed, r])`` (PCG64):
   shifted by lo; for the power-of-two widths used here (2 and 4) both steps are
   exact, so every value is a representable float32 in [lo, hi).
 * ``normal(n)``: float32 ``rng.standard_normal``.
-* ``bits16(n)``: uniform raw 16-bit patterns (NaN, Inf and subnormal bf16
-  encodings included).
+* ``bits16(n)``, ``bits32(n)``: uniform raw 16- and 32-bit patterns (NaN, Inf
+  and subnormal encodings included).
 * ``as_bf16_bits``: a float32 array rounded to bf16 with torch's CPU
   conversion (round-to-nearest-even), returned as raw uint16 bit patterns.
 """
@@ -33,6 +33,10 @@ def normal(n, seed, rank):
 
 def bits16(n, seed, rank):
     return rng(seed, rank).integers(0, 1 << 16, size=n, dtype=np.uint16)
+
+
+def bits32(n, seed, rank):
+    return rng(seed, rank).integers(0, 1 << 32, size=n, dtype=np.uint32)
 
 
 def small_ints(n, lim, seed, rank):

@@ -40,3 +40,39 @@ def test_more_than_one_gpu_is_refused():
                           capture_output=True, text=True, timeout=120)
     assert proc.returncode == 2
     assert "one GPU" in proc.stderr and proc.stdout == ""
+
+
+M2 = 2 << 20  # a 2 MiB bf16 message: every chunk formula divides evenly but the all-to-all's
+
+
+def _role_bytes(jobs):
+    out = {}
+    for role, nb, _ in jobs:
+        out[role] = out.get(role, 0) + nb
+    return out
+
+
+def test_oracle_jobs_cover_the_step_bytes_per_role():
+    """The CPU baseline runs the same jobs as the GPU step: per role, the
+    algorithmic bytes of one GPU's share (9M/8, 0.75M, 1.5M, 5M/8, 5M/8, M/2,
+    M and 24 all-to-all chunks each way), and 2-4x that for the group."""
+    inp = bench.host_inputs(M2, rows=("ar2", "rs2", "ar4", "rs4", "a2a"))
+    prep = bench.oracle_prep(inp, bench.BF16_CODE)
+    a2a_chunk = (M2 // 8 // 5) // 128 * 128
+    share = {"ar2_helper": 9 * M2 // 8, "ar2_active": 3 * M2 // 4, "rs2_owner": 3 * M2 // 2,
+             "ar4_helper": 5 * M2 // 8, "ar4_active": 5 * M2 // 8, "rs4_pass1": M2 // 2, "rs4_pass2": M2,
+             "a2a_pack": 24 * a2a_chunk * 2, "a2a_unpack": 24 * a2a_chunk * 2}
+    assert _role_bytes(bench.oracle_jobs(inp, prep, bench.BF16_CODE, "share")) == share
+    times = {"ar2_helper": 2, "ar2_active": 2, "rs2_owner": 2}
+    group = {r: b * times.get(r, 4) for r, b in share.items()}
+    assert _role_bytes(bench.oracle_jobs(inp, prep, bench.BF16_CODE, "group")) == group
+
+
+def test_oracle_timers_run_on_one_and_several_threads():
+    inp = bench.host_inputs(M2, rows=("ar2",))
+    prep = bench.oracle_prep(inp, bench.BF16_CODE)
+    jobs = lambda: bench.oracle_jobs(inp, prep, bench.BF16_CODE, "share")
+    t, b, reps = bench.oracle_one_thread(jobs(), 0.0)
+    assert reps == 1 and t > 0 and b == sum(nb for _, nb, _ in jobs())
+    t, b, passes = bench.oracle_threads(jobs, 3, 0.0)
+    assert passes == 3 and t > 0 and b == 3 * sum(nb for _, nb, _ in jobs())
