@@ -512,24 +512,21 @@ public:
         q_[1].shifted = true;
     }
 
-    // Head bytes up to the destination's 16-byte boundary, a 16-byte body
-    // (aligned, or realigned from a source at another offset), and a tail.
+    // One segment per move (tile 0 also copies its head and tail bytes), in
+    // the aligned kernel's queue when source and destination agree modulo 16
+    // bytes and in the realigning kernel's otherwise.
     void add(const void *src, void *dst, int64_t nbytes)
     {
         if (nbytes <= 0)
             return;
         const unsigned char *s = static_cast<const unsigned char *>(src);
         unsigned char *d = static_cast<unsigned char *>(dst);
-        const int64_t head = std::min<int64_t>(nbytes, int64_t((16 - addr(d) % 16) % 16));
-        const int64_t body = ((nbytes - head) / 16) * 16;
-        piece(s, d, head, rr::kCopyBytes, 0);
-        const unsigned char *bs = s + head;
-        const uintptr_t delta = addr(bs) % 16;
-        if (delta == 0)
-            piece(bs, d + head, body, rr::kCopyAligned, 0);
-        else
-            piece(bs - delta, d + head, body, rr::kCopyShifted, int32_t(delta));
-        piece(s + head + body, d + head + body, nbytes - head - body, rr::kCopyBytes, 0);
+        if (addr(s) % 16 == addr(d) % 16) {
+            piece(s, d, nbytes, rr::kCopyAligned, 0);
+        } else {
+            const int64_t head = rr::copy_split(d, nbytes).head;
+            piece(s, d, nbytes, rr::kCopyShifted, int32_t(addr(s + head) % 16));
+        }
     }
 
     hipError_t finish()
@@ -550,27 +547,32 @@ private:
                int32_t shift)
     {
         Queue &q = q_[mode == rr::kCopyShifted ? 1 : 0];
+        const int64_t tv = rr::copy_tile_vecs(mode);
         while (nbytes > 0) {
+            if (q.b.nseg == rr::kMaxCopySegs || q.tiles >= rr::kMaxTilesPerLaunch)
+                flush(q);
+            const rr::CopySplit sp = rr::copy_split(dst, nbytes);
+            int64_t tiles = std::max<int64_t>(1, (sp.nv + tv - 1) / tv);
+            int64_t take = nbytes;
+            const int64_t room = rr::kMaxTilesPerLaunch - q.tiles;
+            if (tiles > room) {
+                // whole tiles of the body only: the rest starts on a 16-byte
+                // destination boundary with the same source shift
+                tiles = room;
+                take = sp.head + room * tv * 16;
+            }
             rr::CopySeg s{};
             s.src = src;
             s.dst = dst;
-            s.nbytes = nbytes;
+            s.nbytes = take;
             s.mode = mode;
             s.shift = shift;
-            if (q.b.nseg == rr::kMaxCopySegs || q.tiles >= rr::kMaxTilesPerLaunch)
-                flush(q);
-            const int64_t per_tile = rr::copy_tile_bytes(mode);
-            const int64_t room = rr::kMaxTilesPerLaunch - q.tiles;
-            if ((s.nbytes + per_tile - 1) / per_tile > room)
-                s.nbytes = room * per_tile;
             q.b.tile0[q.b.nseg] = int32_t(q.tiles);
             q.b.seg[q.b.nseg++] = s;
-            q.tiles += (s.nbytes + per_tile - 1) / per_tile;
-            // a shifted body's source pointer is its aligned base: advancing
-            // it by whole 16-byte vectors keeps both the base and the shift
-            src += s.nbytes;
-            dst += s.nbytes;
-            nbytes -= s.nbytes;
+            q.tiles += tiles;
+            src += take;
+            dst += take;
+            nbytes -= take;
         }
     }
 

@@ -21,7 +21,10 @@ constexpr int kBlock = RR_BLOCK;
 constexpr int kMaxIn = 4;            // inputs per reduction segment (A <= 4)
 constexpr int kMaxRedSegs = 40;      // segments per reduction launch
 constexpr int kMaxCopySegs = 64;     // segments per copy launch
-constexpr int64_t kMaxTilesPerLaunch = int64_t(1) << 22;
+#ifndef RR_MAX_TILES_PER_LAUNCH
+#define RR_MAX_TILES_PER_LAUNCH (int64_t(1) << 22)  // longer batches continue in further launches
+#endif
+constexpr int64_t kMaxTilesPerLaunch = RR_MAX_TILES_PER_LAUNCH;
 
 #ifndef RR_UNROLL
 #define RR_UNROLL 4                  // 16-byte vectors per thread per input
@@ -55,7 +58,6 @@ constexpr int kShiftUnroll = RR_SHIFT_UNROLL;
 // 2-4% faster.  Reductions and short copies measured best at full occupancy.
 constexpr int64_t kCopyThrottleTiles = 4096;
 constexpr unsigned kCopyThrottleLds = 26 * 1024;
-constexpr int kCopyBytesPerThread = 16;
 
 // One reduction segment: out[i] = RND(scale * fold_k in[k][i]) for i < n.
 // vec == 1: every pointer is 16-byte aligned and n is a multiple of the
@@ -80,13 +82,15 @@ struct RedBatch {
     RedSeg seg[kMaxRedSegs];
 };
 
-enum CopyMode : int32_t { kCopyBytes = 0, kCopyAligned = 1, kCopyShifted = 2 };
+enum CopyMode : int32_t { kCopyAligned = 1, kCopyShifted = 2 };
 
-// One copy segment of nbytes.  kCopyAligned: src and dst 16-byte aligned,
-// nbytes a multiple of 16.  kCopyShifted: dst 16-byte aligned, nbytes a
-// multiple of 16, and the source starts `shift` bytes (1..15) past the
-// 16-byte aligned address `src`.  kCopyBytes: anything (heads and tails
-// shorter than 16 bytes).
+// One copy segment: nbytes from src to dst, both at any byte address.  The
+// bytes before dst's first 16-byte boundary (the head) and those after the
+// last whole 16-byte vector (the tail) are copied byte by byte by tile 0;
+// the vectors between them (the body) are spread over the segment's tiles.
+// kCopyAligned: src and dst agree modulo 16 bytes, so the body's source is
+// 16-byte aligned too.  kCopyShifted: they disagree; the body's first source
+// byte lies `shift` bytes (1..15) past a 16-byte boundary.
 struct CopySeg {
     const unsigned char *src;
     unsigned char *dst;
@@ -97,6 +101,20 @@ struct CopySeg {
 
 static_assert(sizeof(CopySeg) == 32, "a copy descriptor is one 32-byte scalar load");
 
+// Head bytes (at most 15), 16-byte body vectors and tail bytes (at most 15)
+// of a copy of nbytes to dst.
+struct CopySplit {
+    int64_t head, nv, tail;
+};
+
+__host__ __device__ inline CopySplit copy_split(const unsigned char *dst, int64_t nbytes)
+{
+    const int64_t to_line = int64_t((16u - unsigned(reinterpret_cast<uintptr_t>(dst) & 15u)) & 15u);
+    const int64_t head = to_line < nbytes ? to_line : nbytes;
+    const int64_t nv = (nbytes - head) / 16;
+    return CopySplit{head, nv, nbytes - head - 16 * nv};
+}
+
 struct CopyBatch {
     int32_t tile0[kMaxCopySegs];
     int32_t nseg;
@@ -104,9 +122,10 @@ struct CopyBatch {
     CopySeg seg[kMaxCopySegs];
 };
 
-// Work per tile (one workgroup), matching the kernels' tiling.
+// Work per tile (one workgroup), matching the kernels' tiling.  A copy
+// segment spans max(1, ceil(nv / copy_tile_vecs(mode))) tiles.
 int64_t red_tile_elems(bool vec, bool bf16);
-int64_t copy_tile_bytes(int32_t mode);
+int64_t copy_tile_vecs(int32_t mode);
 
 // How a batch is launched.  Every form runs the same work per tile; they
 // differ in how a workgroup learns its segment before its first load:

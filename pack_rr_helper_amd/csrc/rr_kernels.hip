@@ -260,12 +260,28 @@ __global__ __launch_bounds__(kBlock) void reduce_one_kernel(const void *in0, con
 // Copy
 // ---------------------------------------------------------------------------
 
+constexpr int kWave = 64;  // gfx950 runs wave64
+
+// Tile 0 of a copy segment also moves its head and tail bytes (at most 15
+// each): the first wave's lanes the head, the second wave's the tail.
+__device__ __forceinline__ void copy_edges(const CopySeg &sg, const CopySplit &sp)
+{
+    const int x = (int)threadIdx.x;
+    if (x < sp.head) {
+        sg.dst[x] = sg.src[x];
+    } else if (x >= kWave && x - kWave < sp.tail) {
+        const int64_t i = sp.head + 16 * sp.nv + (x - kWave);
+        sg.dst[i] = sg.src[i];
+    }
+}
+
 __device__ __forceinline__ void copy_aligned(const CopySeg &sg, int64_t lt)
 {
     constexpr int64_t kTileVecs = int64_t(kBlock) * kCopyUnroll;
-    const int64_t nv = sg.nbytes / 16;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(sg.src);
-    u32x4 *dst = reinterpret_cast<u32x4 *>(sg.dst);
+    const CopySplit sp = copy_split(sg.dst, sg.nbytes);
+    const int64_t nv = sp.nv;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(sg.src + sp.head);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(sg.dst + sp.head);
     if ((lt + 1) * kTileVecs <= nv) {
         u32x4 x[kCopyUnroll];
 #pragma unroll
@@ -282,9 +298,9 @@ __device__ __forceinline__ void copy_aligned(const CopySeg &sg, int64_t lt)
             st16(dst + v, ld16(src + v));
         }
     }
+    if (lt == 0)
+        copy_edges(sg, sp);
 }
-
-constexpr int kWave = 64;  // gfx950 runs wave64
 
 // The 16-byte vector held by the next lane of this wave (ds_bpermute).  Call
 // it outside any lane-dependent branch: a lane reading from a lane that is
@@ -309,24 +325,25 @@ __device__ __forceinline__ u32x4 realign(u32x4 a, u32x4 b, unsigned r)
     return o;
 }
 
-// Output vector v is bytes [shift + 16v, shift + 16v + 16) of the aligned
-// source: the tail of source word v and the head of word v+1.  Each lane
-// loads its own word once (non-temporal) and takes word v+1 from the next
-// lane of its wave; the wave's last lane, whose neighbour word belongs to
-// another wave or tile, loads word v+1 itself, issued with the other loads.
-// In a partial tile a lane also loads word nv, which its left neighbour
-// needs, and stores nothing.  Word nv always holds at least one byte of this
-// move (shift > 0), and an aligned 16-byte word never straddles a page, so
-// that read stays in mapped memory even where the source buffer ends inside
-// the word.
+// Body vector v is bytes [shift + 16v, shift + 16v + 16) of the aligned
+// source base (the body's first source byte less `shift`): the tail of
+// source word v and the head of word v+1.  Each lane loads its own word once
+// (non-temporal) and takes word v+1 from the next lane of its wave; the
+// wave's last lane, whose neighbour word belongs to another wave or tile,
+// loads word v+1 itself, issued with the other loads.  In a partial tile a
+// lane also loads word nv, which its left neighbour needs, and stores
+// nothing.  Word nv always holds at least one byte of the body (shift > 0),
+// and an aligned 16-byte word never straddles a page, so that read stays in
+// mapped memory even where the source buffer ends inside the word.
 template <int Q>
 __device__ __forceinline__ void copy_shifted(const CopySeg &sg, int64_t lt)
 {
     constexpr int64_t kTileVecs = int64_t(kBlock) * kShiftUnroll;
-    const int64_t nv = sg.nbytes / 16;
+    const CopySplit sp = copy_split(sg.dst, sg.nbytes);
+    const int64_t nv = sp.nv;
     const unsigned r = (unsigned)(sg.shift & 3);
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(sg.src);
-    u32x4 *dst = reinterpret_cast<u32x4 *>(sg.dst);
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(sg.src + sp.head - sg.shift);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(sg.dst + sp.head);
     const bool wave_end = (threadIdx.x & (kWave - 1)) == kWave - 1;
     const u32x4 zero = {0u, 0u, 0u, 0u};
     u32x4 a[kShiftUnroll], c[kShiftUnroll];
@@ -343,7 +360,7 @@ __device__ __forceinline__ void copy_shifted(const CopySeg &sg, int64_t lt)
             const u32x4 b = wave_end ? c[u] : nb;
             st16(dst + vec_index<kShiftUnroll>(lt, u), realign<Q>(a[u], b, r));
         }
-    } else {
+    } else if (nv > 0) {  // uniform across the workgroup
 #pragma unroll
         for (int u = 0; u < kShiftUnroll; ++u) {
             const int64_t v = vec_index<kShiftUnroll>(lt, u);
@@ -359,26 +376,14 @@ __device__ __forceinline__ void copy_shifted(const CopySeg &sg, int64_t lt)
                 st16(dst + v, realign<Q>(a[u], b, r));
         }
     }
+    if (lt == 0)
+        copy_edges(sg, sp);
 }
 
-__device__ __forceinline__ void copy_bytes(const CopySeg &sg, int64_t lt)
-{
-    const int64_t base = lt * (int64_t)(kBlock * kCopyBytesPerThread) + threadIdx.x;
-    for (int j = 0; j < kCopyBytesPerThread; ++j) {
-        const int64_t i = base + (int64_t)j * kBlock;
-        if (i >= sg.nbytes)
-            return;
-        sg.dst[i] = sg.src[i];
-    }
-}
-
-// Aligned bodies and byte heads/tails.
+// Segments whose source and destination agree modulo 16 bytes.
 __device__ __forceinline__ void copy_seg(const CopySeg &sg, int64_t lt)
 {
-    if (sg.mode == kCopyAligned)
-        copy_aligned(sg, lt);
-    else
-        copy_bytes(sg, lt);
+    copy_aligned(sg, lt);
 }
 
 __global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch b)
@@ -424,11 +429,9 @@ int64_t red_tile_elems(bool vec, bool bf16)
     return vec ? int64_t(kBlock) * kUnroll * (bf16 ? 8 : 4) : int64_t(kBlock) * kScalarPerThread;
 }
 
-int64_t copy_tile_bytes(int32_t mode)
+int64_t copy_tile_vecs(int32_t mode)
 {
-    if (mode == kCopyBytes)
-        return int64_t(kBlock) * kCopyBytesPerThread;
-    return int64_t(kBlock) * (mode == kCopyShifted ? kShiftUnroll : kCopyUnroll) * 16;
+    return int64_t(kBlock) * (mode == kCopyShifted ? kShiftUnroll : kCopyUnroll);
 }
 
 namespace {

@@ -16,22 +16,30 @@ HEADERS = [os.path.join(ROOT, "pack_rr_helper_amd", "csrc", "rr_internal.h"),
            os.path.join(ROOT, "include", "rr.h")]
 
 
-def build():
-    tmp = LIB + ".tmp"
+# a variant with at most 5 tiles per launch: batches and single moves or
+# items longer than that continue in further launches
+CAPPED_LIB = os.path.join(HERE, "libhostsim_cap5.so")
+CAPPED_DEFINES = ("RR_MAX_TILES_PER_LAUNCH=5",)
+
+
+def build(lib=LIB, defines=()):
+    tmp = lib + ".tmp"
     subprocess.run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-D__HIP_PLATFORM_AMD__",
+                    *[f"-D{d}" for d in defines],
                     "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
                     "-I", os.path.join(ROOT, "pack_rr_helper_amd", "csrc"),
                     "-o", tmp, *SOURCES, "-L/opt/rocm/lib", "-lamdhip64"], check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 class Sim:
-    def __init__(self):
-        if not os.path.exists(LIB) or any(os.path.getmtime(s) > os.path.getmtime(LIB)
+    def __init__(self, capped=False):
+        lib, defines = (CAPPED_LIB, CAPPED_DEFINES) if capped else (LIB, ())
+        if not os.path.exists(lib) or any(os.path.getmtime(s) > os.path.getmtime(lib)
                                           for s in SOURCES + HEADERS):
-            build()
-        self.L = ctypes.CDLL(LIB)
+            build(lib, defines)
+        self.L = ctypes.CDLL(lib)
         self.L.sim_message.restype = ctypes.c_char_p
         self.L.sim_register.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
         self.L.rr_last_error.restype = ctypes.c_char_p

@@ -11,6 +11,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <utility>
 #include <vector>
 
@@ -159,11 +160,9 @@ int64_t red_tile_elems(bool vec, bool bf16)
     return vec ? int64_t(kBlock) * kUnroll * (bf16 ? 8 : 4) : int64_t(kBlock) * kScalarPerThread;
 }
 
-int64_t copy_tile_bytes(int32_t mode)
+int64_t copy_tile_vecs(int32_t mode)
 {
-    if (mode == kCopyBytes)
-        return int64_t(kBlock) * kCopyBytesPerThread;
-    return int64_t(kBlock) * (mode == kCopyShifted ? kShiftUnroll : kCopyUnroll) * 16;
+    return int64_t(kBlock) * (mode == kCopyShifted ? kShiftUnroll : kCopyUnroll);
 }
 
 hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, hipStream_t)
@@ -219,48 +218,63 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
         const int64_t lt = st.second;
         if ((sg.mode == kCopyShifted) != shifted)
             violation("copy mode in the wrong kernel", uintptr_t(sg.dst), sg.mode);
-        if (sg.mode == kCopyBytes) {
-            for (int x = 0; x < kBlock; ++x)
-                for (int j = 0; j < kCopyBytesPerThread; ++j) {
-                    const int64_t i = lt * (int64_t(kBlock) * kCopyBytesPerThread) + x + int64_t(j) * kBlock;
-                    if (i >= sg.nbytes)
-                        break;
-                    copy_byte(sg.src, sg.dst, i);
-                }
-            continue;
-        }
-        const int unroll = sg.mode == kCopyShifted ? kShiftUnroll : kCopyUnroll;
-        const int64_t nv = sg.nbytes / 16, tv = int64_t(kBlock) * unroll;
-        if (uintptr_t(sg.dst) % 16 || uintptr_t(sg.src) % 16 || sg.nbytes % 16)
-            violation("unaligned copy body", uintptr_t(sg.dst), sg.nbytes);
+        if (sg.mode != kCopyAligned && sg.mode != kCopyShifted)
+            violation("unknown copy mode", uintptr_t(sg.dst), sg.mode);
+        // the move's split, recomputed from its definition: head bytes up to
+        // the destination's 16-byte boundary, whole 16-byte body vectors, tail
+        const uintptr_t d = uintptr_t(sg.dst);
+        const int64_t head = std::min<int64_t>(sg.nbytes, int64_t((16 - d % 16) % 16));
+        const int64_t nv = (sg.nbytes - head) / 16, tail = sg.nbytes - head - 16 * nv;
+        const unsigned char *bsrc = sg.src + head;
+        const bool shift_mode = sg.mode == kCopyShifted;
+        if ((d + uintptr_t(head)) % 16 && nv > 0)
+            violation("copy body destination not 16-byte aligned", d, head);
+        if (!shift_mode && uintptr_t(bsrc) % 16 && nv > 0)
+            violation("aligned copy body with an unaligned source", uintptr_t(bsrc), 16);
+        if (shift_mode && (sg.shift < 1 || sg.shift > 15 || int64_t(uintptr_t(bsrc) % 16) != sg.shift))
+            violation("realigned copy with a wrong source shift", uintptr_t(bsrc), sg.shift);
+        const int unroll = shift_mode ? kShiftUnroll : kCopyUnroll;
+        const int64_t tv = int64_t(kBlock) * unroll;
+        const int s = st.first;
+        const int64_t seg_tiles = (s + 1 < b.nseg ? int64_t(b.tile0[s + 1]) : total_tiles) - b.tile0[s];
+        if (seg_tiles != std::max<int64_t>(1, (nv + tv - 1) / tv))
+            violation("copy segment tile count differs from its body", d, seg_tiles);
+        const unsigned char *base = bsrc - (shift_mode ? sg.shift : 0);  // aligned words read
         const bool full = (lt + 1) * tv <= nv;
-        for (int x = 0; x < kBlock; ++x)
-            for (int u = 0; u < unroll; ++u) {
-                const int64_t v = lt * tv + x + int64_t(u) * kBlock;
-                if (!full && v >= nv)
-                    break;
-                if (sg.mode == kCopyAligned) {
+        if (full || nv > 0)
+            for (int x = 0; x < kBlock; ++x)
+                for (int u = 0; u < unroll; ++u) {
+                    const int64_t v = lt * tv + x + int64_t(u) * kBlock;
+                    if (!full && v >= nv)
+                        break;
+                    if (shift_mode) {
+                        // each lane loads aligned word v whole; the wave's last lane
+                        // also loads word v+1 (the others take it from the next lane)
+                        const bool wave_end = x % 64 == 63;
+                        if (!touches(uintptr_t(base) + uintptr_t(v * 16), 16) ||
+                            (wave_end && !touches(uintptr_t(base) + uintptr_t((v + 1) * 16), 16)))
+                            violation("realigned word outside every buffer", uintptr_t(base) + v * 16, 32);
+                    }
                     for (int e = 0; e < 16; ++e)
-                        copy_byte(sg.src, sg.dst, v * 16 + e);
-                } else {
-                    // each lane loads aligned word v whole; the wave's last lane
-                    // also loads word v+1 (the others take it from the next lane)
-                    const bool wave_end = x % 64 == 63;
-                    if (!touches(uintptr_t(sg.src) + uintptr_t(v * 16), 16) ||
-                        (wave_end && !touches(uintptr_t(sg.src) + uintptr_t((v + 1) * 16), 16)))
-                        violation("realigned word outside every buffer", uintptr_t(sg.src) + v * 16, 32);
-                    for (int e = 0; e < 16; ++e)
-                        copy_byte(sg.src + sg.shift, sg.dst, v * 16 + e);
+                        copy_byte(sg.src, sg.dst, head + v * 16 + e);
                 }
-            }
-        if (sg.mode == kCopyShifted && !full)
+        if (shift_mode && !full && nv > 0)
             // a partial tile's lanes also load word nv for their left neighbour
             for (int x = 0; x < kBlock; ++x)
                 for (int u = 0; u < unroll; ++u) {
                     const int64_t v = lt * tv + x + int64_t(u) * kBlock;
-                    if (v == nv && !touches(uintptr_t(sg.src) + uintptr_t(v * 16), 16))
-                        violation("realigned word outside every buffer", uintptr_t(sg.src) + v * 16, 16);
+                    if (v == nv && !touches(uintptr_t(base) + uintptr_t(v * 16), 16))
+                        violation("realigned word outside every buffer", uintptr_t(base) + v * 16, 16);
                 }
+        if (lt == 0) {
+            // tile 0's first wave copies the head bytes, its second wave the tail
+            if (head > 15 || tail > 15)
+                violation("copy head or tail longer than 15 bytes", d, head + tail);
+            for (int64_t i = 0; i < head; ++i)
+                copy_byte(sg.src, sg.dst, i);
+            for (int64_t i = 0; i < tail; ++i)
+                copy_byte(sg.src, sg.dst, head + 16 * nv + i);
+        }
     }
     return hipSuccess;
 }

@@ -455,10 +455,12 @@ def test_every_launch_form_is_replayed(sim, orc):
     assert np.array_equal(ob[lead:lead + R], ref)
     assert forms(0) == [1, 1, 1]
 
-    # copies: an aligned all-to-all pack (twelve equal moves) runs on the
-    # uniform grid; a ragged unpack's byte heads and tails do not
+    # copies: pack and unpack issue one segment per chunk move (tile 0 also
+    # copies its head and tail bytes), so the aligned case (twelve moves, one
+    # launch per call) and a ragged segmentCount (aligned and realigning
+    # moves, two launches per call) all run on the uniform grid
     A, H, nc = 4, 4, 5
-    for seg, want in ((5 * 128 * 40, 1), (5 * 128 * 40 + 3, 0)):   # chunks of several tiles
+    for seg, launches in ((5 * 128 * 40, 2), (5 * 128 * 40 + 3, 4)):   # chunks of several tiles
         before = forms(1)
         c = orc.geometry(A, H, nc, 0, seg, A2A, BF16)["chunk"]
         src = [sim.buf(bits(A * seg, 44, s), writable=False) for s in range(A)]
@@ -477,5 +479,62 @@ def test_every_launch_form_is_replayed(sim, orc):
         for d in range(A):
             assert np.array_equal(outs[d], expect[d])
         after = forms(1)
-        assert after[1] > before[1]                      # uniform grid used
-        assert (after[0] > before[0]) == (want == 0)     # table only for the ragged case
+        assert after[0] == before[0] and after[2] == before[2]
+        assert after[1] - before[1] == launches
+
+
+# --------------------------------------------------------------------------
+# launches capped at 5 tiles: long moves and items continue in further launches
+# --------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def capped():
+    return Sim(capped=True)
+
+
+@pytest.mark.parametrize("seg,out_lead", [(5 * 128 * 200, 0), (5 * 128 * 200 + 3, 0), (5 * 128 * 200, 1),
+                                          (5 * 128 * 37 + 5, 3)])
+def test_copies_longer_than_a_launch_continue(capped, orc, seg, out_lead):
+    """Each chunk move spans 7 body tiles, more than one launch holds: the
+    launcher cuts it after whole tiles, and the rest starts on a 16-byte
+    destination boundary with the same source shift in the next launch."""
+    sim = capped
+    sim.reset()
+    A, H, nc, h = 4, 4, 5, 1
+    c = orc.geometry(A, H, nc, 0, seg, A2A, BF16)["chunk"]
+    src = [sim.buf(bits(A * seg, 60, s), writable=False) for s in range(A)]
+    dst = [sim.buf(np.zeros((A - 1) * c, np.uint16)) for _ in range(A)]
+    L0 = sim.L.sim_launches()
+    sim.call("rr_a2a_pack", rel(A, H, nc, 0, seg), BF16, h, parr(*[ptr(s) for s in src]),
+             parr(*[ptr(d) for d in dst]), None)
+    tiles = -(-(c * 2) // 8192)
+    assert sim.L.sim_launches() - L0 >= 12 * tiles // 5
+    ref = orc.a2a_pack(2, A, seg, c, h, src)
+    for d in range(A):
+        assert np.array_equal(dst[d].view(np.uint8), ref[d])
+    recv = [sim.buf(d.copy(), writable=False) for d in dst]
+    outs = [sim.buf(np.full(A * seg + out_lead + 8, 0x3C, np.uint16)) for _ in range(A)]
+    sim.call("rr_a2a_unpack", rel(A, H, nc, 0, seg), BF16, h, parr(*[ptr(r) for r in recv]),
+             parr(*[ptr(o, out_lead) for o in outs]), None)
+    expect = [np.full(A * seg, 0x3C, np.uint16) for _ in range(A)]
+    orc.a2a_unpack(2, A, seg, c, h, ref, expect)
+    for d in range(A):
+        assert np.array_equal(outs[d][out_lead:out_lead + A * seg], expect[d])
+        assert np.all(outs[d][:out_lead] == 0x3C) and np.all(outs[d][out_lead + A * seg:] == 0x3C)
+
+
+@pytest.mark.parametrize("lead", [0, 3])
+def test_reductions_longer_than_a_launch_continue(capped, orc, lead):
+    sim = capped
+    sim.reset()
+    R = 8192 * 23 + 77                     # 23 vector tiles and a tail, plus a head when lead > 0
+    x0, x1 = bits(R, 61, 0), bits(R, 61, 1)
+    a = sim.buf(padded(x0, lead), writable=False)
+    b = sim.buf(padded(x1, lead), writable=False)
+    out = sim.buf(np.zeros(R + lead + 16, np.uint16))
+    L0 = sim.L.sim_launches()
+    sim.call("rr_active_add_scale", rel(2, 6, 8, 0, R), RS, BF16, AVG, 0, parr(ptr(a, lead), ptr(b, lead)), 2,
+             ptr(out, lead), None)
+    assert sim.L.sim_launches() - L0 >= 5
+    assert np.array_equal(out[lead:lead + R], orc.rs2_active(BF16, AVG, x0, x1))
+    assert np.all(out[:lead] == 0) and np.all(out[lead + R:] == 0)
