@@ -25,7 +25,10 @@ between the launches, in GB/s (10^9 bytes/s).  A second timed region puts a
 timing-only HIP event between consecutive launches on their stream; less the
 events' own cost per launch, it gives each launch's duration, and the kernel
 family with the largest share of the step's time is reported against the
-8 TB/s HBM peak in ``roofline``.  ``cpu_baseline`` times the CPU oracle on
+8 TB/s HBM peak in ``roofline``.  ``other_variants`` repeats the first timed
+region with the launches of the other variants (``--no-other-variants`` skips
+it; profiling runs use that flag so that they hold only the named variant's
+launches).  ``cpu_baseline`` times the CPU oracle on
 the same jobs, on the host's cores (up to 16 threads, the value) and on one
 thread; the sweep records both oracle rates beside every row.
 
@@ -72,6 +75,8 @@ def parse():
     p.add_argument("--message-mib", type=float, default=64.0)
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU oracle timings (the step's cpu_baseline, the sweep rows' oracle)")
+    p.add_argument("--no-other-variants", action="store_true",
+                   help="skip timing the step in the variants other than --variant")
     p.add_argument("--calibrate-copy-mib", type=float, default=0.0,
                    help="run a plain device copy of this size first (HBM counter calibration)")
     p.add_argument("--variant", choices=("share", "group", "job"), default="share",
@@ -405,6 +410,33 @@ def hip_runtime():
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hip_runtime_api.h: timing-only events
 
 
+def time_variant(inp, mode, steps, warmup, stream):
+    """Timed region 1 alone (K whole steps, nothing between launches) for the
+    rows built in another variant: step bytes, launches and ms per step."""
+    import torch
+    wls = build_rows(inp, mode=mode)
+    calls = [c for wl in wls.values() for c in wl.calls(stream)]
+    for _ in range(warmup):
+        for _, _, _, fn in calls:
+            fn()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(steps):
+        for _, _, _, fn in calls:
+            fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    b, n = sum(c[2] for c in calls), len(calls)
+    del wls, calls
+    torch.cuda.empty_cache()
+    gbs = b / (ms * 1e-3) / 1e9
+    return {"value": round(gbs, 1), "unit": "GB/s", "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
+            "ms_per_step": round(ms, 5), "launches_per_step": n, "algorithmic_bytes_per_step": b,
+            "variant_means": VARIANTS[mode]}
+
+
 def step_bench(args):
     import ctypes
     import torch
@@ -551,6 +583,14 @@ def step_bench(args):
         },
         "cpu_baseline": None,
     }
+    if not args.no_other_variants:
+        # the same inputs and K steps with each role's launch covering the
+        # jobs of the other variants (first timed region only)
+        result["other_variants"] = {}
+        for other in VARIANTS:
+            if other != args.variant:
+                print(f"[bench] timing the {other} variant", file=sys.stderr, flush=True)
+                result["other_variants"][other] = time_variant(inp, other, args.steps, args.warmup, stream)
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on the step's jobs: one thread, then {host_threads()} threads",
               file=sys.stderr, flush=True)
