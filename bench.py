@@ -52,8 +52,10 @@ PEAK_GBS = 8000.0  # MI355X HBM3E, published
 KERNEL_FORMS = {
     "reduce<bf16>": "reduce_one_kernel<bf16,K> (one aligned segment), reduce_uniform_kernel<bf16> "
                     "(equal segments), reduce_kernel<bf16> (tile table): one per-tile code, three "
-                    "launch forms",
-    "reduce<f32>": "reduce_one_kernel<f32,K>, reduce_uniform_kernel<f32>, reduce_kernel<f32>",
+                    "launch forms (reduce_shifted_*<bf16> realign views at other offsets; the "
+                    "benchmark's buffers are aligned)",
+    "reduce<f32>": "reduce_one_kernel<f32,K>, reduce_uniform_kernel<f32>, reduce_kernel<f32> "
+                   "(reduce_shifted_*<f32> for views at other offsets)",
     "copy": "copy_uniform_kernel, copy_kernel, copy_shifted_uniform_kernel, copy_shifted_kernel",
 }
 VARIANTS = {

@@ -28,6 +28,12 @@
  *     on different streams must not write the same buffers.
  *   - Buffer sizes are the caller's contract (they are stated per entry
  *     point); the library cannot check them.
+ *   - Every device pointer must be aligned to the element size (RR_EINVAL
+ *     otherwise); any such offset is served by 16-byte vector loads and
+ *     stores.  Buffers at 16-byte boundaries take the direct path; views at
+ *     other offsets are realigned in registers, and the few elements before
+ *     the first and after the last whole 16-byte output vector are computed
+ *     one by one.
  *   - Every call validates its arguments before any HIP call and returns an
  *     rr_status; a thread-local message is available from rr_last_error().
  *     No exception crosses the ABI.  RR_EHIP means a HIP launch failed.

@@ -191,79 +191,86 @@ class RedLauncher {
 public:
     RedLauncher(bool bf16, hipStream_t st) : bf16_(bf16), st_(st)
     {
-        memset(&b_, 0, sizeof b_);
-        b_.bf16 = bf16;
+        memset(q_, 0, sizeof q_);
+        q_[0].b.bf16 = q_[1].b.bf16 = bf16;
+        q_[1].shifted = true;
     }
 
-    // Splits one item into an unaligned head, a 16-byte vector body and a
-    // tail when every pointer agrees modulo 16 bytes; otherwise the whole
-    // item takes the element-wise path.
+    // One segment per item (tile 0 also computes its element-wise head and
+    // tail): in the aligned kernels' queue when every pointer is 16-byte
+    // aligned, in the realigning kernels' queue otherwise.
     void add(const RedItem &it, int64_t es)
     {
         if (it.n <= 0)
             return;
-        const uintptr_t m = addr(it.out) % 16;
-        bool agree = true;
+        bool aligned = addr(it.out) % 16 == 0;
         for (int k = 0; k < it.k; ++k)
-            agree = agree && (addr(it.in[k]) % 16 == m);
-        if (!agree) {
-            piece(it, 0, it.n, false, es);
-            return;
-        }
-        const int64_t ve = 16 / es;
-        const int64_t head = std::min<int64_t>(it.n, int64_t((16 - m) % 16) / es);
-        const int64_t body = ((it.n - head) / ve) * ve;
-        piece(it, 0, head, false, es);
-        piece(it, head, body, true, es);
-        piece(it, head + body, it.n - head - body, false, es);
+            aligned = aligned && addr(it.in[k]) % 16 == 0;
+        piece(it, aligned ? rr::kRedAligned : rr::kRedShifted, es);
     }
 
     hipError_t finish()
     {
-        flush();
+        flush(q_[0]);
+        flush(q_[1]);
         return err_;
     }
 
 private:
-    void piece(const RedItem &it, int64_t off, int64_t n, bool vec, int64_t es)
+    struct Queue {
+        rr::RedBatch b;
+        int64_t tiles;
+        bool shifted;
+    };
+
+    void piece(const RedItem &it, int32_t mode, int64_t es)
     {
+        Queue &q = q_[mode == rr::kRedShifted ? 1 : 0];
+        const int64_t tv = rr::red_tile_vecs(mode), ve = 16 / es;
+        int64_t off = 0, n = it.n;
         while (n > 0) {
+            if (q.b.nseg == rr::kMaxRedSegs || q.tiles >= rr::kMaxTilesPerLaunch)
+                flush(q);
             rr::RedSeg s{};
             for (int k = 0; k < it.k; ++k)
                 s.in[k] = static_cast<const char *>(it.in[k]) + off * es;
             s.out = static_cast<char *>(it.out) + off * es;
+            const rr::RedSplit sp = rr::red_split(s.out, n, es);
+            int64_t tiles = std::max<int64_t>(1, (sp.nv + tv - 1) / tv);
+            int64_t take = n;
+            const int64_t room = rr::kMaxTilesPerLaunch - q.tiles;
+            if (tiles > room) {
+                // whole tiles of the body only: the rest starts on a 16-byte
+                // output boundary with every input's shift unchanged
+                tiles = room;
+                take = sp.head + room * tv * ve;
+            }
             s.k = it.k;
-            s.vec = vec;
+            s.mode = mode;
             s.scale = it.scale;
-            s.n = n;
-            if (b_.nseg == rr::kMaxRedSegs || tiles_ >= rr::kMaxTilesPerLaunch)
-                flush();
-            const int64_t per_tile = rr::red_tile_elems(vec, bf16_);
-            const int64_t room = rr::kMaxTilesPerLaunch - tiles_;
-            if ((s.n + per_tile - 1) / per_tile > room)
-                s.n = room * per_tile;
-            b_.tile0[b_.nseg] = int32_t(tiles_);
-            b_.seg[b_.nseg++] = s;
-            tiles_ += (s.n + per_tile - 1) / per_tile;
-            off += s.n;
-            n -= s.n;
+            s.n = take;
+            q.b.tile0[q.b.nseg] = int32_t(q.tiles);
+            q.b.seg[q.b.nseg++] = s;
+            q.tiles += tiles;
+            off += take;
+            n -= take;
         }
     }
 
-    void flush()
+    void flush(Queue &q)
     {
-        if (b_.nseg == 0)
+        if (q.b.nseg == 0)
             return;
-        const hipError_t e = rr::launch_reduce(b_, tiles_, st_);
+        const hipError_t e = rr::launch_reduce(q.b, q.tiles, q.shifted, st_);
         if (e != hipSuccess && err_ == hipSuccess)
             err_ = e;
-        memset(&b_, 0, sizeof b_);
-        b_.bf16 = bf16_;
-        tiles_ = 0;
+        const bool shifted = q.shifted;
+        memset(&q, 0, sizeof q);
+        q.b.bf16 = bf16_;
+        q.shifted = shifted;
     }
 
-    rr::RedBatch b_;
-    int64_t tiles_ = 0;
+    Queue q_[2];
     bool bf16_;
     hipStream_t st_;
     hipError_t err_ = hipSuccess;
@@ -700,7 +707,7 @@ LaunchShape uniform_or_table(const Batch &b, int64_t total_tiles)
 
 LaunchShape reduce_shape(const RedBatch &b, int64_t total_tiles)
 {
-    if (b.nseg == 1 && b.seg[0].vec && b.seg[0].k >= 1 && b.seg[0].k <= kMaxIn)
+    if (b.nseg == 1 && b.seg[0].mode == kRedAligned && b.seg[0].k >= 1 && b.seg[0].k <= kMaxIn)
         return LaunchShape{kFormOne, total_tiles, 1};
     return uniform_or_table(b, total_tiles);
 }

@@ -43,8 +43,13 @@ constexpr int64_t kMaxTilesPerLaunch = RR_MAX_TILES_PER_LAUNCH;
                                      // in flight
 #endif
 
+#ifndef RR_SHIFT_RED_UNROLL
+#define RR_SHIFT_RED_UNROLL 2        // 16-byte vectors per thread per input in a realigning
+                                     // reduction tile (8 KiB per input)
+#endif
+
 constexpr int kUnroll = RR_UNROLL;
-constexpr int kScalarPerThread = 4;  // elements per thread in a scalar tile
+constexpr int kShiftRedUnroll = RR_SHIFT_RED_UNROLL;
 constexpr int kCopyUnroll = RR_COPY_UNROLL;
 #ifndef RR_SHIFT_UNROLL
 #define RR_SHIFT_UNROLL 2            // 16-byte vectors per thread in a realigning copy tile
@@ -59,16 +64,21 @@ constexpr int kShiftUnroll = RR_SHIFT_UNROLL;
 constexpr int64_t kCopyThrottleTiles = 4096;
 constexpr unsigned kCopyThrottleLds = 26 * 1024;
 
-// One reduction segment: out[i] = RND(scale * fold_k in[k][i]) for i < n.
-// vec == 1: every pointer is 16-byte aligned and n is a multiple of the
-// elements in 16 bytes; vec == 0: element-wise path (heads, tails, and
-// segments whose pointers disagree modulo 16 bytes).
+enum RedMode : int32_t { kRedAligned = 1, kRedShifted = 2 };
+
+// One reduction segment: out[i] = RND(scale * fold_k in[k][i]) for i < n,
+// every pointer aligned to the element.  The elements before out's first
+// 16-byte boundary (the head) and those after the last whole 16-byte output
+// vector (the tail) are computed element by element by tile 0; the vectors
+// between them (the body) are spread over the segment's tiles.
+// kRedAligned: every pointer is 16-byte aligned (no head).  kRedShifted: any
+// alignment; each input's body is realigned to the output's vectors.
 struct RedSeg {
     const void *in[kMaxIn];
     void *out;
     int64_t n;
     int32_t k;
-    int32_t vec;
+    int32_t mode;
     float scale;
     int32_t pad;
 };
@@ -101,6 +111,20 @@ struct CopySeg {
 
 static_assert(sizeof(CopySeg) == 32, "a copy descriptor is one 32-byte scalar load");
 
+// Head elements, 16-byte body vectors and tail elements of a reduction of n
+// elements of es bytes into out (out aligned to es).
+struct RedSplit {
+    int64_t head, nv, tail;
+};
+
+__host__ __device__ inline RedSplit red_split(const void *out, int64_t n, int64_t es)
+{
+    const int64_t to_line = int64_t((16u - unsigned(reinterpret_cast<uintptr_t>(out) & 15u)) & 15u) / es;
+    const int64_t head = to_line < n ? to_line : n;
+    const int64_t nv = (n - head) / (16 / es);
+    return RedSplit{head, nv, n - head - (16 / es) * nv};
+}
+
 // Head bytes (at most 15), 16-byte body vectors and tail bytes (at most 15)
 // of a copy of nbytes to dst.
 struct CopySplit {
@@ -122,9 +146,9 @@ struct CopyBatch {
     CopySeg seg[kMaxCopySegs];
 };
 
-// Work per tile (one workgroup), matching the kernels' tiling.  A copy
-// segment spans max(1, ceil(nv / copy_tile_vecs(mode))) tiles.
-int64_t red_tile_elems(bool vec, bool bf16);
+// Work per tile (one workgroup), matching the kernels' tiling: a segment
+// spans max(1, ceil(nv / tile vectors)) tiles.
+int64_t red_tile_vecs(int32_t mode);
 int64_t copy_tile_vecs(int32_t mode);
 
 // How a batch is launched.  Every form runs the same work per tile; they
@@ -134,7 +158,7 @@ int64_t copy_tile_vecs(int32_t mode);
 //                 loads from the kernel arguments);
 //   kFormUniform: every segment has gx tiles: 2-D grid (gx, nseg), the
 //                 segment is blockIdx.y and the tile blockIdx.x;
-//   kFormOne:     one 16-byte aligned reduction segment: 1-D grid of gx
+//   kFormOne:     one kRedAligned reduction segment: 1-D grid of gx
 //                 tiles, the descriptor passed as scalar kernel arguments
 //                 that the hardware preloads into registers.
 enum LaunchForm : int32_t { kFormTable = 0, kFormUniform = 1, kFormOne = 2 };
@@ -148,7 +172,9 @@ LaunchShape copy_shape(const CopyBatch &b, int64_t total_tiles);
 
 // Enqueue one launch; the batch's tile0/nseg must be filled and the total
 // tile count must not exceed kMaxTilesPerLaunch.  Returns the HIP status.
-hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, hipStream_t stream);
+// A reduction batch holds either only kRedShifted segments (shifted = true)
+// or none of them.
+hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, bool shifted, hipStream_t stream);
 // A copy batch holds either only kCopyShifted segments (shifted = true) or
 // none of them.
 hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hipStream_t stream);

@@ -109,6 +109,35 @@ __device__ __forceinline__ Seg load_seg(const Seg &p)
 }
 
 // ---------------------------------------------------------------------------
+// Cross-lane realignment (the realigning reduction and copy)
+// ---------------------------------------------------------------------------
+
+constexpr int kWave = 64;  // gfx950 runs wave64
+
+// The 16-byte vector held by the next lane of this wave (ds_bpermute).  Call
+// it outside any lane-dependent branch: a lane reading from a lane that is
+// switched off gets no data.  The last lane receives its own value.
+__device__ __forceinline__ u32x4 next_lane(u32x4 x)
+{
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = (unsigned)__shfl_down((int)x[j], 1, kWave);
+    return o;
+}
+
+template <int Q>
+__device__ __forceinline__ u32x4 realign(u32x4 a, u32x4 b, unsigned r)
+{
+    const unsigned w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = __builtin_amdgcn_alignbyte(w[j + Q + 1], w[j + Q], r);
+    return o;
+}
+
+// ---------------------------------------------------------------------------
 // Reduction
 // ---------------------------------------------------------------------------
 
@@ -139,6 +168,32 @@ __device__ __forceinline__ u32x4 fold_vec(const u32x4 (&x)[K], float scale)
     return r;
 }
 
+// Element i of a segment through the same fp32 fold, one element at a time
+// (heads and tails).
+template <bool BF16, int K>
+__device__ __forceinline__ void reduce_elem(const RedSeg &sg, int64_t i)
+{
+    float acc = load_elem<BF16>(sg.in[0], i);
+#pragma unroll
+    for (int k = 1; k < K; ++k)
+        acc = acc + load_elem<BF16>(sg.in[k], i);
+    store_elem<BF16>(sg.out, i, acc * sg.scale);
+}
+
+// Tile 0 of a segment also computes its element-wise edges: the first
+// wave's lanes the head (elements [0, head)), the second wave's the tail
+// (elements [tail0, tail0 + tail)); each is shorter than one 16-byte vector.
+template <bool BF16, int K>
+__device__ __forceinline__ void reduce_edges(const RedSeg &sg, int64_t head, int64_t tail0, int64_t tail)
+{
+    const int x = (int)threadIdx.x;
+    if (x < head)
+        reduce_elem<BF16, K>(sg, x);
+    else if (x >= kWave && x - kWave < tail)
+        reduce_elem<BF16, K>(sg, tail0 + (x - kWave));
+}
+
+// kRedAligned segment: every pointer 16-byte aligned.
 template <bool BF16, int K>
 __device__ __forceinline__ void reduce_vec(const RedSeg &sg, int64_t lt)
 {
@@ -177,39 +232,115 @@ __device__ __forceinline__ void reduce_vec(const RedSeg &sg, int64_t lt)
             st16(out + v, fold_vec<BF16, K>(x, scale));
         }
     }
+    if (lt == 0)
+        reduce_edges<BF16, K>(sg, 0, nv * kVecElems, sg.n - nv * kVecElems);
 }
 
-template <bool BF16>
-__device__ __forceinline__ void reduce_scalar(const RedSeg &sg, int64_t lt)
+// Body vector v of an input whose body starts s bytes (uniform across the
+// workgroup) past aligned word v: bytes [s, 16) of word v (a) and [0, s) of
+// word v+1, which the next lane holds; the wave's last lane loaded word v+1
+// itself (c).
+__device__ __forceinline__ u32x4 shifted_word(u32x4 a, u32x4 c, unsigned s, bool wave_end)
 {
-    const int64_t base = lt * (int64_t)(kBlock * kScalarPerThread) + threadIdx.x;
-    for (int j = 0; j < kScalarPerThread; ++j) {
-        const int64_t i = base + (int64_t)j * kBlock;
-        if (i >= sg.n)
-            return;
-        float acc = load_elem<BF16>(sg.in[0], i);
-#pragma unroll
-        for (int k = 1; k < kMaxIn; ++k)  // static indices keep the descriptor in registers
-            if (k < sg.k)
-                acc = acc + load_elem<BF16>(sg.in[k], i);
-        store_elem<BF16>(sg.out, i, acc * sg.scale);
+    if (s == 0)
+        return a;
+    const u32x4 nb = next_lane(a);  // every lane is active here: s is uniform
+    const u32x4 b = wave_end ? c : nb;
+    switch (s >> 2) {
+    case 0: return realign<0>(a, b, s & 3);
+    case 1: return realign<1>(a, b, s & 3);
+    case 2: return realign<2>(a, b, s & 3);
+    default: return realign<3>(a, b, s & 3);
     }
+}
+
+// One tile of a realigning body.  Every lane loads aligned word v of each
+// input once; for an input with s > 0 the wave's last lane also loads word
+// v+1, and in a partial tile a lane loads word nv, which its left neighbour
+// needs, and stores nothing.  Word nv of such an input holds at least one
+// byte of its body, and an aligned 16-byte word never straddles a page.
+template <bool BF16, int K, bool kFull>
+__device__ __forceinline__ void shifted_tile(const u32x4 *const (&base)[K], const unsigned (&sh)[K],
+                                             u32x4 *out, int64_t lt, int64_t nv, float scale)
+{
+    constexpr int U = kShiftRedUnroll;
+    const bool wave_end = (threadIdx.x & (kWave - 1)) == kWave - 1;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    u32x4 a[U][K], c[U][K];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t v = vec_index<U>(lt, u);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (kFull) {
+                a[u][k] = ld16(base[k] + v);
+                c[u][k] = wave_end && sh[k] != 0 ? ld16(base[k] + v + 1) : zero;
+            } else {
+                a[u][k] = v < nv || (v == nv && sh[k] != 0) ? ld16(base[k] + v) : zero;
+                c[u][k] = wave_end && sh[k] != 0 && v < nv ? ld16(base[k] + v + 1) : zero;
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t v = vec_index<U>(lt, u);
+        u32x4 x[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            x[k] = shifted_word(a[u][k], c[u][k], sh[k], wave_end);
+        if (kFull || v < nv)
+            st16(out + v, fold_vec<BF16, K>(x, scale));
+    }
+}
+
+// kRedShifted segment: pointers at any element alignment.  The body covers
+// the output's whole 16-byte vectors; each input's body is read as aligned
+// words and realigned in registers (v_alignbyte).
+template <bool BF16, int K>
+__device__ __forceinline__ void reduce_shifted(const RedSeg &sg, int64_t lt)
+{
+    constexpr int64_t es = BF16 ? 2 : 4;
+    constexpr int64_t kTileVecs = int64_t(kBlock) * kShiftRedUnroll;
+    const RedSplit sp = red_split(sg.out, sg.n, es);
+    const u32x4 *base[K];
+    unsigned sh[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const unsigned char *p = static_cast<const unsigned char *>(sg.in[k]) + sp.head * es;
+        sh[k] = (unsigned)(reinterpret_cast<uintptr_t>(p) & 15u);
+        base[k] = reinterpret_cast<const u32x4 *>(p - sh[k]);
+    }
+    u32x4 *out = reinterpret_cast<u32x4 *>(static_cast<unsigned char *>(sg.out) + sp.head * es);
+    if ((lt + 1) * kTileVecs <= sp.nv)
+        shifted_tile<BF16, K, true>(base, sh, out, lt, sp.nv, sg.scale);
+    else if (sp.nv > 0)  // uniform across the workgroup
+        shifted_tile<BF16, K, false>(base, sh, out, lt, sp.nv, sg.scale);
+    if (lt == 0)
+        reduce_edges<BF16, K>(sg, sp.head, sp.head + sp.nv * (16 / es), sp.tail);
 }
 
 // Tile lt of one segment.
 template <bool BF16>
 __device__ __forceinline__ void reduce_seg(const RedSeg &sg, int64_t lt)
 {
-    if (sg.vec) {
-        switch (sg.k) {
-        case 1: reduce_vec<BF16, 1>(sg, lt); break;
-        case 2: reduce_vec<BF16, 2>(sg, lt); break;
-        case 3: reduce_vec<BF16, 3>(sg, lt); break;
-        case 4: reduce_vec<BF16, 4>(sg, lt); break;
-        default: break;
-        }
-    } else {
-        reduce_scalar<BF16>(sg, lt);
+    switch (sg.k) {
+    case 1: reduce_vec<BF16, 1>(sg, lt); break;
+    case 2: reduce_vec<BF16, 2>(sg, lt); break;
+    case 3: reduce_vec<BF16, 3>(sg, lt); break;
+    case 4: reduce_vec<BF16, 4>(sg, lt); break;
+    default: break;
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void reduce_shifted_seg(const RedSeg &sg, int64_t lt)
+{
+    switch (sg.k) {
+    case 1: reduce_shifted<BF16, 1>(sg, lt); break;
+    case 2: reduce_shifted<BF16, 2>(sg, lt); break;
+    case 3: reduce_shifted<BF16, 3>(sg, lt); break;
+    case 4: reduce_shifted<BF16, 4>(sg, lt); break;
+    default: break;
     }
 }
 
@@ -234,6 +365,21 @@ __global__ __launch_bounds__(kBlock) void reduce_uniform_kernel(RedBatch b)
     reduce_seg<BF16>(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
 }
 
+// The realigning reduction, in the table and uniform forms.
+template <bool BF16>
+__global__ __launch_bounds__(kBlock) void reduce_shifted_kernel(RedBatch b)
+{
+    const int32_t t = (int32_t)blockIdx.x;
+    const int s = find_seg(b.tile0, b.nseg, t);
+    reduce_shifted_seg<BF16>(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kBlock) void reduce_shifted_uniform_kernel(RedBatch b)
+{
+    reduce_shifted_seg<BF16>(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
+}
+
 // Single-segment form: the aligned segment's pointers, length and scale are
 // plain arguments, preloaded into scalar registers at wave launch, and K is
 // a template parameter, so the first vector load issues at once.
@@ -250,7 +396,7 @@ __global__ __launch_bounds__(kBlock) void reduce_one_kernel(const void *in0, con
     sg.out = out;
     sg.n = n;
     sg.k = K;
-    sg.vec = 1;
+    sg.mode = kRedAligned;
     sg.scale = scale;
     sg.pad = 0;
     reduce_vec<BF16, K>(sg, (int64_t)blockIdx.x);
@@ -259,8 +405,6 @@ __global__ __launch_bounds__(kBlock) void reduce_one_kernel(const void *in0, con
 // ---------------------------------------------------------------------------
 // Copy
 // ---------------------------------------------------------------------------
-
-constexpr int kWave = 64;  // gfx950 runs wave64
 
 // Tile 0 of a copy segment also moves its head and tail bytes (at most 15
 // each): the first wave's lanes the head, the second wave's the tail.
@@ -300,29 +444,6 @@ __device__ __forceinline__ void copy_aligned(const CopySeg &sg, int64_t lt)
     }
     if (lt == 0)
         copy_edges(sg, sp);
-}
-
-// The 16-byte vector held by the next lane of this wave (ds_bpermute).  Call
-// it outside any lane-dependent branch: a lane reading from a lane that is
-// switched off gets no data.  The last lane receives its own value.
-__device__ __forceinline__ u32x4 next_lane(u32x4 x)
-{
-    u32x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        o[j] = (unsigned)__shfl_down((int)x[j], 1, kWave);
-    return o;
-}
-
-template <int Q>
-__device__ __forceinline__ u32x4 realign(u32x4 a, u32x4 b, unsigned r)
-{
-    const unsigned w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    u32x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        o[j] = __builtin_amdgcn_alignbyte(w[j + Q + 1], w[j + Q], r);
-    return o;
 }
 
 // Body vector v is bytes [shift + 16v, shift + 16v + 16) of the aligned
@@ -424,9 +545,9 @@ __global__ __launch_bounds__(kBlock) void copy_shifted_uniform_kernel(CopyBatch 
 
 }  // namespace
 
-int64_t red_tile_elems(bool vec, bool bf16)
+int64_t red_tile_vecs(int32_t mode)
 {
-    return vec ? int64_t(kBlock) * kUnroll * (bf16 ? 8 : 4) : int64_t(kBlock) * kScalarPerThread;
+    return int64_t(kBlock) * (mode == kRedShifted ? kShiftRedUnroll : kUnroll);
 }
 
 int64_t copy_tile_vecs(int32_t mode)
@@ -462,14 +583,28 @@ void launch_one(const RedSeg &sg, int64_t tiles, hipStream_t stream)
 
 }  // namespace
 
-hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, hipStream_t stream)
+hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, bool shifted, hipStream_t stream)
 {
     if (total_tiles <= 0)
         return hipSuccess;
     (void)hipGetLastError();  // report this launch's status only
     const LaunchShape sh = reduce_shape(b, total_tiles);
     const dim3 block(kBlock);
-    if (sh.form == kFormOne) {
+    if (shifted) {
+        if (sh.form == kFormUniform) {
+            const dim3 grid((unsigned)sh.gx, (unsigned)sh.gy);
+            if (b.bf16)
+                reduce_shifted_uniform_kernel<true><<<grid, block, 0, stream>>>(b);
+            else
+                reduce_shifted_uniform_kernel<false><<<grid, block, 0, stream>>>(b);
+        } else {
+            const dim3 grid((unsigned)total_tiles);
+            if (b.bf16)
+                reduce_shifted_kernel<true><<<grid, block, 0, stream>>>(b);
+            else
+                reduce_shifted_kernel<false><<<grid, block, 0, stream>>>(b);
+        }
+    } else if (sh.form == kFormOne) {
         if (b.bf16)
             launch_one<true>(b.seg[0], sh.gx, stream);
         else

@@ -155,9 +155,9 @@ std::vector<std::pair<int, int64_t>> tiles_of(const Batch &b, int64_t total, con
 
 namespace rr {
 
-int64_t red_tile_elems(bool vec, bool bf16)
+int64_t red_tile_vecs(int32_t mode)
 {
-    return vec ? int64_t(kBlock) * kUnroll * (bf16 ? 8 : 4) : int64_t(kBlock) * kScalarPerThread;
+    return int64_t(kBlock) * (mode == kRedShifted ? kShiftRedUnroll : kUnroll);
 }
 
 int64_t copy_tile_vecs(int32_t mode)
@@ -165,42 +165,86 @@ int64_t copy_tile_vecs(int32_t mode)
     return int64_t(kBlock) * (mode == kCopyShifted ? kShiftUnroll : kCopyUnroll);
 }
 
-hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, hipStream_t)
+hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, bool shifted, hipStream_t)
 {
     ++g_launches;
     const bool bf16 = b.bf16;
-    const int ve = bf16 ? 8 : 4;
+    const int64_t es = bf16 ? 2 : 4, ve = 16 / es;
     const LaunchShape sh = reduce_shape(b, total_tiles);
     ++g_forms[0][sh.form];
-    if (sh.form == kFormOne && (!b.seg[0].vec || b.seg[0].k < 1 || b.seg[0].k > kMaxIn))
+    if (sh.form == kFormOne && (shifted || b.seg[0].mode != kRedAligned || b.seg[0].k < 1 || b.seg[0].k > kMaxIn))
         violation("single-segment form for a segment it cannot run", uintptr_t(b.seg[0].out), b.seg[0].k);
     for (const auto &st : tiles_of(b, total_tiles, sh)) {
         const RedSeg &sg = b.seg[st.first];
         const int64_t lt = st.second;
-        if (sg.vec) {
+        const bool shift_mode = sg.mode == kRedShifted;
+        if (shift_mode != shifted)
+            violation("reduction mode in the wrong kernel", uintptr_t(sg.out), sg.mode);
+        if (sg.mode != kRedAligned && sg.mode != kRedShifted)
+            violation("unknown reduction mode", uintptr_t(sg.out), sg.mode);
+        if (sg.k < 1 || sg.k > kMaxIn) {
+            violation("reduction with no kernel for its input count", uintptr_t(sg.out), sg.k);
+            continue;
+        }
+        const uintptr_t o = uintptr_t(sg.out);
+        if (!shift_mode) {
+            bool aligned = o % 16 == 0;
             for (int k = 0; k < sg.k; ++k)
-                if (uintptr_t(sg.in[k]) % 16)
-                    violation("unaligned vector input", uintptr_t(sg.in[k]), 16);
-            if (uintptr_t(sg.out) % 16 || sg.n % ve)
-                violation("unaligned vector output", uintptr_t(sg.out), sg.n);
-            const int64_t nv = sg.n / ve, tv = int64_t(kBlock) * kUnroll;
-            const bool full = (lt + 1) * tv <= nv;
+                aligned = aligned && uintptr_t(sg.in[k]) % 16 == 0;
+            if (!aligned)
+                violation("unaligned pointer in an aligned reduction", o, sg.n);
+        }
+        // the split, recomputed from its definition: head elements up to the
+        // output's 16-byte boundary, whole output vectors, tail elements
+        const int64_t head = std::min<int64_t>(sg.n, int64_t((16 - o % 16) % 16) / es);
+        const int64_t nv = (sg.n - head) / ve, tail = sg.n - head - nv * ve;
+        const int unroll = shift_mode ? kShiftRedUnroll : kUnroll;
+        const int64_t tv = int64_t(kBlock) * unroll;
+        const int s = st.first;
+        const int64_t seg_tiles = (s + 1 < b.nseg ? int64_t(b.tile0[s + 1]) : total_tiles) - b.tile0[s];
+        if (seg_tiles != std::max<int64_t>(1, (nv + tv - 1) / tv))
+            violation("reduction segment tile count differs from its body", o, seg_tiles);
+        // realigned inputs: the aligned words each lane reads
+        uintptr_t base[kMaxIn];
+        int64_t shift[kMaxIn];
+        for (int k = 0; k < sg.k; ++k) {
+            const uintptr_t p = uintptr_t(sg.in[k]) + uintptr_t(head * es);
+            shift[k] = shift_mode ? int64_t(p % 16) : 0;
+            base[k] = p - uintptr_t(shift[k]);
+        }
+        const bool full = (lt + 1) * tv <= nv;
+        if (full || nv > 0) {
             for (int x = 0; x < kBlock; ++x)
-                for (int u = 0; u < kUnroll; ++u) {
+                for (int u = 0; u < unroll; ++u) {
                     const int64_t v = lt * tv + x + int64_t(u) * kBlock;
                     if (!full && v >= nv)
                         break;
-                    for (int e = 0; e < ve; ++e)
-                        fold(sg, v * ve + e, bf16);
+                    const bool wave_end = x % 64 == 63;
+                    for (int k = 0; k < sg.k; ++k)
+                        if (shift[k] && (!touches(base[k] + uintptr_t(v * 16), 16) ||
+                                         (wave_end && !touches(base[k] + uintptr_t((v + 1) * 16), 16))))
+                            violation("realigned input word outside every buffer", base[k] + v * 16, 32);
+                    for (int64_t e = 0; e < ve; ++e)
+                        fold(sg, head + v * ve + e, bf16);
                 }
-        } else {
-            for (int x = 0; x < kBlock; ++x)
-                for (int j = 0; j < kScalarPerThread; ++j) {
-                    const int64_t i = lt * (int64_t(kBlock) * kScalarPerThread) + x + int64_t(j) * kBlock;
-                    if (i >= sg.n)
-                        break;
-                    fold(sg, i, bf16);
-                }
+            if (!full)
+                // a partial tile's lanes also load word nv for their left neighbour
+                for (int x = 0; x < kBlock; ++x)
+                    for (int u = 0; u < unroll; ++u) {
+                        const int64_t v = lt * tv + x + int64_t(u) * kBlock;
+                        for (int k = 0; k < sg.k; ++k)
+                            if (v == nv && shift[k] && !touches(base[k] + uintptr_t(v * 16), 16))
+                                violation("realigned input word outside every buffer", base[k] + v * 16, 16);
+                    }
+        }
+        if (lt == 0) {
+            // tile 0's first wave computes the head elements, its second wave the tail
+            if (head >= ve || tail >= ve)
+                violation("reduction head or tail of a whole vector or more", o, head + tail);
+            for (int64_t i = 0; i < head; ++i)
+                fold(sg, i, bf16);
+            for (int64_t i = 0; i < tail; ++i)
+                fold(sg, head + nv * ve + i, bf16);
         }
     }
     return hipSuccess;

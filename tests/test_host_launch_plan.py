@@ -103,9 +103,10 @@ def test_ar4_helper_and_active(sim, orc, count):
         assert np.array_equal(out, ref)
 
 
-@pytest.mark.parametrize("H,R,lead", [(4, 8 * 128 * 4 + 24, 0), (4, 8 * 128 * 2 + 5, 1), (16, 32 * 128 * 2 + 40, 3)])
+@pytest.mark.parametrize("H,R,lead", [(4, 8 * 128 * 4 + 24, 0), (4, 8 * 128 * 2 + 5, 1), (24, 48 * 128 * 2 + 40, 3)])
 def test_rs4_passes(sim, orc, H, R, lead):
-    """H=16 with misaligned views makes pass 2 exceed one segment table."""
+    """H=24 makes pass 2 exceed one segment table (24 offload slices and 25
+    direct pieces), here with misaligned views."""
     sim.reset()
     A = 4
     g = orc.geometry(A, H, 0, 500, R, RS, BF16)
@@ -118,11 +119,11 @@ def test_rs4_passes(sim, orc, H, R, lead):
     assert np.array_equal(red[lead:lead + A * c], orc.rs4_pass1(BF16, A, c, scratch))
     blk = [bits(R, 2, s) for s in range(A)]
     reds = [bits(c, 3, h) for h in range(H)]
-    # H=16: every view shares one misalignment, so each item splits into a
-    # head, a vector body and a tail (51 segments, more than one table);
-    # otherwise the views disagree modulo 16 bytes and take the scalar path.
-    bl = [lead if (H == 16 or s % 2) else 0 for s in range(A)]
-    ol = lead if H == 16 else 0
+    # H=24: every view shares one misalignment (element-wise head and tail,
+    # no realignment); otherwise the views disagree modulo 16 bytes and the
+    # inputs are realigned.
+    bl = [lead if (H == 24 or s % 2) else 0 for s in range(A)]
+    ol = lead if H == 24 else 0
     bb = [sim.buf(padded(b, bl[s]), writable=False) for s, b in enumerate(blk)]
     rb = [sim.buf(padded(r, lead), writable=False) for r in reds]
     for o in range(A):
@@ -132,7 +133,7 @@ def test_rs4_passes(sim, orc, H, R, lead):
                  parr(*[ptr(b, bl[s]) for s, b in enumerate(bb)], *[ptr(r, lead) for r in rb]),
                  A + H, ptr(out, ol), None)
         assert np.array_equal(out[ol:ol + R], orc.rs4_pass2(BF16, AVG, A, H, 500, R, o, blk, reds))
-        if H == 16 and lead:
+        if H == 24:
             assert sim.L.sim_launches() - launches0 >= 2
 
 
@@ -444,8 +445,8 @@ def test_every_launch_form_is_replayed(sim, orc):
         assert np.array_equal(outs[h], ref)
     assert forms(0) == [0, 1, 1]
 
-    # unequal segments: every buffer 6 bytes past a 16-byte boundary, so the
-    # item splits into an element-wise head, a vector body and a tail
+    # every buffer 6 bytes past a 16-byte boundary: one realigning segment
+    # (element-wise head and tail in tile 0) on a uniform grid of one row
     lead = 3
     xb = [sim.buf(padded(bits(R, 43, s), lead), writable=False) for s in range(2)]
     ob = sim.buf(np.zeros(R + lead + 16, np.uint16))
@@ -453,7 +454,25 @@ def test_every_launch_form_is_replayed(sim, orc):
              parr(ptr(xb[0], lead), ptr(xb[1], lead)), 2, ptr(ob, lead), None)
     ref = orc.rs2_active(BF16, SUM, xb[0][lead:lead + R].copy(), xb[1][lead:lead + R].copy())
     assert np.array_equal(ob[lead:lead + R], ref)
-    assert forms(0) == [1, 1, 1]
+    assert forms(0) == [0, 2, 1]
+
+    # unequal segments: helper jobs of two groups whose chunks span different
+    # tile counts take the tile table
+    counts = [8 * 8192 * 3, 8 * 8192 * 5 + 8 * 128]
+    hj = (_rr._HelperJob * 2)()
+    hrefs = []
+    for j, n2 in enumerate(counts):
+        xs2 = [sim.buf(bits(n2, 45 + j, s), writable=False) for s in range(2)]
+        c2 = orc.geometry(2, 6, 8, 0, n2, AR, BF16)["chunk"]
+        o2 = sim.buf(np.zeros(c2, np.uint16))
+        hj[j].relay, hj[j].helper, hj[j].nSlots = _relay(2, 6, 8, 0, n2), 1, 2
+        hj[j].slots[0], hj[j].slots[1] = ptr(xs2[0], c2).value, ptr(xs2[1], c2).value
+        hj[j].out = ptr(o2).value
+        hrefs.append((o2, orc.ar2_helper(BF16, AVG, xs2[0][c2:2 * c2].copy(), xs2[1][c2:2 * c2].copy())))
+    sim.call("rr_helper_reduce_many", AR, BF16, AVG, hj, 2, None)
+    for o2, ref2 in hrefs:
+        assert np.array_equal(o2, ref2)
+    assert forms(0) == [1, 2, 1]
 
     # copies: pack and unpack issue one segment per chunk move (tile 0 also
     # copies its head and tail bytes), so the aligned case (twelve moves, one
