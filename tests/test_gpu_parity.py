@@ -248,7 +248,7 @@ def test_a2a_pack_unpack(orc, M):
 # edge cases
 # --------------------------------------------------------------------------
 
-def test_misaligned_views_take_the_scalar_and_realigned_paths(orc):
+def test_misaligned_views_are_realigned(orc):
     say("misaligned")
     count = 8 * 128 * 20 + 13
     xs = [synth.as_bf16_bits(synth.normal(count, 7, a)) for a in range(2)]
@@ -277,6 +277,65 @@ def test_misaligned_views_take_the_scalar_and_realigned_paths(orc):
         orc.a2a_unpack(2, A, seg, c, h, orc.a2a_pack(2, A, seg, c, h, src), expect)
     for d in range(A):
         assert np.array_equal(host(wl.out[d]), expect[d])
+
+
+def _view(host_arr, lead, dt):
+    """host_arr placed `lead` elements into a device buffer with 16 guard
+    elements on each side; returns (view, whole buffer)."""
+    npdt = np.float32 if dt == F32 else np.uint16
+    big = np.full(host_arr.size + lead + 32, npdt(0x7FA5) if dt == BF16 else npdt(-3.5), npdt)
+    big[16 + lead:16 + lead + host_arr.size] = host_arr
+    t = dev(big, dt)
+    return t[16 + lead:16 + lead + host_arr.size], t
+
+
+def _guards_ok(whole, view_lead, n, dt):
+    b = host(whole)
+    g = np.float32(-3.5) if dt == F32 else np.uint16(0x7FA5)
+    return bool(np.all(b[:16 + view_lead] == g) and np.all(b[16 + view_lead + n:] == g))
+
+
+@pytest.mark.parametrize("dt", [BF16, F32])
+def test_realigned_reductions_every_input_shift(orc, dt):
+    """Reductions whose inputs each start at a different element offset from
+    a 16-byte boundary (and from the output): the 4-input A=4 helper, the
+    3-input reduce-scatter pass 1 and the 2-input reduce-scatter owner, over
+    many realigning tiles and a ragged last one, bit for bit against the
+    oracle, with the guard elements around every output untouched."""
+    say("realigned reductions", dt)
+    es = 4 if dt == F32 else 2
+    vals = lambda n, seed, r: synth.normal(n, seed, r) if dt == F32 else synth.as_bf16_bits(synth.normal(n, seed, r))
+    # 4 inputs: A=4 allreduce helper 2, chunk of 32+ tiles
+    count = (1 << 20) + 8 * 128 * 3
+    relay = rr.Relay(4, 4, 0, 500, count)
+    c = rr.rr_geometry(relay, AR, dt)["chunk"]
+    xs = [vals(count, 20, a) for a in range(4)]
+    slots = [_view(x[2 * c:3 * c].copy(), lead, dt)[0] for x, lead in zip(xs, (0, 1, 3, 6))]
+    ov, ow = _view(np.zeros(c, xs[0].dtype), 5, dt)
+    rr.rr_helper_reduce(relay, AR, dt, AVG, 2, slots, ov)
+    ref = orc.ar4_helper(dt, AVG, [x[2 * c:3 * c] for x in xs])
+    assert np.array_equal(host(ov).view(np.uint8), ref.view(np.uint8)), "4-input helper"
+    assert _guards_ok(ow, 5, c, dt)
+    # 3 inputs: reduce-scatter pass 1 over a scratch view at one offset, output at another
+    R = 8 * 4096 * 9 + 8 * 128 + 40
+    relay = rr.Relay(4, 4, 0, 500, R)
+    c = rr.rr_geometry(relay, RS, dt)["chunk"]
+    scratch = vals(12 * c, 21, 0)
+    sv, _ = _view(scratch, 1, dt)
+    ov, ow = _view(np.zeros(4 * c, scratch.dtype), 6, dt)
+    rr.rr_rs_multi_reduce(relay, dt, SUM, 1, 0, [sv], ov)
+    assert np.array_equal(host(ov).view(np.uint8), orc.rs4_pass1(dt, 4, c, scratch).view(np.uint8)), "pass 1"
+    assert _guards_ok(ow, 6, 4 * c, dt)
+    # 2 inputs: A=2 reduce-scatter owner, inputs and output at three offsets
+    R = 4096 * 7 + 77
+    relay = rr.Relay(2, 6, 8, 0, R)
+    b0, b1 = vals(R, 22, 0), vals(R, 22, 1)
+    v0, _ = _view(b0, 1, dt)
+    v1, _ = _view(b1, 6, dt)
+    ov, ow = _view(np.zeros(R, b0.dtype), 3, dt)
+    rr.rr_active_add_scale(relay, RS, dt, AVG, 0, [v0, v1], ov)
+    assert np.array_equal(host(ov).view(np.uint8), orc.rs2_active(dt, AVG, b0, b1).view(np.uint8)), "owner"
+    assert _guards_ok(ow, 3, R, dt)
 
 
 def test_special_values_subnormals_and_infinities(orc):
@@ -419,6 +478,60 @@ def test_reduction_beyond_2_31_elements(orc):
         ref = orc.rs2_active(BF16, AVG, _pattern_host(idx, 3), _pattern_host(idx, 7))
         check_bf16(got, ref, f"window [{lo}, {hi}) past 2^31")
     del a, b, out
+    torch.cuda.empty_cache()
+
+
+def _bits_pattern(n, s, step=1 << 26):
+    """Raw 16-bit words that identify (source s, position i), built on the
+    device in pieces: ((i * 40503 + (i >> 16) * 97 + s * 7919) mod 2^16)."""
+    out = torch.empty(n, dtype=torch.int16, device="cuda")
+    for lo in range(0, n, step):
+        hi = min(n, lo + step)
+        i = torch.arange(lo, hi, dtype=torch.int64, device="cuda")
+        out[lo:hi] = ((i * 40503 + (i >> 16) * 97 + s * 7919) % 65536 - 32768).to(torch.int16)
+    return out
+
+
+def _bits_pattern_host(idx, s):
+    return (((idx * 40503 + (idx >> 16) * 97 + s * 7919) % 65536 + 32768) % 65536).astype(np.uint16)
+
+
+def test_all_to_all_beyond_4_GiB_offsets(orc):
+    """Pack and unpack of helper slice 3 with segmentCount = 2^30 + 5 bf16
+    elements: 8 GiB per source and output buffer, the chunks of destinations 2
+    and 3 wholly past byte offset 4 GiB of their sources, 9 of the 12 moves
+    realigned.  Sampled windows of every packed chunk
+    and of every scattered slice equal the all-to-all transpose (unpack of
+    pack gives out_d[s*seg + p] = src_s[d*seg + p] on slice positions), and
+    the words just outside each slice keep their sentinel.  About 70 GB of
+    device memory."""
+    A, H, nc, h = 4, 4, 5, 3
+    seg = 2 ** 30 + 5
+    c = orc.geometry(A, H, nc, 0, seg, A2A, BF16)["chunk"]
+    say("all-to-all beyond 4 GiB offsets", seg, c)
+    relay = rr.Relay(A, H, nc, 0, seg)
+    src = [_bits_pattern(A * seg, s) for s in range(A)]
+    packed = [torch.empty((A - 1) * c, dtype=torch.int16, device="cuda") for _ in range(A)]
+    rr.rr_a2a_pack(relay, BF16, h, src, packed)
+    out = [torch.full((A * seg,), 0x2222, dtype=torch.int16, device="cuda") for _ in range(A)]
+    rr.rr_a2a_unpack(relay, BF16, h, packed, out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    for d in range(A):
+        for j, s in enumerate(x for x in range(A) if x != d):
+            at = d * seg + h * c            # the chunk's first element in source s
+            dst = s * seg + h * c           # its first element in output d
+            starts = [0, c - 2048] + [int(v) for v in rng.integers(0, c - 2048, 6)]
+            for lo in starts:
+                hi = lo + 2048
+                ref = _bits_pattern_host(np.arange(at + lo, at + hi, dtype=np.int64), s)
+                got = synth.to_host(packed[d][j * c + lo:j * c + hi])
+                assert np.array_equal(got, ref), f"packed d={d} j={j} [{lo}, {hi})"
+                got = synth.to_host(out[d][dst + lo:dst + hi])
+                assert np.array_equal(got, ref), f"unpacked d={d} s={s} [{lo}, {hi})"
+            edge = np.concatenate([synth.to_host(out[d][dst - 8:dst]), synth.to_host(out[d][dst + c:dst + c + 8])])
+            assert np.all(edge == 0x2222), f"unpack wrote outside slice d={d} s={s}"
+    del src, packed, out
     torch.cuda.empty_cache()
 
 
