@@ -2,7 +2,7 @@
 libhostsim.so on host buffers, must (a) touch only the registered buffers when
 its segment tables are replayed with the kernels' index arithmetic and
 (b) produce the oracle's bytes.  Covers ragged tails, zero chunks, views at
-every 2-byte misalignment (scalar reduction path, realigned copies), in-place
+every 2-byte misalignment (realigned reductions and copies), in-place
 aliases and segment tables large enough to split a call into several
 launches."""
 import ctypes
