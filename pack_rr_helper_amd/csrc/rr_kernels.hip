@@ -8,10 +8,11 @@
 // them in flight per input before any arithmetic, non-temporal hints on data
 // that is touched exactly once, fp32 accumulation in registers, and one
 // packed bf16 conversion (v_cvt_pk_bf16_f32, round-to-nearest-even) per pair
-// of outputs.  No LDS allocation: nothing is reused, and the copy engine
-// realigns strided sources in registers (v_alignbyte), taking each lane's
-// neighbouring source word from the next lane (ds_bpermute) instead of
-// loading it a second time or staging the tile.
+// of outputs.  No LDS allocation: nothing is reused, and where a source and
+// its destination disagree modulo 16 bytes (strided all-to-all chunks, views
+// at other element offsets) the data is realigned in registers
+// (v_alignbyte), each lane taking its neighbouring source word from the next
+// lane (ds_bpermute) instead of loading it a second time or staging the tile.
 //
 // Tiling: one workgroup of 256 threads processes one tile of one segment.  A
 // launch's segments live in the kernel arguments; how a workgroup finds its
@@ -126,6 +127,7 @@ __device__ __forceinline__ u32x4 next_lane(u32x4 x)
     return o;
 }
 
+// Bytes [4Q + r, 4Q + r + 16) of the 32 bytes a (low) and b (high).
 template <int Q>
 __device__ __forceinline__ u32x4 realign(u32x4 a, u32x4 b, unsigned r)
 {
