@@ -3,7 +3,10 @@
 
 One step is one pass of every relay kernel of the method over one batch of
 synthetic input at one message size M (per-active-rank input bytes, bf16),
-in the fused 8-GPU collectives' layout (A=2: four sparse groups; A=4: two):
+in the fused 8-GPU collectives' layout (A=2: four sparse groups; A=4: two).
+Consecutive steps use three independent sets of buffers in turn
+(--buffer-sets), so no step finds its data left in the 256 MB Infinity Cache
+by the step before:
 
   A=2 allreduce  (H=6, numChunks=8):  helper reduce-at-helper, active epilogue
   A=2 reduce-scatter:                 owner epilogue (recvCount = M/4 elems)
@@ -77,6 +80,9 @@ def parse():
     p.add_argument("--message-mib", type=float, default=64.0)
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU oracle timings (the step's cpu_baseline, the sweep rows' oracle)")
+    p.add_argument("--buffer-sets", type=int, default=3,
+                   help="independent copies of every buffer, used by consecutive steps in turn "
+                        "(3: no step finds its data left in a cache by the previous steps)")
     p.add_argument("--no-other-variants", action="store_true",
                    help="skip timing the step in the variants other than --variant")
     p.add_argument("--calibrate-copy-mib", type=float, default=0.0,
@@ -412,26 +418,27 @@ def hip_runtime():
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hip_runtime_api.h: timing-only events
 
 
-def time_variant(inp, mode, steps, warmup, stream):
-    """Timed region 1 alone (K whole steps, nothing between launches) for the
-    rows built in another variant: step bytes, launches and ms per step."""
+def time_variant(inp, mode, steps, warmup, stream, buffer_sets):
+    """Timed region 1 alone (K whole steps, nothing between launches, the
+    buffer sets used in turn) for the rows built in another variant: step
+    bytes, launches and ms per step."""
     import torch
-    wls = build_rows(inp, mode=mode)
-    calls = [c for wl in wls.values() for c in wl.calls(stream)]
-    for _ in range(warmup):
-        for _, _, _, fn in calls:
+    sets = [build_rows(inp, mode=mode) for _ in range(buffer_sets)]
+    set_calls = [[c for wl in wls.values() for c in wl.calls(stream)] for wls in sets]
+    for i in range(warmup):
+        for _, _, _, fn in set_calls[i % buffer_sets]:
             fn()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
-    for _ in range(steps):
-        for _, _, _, fn in calls:
+    for i in range(steps):
+        for _, _, _, fn in set_calls[i % buffer_sets]:
             fn()
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
-    b, n = sum(c[2] for c in calls), len(calls)
-    del wls, calls
+    b, n = sum(c[2] for c in set_calls[0]), len(set_calls[0])
+    del sets, set_calls
     torch.cuda.empty_cache()
     gbs = b / (ms * 1e-3) / 1e9
     return {"value": round(gbs, 1), "unit": "GB/s", "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
@@ -448,11 +455,18 @@ def step_bench(args):
     M = int(args.message_mib * MIB)
     print(f"[bench] generating inputs, M={args.message_mib} MiB", file=sys.stderr, flush=True)
     inp = host_inputs(M)
-    wls = build_rows(inp, mode=args.variant)
+    # --buffer-sets N: N independent copies of every buffer, used by
+    # consecutive steps in turn, so that no step finds its data in a cache
+    # left warm by the previous one
+    sets = [build_rows(inp, mode=args.variant) for _ in range(args.buffer_sets)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    calls = [c for wl in wls.values() for c in wl.calls(stream)]
+    set_calls = [[c for wl in wls.values() for c in wl.calls(stream)] for wls in sets]
+    calls = set_calls[0]  # rows, kernels and bytes are the same in every set
     step_bytes = sum(b for _, _, b, _ in calls)
+
+    def step_fns(i):
+        return [fn for _, _, _, fn in set_calls[i % len(set_calls)]]
 
     if args.calibrate_copy_mib:
         # a plain device copy of known size, for scaling the HBM byte counters
@@ -465,8 +479,8 @@ def step_bench(args):
         del a, b
 
     print(f"[bench] warmup {args.warmup} steps, {len(calls)} launches per step", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        for _, _, _, fn in calls:
+    for i in range(args.warmup):
+        for fn in step_fns(i):
             fn()
     torch.cuda.synchronize()
 
@@ -475,8 +489,8 @@ def step_bench(args):
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
-    for _ in range(args.steps):
-        for _, _, _, fn in calls:
+    for i in range(args.steps):
+        for fn in step_fns(i):
             fn()
     t1.record(stream)
     torch.cuda.synchronize()
@@ -499,8 +513,8 @@ def step_bench(args):
         evs.append(e)
     i = 0
     hip.hipEventRecord(evs[0], sp)
-    for _ in range(args.steps):
-        for _, _, _, fn in calls:
+    for step in range(args.steps):
+        for fn in step_fns(step):
             fn()
             i += 1
             hip.hipEventRecord(evs[i], sp)
@@ -558,6 +572,7 @@ def step_bench(args):
             "message_bytes": M,
             "launches_per_step": len(calls),
             "algorithmic_bytes_per_step": step_bytes,
+            "buffer_sets": args.buffer_sets,
             "timed_region_1": "K steps, no events between launches (value, ms_per_step)",
             "rows_gbs": {row: round(b / n / (launch_ms(ms, n) * 1e-3) / 1e9, 1)
                          for row, (ms, b, n) in per_row.items()},
@@ -592,7 +607,8 @@ def step_bench(args):
         for other in VARIANTS:
             if other != args.variant:
                 print(f"[bench] timing the {other} variant", file=sys.stderr, flush=True)
-                result["other_variants"][other] = time_variant(inp, other, args.steps, args.warmup, stream)
+                result["other_variants"][other] = time_variant(inp, other, args.steps, args.warmup, stream,
+                                                               args.buffer_sets)
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on the step's jobs: one thread, then {host_threads()} threads",
               file=sys.stderr, flush=True)
