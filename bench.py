@@ -37,6 +37,8 @@ thread; the sweep records both oracle rates beside every row.
 
   python bench.py [--steps K] [--warmup W] [--message-mib M] [--variant share|group|job]
   python bench.py --sweep [--sweep-out FILE]   # per-role GB/s, 2 MiB .. 1 GiB, bf16 and fp32
+  python bench.py --calibrate                  # plain read/write stream mixes alone
+  python bench.py --calibrate-step             # the step beside plain streams of its mixes and bytes
 """
 import argparse
 import hashlib
@@ -93,6 +95,8 @@ def parse():
     p.add_argument("--sweep", action="store_true", help="per-row sweep instead of the step benchmark")
     p.add_argument("--calibrate", action="store_true",
                    help="time plain read/write stream mixes (bench_calib.so) instead of the step")
+    p.add_argument("--calibrate-step", action="store_true",
+                   help="time the step beside a stand-in step of plain streams with the same mixes and bytes")
     p.add_argument("--calibrate-sizes", default="256,1024", help="MiB per stream")
     p.add_argument("--calibrate-out", default=None)
     p.add_argument("--sweep-sizes", default="2,4,8,16,32,64,128,256,512,1024")
@@ -761,14 +765,9 @@ def calibrate(args):
     the reps."""
     import ctypes
     import torch
-    path = os.path.join(ROOT, "bench_calib.so")
-    if not os.path.exists(path):
-        raise RuntimeError(f"{path} is missing: run __graft_entry__.build()")
+    lib = _calib_lib()
     torch.cuda.set_device(0)
-    lib = ctypes.CDLL(path)
     vp = ctypes.c_void_p
-    lib.calib_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), vp,
-                                 ctypes.c_int64, vp]
     stream = torch.cuda.current_stream()
     sp = vp(stream.cuda_stream)
     hip = hip_runtime()
@@ -813,6 +812,107 @@ def calibrate(args):
         hip.hipEventDestroy(e)
 
 
+# Read and write streams per element of each launch of the step, for its
+# plain-stream stand-in: a K-input reduction reads K and writes 1; the
+# reduce-scatter owner pass mixes 4+1 and 2+1 segments (24 reads to 8 writes
+# per chunk), taken as 3+1; a copy reads 1 and writes 1.
+STEP_MIX = {"ar2_helper": (2, 1), "ar2_active": (2, 1), "rs2_owner": (2, 1), "ar4_helper": (4, 1),
+            "ar4_active": (4, 1), "rs4_pass1": (3, 1), "rs4_pass2": (3, 1), "a2a_pack": (1, 1),
+            "a2a_unpack": (1, 1)}
+
+
+def _calib_lib():
+    import ctypes
+    path = os.path.join(ROOT, "bench_calib.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    lib.calib_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), vp,
+                                 ctypes.c_int64, vp]
+    return lib
+
+
+def time_steps(step_fns, steps, warmup, stream):
+    """ms per step of K steps back to back (nothing between the launches),
+    after the warm-up steps; step_fns(i) gives step i's launches."""
+    import torch
+    for i in range(warmup):
+        for fn in step_fns(i):
+            fn()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        for fn in step_fns(i):
+            fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def calibrate_step(args):
+    """The benchmark step beside a stand-in step of plain streams: every
+    launch replaced by one bench_calib.hip stream kernel with the same
+    read/write mix and the same bytes (to within 16 KiB per stream), timed
+    the same way (K steps back to back, the buffer sets in turn), twice in
+    alternation.  What the stand-in reaches is what this launch sequence can
+    reach on this GPU with the relay kernels' access pattern."""
+    import ctypes
+    import functools
+    import torch
+    import pack_rr_helper_amd as rr
+    rr.load()
+    lib = _calib_lib()
+    torch.cuda.set_device(0)
+    vp = ctypes.c_void_p
+    M = int(args.message_mib * MIB)
+    inp = host_inputs(M)
+    stream = torch.cuda.current_stream()
+    sp = vp(stream.cuda_stream)
+    nsets = args.buffer_sets
+    sets = [build_rows(inp, mode=args.variant) for _ in range(nsets)]
+    set_calls = [[c for wl in wls.values() for c in wl.calls(stream)] for wls in sets]
+    calls = set_calls[0]
+    relay_bytes = sum(c[2] for c in calls)
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    launches = []
+    for row, _, b, _ in calls:
+        R, W = STEP_MIX[row]
+        launches.append((row, R, W, max(1024, round(b / (16 * (R + W)) / 1024) * 1024), b))
+    stream_sets = []
+    for _ in range(nsets):
+        fns = []
+        for row, R, W, vectors, _ in launches:
+            bufs = [torch.empty(vectors * 16, dtype=torch.uint8, device="cuda") for _ in range(R + W)]
+            ins = (vp * 4)(*([x.data_ptr() for x in bufs[:R]] + [0] * (4 - R)))
+            outs = (vp * 4)(*([x.data_ptr() for x in bufs[R:]] + [0] * (4 - W)))
+            fn = functools.partial(lib.calib_stream, R, W, ins, outs, vp(sink.data_ptr()), vectors, sp)
+            fn.keep = (bufs, ins, outs)
+            if fn() != 0:
+                raise RuntimeError(f"calib_stream({R}, {W}, {vectors}) failed")
+            fns.append(fn)
+        stream_sets.append(fns)
+    stream_bytes = sum((R + W) * v * 16 for _, R, W, v, _ in launches)
+    relay_ms, stream_ms = [], []
+    for _ in range(2):
+        relay_ms.append(time_steps(lambda i: [c[3] for c in set_calls[i % nsets]], args.steps, args.warmup, stream))
+        stream_ms.append(time_steps(lambda i: stream_sets[i % nsets], args.steps, args.warmup, stream))
+    rm, sm = min(relay_ms), min(stream_ms)
+    rg, sg = relay_bytes / (rm * 1e-3) / 1e9, stream_bytes / (sm * 1e-3) / 1e9
+    print(json.dumps({
+        "calibrate_step": True, "message_mib": args.message_mib, "variant": args.variant,
+        "buffer_sets": nsets, "steps": args.steps,
+        "relay": {"ms_per_step": [round(v, 5) for v in relay_ms], "bytes_per_step": relay_bytes,
+                  "gbs": round(rg, 1), "pct_of_peak": round(100 * rg / PEAK_GBS, 2)},
+        "streams": {"ms_per_step": [round(v, 5) for v in stream_ms], "bytes_per_step": stream_bytes,
+                    "gbs": round(sg, 1), "pct_of_peak": round(100 * sg / PEAK_GBS, 2)},
+        "relay_over_streams": round(rg / sg, 4),
+        "launches": [{"row": row, "reads": R, "writes": W, "relay_bytes": b, "stream_bytes": (R + W) * v * 16}
+                     for row, R, W, v, b in launches],
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -821,6 +921,8 @@ def main():
         sys.exit(2)
     if args.sweep:
         sweep(args)
+    elif args.calibrate_step:
+        calibrate_step(args)
     elif args.calibrate:
         calibrate(args)
     else:

@@ -76,3 +76,16 @@ def test_oracle_timers_run_on_one_and_several_threads():
     assert reps == 1 and t > 0 and b == sum(nb for _, nb, _ in jobs())
     t, b, passes = bench.oracle_threads(jobs, 3, 0.0)
     assert passes == 3 and t > 0 and b == 3 * sum(nb for _, nb, _ in jobs())
+
+
+def test_stand_in_step_covers_every_launch():
+    """--calibrate-step gives every launch of the step a plain-stream stand-in
+    whose read/write mix matches the role's algorithmic bytes: K inputs and
+    one output for a K-input reduction, one and one for a copy."""
+    inp = bench.host_inputs(M2, rows=("ar2", "rs2", "ar4", "rs4", "a2a"))
+    prep = bench.oracle_prep(inp, bench.BF16_CODE)
+    roles = {r for r, _, _ in bench.oracle_jobs(inp, prep, bench.BF16_CODE, "share")}
+    assert roles == set(bench.STEP_MIX)
+    for role in ("ar2_helper", "rs2_owner", "ar4_active", "rs4_pass1", "a2a_pack"):
+        R, W = bench.STEP_MIX[role]
+        assert W == 1 and R == {"ar2": 2, "rs2": 2, "ar4": 4, "rs4": 3, "a2a": 1}[role[:3]]
