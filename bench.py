@@ -29,9 +29,10 @@ timing-only HIP event between consecutive launches on their stream; less the
 events' own cost per launch, it gives each launch's duration, and the kernel
 family with the largest share of the step's time is reported against the
 8 TB/s HBM peak in ``roofline``.  ``other_variants`` repeats the first timed
-region with the launches of the other variants (``--no-other-variants`` skips
-it; profiling runs use that flag so that they hold only the named variant's
-launches).  ``cpu_baseline`` times the CPU oracle on
+region with the launches of the other variants, and ``stand_in_step`` with
+every launch replaced by a plain stream kernel of its read/write mix and bytes
+(``--no-other-variants`` skips both; profiling runs use that flag so that they
+hold only the named variant's relay launches).  ``cpu_baseline`` times the CPU oracle on
 the same jobs, on the host's cores (up to 16 threads, the value) and on one
 thread; the sweep records both oracle rates beside every row.
 
@@ -86,7 +87,7 @@ def parse():
                    help="independent copies of every buffer, used by consecutive steps in turn "
                         "(3: no step finds its data left in a cache by the previous steps)")
     p.add_argument("--no-other-variants", action="store_true",
-                   help="skip timing the step in the variants other than --variant")
+                   help="skip timing the other variants and the plain-stream stand-in step")
     p.add_argument("--calibrate-copy-mib", type=float, default=0.0,
                    help="run a plain device copy of this size first (HBM counter calibration)")
     p.add_argument("--variant", choices=("share", "group", "job"), default="share",
@@ -613,6 +614,20 @@ def step_bench(args):
                 print(f"[bench] timing the {other} variant", file=sys.stderr, flush=True)
                 result["other_variants"][other] = time_variant(inp, other, args.steps, args.warmup, stream,
                                                                args.buffer_sets)
+    if not args.no_other_variants:
+        # the same launch sequence as plain stream kernels of each launch's
+        # read/write mix and bytes (bench_calib.hip), timed like timed region 1
+        print("[bench] timing the plain-stream stand-in step", file=sys.stderr, flush=True)
+        st_sets, _, st_bytes = stand_in_step(calls, args.buffer_sets, stream)
+        st_ms = time_steps(lambda i: st_sets[i % len(st_sets)], args.steps, args.warmup, stream)
+        st_gbs = st_bytes / (st_ms * 1e-3) / 1e9
+        result["stand_in_step"] = {
+            "what": ("the same launch sequence with every launch replaced by a plain stream kernel "
+                     "(bench_calib.hip) of its read/write mix and bytes, timed like timed region 1"),
+            "value": round(st_gbs, 1), "unit": "GB/s", "pct_of_peak": round(100.0 * st_gbs / PEAK_GBS, 2),
+            "ms_per_step": round(st_ms, 5), "relay_over_stand_in": round(value / st_gbs, 4)}
+        del st_sets
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on the step's jobs: one thread, then {host_threads()} threads",
               file=sys.stderr, flush=True)
@@ -851,36 +866,23 @@ def time_steps(step_fns, steps, warmup, stream):
     return t0.elapsed_time(t1) / steps
 
 
-def calibrate_step(args):
-    """The benchmark step beside a stand-in step of plain streams: every
-    launch replaced by one bench_calib.hip stream kernel with the same
-    read/write mix and the same bytes (to within 16 KiB per stream), timed
-    the same way (K steps back to back, the buffer sets in turn), twice in
-    alternation.  What the stand-in reaches is what this launch sequence can
-    reach on this GPU with the relay kernels' access pattern."""
+def stand_in_step(calls, nsets, stream):
+    """Plain-stream stand-ins for a step's launches (row, kernel, bytes, fn):
+    per buffer set, one bench_calib.hip launch per relay launch with the row's
+    read/write mix and bytes.  Returns (per-set launch lists, launches as
+    (row, reads, writes, vectors per stream, relay bytes), stand-in bytes)."""
     import ctypes
     import functools
     import torch
-    import pack_rr_helper_amd as rr
-    rr.load()
     lib = _calib_lib()
-    torch.cuda.set_device(0)
     vp = ctypes.c_void_p
-    M = int(args.message_mib * MIB)
-    inp = host_inputs(M)
-    stream = torch.cuda.current_stream()
     sp = vp(stream.cuda_stream)
-    nsets = args.buffer_sets
-    sets = [build_rows(inp, mode=args.variant) for _ in range(nsets)]
-    set_calls = [[c for wl in wls.values() for c in wl.calls(stream)] for wls in sets]
-    calls = set_calls[0]
-    relay_bytes = sum(c[2] for c in calls)
     sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
     launches = []
     for row, _, b, _ in calls:
         R, W = STEP_MIX[row]
         launches.append((row, R, W, max(1024, round(b / (16 * (R + W)) / 1024) * 1024), b))
-    stream_sets = []
+    sets = []
     for _ in range(nsets):
         fns = []
         for row, R, W, vectors, _ in launches:
@@ -888,12 +890,32 @@ def calibrate_step(args):
             ins = (vp * 4)(*([x.data_ptr() for x in bufs[:R]] + [0] * (4 - R)))
             outs = (vp * 4)(*([x.data_ptr() for x in bufs[R:]] + [0] * (4 - W)))
             fn = functools.partial(lib.calib_stream, R, W, ins, outs, vp(sink.data_ptr()), vectors, sp)
-            fn.keep = (bufs, ins, outs)
+            fn.keep = (bufs, ins, outs, sink)
             if fn() != 0:
                 raise RuntimeError(f"calib_stream({R}, {W}, {vectors}) failed")
             fns.append(fn)
-        stream_sets.append(fns)
-    stream_bytes = sum((R + W) * v * 16 for _, R, W, v, _ in launches)
+        sets.append(fns)
+    return sets, launches, sum((R + W) * v * 16 for _, R, W, v, _ in launches)
+
+
+def calibrate_step(args):
+    """The benchmark step beside a stand-in step of plain streams: every
+    launch replaced by one bench_calib.hip stream kernel with the same
+    read/write mix and the same bytes (to within 16 KiB per stream), timed
+    the same way (K steps back to back, the buffer sets in turn), twice in
+    alternation.  What the stand-in reaches is what this launch sequence can
+    reach on this GPU with the relay kernels' access pattern."""
+    import torch
+    import pack_rr_helper_amd as rr
+    rr.load()
+    torch.cuda.set_device(0)
+    inp = host_inputs(int(args.message_mib * MIB))
+    stream = torch.cuda.current_stream()
+    nsets = args.buffer_sets
+    sets = [build_rows(inp, mode=args.variant) for _ in range(nsets)]
+    set_calls = [[c for wl in wls.values() for c in wl.calls(stream)] for wls in sets]
+    relay_bytes = sum(c[2] for c in set_calls[0])
+    stream_sets, launches, stream_bytes = stand_in_step(set_calls[0], nsets, stream)
     relay_ms, stream_ms = [], []
     for _ in range(2):
         relay_ms.append(time_steps(lambda i: [c[3] for c in set_calls[i % nsets]], args.steps, args.warmup, stream))
