@@ -40,6 +40,7 @@ thread; the sweep records both oracle rates beside every row.
   python bench.py --sweep [--sweep-out FILE]   # per-role GB/s, 2 MiB .. 1 GiB, bf16 and fp32
   python bench.py --calibrate                  # plain read/write stream mixes alone
   python bench.py --calibrate-step             # the step beside plain streams of its mixes and bytes
+  python bench.py --step-sweep [--sweep-out F] # both at 2 MiB .. 1 GiB messages, share and group
 """
 import argparse
 import hashlib
@@ -94,6 +95,8 @@ def parse():
                    help="jobs per launch: one GPU's share of the fused call (default), the "
                         "whole simulated group, or one job")
     p.add_argument("--sweep", action="store_true", help="per-row sweep instead of the step benchmark")
+    p.add_argument("--step-sweep", action="store_true",
+                   help="the step and its plain-stream stand-in at each of --sweep-sizes")
     p.add_argument("--calibrate", action="store_true",
                    help="time plain read/write stream mixes (bench_calib.so) instead of the step")
     p.add_argument("--calibrate-step", action="store_true",
@@ -134,11 +137,30 @@ def host_inputs(M, dtype="bf16", rows=("ar2", "rs2", "ar4", "rs4", "a2a")):
     return {r: make[r]() for r in rows}
 
 
+def device_inputs(M, seed):
+    """Seeded inputs of every row at message M drawn on the device, for timing
+    only (the kernels' work does not depend on the values): N(0,1) rounded to
+    bf16, raw 16-bit patterns for the all-to-all."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    n = M // 2
+    normal = lambda: torch.randn(n, device="cuda", generator=g).to(torch.bfloat16)
+    bits = lambda: torch.randint(-32768, 32768, (n,), dtype=torch.int16, device="cuda", generator=g)
+    return {"ar2": [normal() for _ in range(2)], "rs2": [normal() for _ in range(2)],
+            "ar4": [normal() for _ in range(4)], "rs4": [normal() for _ in range(4)],
+            "a2a": [bits() for _ in range(4)]}
+
+
 def build_rows(inp, rows=("ar2", "rs2", "ar4", "rs4", "a2a"), mode="share"):
+    """The rows' workloads on device copies of `inp` (host arrays, or device
+    tensors, which are cloned so that every call owns its buffers)."""
+    import torch
     import pack_rr_helper_amd as rr
     from pack_rr_helper_amd import synth
     from pack_rr_helper_amd import workloads as W
-    dev = lambda arrs, code=rr.BF16: [synth.to_device(a, code) for a in arrs]
+    dev = lambda arrs, code=rr.BF16: [a.clone() if isinstance(a, torch.Tensor) else synth.to_device(a, code)
+                                      for a in arrs]
     out = {}
     if "ar2" in rows:
         out["ar2"] = W.AR2(dev(inp["ar2"]), rr.BF16, rr.AVG, mode=mode)
@@ -935,13 +957,54 @@ def calibrate_step(args):
     }), flush=True)
 
 
+def step_sweep(args):
+    """The step (one GPU's share and the whole group) and its plain-stream
+    stand-in at each message size: K steps back to back, three buffer sets in
+    turn while a step moves under 2 GB (one set above: a step then streams far
+    more than the 256 MB Infinity Cache holds).  Inputs are drawn on the
+    device (timing only).  One JSON line per (size, variant)."""
+    import torch
+    import pack_rr_helper_amd as rr
+    rr.load()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    out = open(args.sweep_out, "w") if args.sweep_out else sys.stdout
+    for mib in [float(v) for v in args.sweep_sizes.split(",")]:
+        M = int(mib * MIB)
+        inp = device_inputs(M, 1000 + int(mib * 16))
+        for variant in ("share", "group"):
+            first = build_rows(inp, mode=variant)
+            calls0 = [c for wl in first.values() for c in wl.calls(stream)]
+            step_bytes = sum(c[2] for c in calls0)
+            nsets = 3 if step_bytes < 2e9 else 1
+            sets = [first] + [build_rows(inp, mode=variant) for _ in range(nsets - 1)]
+            set_calls = [calls0] + [[c for wl in wls.values() for c in wl.calls(stream)] for wls in sets[1:]]
+            steps = max(args.steps, 50)
+            relay_ms = time_steps(lambda i: [c[3] for c in set_calls[i % nsets]], steps, args.warmup, stream)
+            st_sets, _, st_bytes = stand_in_step(calls0, nsets, stream)
+            st_ms = time_steps(lambda i: st_sets[i % nsets], steps, args.warmup, stream)
+            rg, sg = step_bytes / (relay_ms * 1e-3) / 1e9, st_bytes / (st_ms * 1e-3) / 1e9
+            print(json.dumps({"message_mib": mib, "variant": variant, "buffer_sets": nsets, "steps": steps,
+                              "launches": len(calls0), "bytes_per_step": step_bytes,
+                              "relay_ms_per_step": round(relay_ms, 5), "relay_gbs": round(rg, 1),
+                              "relay_pct_of_peak": round(100 * rg / PEAK_GBS, 2),
+                              "stand_in_gbs": round(sg, 1), "stand_in_pct_of_peak": round(100 * sg / PEAK_GBS, 2),
+                              "relay_over_stand_in": round(rg / sg, 4)}), file=out, flush=True)
+            del first, sets, set_calls, calls0, st_sets
+            torch.cuda.empty_cache()
+        del inp
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (--gpus {args.gpus} "
               "requested). The relay's local kernels shard per rank; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    if args.sweep:
+    if args.step_sweep:
+        step_sweep(args)
+    elif args.sweep:
         sweep(args)
     elif args.calibrate_step:
         calibrate_step(args)

@@ -189,11 +189,16 @@ rr_status check_items(const std::vector<RedItem> &items, int64_t es)
 
 class RedLauncher {
 public:
+    // Only the counts are reset: table entries are written before they are
+    // read, and clearing the full-capacity tables costs host time per call.
     RedLauncher(bool bf16, hipStream_t st) : bf16_(bf16), st_(st)
     {
-        memset(q_, 0, sizeof q_);
-        q_[0].b.bf16 = q_[1].b.bf16 = bf16;
-        q_[1].shifted = true;
+        for (int i = 0; i < 2; ++i) {
+            q_[i].b.nseg = 0;
+            q_[i].b.bf16 = bf16;
+            q_[i].tiles = 0;
+            q_[i].shifted = i == 1;
+        }
     }
 
     // One segment per item (tile 0 also computes its element-wise head and
@@ -264,10 +269,8 @@ private:
         const hipError_t e = rr::launch_reduce(q.b, q.tiles, q.shifted, st_);
         if (e != hipSuccess && err_ == hipSuccess)
             err_ = e;
-        const bool shifted = q.shifted;
-        memset(&q, 0, sizeof q);
-        q.b.bf16 = bf16_;
-        q.shifted = shifted;
+        q.b.nseg = 0;
+        q.tiles = 0;
     }
 
     Queue q_[2];
@@ -515,8 +518,12 @@ class CopyLauncher {
 public:
     explicit CopyLauncher(hipStream_t st) : st_(st)
     {
-        memset(q_, 0, sizeof q_);
-        q_[1].shifted = true;
+        for (int i = 0; i < 2; ++i) {
+            q_[i].b.nseg = 0;
+            q_[i].b.pad = 0;
+            q_[i].tiles = 0;
+            q_[i].shifted = i == 1;
+        }
     }
 
     // One segment per move (tile 0 also copies its head and tail bytes), in
@@ -590,9 +597,8 @@ private:
         const hipError_t e = rr::launch_copy(q.b, q.tiles, q.shifted, st_);
         if (e != hipSuccess && err_ == hipSuccess)
             err_ = e;
-        const bool shifted = q.shifted;
-        memset(&q, 0, sizeof q);
-        q.shifted = shifted;
+        q.b.nseg = 0;
+        q.tiles = 0;
     }
 
     Queue q_[2];

@@ -351,8 +351,8 @@ __device__ __forceinline__ void reduce_shifted_seg(const RedSeg &sg, int64_t lt)
 // interleave measured faster than giving each XCD a contiguous range of tiles.
 
 // Table form: tile t of the whole batch.
-template <bool BF16>
-__global__ __launch_bounds__(kBlock) void reduce_kernel(RedBatch b)
+template <bool BF16, int CAP>
+__global__ __launch_bounds__(kBlock) void reduce_kernel(RedBatchT<CAP> b)
 {
     const int32_t t = (int32_t)blockIdx.x;
     const int s = find_seg(b.tile0, b.nseg, t);
@@ -361,23 +361,23 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(RedBatch b)
 
 // Uniform form: segment blockIdx.y, tile blockIdx.x (every segment has
 // gridDim.x tiles), so no table is searched.
-template <bool BF16>
-__global__ __launch_bounds__(kBlock) void reduce_uniform_kernel(RedBatch b)
+template <bool BF16, int CAP>
+__global__ __launch_bounds__(kBlock) void reduce_uniform_kernel(RedBatchT<CAP> b)
 {
     reduce_seg<BF16>(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
 }
 
 // The realigning reduction, in the table and uniform forms.
-template <bool BF16>
-__global__ __launch_bounds__(kBlock) void reduce_shifted_kernel(RedBatch b)
+template <bool BF16, int CAP>
+__global__ __launch_bounds__(kBlock) void reduce_shifted_kernel(RedBatchT<CAP> b)
 {
     const int32_t t = (int32_t)blockIdx.x;
     const int s = find_seg(b.tile0, b.nseg, t);
     reduce_shifted_seg<BF16>(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kBlock) void reduce_shifted_uniform_kernel(RedBatch b)
+template <bool BF16, int CAP>
+__global__ __launch_bounds__(kBlock) void reduce_shifted_uniform_kernel(RedBatchT<CAP> b)
 {
     reduce_shifted_seg<BF16>(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
 }
@@ -509,14 +509,16 @@ __device__ __forceinline__ void copy_seg(const CopySeg &sg, int64_t lt)
     copy_aligned(sg, lt);
 }
 
-__global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch b)
+template <int CAP>
+__global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatchT<CAP> b)
 {
     const int32_t t = (int32_t)blockIdx.x;
     const int s = find_seg(b.tile0, b.nseg, t);
     copy_seg(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
 }
 
-__global__ __launch_bounds__(kBlock) void copy_uniform_kernel(CopyBatch b)
+template <int CAP>
+__global__ __launch_bounds__(kBlock) void copy_uniform_kernel(CopyBatchT<CAP> b)
 {
     copy_seg(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
 }
@@ -533,14 +535,16 @@ __device__ __forceinline__ void copy_shifted_seg(const CopySeg &sg, int64_t lt)
     }
 }
 
-__global__ __launch_bounds__(kBlock) void copy_shifted_kernel(CopyBatch b)
+template <int CAP>
+__global__ __launch_bounds__(kBlock) void copy_shifted_kernel(CopyBatchT<CAP> b)
 {
     const int32_t t = (int32_t)blockIdx.x;
     const int s = find_seg(b.tile0, b.nseg, t);
     copy_shifted_seg(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
 }
 
-__global__ __launch_bounds__(kBlock) void copy_shifted_uniform_kernel(CopyBatch b)
+template <int CAP>
+__global__ __launch_bounds__(kBlock) void copy_shifted_uniform_kernel(CopyBatchT<CAP> b)
 {
     copy_shifted_seg(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
 }
@@ -585,44 +589,93 @@ void launch_one(const RedSeg &sg, int64_t tiles, hipStream_t stream)
 
 }  // namespace
 
+namespace {
+
+// The first n entries of a full-capacity table in a table of capacity CAP.
+template <typename Small, typename Full>
+Small shrink(const Full &b)
+{
+    Small t{};
+    t.nseg = b.nseg;
+    for (int i = 0; i < b.nseg; ++i) {
+        t.tile0[i] = b.tile0[i];
+        t.seg[i] = b.seg[i];
+    }
+    return t;
+}
+
+template <bool BF16, int CAP>
+void launch_reduce_table(const RedBatchT<CAP> &b, const LaunchShape &sh, int64_t total_tiles, bool shifted,
+                         hipStream_t stream)
+{
+    const dim3 block(kBlock);
+    if (sh.form == kFormUniform) {
+        const dim3 grid((unsigned)sh.gx, (unsigned)sh.gy);
+        if (shifted)
+            reduce_shifted_uniform_kernel<BF16, CAP><<<grid, block, 0, stream>>>(b);
+        else
+            reduce_uniform_kernel<BF16, CAP><<<grid, block, 0, stream>>>(b);
+    } else {
+        const dim3 grid((unsigned)total_tiles);
+        if (shifted)
+            reduce_shifted_kernel<BF16, CAP><<<grid, block, 0, stream>>>(b);
+        else
+            reduce_kernel<BF16, CAP><<<grid, block, 0, stream>>>(b);
+    }
+}
+
+template <bool BF16>
+void launch_reduce_sized(const RedBatch &b, const LaunchShape &sh, int64_t total_tiles, bool shifted,
+                         hipStream_t stream)
+{
+    if (b.nseg <= kSmallRedSegs) {
+        RedBatchT<kSmallRedSegs> t = shrink<RedBatchT<kSmallRedSegs>>(b);
+        t.bf16 = b.bf16;
+        launch_reduce_table<BF16>(t, sh, total_tiles, shifted, stream);
+    } else {
+        launch_reduce_table<BF16>(b, sh, total_tiles, shifted, stream);
+    }
+}
+
+template <int CAP>
+void launch_copy_table(const CopyBatchT<CAP> &b, const LaunchShape &sh, int64_t total_tiles, bool shifted,
+                       hipStream_t stream)
+{
+    const dim3 block(kBlock);
+    if (sh.form == kFormUniform) {
+        const dim3 grid((unsigned)sh.gx, (unsigned)sh.gy);
+        if (shifted) {
+            copy_shifted_uniform_kernel<CAP><<<grid, block, 0, stream>>>(b);
+        } else {
+            const unsigned lds = total_tiles >= kCopyThrottleTiles ? kCopyThrottleLds : 0u;
+            copy_uniform_kernel<CAP><<<grid, block, lds, stream>>>(b);
+        }
+    } else {
+        const dim3 grid((unsigned)total_tiles);
+        if (shifted)
+            copy_shifted_kernel<CAP><<<grid, block, 0, stream>>>(b);
+        else
+            copy_kernel<CAP><<<grid, block, 0, stream>>>(b);
+    }
+}
+
+}  // namespace
+
 hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, bool shifted, hipStream_t stream)
 {
     if (total_tiles <= 0)
         return hipSuccess;
     (void)hipGetLastError();  // report this launch's status only
     const LaunchShape sh = reduce_shape(b, total_tiles);
-    const dim3 block(kBlock);
-    if (shifted) {
-        if (sh.form == kFormUniform) {
-            const dim3 grid((unsigned)sh.gx, (unsigned)sh.gy);
-            if (b.bf16)
-                reduce_shifted_uniform_kernel<true><<<grid, block, 0, stream>>>(b);
-            else
-                reduce_shifted_uniform_kernel<false><<<grid, block, 0, stream>>>(b);
-        } else {
-            const dim3 grid((unsigned)total_tiles);
-            if (b.bf16)
-                reduce_shifted_kernel<true><<<grid, block, 0, stream>>>(b);
-            else
-                reduce_shifted_kernel<false><<<grid, block, 0, stream>>>(b);
-        }
-    } else if (sh.form == kFormOne) {
+    if (!shifted && sh.form == kFormOne) {
         if (b.bf16)
             launch_one<true>(b.seg[0], sh.gx, stream);
         else
             launch_one<false>(b.seg[0], sh.gx, stream);
-    } else if (sh.form == kFormUniform) {
-        const dim3 grid((unsigned)sh.gx, (unsigned)sh.gy);
-        if (b.bf16)
-            reduce_uniform_kernel<true><<<grid, block, 0, stream>>>(b);
-        else
-            reduce_uniform_kernel<false><<<grid, block, 0, stream>>>(b);
+    } else if (b.bf16) {
+        launch_reduce_sized<true>(b, sh, total_tiles, shifted, stream);
     } else {
-        const dim3 grid((unsigned)total_tiles);
-        if (b.bf16)
-            reduce_kernel<true><<<grid, block, 0, stream>>>(b);
-        else
-            reduce_kernel<false><<<grid, block, 0, stream>>>(b);
+        launch_reduce_sized<false>(b, sh, total_tiles, shifted, stream);
     }
     return hipGetLastError();
 }
@@ -633,22 +686,10 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
         return hipSuccess;
     (void)hipGetLastError();  // report this launch's status only
     const LaunchShape sh = copy_shape(b, total_tiles);
-    const dim3 block(kBlock);
-    if (sh.form == kFormUniform) {
-        const dim3 grid((unsigned)sh.gx, (unsigned)sh.gy);
-        if (shifted) {
-            copy_shifted_uniform_kernel<<<grid, block, 0, stream>>>(b);
-        } else {
-            const unsigned lds = total_tiles >= kCopyThrottleTiles ? kCopyThrottleLds : 0u;
-            copy_uniform_kernel<<<grid, block, lds, stream>>>(b);
-        }
-    } else {
-        const dim3 grid((unsigned)total_tiles);
-        if (shifted)
-            copy_shifted_kernel<<<grid, block, 0, stream>>>(b);
-        else
-            copy_kernel<<<grid, block, 0, stream>>>(b);
-    }
+    if (b.nseg <= kSmallCopySegs)
+        launch_copy_table(shrink<CopyBatchT<kSmallCopySegs>>(b), sh, total_tiles, shifted, stream);
+    else
+        launch_copy_table(b, sh, total_tiles, shifted, stream);
     return hipGetLastError();
 }
 
