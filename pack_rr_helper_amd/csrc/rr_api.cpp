@@ -160,6 +160,36 @@ struct RedItem {
     float scale;
 };
 
+// Output ranges sorted by start, after checking that no two overlap (one
+// sort, then neighbours).  Empty ranges are left out: they overlap nothing.
+struct OutRange {
+    Range r;
+    int item;
+};
+
+bool sorted_disjoint_outputs(std::vector<OutRange> &outs)
+{
+    std::sort(outs.begin(), outs.end(), [](const OutRange &a, const OutRange &b) { return a.r.lo < b.r.lo; });
+    for (size_t i = 1; i < outs.size(); ++i)
+        if (outs[i].r.lo < outs[i - 1].r.hi)
+            return false;
+    return true;
+}
+
+// Calls f(output) for every output in the sorted, disjoint list that overlaps x.
+template <typename F>
+bool each_overlapping(const std::vector<OutRange> &outs, Range x, F f)
+{
+    // disjoint and sorted by start, so also sorted by end: the first output
+    // ending after x.lo is the first that can overlap x
+    auto it = std::upper_bound(outs.begin(), outs.end(), x.lo,
+                               [](uintptr_t lo, const OutRange &o) { return lo < o.r.hi; });
+    for (; it != outs.end() && it->r.lo < x.hi; ++it)
+        if (!f(*it))
+            return false;
+    return true;
+}
+
 // An element-wise output is safe when its range equals an input's range
 // exactly (each lane reads its inputs before writing the same elements) or is
 // disjoint from it; everything else is a forbidden alias.  Outputs must also
@@ -167,23 +197,27 @@ struct RedItem {
 // one call run concurrently.
 rr_status check_items(const std::vector<RedItem> &items, int64_t es)
 {
-    const int n = int(items.size());
-    for (int i = 0; i < n; ++i) {
+    std::vector<OutRange> outs;
+    outs.reserve(items.size());
+    for (size_t i = 0; i < items.size(); ++i) {
         const Range o = range_of(items[i].out, 0, items[i].n, es);
-        for (int j = 0; j < n; ++j) {
-            for (int k = 0; k < items[j].k; ++k) {
-                const Range x = range_of(items[j].in[k], 0, items[j].n, es);
-                if (!overlap(o, x))
-                    continue;
-                if (i == j && same(o, x))
-                    continue;
+        if (!o.empty())
+            outs.push_back(OutRange{o, int(i)});
+    }
+    if (!sorted_disjoint_outputs(outs))
+        return fail(RR_EALIAS, "two output ranges overlap");
+    for (size_t j = 0; j < items.size(); ++j)
+        for (int k = 0; k < items[j].k; ++k) {
+            const Range x = range_of(items[j].in[k], 0, items[j].n, es);
+            if (x.empty())
+                continue;
+            const bool ok = each_overlapping(outs, x, [&](const OutRange &o) {
+                return o.item == int(j) && same(o.r, x);
+            });
+            if (!ok)
                 return fail(RR_EALIAS,
                             "an output range overlaps an input range other than an exact in-place alias");
-            }
-            if (j != i && overlap(o, range_of(items[j].out, 0, items[j].n, es)))
-                return fail(RR_EALIAS, "two output ranges overlap");
         }
-    }
     return RR_OK;
 }
 
@@ -497,19 +531,19 @@ struct Move {
 // Every destination range is written by one move only and is read by none.
 rr_status check_moves(const std::vector<Move> &mv)
 {
-    const size_t n = mv.size();
-    for (size_t i = 0; i < n; ++i) {
+    std::vector<OutRange> dsts;
+    dsts.reserve(mv.size());
+    for (size_t i = 0; i < mv.size(); ++i) {
         const Range d{addr(mv[i].dst), addr(mv[i].dst) + uintptr_t(mv[i].nbytes)};
-        for (size_t j = 0; j < n; ++j) {
-            const Range s{addr(mv[j].src), addr(mv[j].src) + uintptr_t(mv[j].nbytes)};
-            if (overlap(d, s))
-                return fail(RR_EALIAS, "a destination chunk overlaps a source chunk");
-            if (j != i) {
-                const Range d2{addr(mv[j].dst), addr(mv[j].dst) + uintptr_t(mv[j].nbytes)};
-                if (overlap(d, d2))
-                    return fail(RR_EALIAS, "two destination chunks overlap");
-            }
-        }
+        if (!d.empty())
+            dsts.push_back(OutRange{d, int(i)});
+    }
+    if (!sorted_disjoint_outputs(dsts))
+        return fail(RR_EALIAS, "two destination chunks overlap");
+    for (const Move &m : mv) {
+        const Range src{addr(m.src), addr(m.src) + uintptr_t(m.nbytes)};
+        if (!src.empty() && !each_overlapping(dsts, src, [](const OutRange &) { return false; }))
+            return fail(RR_EALIAS, "a destination chunk overlaps a source chunk");
     }
     return RR_OK;
 }

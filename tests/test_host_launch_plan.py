@@ -557,3 +557,54 @@ def test_reductions_longer_than_a_launch_continue(capped, orc, lead):
     assert sim.L.sim_launches() - L0 >= 5
     assert np.array_equal(out[lead:lead + R], orc.rs2_active(BF16, AVG, x0, x1))
     assert np.all(out[:lead] == 0) and np.all(out[lead + R:] == 0)
+
+
+# --------------------------------------------------------------------------
+# aliasing rule on random overlapping views
+# --------------------------------------------------------------------------
+
+def _overlap(a, b):
+    return a[0] < a[1] and b[0] < b[1] and a[0] < b[1] and b[0] < a[1]
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_views_follow_the_aliasing_rule(sim, orc, seed):
+    """Random A=2 helper jobs over views of one buffer, on a coarse grid so
+    that overlaps and exact in-place aliases are common: the call is accepted
+    exactly when, checked pair by pair, no output overlaps another job's output
+    or any input other than its own identical slot, and an accepted call
+    writes the oracle's values."""
+    sim.reset()
+    rng = np.random.default_rng(7700 + seed)
+    count = 8 * 256
+    c = orc.geometry(2, 6, 8, 0, count, AR, BF16)["chunk"]
+    N = 6 * c
+    snap = bits(N, 70 + seed, 0)
+    buf = sim.buf(snap.copy())
+    grid = np.arange(0, N - c + 1, 64)
+    jobs = []
+    for _ in range(int(rng.integers(1, 6))):
+        s0, s1 = (int(v) for v in rng.choice(grid, 2))
+        out = s0 if rng.random() < 0.3 else int(rng.choice(grid))
+        jobs.append((s0, s1, out))
+    ok = True
+    for i, (_, _, oi) in enumerate(jobs):
+        o = (oi, oi + c)
+        for j, (s0, s1, oj) in enumerate(jobs):
+            for x in ((s0, s0 + c), (s1, s1 + c)):
+                if _overlap(o, x) and not (i == j and o == x):
+                    ok = False
+            if j != i and _overlap(o, (oj, oj + c)):
+                ok = False
+    arr = (_rr._HelperJob * len(jobs))()
+    for k, (s0, s1, o) in enumerate(jobs):
+        arr[k].relay, arr[k].helper, arr[k].nSlots = _relay(2, 6, 8, 0, count), k, 2
+        arr[k].slots[0], arr[k].slots[1] = ptr(buf, s0).value, ptr(buf, s1).value
+        arr[k].out = ptr(buf, o).value
+    st = sim.L.rr_helper_reduce_many(AR, BF16, AVG, arr, len(jobs), None)
+    assert st == (0 if ok else 2), (jobs, sim.L.rr_last_error())
+    sim.check()
+    if ok:
+        for s0, s1, o in jobs:
+            ref = orc.ar2_helper(BF16, AVG, snap[s0:s0 + c].copy(), snap[s1:s1 + c].copy())
+            assert np.array_equal(buf[o:o + c], ref)
