@@ -957,12 +957,33 @@ def calibrate_step(args):
     }), flush=True)
 
 
+def graphs_of(step_lists, capture_stream):
+    """One HIP graph per list of launches (prepared on capture_stream), each
+    run once eagerly first."""
+    import torch
+    with torch.cuda.stream(capture_stream):
+        for fns in step_lists:
+            for fn in fns:
+                fn()
+    torch.cuda.synchronize()
+    graphs = []
+    for fns in step_lists:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=capture_stream):
+            for fn in fns:
+                fn()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
 def step_sweep(args):
     """The step (one GPU's share and the whole group) and its plain-stream
     stand-in at each message size: K steps back to back, three buffer sets in
     turn while a step moves under 2 GB (one set above: a step then streams far
-    more than the 256 MB Infinity Cache holds).  Inputs are drawn on the
-    device (timing only).  One JSON line per (size, variant)."""
+    more than the 256 MB Infinity Cache holds), issued from Python and
+    replayed from HIP graphs.  Inputs are drawn on the device (timing only).
+    One JSON line per (size, variant)."""
     import torch
     import pack_rr_helper_amd as rr
     rr.load()
@@ -983,14 +1004,29 @@ def step_sweep(args):
             relay_ms = time_steps(lambda i: [c[3] for c in set_calls[i % nsets]], steps, args.warmup, stream)
             st_sets, _, st_bytes = stand_in_step(calls0, nsets, stream)
             st_ms = time_steps(lambda i: st_sets[i % nsets], steps, args.warmup, stream)
+            # the same steps replayed from HIP graphs (one per buffer set): no
+            # host work per launch, so small messages show the GPU's own rate
+            cs = torch.cuda.Stream()
+            cs.wait_stream(stream)
+            relay_cs = [[c[3] for wl in wls.values() for c in wl.calls(cs)] for wls in sets]
+            st_cs = stand_in_step(calls0, nsets, cs)[0]  # holds the stand-in buffers the graphs write
+            g_relay, g_st = graphs_of(relay_cs, cs), graphs_of(st_cs, cs)
+            relay_g_ms = time_steps(lambda i: [g_relay[i % nsets].replay], steps, args.warmup, stream)
+            st_g_ms = time_steps(lambda i: [g_st[i % nsets].replay], steps, args.warmup, stream)
             rg, sg = step_bytes / (relay_ms * 1e-3) / 1e9, st_bytes / (st_ms * 1e-3) / 1e9
+            rgg, sgg = step_bytes / (relay_g_ms * 1e-3) / 1e9, st_bytes / (st_g_ms * 1e-3) / 1e9
             print(json.dumps({"message_mib": mib, "variant": variant, "buffer_sets": nsets, "steps": steps,
                               "launches": len(calls0), "bytes_per_step": step_bytes,
                               "relay_ms_per_step": round(relay_ms, 5), "relay_gbs": round(rg, 1),
                               "relay_pct_of_peak": round(100 * rg / PEAK_GBS, 2),
                               "stand_in_gbs": round(sg, 1), "stand_in_pct_of_peak": round(100 * sg / PEAK_GBS, 2),
-                              "relay_over_stand_in": round(rg / sg, 4)}), file=out, flush=True)
-            del first, sets, set_calls, calls0, st_sets
+                              "relay_over_stand_in": round(rg / sg, 4),
+                              "graph_relay_gbs": round(rgg, 1), "graph_relay_pct_of_peak": round(100 * rgg / PEAK_GBS, 2),
+                              "graph_stand_in_gbs": round(sgg, 1),
+                              "graph_relay_over_stand_in": round(rgg / sgg, 4)}), file=out, flush=True)
+            torch.cuda.synchronize()
+            del g_relay, g_st          # the graphs go before the buffers they write
+            del first, sets, set_calls, calls0, st_sets, relay_cs, st_cs
             torch.cuda.empty_cache()
         del inp
         torch.cuda.empty_cache()
