@@ -452,18 +452,7 @@ def time_variant(inp, mode, steps, warmup, stream, buffer_sets):
     import torch
     sets = [build_rows(inp, mode=mode) for _ in range(buffer_sets)]
     set_calls = [[c for wl in wls.values() for c in wl.calls(stream)] for wls in sets]
-    for i in range(warmup):
-        for _, _, _, fn in set_calls[i % buffer_sets]:
-            fn()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(steps):
-        for _, _, _, fn in set_calls[i % buffer_sets]:
-            fn()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    ms = time_steps(lambda i: [c[3] for c in set_calls[i % buffer_sets]], steps, warmup, stream)
     b, n = sum(c[2] for c in set_calls[0]), len(set_calls[0])
     del sets, set_calls
     torch.cuda.empty_cache()
