@@ -725,3 +725,47 @@ def test_every_entry_point_writes_only_its_output(orc, lead):
     for (big, v), e in zip(outs, expect):
         _guards_intact(big, A * seg, lead)
         assert np.array_equal(synth.to_host(v), e)
+
+
+@pytest.mark.parametrize("njobs", [1, 8, 9, 40, 41])
+@pytest.mark.parametrize("equal", [True, False])
+def test_batches_at_the_segment_table_sizes(orc, njobs, equal):
+    """A launch passes an 8- or 40-entry reduction table (a 16- or 64-entry
+    copy table) by the size of its batch, and a call of more segments
+    continues in a further launch: A=2 helper jobs of equal counts (uniform
+    grid) or of different counts (tile table) at and across those sizes, bit
+    for bit against the oracle."""
+    say("segment table sizes", njobs, equal)
+    rng = np.random.default_rng(njobs * 2 + int(equal))
+    jobs, refs = [], []
+    for j in range(njobs):
+        count = 8 * 128 * (6 if equal else int(rng.integers(3, 12)))
+        c = orc.geometry(2, 6, 8, 0, count, AR, BF16)["chunk"]
+        x = [synth.as_bf16_bits(synth.normal(count, 300 + j, a)) for a in range(2)]
+        h = j % 6
+        out = torch.zeros(c, dtype=torch.bfloat16, device="cuda")
+        jobs.append((rr.Relay(2, 6, 8, 0, count), h, [dev(v[h * c:(h + 1) * c].copy()) for v in x], out))
+        refs.append(orc.ar2_helper(BF16, AVG, x[0][h * c:(h + 1) * c].copy(), x[1][h * c:(h + 1) * c].copy()))
+    rr.rr_helper_reduce_many(AR, BF16, AVG, jobs)
+    for j, ref in enumerate(refs):
+        assert np.array_equal(host(jobs[j][3]), ref), f"job {j}"
+
+
+@pytest.mark.parametrize("nslices,ragged", [(1, False), (2, False), (1, True), (2, True)])
+def test_copy_batches_at_the_segment_table_sizes(orc, nslices, ragged):
+    """All-to-all packs of one or two helper slices (12 or 24 chunk moves, in
+    the 16- and the 64-entry copy table), aligned and with segmentCount = 5
+    mod 8 (aligned and realigned moves in separate launches)."""
+    say("copy table sizes", nslices, ragged)
+    A, H, nc = 4, 4, 5
+    seg = 5 * 128 * 6 + (5 if ragged else 0)
+    c = orc.geometry(A, H, nc, 0, seg, A2A, BF16)["chunk"]
+    src = [synth.bits16(A * seg, 310, s) for s in range(A)]
+    sdev = [dev(s, None) for s in src]
+    relay = rr.Relay(A, H, nc, 0, seg)
+    packed = [[torch.zeros((A - 1) * c, dtype=torch.int16, device="cuda") for _ in range(A)] for _ in range(nslices)]
+    rr.rr_a2a_pack_many(BF16, [(relay, h, sdev, packed[h]) for h in range(nslices)])
+    for h in range(nslices):
+        ref = orc.a2a_pack(2, A, seg, c, h, src)
+        for d in range(A):
+            assert np.array_equal(host(packed[h][d]).view(np.uint8), ref[d]), f"slice {h} dest {d}"
