@@ -61,7 +61,8 @@ typedef enum {
     RR_OK = 0,
     RR_EINVAL = 1,        /* argument outside the method's domain */
     RR_EALIAS = 2,        /* forbidden overlap between inputs and outputs */
-    RR_EUNSUPPORTED = 3,  /* valid in the method, not provided by this library */
+    RR_EUNSUPPORTED = 3,  /* reserved for calls valid in the method but not provided;
+                             no entry point of this version returns it */
     RR_EHIP = 4           /* the HIP runtime reported an error */
 } rr_status;
 
