@@ -253,8 +253,9 @@ rr_status rr_a2a_unpack(const rr_relay *relay, int dtype, int helper,
  * All jobs are validated before anything is enqueued; an invalid job fails
  * the whole call with its status and a message naming the job index.  The
  * jobs of one call run concurrently: one kernel launch for up to 40 reduction
- * segments (a helper or active job is one; an A=4 reduce-scatter owner pass
- * with the balanced split is 2H) or 64 chunk moves whose buffers are 16-byte
+ * segments (a helper or active job is one, an A=4 reduce-scatter pass-1 job
+ * A, an owner pass with the balanced split 2H) or 64 chunk moves whose
+ * buffers are 16-byte
  * aligned, one more for those at other offsets, and further launches on the
  * same stream for larger calls.  So no job may write memory another job of the call reads or writes
  * (RR_EALIAS); the exact in-place aliases of the single-job calls stay
