@@ -255,11 +255,10 @@ rr_status rr_a2a_unpack(const rr_relay *relay, int dtype, int helper,
  * jobs of one call run concurrently: one kernel launch for up to 40 reduction
  * segments (a helper or active job is one, an A=4 reduce-scatter pass-1 job
  * A, an owner pass with the balanced split 2H) or 64 chunk moves whose
- * buffers are 16-byte
- * aligned, one more for those at other offsets, and further launches on the
- * same stream for larger calls.  So no job may write memory another job of the call reads or writes
- * (RR_EALIAS); the exact in-place aliases of the single-job calls stay
- * allowed within a job.  Pointer arrays inside the job structs are host
+ * buffers are 16-byte aligned, one more for those at other offsets, and
+ * further launches on the same stream for larger calls.  So no job may write
+ * memory another job of the call reads or writes (RR_EALIAS); the exact
+ * in-place aliases of the single-job calls stay allowed within a job.  Pointer arrays inside the job structs are host
  * memory, read during the call only.
  */
 typedef struct {
