@@ -258,8 +258,9 @@ rr_status rr_a2a_unpack(const rr_relay *relay, int dtype, int helper,
  * buffers are 16-byte aligned, one more for those at other offsets, and
  * further launches on the same stream for larger calls.  So no job may write
  * memory another job of the call reads or writes (RR_EALIAS); the exact
- * in-place aliases of the single-job calls stay allowed within a job.  Pointer arrays inside the job structs are host
- * memory, read during the call only.
+ * in-place aliases of the single-job calls stay allowed within a job.
+ * Pointer arrays inside the job structs are host memory, read during the
+ * call only.
  */
 typedef struct {
     rr_relay relay;
