@@ -63,7 +63,7 @@ KERNEL_FORMS = {
                     "benchmark's buffers are aligned)",
     "reduce<f32>": "reduce_one_kernel<f32,K>, reduce_uniform_kernel<f32>, reduce_kernel<f32> "
                    "(reduce_shifted_*<f32> for views at other offsets)",
-    "copy": "copy_uniform_kernel, copy_kernel, copy_shifted_uniform_kernel, copy_shifted_kernel",
+    "copy": "copy_uniform_kernel, copy_kernel (aligned moves only), copy_mixed_uniform_kernel, copy_mixed_kernel",
 }
 VARIANTS = {
     "share": "each role's launch covers one GPU's share of the fused 8-GPU call (3 A=2 helper "
@@ -675,7 +675,9 @@ def sweep(args):
     """Per-role GB/s over message sizes and dtypes: one launch of each role
     (covering the jobs --variant selects), timed alone with a fence-free HIP
     event pair after the caches are cleared of its inputs (--flush); best and
-    median of the reps after 3 warm-ups."""
+    median of the reps after 3 warm-ups.  Beside each row: the plain stream
+    of the launch's read/write mix and bytes timed alike, and the CPU oracle
+    on the same jobs."""
     import ctypes
     import zlib
     import torch
@@ -759,6 +761,15 @@ def sweep(args):
                     role_call = next(c for c in calls if c[0] == role)
                     name = role + ("_ragged" if row == "a2a_ragged" else "")
                     rec = record(mib, dt_name, name, role_call[1], role_call[2], times_of(role_call[3]))
+                    # the plain stream of this launch's read/write mix and bytes, timed alike
+                    st_sets, st_launch, st_bytes = stand_in_step([role_call], 1, stream)
+                    st_ts = times_of(st_sets[0][0])
+                    st_gbs = st_bytes / statistics.median(st_ts) / 1e9
+                    rec["stand_in"] = {"reads": st_launch[0][1], "writes": st_launch[0][2], "bytes": st_bytes,
+                                       "gbs_median": round(st_gbs, 1),
+                                       "gbs_best": round(st_bytes / min(st_ts) / 1e9, 1),
+                                       "relay_over_stand_in": round(rec["gbs_median"] / st_gbs, 3)}
+                    del st_sets
                     if name in orates:
                         o = dict(orates[name])
                         o["gpu_over_oracle"] = round(rec["gbs_median"] / o["gbs"], 1)

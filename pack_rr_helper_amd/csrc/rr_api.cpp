@@ -490,20 +490,12 @@ rr_status collect_rs(const rr_relay *relay, int dtype, int op, int pass, int idx
         return st;
     if ((st = check_ptr(out, es, "out", 0)) != RR_OK)
         return st;
-    for (int h = 0; h < H && c > 0; ++h) {
-        RedItem it{};
-        it.in[0] = static_cast<const char *>(in[idx]) + int64_t(h) * c * es;
-        it.in[1] = in[A + h];
-        it.k = 2;
-        it.out = static_cast<char *>(out) + int64_t(h) * c * es;
-        it.n = c;
-        it.scale = op_scale(op, A);
-        items.push_back(it);
-    }
     // The direct region goes out in pieces of one offload chunk, so that with
     // the offload slices every segment of the owner's pass spans the same
     // tiles and the pass launches on the uniform grid (500 permille: the
-    // direct region is exactly H chunks).
+    // direct region is exactly H chunks).  Its A-input pieces come first:
+    // workgroups are dispatched in segment order, and the heavier tiles
+    // started first leave the lighter ones to fill the launch's tail.
     const int64_t piece = c > 0 ? c : g.direct_len;
     for (int64_t lo = 0; lo < g.direct_len; lo += piece) {
         RedItem it{};
@@ -512,6 +504,16 @@ rr_status collect_rs(const rr_relay *relay, int dtype, int op, int pass, int idx
         it.k = A;
         it.out = static_cast<char *>(out) + (g.direct_off + lo) * es;
         it.n = std::min(piece, g.direct_len - lo);
+        it.scale = op_scale(op, A);
+        items.push_back(it);
+    }
+    for (int h = 0; h < H && c > 0; ++h) {
+        RedItem it{};
+        it.in[0] = static_cast<const char *>(in[idx]) + int64_t(h) * c * es;
+        it.in[1] = in[A + h];
+        it.k = 2;
+        it.out = static_cast<char *>(out) + int64_t(h) * c * es;
+        it.n = c;
         it.scale = op_scale(op, A);
         items.push_back(it);
     }
@@ -552,17 +554,14 @@ class CopyLauncher {
 public:
     explicit CopyLauncher(hipStream_t st) : st_(st)
     {
-        for (int i = 0; i < 2; ++i) {
-            q_[i].b.nseg = 0;
-            q_[i].b.pad = 0;
-            q_[i].tiles = 0;
-            q_[i].shifted = i == 1;
-        }
+        b_.nseg = 0;
+        b_.pad = 0;
     }
 
-    // One segment per move (tile 0 also copies its head and tail bytes), in
-    // the aligned kernel's queue when source and destination agree modulo 16
-    // bytes and in the realigning kernel's otherwise.
+    // One segment per move (tile 0 also copies its head and tail bytes), all
+    // in one batch: aligned when source and destination agree modulo 16
+    // bytes, realigned otherwise.  A batch with a realigned move runs in the
+    // mixed-mode kernels, one without in the aligned-only kernels.
     void add(const void *src, void *dst, int64_t nbytes)
     {
         if (nbytes <= 0)
@@ -579,30 +578,22 @@ public:
 
     hipError_t finish()
     {
-        flush(q_[0]);
-        flush(q_[1]);
+        flush();
         return err_;
     }
 
 private:
-    struct Queue {
-        rr::CopyBatch b;
-        int64_t tiles;
-        bool shifted;
-    };
-
     void piece(const unsigned char *src, unsigned char *dst, int64_t nbytes, int32_t mode,
                int32_t shift)
     {
-        Queue &q = q_[mode == rr::kCopyShifted ? 1 : 0];
         const int64_t tv = rr::copy_tile_vecs(mode);
         while (nbytes > 0) {
-            if (q.b.nseg == rr::kMaxCopySegs || q.tiles >= rr::kMaxTilesPerLaunch)
-                flush(q);
+            if (b_.nseg == rr::kMaxCopySegs || tiles_ >= rr::kMaxTilesPerLaunch)
+                flush();
             const rr::CopySplit sp = rr::copy_split(dst, nbytes);
             int64_t tiles = std::max<int64_t>(1, (sp.nv + tv - 1) / tv);
             int64_t take = nbytes;
-            const int64_t room = rr::kMaxTilesPerLaunch - q.tiles;
+            const int64_t room = rr::kMaxTilesPerLaunch - tiles_;
             if (tiles > room) {
                 // whole tiles of the body only: the rest starts on a 16-byte
                 // destination boundary with the same source shift
@@ -615,27 +606,31 @@ private:
             s.nbytes = take;
             s.mode = mode;
             s.shift = shift;
-            q.b.tile0[q.b.nseg] = int32_t(q.tiles);
-            q.b.seg[q.b.nseg++] = s;
-            q.tiles += tiles;
+            b_.tile0[b_.nseg] = int32_t(tiles_);
+            b_.seg[b_.nseg++] = s;
+            tiles_ += tiles;
+            shifted_ = shifted_ || mode == rr::kCopyShifted;
             src += take;
             dst += take;
             nbytes -= take;
         }
     }
 
-    void flush(Queue &q)
+    void flush()
     {
-        if (q.b.nseg == 0)
+        if (b_.nseg == 0)
             return;
-        const hipError_t e = rr::launch_copy(q.b, q.tiles, q.shifted, st_);
+        const hipError_t e = rr::launch_copy(b_, tiles_, shifted_, st_);
         if (e != hipSuccess && err_ == hipSuccess)
             err_ = e;
-        q.b.nseg = 0;
-        q.tiles = 0;
+        b_.nseg = 0;
+        tiles_ = 0;
+        shifted_ = false;
     }
 
-    Queue q_[2];
+    rr::CopyBatch b_;
+    int64_t tiles_ = 0;
+    bool shifted_ = false;
     hipStream_t st_;
     hipError_t err_ = hipSuccess;
 };

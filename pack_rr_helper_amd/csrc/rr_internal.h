@@ -186,8 +186,8 @@ LaunchShape copy_shape(const CopyBatch &b, int64_t total_tiles);
 // A reduction batch holds either only kRedShifted segments (shifted = true)
 // or none of them.
 hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, bool shifted, hipStream_t stream);
-// A copy batch holds either only kCopyShifted segments (shifted = true) or
-// none of them.
+// A copy batch with any kCopyShifted segment runs in the mixed-mode kernels
+// (shifted = true), one without in the aligned-only kernels.
 hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hipStream_t stream);
 
 }  // namespace rr

@@ -523,10 +523,17 @@ __global__ __launch_bounds__(kBlock) void copy_uniform_kernel(CopyBatchT<CAP> b)
     copy_seg(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
 }
 
-// Realigned bodies (source and destination disagree modulo 16 bytes); a
-// kernel of its own so its register budget does not limit the aligned path.
-__device__ __forceinline__ void copy_shifted_seg(const CopySeg &sg, int64_t lt)
+// Any segment: realigned (source and destination disagree modulo 16 bytes)
+// or aligned, by the segment's mode, so that a call whose chunk moves mix
+// both (a segmentCount that is not a multiple of 8) takes one launch.  The
+// aligned-only kernels above keep the smaller register budget for calls
+// without realigned moves.
+__device__ __forceinline__ void copy_mixed_seg(const CopySeg &sg, int64_t lt)
 {
+    if (sg.mode != kCopyShifted) {  // uniform across the workgroup
+        copy_aligned(sg, lt);
+        return;
+    }
     switch (sg.shift >> 2) {
     case 0: copy_shifted<0>(sg, lt); break;
     case 1: copy_shifted<1>(sg, lt); break;
@@ -536,17 +543,17 @@ __device__ __forceinline__ void copy_shifted_seg(const CopySeg &sg, int64_t lt)
 }
 
 template <int CAP>
-__global__ __launch_bounds__(kBlock) void copy_shifted_kernel(CopyBatchT<CAP> b)
+__global__ __launch_bounds__(kBlock) void copy_mixed_kernel(CopyBatchT<CAP> b)
 {
     const int32_t t = (int32_t)blockIdx.x;
     const int s = find_seg(b.tile0, b.nseg, t);
-    copy_shifted_seg(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
+    copy_mixed_seg(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
 }
 
 template <int CAP>
-__global__ __launch_bounds__(kBlock) void copy_shifted_uniform_kernel(CopyBatchT<CAP> b)
+__global__ __launch_bounds__(kBlock) void copy_mixed_uniform_kernel(CopyBatchT<CAP> b)
 {
-    copy_shifted_seg(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
+    copy_mixed_seg(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
 }
 
 }  // namespace
@@ -645,7 +652,7 @@ void launch_copy_table(const CopyBatchT<CAP> &b, const LaunchShape &sh, int64_t 
     if (sh.form == kFormUniform) {
         const dim3 grid((unsigned)sh.gx, (unsigned)sh.gy);
         if (shifted) {
-            copy_shifted_uniform_kernel<CAP><<<grid, block, 0, stream>>>(b);
+            copy_mixed_uniform_kernel<CAP><<<grid, block, 0, stream>>>(b);
         } else {
             const unsigned lds = total_tiles >= kCopyThrottleTiles ? kCopyThrottleLds : 0u;
             copy_uniform_kernel<CAP><<<grid, block, lds, stream>>>(b);
@@ -653,7 +660,7 @@ void launch_copy_table(const CopyBatchT<CAP> &b, const LaunchShape &sh, int64_t 
     } else {
         const dim3 grid((unsigned)total_tiles);
         if (shifted)
-            copy_shifted_kernel<CAP><<<grid, block, 0, stream>>>(b);
+            copy_mixed_kernel<CAP><<<grid, block, 0, stream>>>(b);
         else
             copy_kernel<CAP><<<grid, block, 0, stream>>>(b);
     }

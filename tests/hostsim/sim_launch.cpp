@@ -260,8 +260,8 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
     for (const auto &st : tiles_of(b, total_tiles, sh)) {
         const CopySeg &sg = b.seg[st.first];
         const int64_t lt = st.second;
-        if ((sg.mode == kCopyShifted) != shifted)
-            violation("copy mode in the wrong kernel", uintptr_t(sg.dst), sg.mode);
+        if (sg.mode == kCopyShifted && !shifted)
+            violation("realigned copy segment in the aligned-only kernel", uintptr_t(sg.dst), sg.mode);
         if (sg.mode != kCopyAligned && sg.mode != kCopyShifted)
             violation("unknown copy mode", uintptr_t(sg.dst), sg.mode);
         // the move's split, recomputed from its definition: head bytes up to

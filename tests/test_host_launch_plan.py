@@ -475,11 +475,11 @@ def test_every_launch_form_is_replayed(sim, orc):
     assert forms(0) == [1, 2, 1]
 
     # copies: pack and unpack issue one segment per chunk move (tile 0 also
-    # copies its head and tail bytes), so the aligned case (twelve moves, one
-    # launch per call) and a ragged segmentCount (aligned and realigning
-    # moves, two launches per call) all run on the uniform grid
+    # copies its head and tail bytes) and one launch per call, so the aligned
+    # case (twelve aligned moves) and a ragged segmentCount (aligned and
+    # realigned moves in the mixed-mode kernel) both run on the uniform grid
     A, H, nc = 4, 4, 5
-    for seg, launches in ((5 * 128 * 40, 2), (5 * 128 * 40 + 3, 4)):   # chunks of several tiles
+    for seg, launches in ((5 * 128 * 40, 2), (5 * 128 * 40 + 3, 2)):   # chunks of several tiles
         before = forms(1)
         c = orc.geometry(A, H, nc, 0, seg, A2A, BF16)["chunk"]
         src = [sim.buf(bits(A * seg, 44, s), writable=False) for s in range(A)]

@@ -13,7 +13,7 @@ import pytest
 
 from pack_rr_helper_amd import build as B
 
-KERNELS = ("copy_shifted_kernel", "copy_shifted_uniform_kernel", "reduce_shifted_kernel",
+KERNELS = ("copy_mixed_kernel", "copy_mixed_uniform_kernel", "reduce_shifted_kernel",
            "reduce_shifted_uniform_kernel")
 
 
