@@ -755,7 +755,7 @@ def test_batches_at_the_segment_table_sizes(orc, njobs, equal):
 def test_copy_batches_at_the_segment_table_sizes(orc, nslices, ragged):
     """All-to-all packs of one or two helper slices (12 or 24 chunk moves, in
     the 16- and the 64-entry copy table), aligned and with segmentCount = 5
-    mod 8 (aligned and realigned moves in separate launches)."""
+    mod 8 (aligned and realigned moves in one mixed-mode launch)."""
     say("copy table sizes", nslices, ragged)
     A, H, nc = 4, 4, 5
     seg = 5 * 128 * 6 + (5 if ragged else 0)
