@@ -82,6 +82,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--message-mib", type=float, default=64.0)
+    p.add_argument("--dtype", choices=("bf16", "f32"), default="bf16",
+                   help="buffer dtype of the step (the sweeps take --sweep-dtypes)")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU oracle timings (the step's cpu_baseline, the sweep rows' oracle)")
     p.add_argument("--buffer-sets", type=int, default=3,
@@ -152,26 +154,40 @@ def device_inputs(M, seed):
             "a2a": [bits() for _ in range(4)]}
 
 
-def build_rows(inp, rows=("ar2", "rs2", "ar4", "rs4", "a2a"), mode="share"):
-    """The rows' workloads on device copies of `inp` (host arrays, or device
-    tensors, which are cloned so that every call owns its buffers)."""
+def build_rows(inp, rows=("ar2", "rs2", "ar4", "rs4", "a2a"), mode="share", dtype="bf16"):
+    """The rows' workloads on device copies of `inp` (host arrays from
+    host_inputs of the same dtype, or device tensors, which are cloned so that
+    every call owns its buffers)."""
+    import numpy as np
     import torch
     import pack_rr_helper_amd as rr
     from pack_rr_helper_amd import synth
     from pack_rr_helper_amd import workloads as W
-    dev = lambda arrs, code=rr.BF16: [a.clone() if isinstance(a, torch.Tensor) else synth.to_device(a, code)
-                                      for a in arrs]
+    dt = rr.F32 if dtype == "f32" else rr.BF16
+
+    def dev(arrs, bits=False):
+        out = []
+        for a in arrs:
+            if isinstance(a, torch.Tensor):
+                out.append(a.clone())
+            elif bits:  # raw patterns: 16-bit words as int16, 32-bit words as float32
+                out.append(synth.to_device(a.view(np.float32), rr.F32) if a.itemsize == 4 else
+                           synth.to_device(a, None))
+            else:
+                out.append(synth.to_device(a, dt))
+        return out
+
     out = {}
     if "ar2" in rows:
-        out["ar2"] = W.AR2(dev(inp["ar2"]), rr.BF16, rr.AVG, mode=mode)
+        out["ar2"] = W.AR2(dev(inp["ar2"]), dt, rr.AVG, mode=mode)
     if "rs2" in rows:
-        out["rs2"] = W.RS2(dev(inp["rs2"]), rr.BF16, rr.AVG, mode=mode)
+        out["rs2"] = W.RS2(dev(inp["rs2"]), dt, rr.AVG, mode=mode)
     if "ar4" in rows:
-        out["ar4"] = W.AR4(dev(inp["ar4"]), rr.BF16, rr.AVG, mode=mode)
+        out["ar4"] = W.AR4(dev(inp["ar4"]), dt, rr.AVG, mode=mode)
     if "rs4" in rows:
-        out["rs4"] = W.RS4(dev(inp["rs4"]), rr.BF16, rr.SUM, mode=mode)
+        out["rs4"] = W.RS4(dev(inp["rs4"]), dt, rr.SUM, mode=mode)
     if "a2a" in rows:
-        out["a2a"] = W.A2A(dev(inp["a2a"], None), rr.BF16, mode=mode)
+        out["a2a"] = W.A2A(dev(inp["a2a"], bits=True), dt, mode=mode)
     return out
 
 
@@ -445,12 +461,12 @@ def hip_runtime():
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hip_runtime_api.h: timing-only events
 
 
-def time_variant(inp, mode, steps, warmup, stream, buffer_sets):
+def time_variant(inp, mode, steps, warmup, stream, buffer_sets, dtype="bf16"):
     """Timed region 1 alone (K whole steps, nothing between launches, the
     buffer sets used in turn) for the rows built in another variant: step
     bytes, launches and ms per step."""
     import torch
-    sets = [build_rows(inp, mode=mode) for _ in range(buffer_sets)]
+    sets = [build_rows(inp, mode=mode, dtype=dtype) for _ in range(buffer_sets)]
     set_calls = [[c for wl in wls.values() for c in wl.calls(stream)] for wls in sets]
     ms = time_steps(lambda i: [c[3] for c in set_calls[i % buffer_sets]], steps, warmup, stream)
     b, n = sum(c[2] for c in set_calls[0]), len(set_calls[0])
@@ -470,11 +486,11 @@ def step_bench(args):
     torch.cuda.set_device(0)
     M = int(args.message_mib * MIB)
     print(f"[bench] generating inputs, M={args.message_mib} MiB", file=sys.stderr, flush=True)
-    inp = host_inputs(M)
+    inp = host_inputs(M, args.dtype)
     # --buffer-sets N: N independent copies of every buffer, used by
     # consecutive steps in turn, so that no step finds its data in a cache
     # left warm by the previous one
-    sets = [build_rows(inp, mode=args.variant) for _ in range(args.buffer_sets)]
+    sets = [build_rows(inp, mode=args.variant, dtype=args.dtype) for _ in range(args.buffer_sets)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     set_calls = [[c for wl in wls.values() for c in wl.calls(stream)] for wls in sets]
@@ -576,11 +592,11 @@ def step_bench(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "pct_of_peak": round(100.0 * value / PEAK_GBS, 2),
         "config": {
-            "workload": (f"relay hot path, {args.message_mib:g} MiB per-rank bf16 message: A=2 allreduce "
+            "workload": (f"relay hot path, {args.message_mib:g} MiB per-rank {args.dtype} message: A=2 allreduce "
                          "(H=6) + A=2 reduce-scatter + A=4 allreduce (H=4, 500 permille) + A=4 "
                          "reduce-scatter + A=4 all-to-all pack/unpack, one GPU"),
             "variant": args.variant,
@@ -624,7 +640,7 @@ def step_bench(args):
             if other != args.variant:
                 print(f"[bench] timing the {other} variant", file=sys.stderr, flush=True)
                 result["other_variants"][other] = time_variant(inp, other, args.steps, args.warmup, stream,
-                                                               args.buffer_sets)
+                                                               args.buffer_sets, args.dtype)
     if not args.no_other_variants:
         # the same launch sequence as plain stream kernels of each launch's
         # read/write mix and bytes (bench_calib.hip), timed like timed region 1
@@ -642,7 +658,7 @@ def step_bench(args):
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on the step's jobs: one thread, then {host_threads()} threads",
               file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(inp, BF16_CODE, args.variant,
+        result["cpu_baseline"] = cpu_baseline(inp, F32_CODE if args.dtype == "f32" else BF16_CODE, args.variant,
                                               label=f"{args.message_mib:g} MiB message, every row, ")
     print(json.dumps(result), flush=True)
 
@@ -931,10 +947,10 @@ def calibrate_step(args):
     import pack_rr_helper_amd as rr
     rr.load()
     torch.cuda.set_device(0)
-    inp = host_inputs(int(args.message_mib * MIB))
+    inp = host_inputs(int(args.message_mib * MIB), args.dtype)
     stream = torch.cuda.current_stream()
     nsets = args.buffer_sets
-    sets = [build_rows(inp, mode=args.variant) for _ in range(nsets)]
+    sets = [build_rows(inp, mode=args.variant, dtype=args.dtype) for _ in range(nsets)]
     set_calls = [[c for wl in wls.values() for c in wl.calls(stream)] for wls in sets]
     relay_bytes = sum(c[2] for c in set_calls[0])
     stream_sets, launches, stream_bytes = stand_in_step(set_calls[0], nsets, stream)
