@@ -198,6 +198,7 @@ def _stream(stream):
 # --------------------------------------------------------------------------
 
 def rr_abi_version():
+    """ABI version compiled into librr.so (RR_ABI_VERSION)."""
     return load().rr_abi_version()
 
 
@@ -210,6 +211,7 @@ def rr_geometry(relay, coll, dtype):
 
 
 def rr_passthrough_helper_size(count_g, A, num_chunks):
+    """Elements of a passthrough helper buffer: min(count_g, A * align_down(count_g / num_chunks, 128))."""
     v = load().rr_passthrough_helper_size(count_g, A, num_chunks)
     if v < 0:
         raise RRError(RR_EINVAL, "count_g < 0, A < 1 or num_chunks < 1")
@@ -233,6 +235,10 @@ def _helper_need(relay, coll, dtype):
 
 
 def rr_helper_reduce(relay, coll, dtype, op, helper, slots, out, stream=None, prepare=False):
+    """Allreduce reduce-at-helper: out = scale * (slots[0] + ... + slots[A-1]) over
+    the group's chunk (A=2: the two actives' copies of chunk `helper`; A=4: the
+    four actives' position slices).  `out` may be slots[0] exactly.  A zero
+    chunk is a no-op."""
     n = _helper_need(relay, coll, dtype)
     arr, k = _ptrs(slots, "slots", dtype, n)
     o = _dev(out, "out", dtype, n)
@@ -243,6 +249,10 @@ def rr_helper_reduce(relay, coll, dtype, op, helper, slots, out, stream=None, pr
 
 
 def rr_active_add_scale(relay, coll, dtype, op, active_idx, inputs, out, stream=None, prepare=False):
+    """Active epilogue: out = scale * sum of the A inputs over this active's
+    direct region (allreduce) or over the whole block (A=2 reduce-scatter
+    owner).  Inputs are full buffers of relay.count elements, one per active in
+    rank order; `out` may equal one of them exactly."""
     arr, k = _ptrs(inputs, "in", dtype, relay.count)
     o = _dev(out, "out", dtype, relay.count)
     r = relay._c()
@@ -260,6 +270,10 @@ def _rs_need(relay, dtype, pass_, n_inputs):
 
 
 def rr_rs_multi_reduce(relay, dtype, op, pass_, idx, inputs, out, stream=None, prepare=False):
+    """A=4 reduce-scatter passes.  pass_=1 (helper idx): inputs = [scratch]
+    holding the A*(A-1) (owner, source) chunks; out receives the A reduced
+    chunks.  pass_=2 (owner idx): inputs = the A blocks then the H reduced
+    chunks; out receives the owner's recvCount elements."""
     inputs = list(inputs) if not isinstance(inputs, torch.Tensor) else [inputs]
     need, out_need = _rs_need(relay, dtype, pass_, len(inputs))
     arr, k = _ptrs(inputs, "in", dtype, need)
@@ -286,6 +300,9 @@ def _a2a_arrays(relay, dtype, ins, outs, unpack):
 
 
 def rr_a2a_pack(relay, dtype, helper, src, dst, stream=None, prepare=False):
+    """All-to-all gather for helper slice `helper`: dst[d] receives, in
+    ascending source order skipping d, each source's chunk of segment d.
+    Out-of-place only; raw bits are copied."""
     s, d = _a2a_arrays(relay, dtype, src, dst, False)
     r = relay._c()
     return _issue(load().rr_a2a_pack, (ctypes.byref(r), dtype, helper, s, d, _stream(stream)),
@@ -293,6 +310,8 @@ def rr_a2a_pack(relay, dtype, helper, src, dst, stream=None, prepare=False):
 
 
 def rr_a2a_unpack(relay, dtype, helper, recv, out, stream=None, prepare=False):
+    """The inverse scatter: out[d] receives each source's chunk from recv[d] at
+    the helper slice of that source's segment.  Out-of-place only."""
     s, d = _a2a_arrays(relay, dtype, recv, out, True)
     r = relay._c()
     return _issue(load().rr_a2a_unpack, (ctypes.byref(r), dtype, helper, s, d, _stream(stream)),
