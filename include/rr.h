@@ -250,8 +250,11 @@ rr_status rr_a2a_unpack(const rr_relay *relay, int dtype, int helper,
  * independently).
  *
  * Each job means exactly what the single-job call with the same fields means.
- * All jobs are validated before anything is enqueued; an invalid job fails
- * the whole call with its status and a message naming the job index.  The
+ * All jobs are validated before anything is enqueued: first each job's
+ * arguments, in job order (the first invalid job fails the whole call with
+ * the status and message of its single-job call, prefixed "job j: "), then
+ * the aliasing over all jobs together (RR_EALIAS, prefixed "job j: " for an
+ * alias within one job, "jobs i and j: " for memory two jobs share).  The
  * jobs of one call run concurrently: one kernel launch for up to 40 reduction
  * segments (a helper or active job is one, an A=4 reduce-scatter pass-1 job
  * A, an owner pass with the balanced split 2H) or 64 chunk moves whose

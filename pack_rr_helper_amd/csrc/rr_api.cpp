@@ -158,6 +158,7 @@ struct RedItem {
     void *out;
     int64_t n;
     float scale;
+    int job;  // the job of a batched call the item belongs to
 };
 
 // Output ranges sorted by start, after checking that no two overlap (one
@@ -167,13 +168,15 @@ struct OutRange {
     int item;
 };
 
-bool sorted_disjoint_outputs(std::vector<OutRange> &outs)
+// Sorts `outs` by start; returns a position i whose range overlaps the one
+// before it, or 0 when all are disjoint.
+size_t sort_outputs(std::vector<OutRange> &outs)
 {
     std::sort(outs.begin(), outs.end(), [](const OutRange &a, const OutRange &b) { return a.r.lo < b.r.lo; });
     for (size_t i = 1; i < outs.size(); ++i)
         if (outs[i].r.lo < outs[i - 1].r.hi)
-            return false;
-    return true;
+            return i;
+    return 0;
 }
 
 // Calls f(output) for every output in the sorted, disjoint list that overlaps x.
@@ -194,8 +197,10 @@ bool each_overlapping(const std::vector<OutRange> &outs, Range x, F f)
 // exactly (each lane reads its inputs before writing the same elements) or is
 // disjoint from it; everything else is a forbidden alias.  Outputs must also
 // be disjoint from every other item's inputs and outputs, since all items of
-// one call run concurrently.
-rr_status check_items(const std::vector<RedItem> &items, int64_t es)
+// one call run concurrently.  On RR_EALIAS, culprit[] holds the indices of
+// the two items in conflict (the same index twice for an item whose output
+// overlaps its own input).
+rr_status check_items(const std::vector<RedItem> &items, int64_t es, size_t culprit[2])
 {
     std::vector<OutRange> outs;
     outs.reserve(items.size());
@@ -204,14 +209,19 @@ rr_status check_items(const std::vector<RedItem> &items, int64_t es)
         if (!o.empty())
             outs.push_back(OutRange{o, int(i)});
     }
-    if (!sorted_disjoint_outputs(outs))
+    if (const size_t i = sort_outputs(outs)) {
+        culprit[0] = size_t(outs[i - 1].item);
+        culprit[1] = size_t(outs[i].item);
         return fail(RR_EALIAS, "two output ranges overlap");
+    }
     for (size_t j = 0; j < items.size(); ++j)
         for (int k = 0; k < items[j].k; ++k) {
             const Range x = range_of(items[j].in[k], 0, items[j].n, es);
             if (x.empty())
                 continue;
             const bool ok = each_overlapping(outs, x, [&](const OutRange &o) {
+                culprit[0] = j;
+                culprit[1] = size_t(o.item);
                 return o.item == int(j) && same(o.r, x);
             });
             if (!ok)
@@ -219,6 +229,18 @@ rr_status check_items(const std::vector<RedItem> &items, int64_t es)
                             "an output range overlaps an input range other than an exact in-place alias");
         }
     return RR_OK;
+}
+
+// Prefixes the current message with the job (or the two jobs) at fault.
+rr_status jobs_error(int a, int b, rr_status st)
+{
+    char tmp[sizeof g_err];
+    if (a == b)
+        snprintf(tmp, sizeof tmp, "job %d: %.480s", a, g_err);
+    else
+        snprintf(tmp, sizeof tmp, "jobs %d and %d: %.470s", std::min(a, b), std::max(a, b), g_err);
+    memcpy(g_err, tmp, sizeof g_err);
+    return st;
 }
 
 class RedLauncher {
@@ -313,12 +335,15 @@ private:
     hipError_t err_ = hipSuccess;
 };
 
-rr_status run_reduce(const std::vector<RedItem> &items, int dtype, void *stream)
+// Checks and launches the items of one call.  In a batched call (`batch`)
+// the message of an alias names the job, or the two jobs, it involves.
+rr_status run_reduce(const std::vector<RedItem> &items, int dtype, void *stream, bool batch)
 {
     const int64_t es = elem_size(dtype);
-    rr_status st = check_items(items, es);
+    size_t culprit[2];
+    rr_status st = check_items(items, es, culprit);
     if (st != RR_OK)
-        return st;
+        return batch ? jobs_error(items[culprit[0]].job, items[culprit[1]].job, st) : st;
     RedLauncher L(dtype == RR_BF16, static_cast<hipStream_t>(stream));
     for (const RedItem &it : items)
         L.add(it, es);
@@ -528,10 +553,12 @@ struct Move {
     const void *src;
     void *dst;
     int64_t nbytes;
+    int job;  // the job of a batched call the move belongs to
 };
 
 // Every destination range is written by one move only and is read by none.
-rr_status check_moves(const std::vector<Move> &mv)
+// On RR_EALIAS, culprit[] holds the two moves in conflict.
+rr_status check_moves(const std::vector<Move> &mv, size_t culprit[2])
 {
     std::vector<OutRange> dsts;
     dsts.reserve(mv.size());
@@ -540,11 +567,18 @@ rr_status check_moves(const std::vector<Move> &mv)
         if (!d.empty())
             dsts.push_back(OutRange{d, int(i)});
     }
-    if (!sorted_disjoint_outputs(dsts))
+    if (const size_t i = sort_outputs(dsts)) {
+        culprit[0] = size_t(dsts[i - 1].item);
+        culprit[1] = size_t(dsts[i].item);
         return fail(RR_EALIAS, "two destination chunks overlap");
-    for (const Move &m : mv) {
-        const Range src{addr(m.src), addr(m.src) + uintptr_t(m.nbytes)};
-        if (!src.empty() && !each_overlapping(dsts, src, [](const OutRange &) { return false; }))
+    }
+    for (size_t i = 0; i < mv.size(); ++i) {
+        const Range src{addr(mv[i].src), addr(mv[i].src) + uintptr_t(mv[i].nbytes)};
+        if (!src.empty() && !each_overlapping(dsts, src, [&](const OutRange &o) {
+                culprit[0] = i;
+                culprit[1] = size_t(o.item);
+                return false;
+            }))
             return fail(RR_EALIAS, "a destination chunk overlaps a source chunk");
     }
     return RR_OK;
@@ -635,11 +669,14 @@ private:
     hipError_t err_ = hipSuccess;
 };
 
-rr_status run_copy(const std::vector<Move> &mv, void *stream)
+// Checks and launches the moves of one call (aliases in a batched call are
+// named as in run_reduce).
+rr_status run_copy(const std::vector<Move> &mv, void *stream, bool batch)
 {
-    rr_status st = check_moves(mv);
+    size_t culprit[2];
+    rr_status st = check_moves(mv, culprit);
     if (st != RR_OK)
-        return st;
+        return batch ? jobs_error(mv[culprit[0]].job, mv[culprit[1]].job, st) : st;
     CopyLauncher L(static_cast<hipStream_t>(stream));
     for (const Move &m : mv)
         L.add(m.src, m.dst, m.nbytes);
@@ -696,22 +733,41 @@ rr_status collect_a2a(const rr_relay *relay, int dtype, int helper, const void *
             const int64_t contiguous = int64_t(j) * c * es;
             if (!unpack)
                 mv.push_back(Move{static_cast<const char *>(ins[s]) + strided,
-                                  static_cast<char *>(outs[d]) + contiguous, c * es});
+                                  static_cast<char *>(outs[d]) + contiguous, c * es, 0});
             else
                 mv.push_back(Move{static_cast<const char *>(ins[d]) + contiguous,
-                                  static_cast<char *>(outs[d]) + strided_out, c * es});
+                                  static_cast<char *>(outs[d]) + strided_out, c * es, 0});
             ++j;
         }
     }
     return RR_OK;
 }
 
-rr_status job_error(int j, rr_status st)
+// Job j of a batched call: `collect` validates the job's arguments and
+// appends its items (or moves), which are tagged with j so that an alias
+// found later over the whole call can name the job(s) at fault.
+template <typename Collect>
+rr_status add_reduce_job(int j, std::vector<RedItem> &items, Collect collect)
 {
-    char tmp[sizeof g_err];
-    snprintf(tmp, sizeof tmp, "job %d: %.480s", j, g_err);
-    memcpy(g_err, tmp, sizeof g_err);
-    return st;
+    const size_t first = items.size();
+    const rr_status st = collect();
+    if (st != RR_OK)
+        return jobs_error(j, j, st);
+    for (size_t i = first; i < items.size(); ++i)
+        items[i].job = j;
+    return RR_OK;
+}
+
+template <typename Collect>
+rr_status add_copy_job(int j, std::vector<Move> &mv, Collect collect)
+{
+    const size_t first = mv.size();
+    const rr_status st = collect();
+    if (st != RR_OK)
+        return jobs_error(j, j, st);
+    for (size_t i = first; i < mv.size(); ++i)
+        mv[i].job = j;
+    return RR_OK;
 }
 
 }  // namespace
@@ -787,7 +843,7 @@ rr_status rr_helper_reduce(const rr_relay *relay, int coll, int dtype, int op, i
 {
     std::vector<RedItem> items;
     rr_status st = collect_helper(relay, coll, dtype, op, helper, slots, nSlots, out, items);
-    return st != RR_OK ? st : run_reduce(items, dtype, stream);
+    return st != RR_OK ? st : run_reduce(items, dtype, stream, false);
 }
 
 rr_status rr_active_add_scale(const rr_relay *relay, int coll, int dtype, int op, int activeIdx,
@@ -795,7 +851,7 @@ rr_status rr_active_add_scale(const rr_relay *relay, int coll, int dtype, int op
 {
     std::vector<RedItem> items;
     rr_status st = collect_active(relay, coll, dtype, op, activeIdx, in, nIn, out, items);
-    return st != RR_OK ? st : run_reduce(items, dtype, stream);
+    return st != RR_OK ? st : run_reduce(items, dtype, stream, false);
 }
 
 rr_status rr_rs_multi_reduce(const rr_relay *relay, int dtype, int op, int pass, int idx,
@@ -803,7 +859,7 @@ rr_status rr_rs_multi_reduce(const rr_relay *relay, int dtype, int op, int pass,
 {
     std::vector<RedItem> items;
     rr_status st = collect_rs(relay, dtype, op, pass, idx, in, nIn, out, items);
-    return st != RR_OK ? st : run_reduce(items, dtype, stream);
+    return st != RR_OK ? st : run_reduce(items, dtype, stream, false);
 }
 
 rr_status rr_a2a_pack(const rr_relay *relay, int dtype, int helper, const void *const *src,
@@ -811,7 +867,7 @@ rr_status rr_a2a_pack(const rr_relay *relay, int dtype, int helper, const void *
 {
     std::vector<Move> mv;
     rr_status st = collect_a2a(relay, dtype, helper, src, dst, false, mv);
-    return st != RR_OK ? st : run_copy(mv, stream);
+    return st != RR_OK ? st : run_copy(mv, stream, false);
 }
 
 rr_status rr_a2a_unpack(const rr_relay *relay, int dtype, int helper, const void *const *recv,
@@ -819,7 +875,7 @@ rr_status rr_a2a_unpack(const rr_relay *relay, int dtype, int helper, const void
 {
     std::vector<Move> mv;
     rr_status st = collect_a2a(relay, dtype, helper, recv, out, true, mv);
-    return st != RR_OK ? st : run_copy(mv, stream);
+    return st != RR_OK ? st : run_copy(mv, stream, false);
 }
 
 rr_status rr_helper_reduce_many(int coll, int dtype, int op, const rr_helper_job *jobs, int nJobs,
@@ -830,11 +886,13 @@ rr_status rr_helper_reduce_many(int coll, int dtype, int op, const rr_helper_job
     std::vector<RedItem> items;
     for (int j = 0; j < nJobs; ++j) {
         const rr_helper_job &b = jobs[j];
-        rr_status st = collect_helper(&b.relay, coll, dtype, op, b.helper, b.slots, b.nSlots, b.out, items);
+        rr_status st = add_reduce_job(j, items, [&] {
+            return collect_helper(&b.relay, coll, dtype, op, b.helper, b.slots, b.nSlots, b.out, items);
+        });
         if (st != RR_OK)
-            return job_error(j, st);
+            return st;
     }
-    return run_reduce(items, dtype, stream);
+    return run_reduce(items, dtype, stream, true);
 }
 
 rr_status rr_active_add_scale_many(int coll, int dtype, int op, const rr_active_job *jobs, int nJobs,
@@ -845,11 +903,13 @@ rr_status rr_active_add_scale_many(int coll, int dtype, int op, const rr_active_
     std::vector<RedItem> items;
     for (int j = 0; j < nJobs; ++j) {
         const rr_active_job &b = jobs[j];
-        rr_status st = collect_active(&b.relay, coll, dtype, op, b.activeIdx, b.in, b.nIn, b.out, items);
+        rr_status st = add_reduce_job(j, items, [&] {
+            return collect_active(&b.relay, coll, dtype, op, b.activeIdx, b.in, b.nIn, b.out, items);
+        });
         if (st != RR_OK)
-            return job_error(j, st);
+            return st;
     }
-    return run_reduce(items, dtype, stream);
+    return run_reduce(items, dtype, stream, true);
 }
 
 rr_status rr_rs_multi_reduce_many(int dtype, int op, const rr_rs_job *jobs, int nJobs, void *stream)
@@ -859,11 +919,13 @@ rr_status rr_rs_multi_reduce_many(int dtype, int op, const rr_rs_job *jobs, int 
     std::vector<RedItem> items;
     for (int j = 0; j < nJobs; ++j) {
         const rr_rs_job &b = jobs[j];
-        rr_status st = collect_rs(&b.relay, dtype, op, b.pass, b.idx, b.in, b.nIn, b.out, items);
+        rr_status st = add_reduce_job(j, items, [&] {
+            return collect_rs(&b.relay, dtype, op, b.pass, b.idx, b.in, b.nIn, b.out, items);
+        });
         if (st != RR_OK)
-            return job_error(j, st);
+            return st;
     }
-    return run_reduce(items, dtype, stream);
+    return run_reduce(items, dtype, stream, true);
 }
 
 static rr_status a2a_many(int dtype, const rr_a2a_job *jobs, int nJobs, bool unpack, void *stream)
@@ -873,11 +935,13 @@ static rr_status a2a_many(int dtype, const rr_a2a_job *jobs, int nJobs, bool unp
     std::vector<Move> mv;
     for (int j = 0; j < nJobs; ++j) {
         const rr_a2a_job &b = jobs[j];
-        rr_status st = collect_a2a(&b.relay, dtype, b.helper, b.in, b.out, unpack, mv);
+        rr_status st = add_copy_job(j, mv, [&] {
+            return collect_a2a(&b.relay, dtype, b.helper, b.in, b.out, unpack, mv);
+        });
         if (st != RR_OK)
-            return job_error(j, st);
+            return st;
     }
-    return run_copy(mv, stream);
+    return run_copy(mv, stream, true);
 }
 
 rr_status rr_a2a_pack_many(int dtype, const rr_a2a_job *jobs, int nJobs, void *stream)

@@ -241,6 +241,18 @@ def test_many_rejects_cross_job_overlap_and_names_the_job(sim):
     L = sim.L
     L0 = L.sim_launches()
     assert L.rr_helper_reduce_many(AR, BF16, AVG, jobs, 2, None) == 2    # RR_EALIAS
+    assert L.rr_last_error().decode() == "jobs 0 and 1: two output ranges overlap"
+    # job 1 reading job 0's output
+    jobs[1].out = ptr(out, n).value
+    jobs[1].slots[1] = ptr(out, 16).value
+    assert L.rr_helper_reduce_many(AR, BF16, AVG, jobs, 2, None) == 2
+    assert L.rr_last_error().decode().startswith("jobs 0 and 1: an output range overlaps")
+    # an alias within one job is named like any other invalid job
+    jobs[1].slots[1] = ptr(x[1], c).value
+    jobs[1].out = ptr(x[1], c + 1).value
+    assert L.rr_helper_reduce_many(AR, BF16, AVG, jobs, 2, None) == 2
+    assert L.rr_last_error().decode().startswith("job 1: an output range overlaps")
+    jobs[1].out = ptr(out, n).value
     jobs[1].helper = 9
     assert L.rr_helper_reduce_many(AR, BF16, AVG, jobs, 2, None) == 1    # RR_EINVAL
     assert L.rr_last_error().decode().startswith("job 1:")
