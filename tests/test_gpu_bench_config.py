@@ -1,7 +1,8 @@
 """Parity in the exact launch configuration bench.py times: the seeded inputs
 and launches of one benchmark step at the 64 MiB message, for one GPU's share
-(the default) and for the whole-group variant, every output the step writes
-against the CPU oracle."""
+(the default) and for the whole-group variant, in bf16 and (one GPU's share)
+in fp32 as ``--dtype f32`` runs it, every output the step writes against the
+CPU oracle, bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -10,26 +11,23 @@ import bench
 from pack_rr_helper_amd import synth
 
 pytestmark = pytest.mark.gpu
-BF16, SUM, AVG = 1, 0, 1
-
-
-def ords(b):
-    b = b.astype(np.int32)
-    return np.where(b & 0x8000, 0x8000 - (b & 0x7FFF) - 1, b + 0x8000)
+F32, BF16, SUM, AVG = 0, 1, 0, 1
 
 
 def same(got, ref, what):
-    d = np.abs(ords(got) - ords(ref))
-    assert d.max() <= 1, what
-    assert int(np.sum(d == 0)) == d.size, f"{what}: not bit-exact"
+    got, ref = np.ascontiguousarray(got), np.ascontiguousarray(ref)
+    assert got.dtype == ref.dtype and got.shape == ref.shape, what
+    bad = np.flatnonzero(got.view(np.uint8) != ref.view(np.uint8))
+    assert bad.size == 0, f"{what}: {bad.size} bytes differ, first at byte {bad[:1]}"
 
 
-@pytest.mark.parametrize("variant", ["share", "group"])
-def test_benchmark_step_matches_the_oracle(orc, variant):
-    print(f"[gpu-case] bench step 64 MiB, {variant}", flush=True)
+@pytest.mark.parametrize("variant,dtype", [("share", "bf16"), ("group", "bf16"), ("share", "f32")])
+def test_benchmark_step_matches_the_oracle(orc, variant, dtype):
+    print(f"[gpu-case] bench step 64 MiB, {variant}, {dtype}", flush=True)
     M = 64 << 20
-    inp = bench.host_inputs(M)
-    wls = bench.build_rows(inp, mode=variant)
+    DT = F32 if dtype == "f32" else BF16
+    inp = bench.host_inputs(M, dtype)
+    wls = bench.build_rows(inp, mode=variant, dtype=dtype)
     calls = [c for w in wls.values() for c in w.calls()]
     assert len(calls) == 9
     for w in wls.values():
@@ -41,26 +39,26 @@ def test_benchmark_step_matches_the_oracle(orc, variant):
     ar2 = wls["ar2"]
     c = ar2.g["chunk"]
     for k in range(3 if share else 6):
-        same(synth.to_host(ar2.red[k])[:c], orc.ar2_helper(BF16, AVG, x[0][k * c:(k + 1) * c], x[1][k * c:(k + 1) * c]),
+        same(synth.to_host(ar2.red[k])[:c], orc.ar2_helper(DT, AVG, x[0][k * c:(k + 1) * c], x[1][k * c:(k + 1) * c]),
              f"ar2 helper {k}")
     lo = ar2.g["direct_off"]
     for a in range(1 if share else 2):
-        ref = orc.ar_active(BF16, AVG, 2, 6, 8, 0, x[0].size, a, x, np.zeros_like(x[0]))
+        ref = orc.ar_active(DT, AVG, 2, 6, 8, 0, x[0].size, a, x, np.zeros_like(x[0]))
         same(synth.to_host(ar2.out[a])[lo:], ref[lo:], f"ar2 active {a}")
     # A=2 reduce-scatter owners
     x = inp["rs2"]
     R = x[0].size // 2
-    same(synth.to_host(wls["rs2"].out[0]), orc.rs2_active(BF16, AVG, x[0][:R], x[1][:R]), "rs2 owner 0")
+    same(synth.to_host(wls["rs2"].out[0]), orc.rs2_active(DT, AVG, x[0][:R], x[1][:R]), "rs2 owner 0")
     if not share:
-        same(synth.to_host(wls["rs2"].out[1]), orc.rs2_active(BF16, AVG, x[0][R:], x[1][R:]), "rs2 owner 1")
+        same(synth.to_host(wls["rs2"].out[1]), orc.rs2_active(DT, AVG, x[0][R:], x[1][R:]), "rs2 owner 1")
     # A=4 allreduce: helper slices and active direct slices
     x = inp["ar4"]
     ar4 = wls["ar4"]
     c, g = ar4.g["chunk"], ar4.g
     for h in range(1 if share else 4):
-        same(synth.to_host(ar4.red[h])[:c], orc.ar4_helper(BF16, AVG, [v[h * c:(h + 1) * c] for v in x]), f"ar4 helper {h}")
+        same(synth.to_host(ar4.red[h])[:c], orc.ar4_helper(DT, AVG, [v[h * c:(h + 1) * c] for v in x]), f"ar4 helper {h}")
     for a in range(1 if share else 4):
-        ref = orc.ar_active(BF16, AVG, 4, 4, 0, 500, x[0].size, a, x, np.zeros_like(x[0]))
+        ref = orc.ar_active(DT, AVG, 4, 4, 0, 500, x[0].size, a, x, np.zeros_like(x[0]))
         lo = g["direct_off"] + a * g["dslice"]
         hi = lo + g["dslice"] if a < 3 else x[0].size
         same(synth.to_host(ar4.out[a])[lo:hi], ref[lo:hi], f"ar4 active {a}")
@@ -70,19 +68,22 @@ def test_benchmark_step_matches_the_oracle(orc, variant):
     R, c = x[0].size // 4, rs4.g["chunk"]
     for h in range(1 if share else 4):
         hs = np.concatenate([x[s][o * R + h * c:o * R + (h + 1) * c] for o in range(4) for s in range(4) if s != o])
-        same(synth.to_host(rs4.scratch[h])[12 * c:16 * c], orc.rs4_pass1(BF16, 4, c, hs), f"rs4 pass1 helper {h}")
-    ref = orc.rs4_group(BF16, SUM, 4, 500, R, x)
+        same(synth.to_host(rs4.scratch[h])[12 * c:16 * c], orc.rs4_pass1(DT, 4, c, hs), f"rs4 pass1 helper {h}")
+    ref = orc.rs4_group(DT, SUM, 4, 500, R, x)
     for o in range(1 if share else 4):
         same(synth.to_host(rs4.out[o]), ref[o], f"rs4 owner {o}")
     # A=4 all-to-all: pack and unpack of the helper slices the step covers
     x = inp["a2a"]
     a2a = wls["a2a"]
     c, seg = a2a.g["chunk"], a2a.seg
-    expect = [np.zeros(4 * seg, np.uint16) for _ in range(4)]
+    es = x[0].itemsize
+    expect = [np.zeros(4 * seg, x[0].dtype) for _ in range(4)]
     for h in range(1 if share else 4):
-        packed = orc.a2a_pack(2, 4, seg, c, h, x)
+        packed = orc.a2a_pack(es, 4, seg, c, h, x)
         for d in range(4):
-            assert np.array_equal(synth.to_host(a2a.packed[h][d])[:3 * c].view(np.uint8), packed[d])
-        orc.a2a_unpack(2, 4, seg, c, h, packed, expect)
+            got = synth.to_host(a2a.packed[h][d])[:3 * c]
+            assert np.array_equal(got.view(np.uint8), packed[d].view(np.uint8)), f"a2a pack helper {h} dest {d}"
+        orc.a2a_unpack(es, 4, seg, c, h, packed, expect)
     for d in range(4):
-        assert np.array_equal(synth.to_host(a2a.out[d]), expect[d])
+        got = synth.to_host(a2a.out[d])
+        assert np.array_equal(got.view(np.uint8), expect[d].view(np.uint8)), f"a2a unpack dest {d}"
