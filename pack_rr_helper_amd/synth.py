@@ -13,6 +13,10 @@ stream ``numpy.random.default_rng([seed, r])`` (PCG64):
   and subnormal encodings included).
 * ``as_bf16_bits``: a float32 array rounded to bf16 with torch's CPU
   conversion (round-to-nearest-even), returned as raw uint16 bit patterns.
+* ``pattern_pairs(part, parts)``: not random -- one of ``parts`` equal slices
+  of the 2^32 ordered pairs of 16-bit patterns: the pairs whose first pattern
+  is congruent to ``part`` modulo ``parts`` (so every slice spans every sign
+  and exponent).
 """
 import numpy as np
 import torch
@@ -37,6 +41,16 @@ def bits16(n, seed, rank):
 
 def bits32(n, seed, rank):
     return rng(seed, rank).integers(0, 1 << 32, size=n, dtype=np.uint32)
+
+
+def pattern_pairs(part, parts):
+    """Slice `part` (0 <= part < parts, parts a power of two <= 65536) of the
+    2^32 ordered pairs of 16-bit patterns: uint16 arrays (a, b) holding every
+    pair whose first pattern a is congruent to part modulo parts, a ascending,
+    then b from 0 to 65535."""
+    a = np.repeat(np.arange(part, 1 << 16, parts, dtype=np.uint16), 1 << 16)
+    b = np.tile(np.arange(1 << 16, dtype=np.uint16), (1 << 16) // parts)
+    return a, b
 
 
 def small_ints(n, lim, seed, rank):
