@@ -356,26 +356,33 @@ def test_special_values_subnormals_and_infinities(orc):
         check_bf16(host(out), orc.ar2_helper(BF16, op, a[:c].copy(), b[:c].copy()), f"special op={op}")
 
 
-def _f32_classes(n, seed, rank):
-    """float32 inputs mixing, element by element, raw random patterns, subnormals,
-    the smallest normals (which AVG scales into the subnormal range), the largest
-    finite exponent (sums overflow to infinity), signed zeros, infinities and
-    NaNs."""
+def _special_classes(n, seed, rank, dt):
+    """Inputs mixing, element by element, raw random patterns, subnormals, the
+    smallest normals (which AVG scales into the subnormal range), the largest
+    finite binade (sums overflow to infinity), signed zeros, infinities and
+    NaNs: float32 values, or bf16 bit patterns."""
     rng = synth.rng(seed, rank)
-    sign = rng.integers(0, 2, n, dtype=np.uint32) << 31
-    mant = rng.integers(0, 1 << 23, n, dtype=np.uint32)
+    if dt == F32:
+        mbits, sbit, u = 23, 31, synth.bits32(n, seed, 100 + rank)
+        specials = [0x0, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0xFFA00001, 0x00000001,
+                    0x807FFFFF, 0x00800000]
+    else:
+        mbits, sbit, u = 7, 15, synth.bits16(n, seed, 100 + rank).astype(np.uint32)
+        specials = [0x0, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0xFFA1, 0x0001, 0x807F, 0x0080]
+    sign = rng.integers(0, 2, n, dtype=np.uint32) << sbit
+    mant = rng.integers(0, 1 << mbits, n, dtype=np.uint32)
     cls = rng.integers(0, 6, n)
-    u = synth.bits32(n, seed, 100 + rank)
-    u = np.where(cls == 1, sign | mant, u)                               # subnormal (or zero)
-    u = np.where(cls == 2, sign | (np.uint32(1) << 23) | mant, u)         # smallest binade
-    u = np.where(cls == 3, sign | (np.uint32(254) << 23) | mant, u)       # largest binade
-    specials = np.array([0x0, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0xFFA00001, 0x00000001,
-                         0x807FFFFF, 0x00800000], np.uint32)
-    u = np.where(cls == 4, specials[rng.integers(0, specials.size, n)], u)
-    return u.astype(np.uint32).view(np.float32)
+    u = np.where(cls == 1, sign | mant, u)                                  # subnormal (or zero)
+    u = np.where(cls == 2, sign | (np.uint32(1) << mbits) | mant, u)         # smallest binade
+    u = np.where(cls == 3, sign | (np.uint32(254) << mbits) | mant, u)       # largest binade
+    u = np.where(cls == 4, np.array(specials, np.uint32)[rng.integers(0, len(specials), n)], u)
+    return u.astype(np.uint32).view(np.float32) if dt == F32 else u.astype(np.uint16)
 
 
-def check_f32_bits(got, ref, what):
+def check_bits(got, ref, dt, what):
+    """Bit-exact, except that NaN results are compared by position only."""
+    if dt == BF16:
+        return check_bf16(got, ref, what)
     gu, ru = got.view(np.uint32), ref.view(np.uint32)
     gnan = ((gu & 0x7F800000) == 0x7F800000) & ((gu & 0x7FFFFF) != 0)
     rnan = ((ru & 0x7F800000) == 0x7F800000) & ((ru & 0x7FFFFF) != 0)
@@ -386,31 +393,33 @@ def check_f32_bits(got, ref, what):
     assert bad.size == 0, f"{what}: {bad.size} differ, first got {gu[bad[0]]:#010x} oracle {ru[bad[0]]:#010x}"
 
 
+@pytest.mark.parametrize("dt", [F32, BF16])
 @pytest.mark.parametrize("op", [SUM, AVG])
-def test_fp32_subnormals_infinities_and_nans(orc, op):
-    """fp32 sums keep subnormal inputs and results (no flush to zero), overflow
-    to infinity, and give NaN where the oracle does: the two-, four- and
-    three-input folds."""
-    say("fp32 special values", op)
+def test_folds_on_subnormals_infinities_and_nans(orc, dt, op):
+    """Sums keep subnormal inputs and results (no flush to zero), overflow to
+    infinity, and give NaN where the oracle does: the two-, four- and
+    three-input folds, fp32 and bf16."""
+    say("special values", dt, op)
     c = 1 << 17
-    xs = [_f32_classes(c, 11, r) for r in range(4)]
+    xs = [_special_classes(c, 11, r, dt) for r in range(4)]
+    tdt = torch.float32 if dt == F32 else torch.bfloat16
     # A=2 allreduce helper: two slots
-    out = torch.empty(c, dtype=torch.float32, device="cuda")
-    rr.rr_helper_reduce(rr.Relay(2, 6, 8, 0, 8 * c), AR, F32, op, 0, [dev(xs[0], F32), dev(xs[1], F32)], out)
-    check_f32_bits(host(out), orc.ar2_helper(F32, op, xs[0], xs[1]), "fp32 two-input fold")
-    # A=4 allreduce helper: four position slices (count 2^20: oChunk = count/8 at 500 permille)
+    out = torch.empty(c, dtype=tdt, device="cuda")
+    rr.rr_helper_reduce(rr.Relay(2, 6, 8, 0, 8 * c), AR, dt, op, 0, [dev(xs[0], dt), dev(xs[1], dt)], out)
+    check_bits(host(out), orc.ar2_helper(dt, op, xs[0], xs[1]), dt, "two-input fold")
+    # A=4 allreduce helper: four position slices (oChunk = count/8 at 500 permille)
     relay4 = rr.Relay(4, 4, 0, 500, 8 * c)
-    assert rr.rr_geometry(relay4, AR, F32)["chunk"] == c
-    rr.rr_helper_reduce(relay4, AR, F32, op, 0, [dev(x, F32) for x in xs], out)
-    check_f32_bits(host(out), orc.ar4_helper(F32, op, xs), "fp32 four-input fold")
+    assert rr.rr_geometry(relay4, AR, dt)["chunk"] == c
+    rr.rr_helper_reduce(relay4, AR, dt, op, 0, [dev(x, dt) for x in xs], out)
+    check_bits(host(out), orc.ar4_helper(dt, op, xs), dt, "four-input fold")
     # A=4 reduce-scatter pass 1: three-input partial sums per owner (no scale)
     R = 8 * (c // 4)
     rs = rr.Relay(4, 4, 0, 500, R)
-    cc = rr.rr_geometry(rs, RS, F32)["chunk"]
-    scratch = np.concatenate([_f32_classes(12 * cc, 12, 0), np.zeros(2 * R - 12 * cc, np.float32)])
-    ds = dev(scratch, F32)
-    rr.rr_rs_multi_reduce(rs, F32, op, 1, 0, [ds], ds[12 * cc:16 * cc])
-    check_f32_bits(host(ds)[12 * cc:16 * cc], orc.rs4_pass1(F32, 4, cc, scratch), "fp32 three-input fold")
+    cc = rr.rr_geometry(rs, RS, dt)["chunk"]
+    scratch = np.concatenate([_special_classes(12 * cc, 12, 0, dt), np.zeros(2 * R - 12 * cc, xs[0].dtype)])
+    ds = dev(scratch, dt)
+    rr.rr_rs_multi_reduce(rs, dt, op, 1, 0, [ds], ds[12 * cc:16 * cc])
+    check_bits(host(ds)[12 * cc:16 * cc], orc.rs4_pass1(dt, 4, cc, scratch), dt, "three-input fold")
 
 
 def test_empty_and_zero_chunk_calls_are_no_ops(orc):
