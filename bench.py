@@ -74,6 +74,9 @@ VARIANTS = {
 METRIC = "achieved HBM GB/s (and % of peak) of relay reduce/pack kernels, 2MB-1GB msgs"
 MIB = 1 << 20
 BF16_CODE, F32_CODE = 1, 0  # dtype codes of the C ABI and the oracle
+# rows of the per-role sweep (one workload each; the _shifted rows place every
+# input at an odd element offset, the a2a_ragged row has segmentCount = 5 mod 8)
+SWEEP_ROWS = ("ar2", "rs2", "ar4", "rs4", "a2a", "a2a_ragged", "rs2_shifted", "ar4_shifted")
 
 
 def parse():
@@ -108,6 +111,9 @@ def parse():
     p.add_argument("--sweep-sizes", default="2,4,8,16,32,64,128,256,512,1024")
     p.add_argument("--sweep-reps", type=int, default=20)
     p.add_argument("--sweep-dtypes", default="bf16,f32")
+    p.add_argument("--sweep-rows", default=",".join(SWEEP_ROWS),
+                   help="rows of the per-role sweep; the _shifted rows put every input at an odd "
+                        "element offset (the realigning reduction kernels)")
     p.add_argument("--flush", choices=("read", "write", "none"), default="read",
                    help="how the sweep and calibration evict inputs from the caches before each rep")
     p.add_argument("--sweep-out", default=None)
@@ -756,9 +762,10 @@ def sweep(args):
                           file=sys.stderr, flush=True)
                     oracle_cache[key] = oracle_role_rates(sample, dt_name, mode_of(args))
                 orates = oracle_cache[key]
-            for row in ("ar2", "rs2", "ar4", "rs4", "a2a", "a2a_ragged"):
+            for row in args.sweep_rows.split(","):
                 gen.manual_seed(zlib.crc32(f"{row}/{dt_name}/{M}".encode()))
-                ranks = 2 if row in ("ar2", "rs2") else 4
+                base = row.split("_")[0]
+                ranks = 2 if base in ("ar2", "rs2") else 4
                 if row.startswith("a2a"):
                     # ragged: segmentCount = 5 mod 8, so odd destinations' chunks sit at
                     # byte offsets that disagree with the packed buffer modulo 16
@@ -766,16 +773,22 @@ def sweep(args):
                     lim = 1 << (8 * W.ESIZE[dt] - 1)
                     xs = [torch.randint(-lim, lim - 1, (nr,), dtype=bits_dt, device="cuda", generator=gen)
                           for _ in range(ranks)]
+                elif row.endswith("_shifted"):
+                    # rank r's input starts 2r + 1 elements into its buffer: every
+                    # input sits at another offset modulo 16 bytes
+                    xs = [torch.randn(n + 16, device="cuda", generator=gen).to(tdt)[2 * r + 1:2 * r + 1 + n]
+                          for r in range(ranks)]
                 else:
                     xs = [torch.randn(n, device="cuda", generator=gen).to(tdt) for _ in range(ranks)]
                 mode = mode_of(args)
                 wl = {"ar2": lambda: W.AR2(xs, dt, rr.AVG, mode=mode), "rs2": lambda: W.RS2(xs, dt, rr.AVG, mode=mode),
                       "ar4": lambda: W.AR4(xs, dt, rr.AVG, mode=mode), "rs4": lambda: W.RS4(xs, dt, rr.SUM, mode=mode),
-                      "a2a": lambda: W.A2A(xs, dt, mode=mode), "a2a_ragged": lambda: W.A2A(xs, dt, mode=mode)}[row]()
+                      "a2a": lambda: W.A2A(xs, dt, mode=mode)}[base]()
                 calls = wl.calls(stream)
+                suffix = row[len(base):]
                 for role in sorted({c[0] for c in calls}):
                     role_call = next(c for c in calls if c[0] == role)
-                    name = role + ("_ragged" if row == "a2a_ragged" else "")
+                    name = role + suffix
                     rec = record(mib, dt_name, name, role_call[1], role_call[2], times_of(role_call[3]))
                     # the plain stream of this launch's read/write mix and bytes, timed alike
                     st_sets, st_launch, st_bytes = stand_in_step([role_call], 1, stream)
@@ -786,8 +799,10 @@ def sweep(args):
                                        "gbs_best": round(st_bytes / min(st_ts) / 1e9, 1),
                                        "relay_over_stand_in": round(rec["gbs_median"] / st_gbs, 3)}
                     del st_sets
-                    if name in orates:
-                        o = dict(orates[name])
+                    # a realigned view changes where the data sits, not the oracle's work
+                    oname = name if name in orates else role
+                    if oname in orates:
+                        o = dict(orates[oname])
                         o["gpu_over_oracle"] = round(rec["gbs_median"] / o["gbs"], 1)
                         rec["oracle"] = o
                     print(json.dumps(rec), file=out, flush=True)
