@@ -282,12 +282,14 @@ def oracle_jobs(inp, prep, dt, variant="share"):
         count = x[0].size
         g = orc.geometry(4, 4, 0, 500, count, orc.ALLREDUCE, dt)
         c = g["chunk"]
+        # one launch for both roles of the phase, except with one launch per job
+        roles = ("ar4_helper", "ar4_active") if variant == "job" else ("ar4_phase", "ar4_phase")
         for h in range(n_a4):
-            jobs.append(("ar4_helper", 5 * c * es, P(orc.ar4_helper, dt, AVG, [v[h * c:(h + 1) * c] for v in x])))
+            jobs.append((roles[0], 5 * c * es, P(orc.ar4_helper, dt, AVG, [v[h * c:(h + 1) * c] for v in x])))
         out = np.zeros_like(x[0])
         for a in range(n_a4):
             n = g["dslice"] if a < 3 else g["direct_len"] - 3 * g["dslice"]
-            jobs.append(("ar4_active", 5 * n * es, P(orc.ar_active, dt, AVG, 4, 4, 0, 500, count, a, x, out)))
+            jobs.append((roles[1], 5 * n * es, P(orc.ar_active, dt, AVG, 4, 4, 0, 500, count, a, x, out)))
     if "rs4" in inp:
         x = inp["rs4"]
         R = x[0].size // 4
@@ -425,10 +427,11 @@ def kernel_source_digest():
     return code_digest(texts)
 
 
-def traffic_for(kernel, message_mib, variant):
+def traffic_for(kernel, message_mib, variant, algo_bytes_per_launch, launches_per_step):
     """HBM bytes per launch of `kernel` (counter-measured, scaled by a plain
     copy of known size) from profiles/traffic.json, or None if absent, taken
-    on another workload, or taken on other kernel sources."""
+    on another workload or launch sequence (other launches per step, or other
+    algorithmic bytes per launch), or taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -439,7 +442,10 @@ def traffic_for(kernel, message_mib, variant):
     if t.get("message_mib") != message_mib or t.get("variant") != variant:
         return None
     k = t.get("kernels", {}).get(kernel)
-    return None if not k else k.get("hbm_bytes_per_launch")
+    if not k or k.get("algorithmic_bytes_per_launch") != algo_bytes_per_launch \
+            or k.get("launches_per_step") != launches_per_step:
+        return None
+    return k.get("hbm_bytes_per_launch")
 
 
 # --------------------------------------------------------------------------
@@ -584,7 +590,7 @@ def step_bench(args):
     dom = max(per_kernel, key=lambda k: per_kernel[k][0])
     d_ms, d_b, d_n = per_kernel[dom]
     achieved = (d_b / d_n) / (launch_ms(d_ms, d_n) * 1e-3) / 1e9
-    traffic = traffic_for(dom, args.message_mib, args.variant)
+    traffic = traffic_for(dom, args.message_mib, args.variant, d_b // d_n, d_n // args.steps)
 
     value = step_bytes / (ms_step * 1e-3) / 1e9
     result = {
@@ -782,7 +788,7 @@ def sweep(args):
                     xs = [torch.randn(n, device="cuda", generator=gen).to(tdt) for _ in range(ranks)]
                 mode = mode_of(args)
                 wl = {"ar2": lambda: W.AR2(xs, dt, rr.AVG, mode=mode), "rs2": lambda: W.RS2(xs, dt, rr.AVG, mode=mode),
-                      "ar4": lambda: W.AR4(xs, dt, rr.AVG, mode=mode), "rs4": lambda: W.RS4(xs, dt, rr.SUM, mode=mode),
+                      "ar4": lambda: W.AR4(xs, dt, rr.AVG, mode=mode, phase=False), "rs4": lambda: W.RS4(xs, dt, rr.SUM, mode=mode),
                       "a2a": lambda: W.A2A(xs, dt, mode=mode)}[base]()
                 calls = wl.calls(stream)
                 suffix = row[len(base):]
@@ -885,7 +891,7 @@ def calibrate(args):
 # reduce-scatter owner pass mixes 4+1 and 2+1 segments (24 reads to 8 writes
 # per chunk), taken as 3+1; a copy reads 1 and writes 1.
 STEP_MIX = {"ar2_helper": (2, 1), "ar2_active": (2, 1), "rs2_owner": (2, 1), "ar4_helper": (4, 1),
-            "ar4_active": (4, 1), "rs4_pass1": (3, 1), "rs4_pass2": (3, 1), "a2a_pack": (1, 1),
+            "ar4_active": (4, 1), "ar4_phase": (4, 1), "rs4_pass1": (3, 1), "rs4_pass2": (3, 1), "a2a_pack": (1, 1),
             "a2a_unpack": (1, 1)}
 
 

@@ -307,6 +307,29 @@ rr_status rr_rs_multi_reduce_many(int dtype, int op, const rr_rs_job *jobs, int 
 rr_status rr_a2a_pack_many(int dtype, const rr_a2a_job *jobs, int nJobs, void *stream);
 rr_status rr_a2a_unpack_many(int dtype, const rr_a2a_job *jobs, int nJobs, void *stream);
 
+/*
+ * rr_phase_reduce_many -- every helper and active reduction a GPU runs in one
+ * phase, in one batched call.  In the fused A=4 allreduce (summary section 4,
+ * groups of 4 consecutive ranks) a rank is an active of its own group and a
+ * helper of the other one; after the first serialized group of hops it reduces
+ * its own direct slice (the intra-link reduce-scatter) and its position slice
+ * of the other group's offload region (the helper's 4->1 sum) before the
+ * second group returns both.  The two reductions read different buffers and
+ * are ready at the same time, so they share one launch.
+ *   helperJobs[0..nHelper): as rr_helper_reduce_many (numbered as jobs
+ *     0..nHelper-1 in messages); activeJobs[0..nActive): as
+ *     rr_active_add_scale_many (jobs nHelper..nHelper+nActive-1).  All jobs
+ *     share coll, dtype and op.
+ *   Each job means what its single-job call means; validation, aliasing over
+ *   all jobs of both arrays, and launch batching follow the batched forms
+ *   above.  nHelper == nActive == 0 is a no-op.  Either array may be null when
+ *   its count is zero.
+ */
+rr_status rr_phase_reduce_many(int coll, int dtype, int op,
+                               const rr_helper_job *helperJobs, int nHelper,
+                               const rr_active_job *activeJobs, int nActive,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ __all__ = [
     "library_path", "load", "rr_abi_version", "rr_geometry", "rr_passthrough_helper_size",
     "rr_helper_reduce", "rr_active_add_scale", "rr_rs_multi_reduce", "rr_a2a_pack",
     "rr_a2a_unpack", "rr_helper_reduce_many", "rr_active_add_scale_many",
-    "rr_rs_multi_reduce_many", "rr_a2a_pack_many", "rr_a2a_unpack_many",
+    "rr_rs_multi_reduce_many", "rr_a2a_pack_many", "rr_a2a_unpack_many", "rr_phase_reduce_many",
 ]
 
 F32, BF16 = 0, 1
@@ -127,6 +127,8 @@ def load():
         ("rr_rs_multi_reduce_many", ci, [ci, ci, ctypes.POINTER(_RsJob), ci, vp]),
         ("rr_a2a_pack_many", ci, [ci, ctypes.POINTER(_A2AJob), ci, vp]),
         ("rr_a2a_unpack_many", ci, [ci, ctypes.POINTER(_A2AJob), ci, vp]),
+        ("rr_phase_reduce_many", ci, [ci, ci, ci, ctypes.POINTER(_HelperJob), ci,
+                                      ctypes.POINTER(_ActiveJob), ci, vp]),
     ]:
         f = getattr(L, name)
         f.restype, f.argtypes = res, args
@@ -322,31 +324,52 @@ def rr_a2a_unpack(relay, dtype, helper, recv, out, stream=None, prepare=False):
 # batched forms: jobs are tuples in the single-job argument order
 # --------------------------------------------------------------------------
 
-def rr_helper_reduce_many(coll, dtype, op, jobs, stream=None, prepare=False):
-    """jobs: [(relay, helper, slots, out), ...]"""
+def _helper_jobs(coll, dtype, jobs, first=0):
     arr = (_HelperJob * max(len(jobs), 1))()
     for j, (relay, helper, slots, out) in enumerate(jobs):
         n = _helper_need(relay, coll, dtype)
-        p, k = _ptrs(slots, f"job {j} slots", dtype, n)
+        p, k = _ptrs(slots, f"job {first + j} slots", dtype, n)
         arr[j].relay, arr[j].helper, arr[j].nSlots = relay._c(), helper, k
         for i in range(min(k, 4)):
             arr[j].slots[i] = p[i]
-        arr[j].out = _dev(out, f"job {j} out", dtype, n)
+        arr[j].out = _dev(out, f"job {first + j} out", dtype, n)
+    return arr
+
+
+def _active_jobs(dtype, jobs, first=0):
+    arr = (_ActiveJob * max(len(jobs), 1))()
+    for j, (relay, idx, inputs, out) in enumerate(jobs):
+        p, k = _ptrs(inputs, f"job {first + j} in", dtype, relay.count)
+        arr[j].relay, arr[j].activeIdx, arr[j].nIn = relay._c(), idx, k
+        for i in range(min(k, 4)):
+            arr[j].inp[i] = p[i]
+        arr[j].out = _dev(out, f"job {first + j} out", dtype, relay.count)
+    return arr
+
+
+def rr_helper_reduce_many(coll, dtype, op, jobs, stream=None, prepare=False):
+    """jobs: [(relay, helper, slots, out), ...]"""
+    arr = _helper_jobs(coll, dtype, jobs)
     return _issue(load().rr_helper_reduce_many, (coll, dtype, op, arr, len(jobs), _stream(stream)),
                   (arr, jobs), prepare)
 
 
 def rr_active_add_scale_many(coll, dtype, op, jobs, stream=None, prepare=False):
     """jobs: [(relay, active_idx, inputs, out), ...]"""
-    arr = (_ActiveJob * max(len(jobs), 1))()
-    for j, (relay, idx, inputs, out) in enumerate(jobs):
-        p, k = _ptrs(inputs, f"job {j} in", dtype, relay.count)
-        arr[j].relay, arr[j].activeIdx, arr[j].nIn = relay._c(), idx, k
-        for i in range(min(k, 4)):
-            arr[j].inp[i] = p[i]
-        arr[j].out = _dev(out, f"job {j} out", dtype, relay.count)
+    arr = _active_jobs(dtype, jobs)
     return _issue(load().rr_active_add_scale_many, (coll, dtype, op, arr, len(jobs), _stream(stream)),
                   (arr, jobs), prepare)
+
+
+def rr_phase_reduce_many(coll, dtype, op, helper_jobs, active_jobs, stream=None, prepare=False):
+    """The helper and active reductions of one phase in one call:
+    helper_jobs as rr_helper_reduce_many's jobs, active_jobs as
+    rr_active_add_scale_many's (numbered after the helper jobs in messages)."""
+    h = _helper_jobs(coll, dtype, helper_jobs)
+    a = _active_jobs(dtype, active_jobs, first=len(helper_jobs))
+    return _issue(load().rr_phase_reduce_many,
+                  (coll, dtype, op, h, len(helper_jobs), a, len(active_jobs), _stream(stream)),
+                  (h, a, helper_jobs, active_jobs), prepare)
 
 
 def rr_rs_multi_reduce_many(dtype, op, jobs, stream=None, prepare=False):

@@ -928,6 +928,33 @@ rr_status rr_rs_multi_reduce_many(int dtype, int op, const rr_rs_job *jobs, int 
     return run_reduce(items, dtype, stream, true);
 }
 
+rr_status rr_phase_reduce_many(int coll, int dtype, int op, const rr_helper_job *helperJobs, int nHelper,
+                               const rr_active_job *activeJobs, int nActive, void *stream)
+{
+    if (nHelper < 0 || (nHelper > 0 && !helperJobs))
+        return fail(RR_EINVAL, "helper job array is null or nHelper=%d is negative", nHelper);
+    if (nActive < 0 || (nActive > 0 && !activeJobs))
+        return fail(RR_EINVAL, "active job array is null or nActive=%d is negative", nActive);
+    std::vector<RedItem> items;
+    for (int j = 0; j < nHelper; ++j) {
+        const rr_helper_job &b = helperJobs[j];
+        rr_status st = add_reduce_job(j, items, [&] {
+            return collect_helper(&b.relay, coll, dtype, op, b.helper, b.slots, b.nSlots, b.out, items);
+        });
+        if (st != RR_OK)
+            return st;
+    }
+    for (int j = 0; j < nActive; ++j) {
+        const rr_active_job &b = activeJobs[j];
+        rr_status st = add_reduce_job(nHelper + j, items, [&] {
+            return collect_active(&b.relay, coll, dtype, op, b.activeIdx, b.in, b.nIn, b.out, items);
+        });
+        if (st != RR_OK)
+            return st;
+    }
+    return run_reduce(items, dtype, stream, true);
+}
+
 static rr_status a2a_many(int dtype, const rr_a2a_job *jobs, int nJobs, bool unpack, void *stream)
 {
     if (nJobs < 0 || (nJobs > 0 && !jobs))

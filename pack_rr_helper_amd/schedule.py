@@ -47,6 +47,7 @@ from dataclasses import dataclass, field
 
 from . import (ALLREDUCE, ALLTOALL, BF16, F32, REDUCE_SCATTER, Relay, rr_a2a_pack_many,
                rr_a2a_unpack_many, rr_active_add_scale_many, rr_geometry, rr_helper_reduce_many,
+               rr_phase_reduce_many,
                rr_rs_multi_reduce_many)
 
 NODE = 8
@@ -435,10 +436,25 @@ def run_on_gpu(s, inputs, stream=None):
         by_rank_kind = {}
         for st in grp.after:
             by_rank_kind.setdefault((st.rank, st.kind), []).append(st)
+        # a rank's helper and active reductions of one phase (the fused A=4
+        # allreduce: its position slice for the other group and its own direct
+        # slice) go out as one call
+        for rank in {r for r, _ in by_rank_kind}:
+            hs, acts = by_rank_kind.get((rank, "helper_reduce")), by_rank_kind.get((rank, "active"))
+            if hs and acts and len({st.coll for st in hs + acts}) == 1:
+                by_rank_kind[(rank, "phase")] = (hs, acts)
+                del by_rank_kind[(rank, "helper_reduce")], by_rank_kind[(rank, "active")]
         for (rank, kind), steps in sorted(by_rank_kind.items(), key=lambda kv: kv[0]):
             if kind == "copy":
                 for st in steps:
                     view(st.outs[0]).copy_(view(st.ins[0]))
+            elif kind == "phase":
+                hs, acts = steps
+                rr_phase_reduce_many(hs[0].coll, s.dtype, s.op,
+                                     [(st.relay, st.idx, [full(x) for x in st.ins], full(st.outs[0]))
+                                      for st in hs],
+                                     [(st.relay, st.idx, [full(x) for x in st.ins], full(st.outs[0]))
+                                      for st in acts], stream)
             elif kind == "helper_reduce":
                 rr_helper_reduce_many(steps[0].coll, s.dtype, s.op,
                                       [(st.relay, st.idx, [full(x) for x in st.ins], full(st.outs[0]))

@@ -41,7 +41,7 @@ import torch
 from . import (ALLREDUCE, ALLTOALL, AVG, BF16, F32, REDUCE_SCATTER, SUM, Relay, rr_a2a_pack,
                rr_a2a_pack_many, rr_a2a_unpack, rr_a2a_unpack_many, rr_active_add_scale,
                rr_active_add_scale_many, rr_geometry, rr_helper_reduce, rr_helper_reduce_many,
-               rr_rs_multi_reduce, rr_rs_multi_reduce_many)
+               rr_phase_reduce_many, rr_rs_multi_reduce, rr_rs_multi_reduce_many)
 
 TORCH = {F32: torch.float32, BF16: torch.bfloat16}
 ESIZE = {F32: 4, BF16: 2}
@@ -170,10 +170,14 @@ class RS2(_Row):
 class AR4(_Row):
     """A=4 allreduce at an offload fraction (summary section 4): the H helpers
     reduce their position slices 4->1, the A actives reduce their direct
-    slices."""
+    slices.  Both happen in the same phase of the fused call (a rank is an
+    active of its group and a helper of the other), so with ``phase`` the
+    "share" and "group" forms issue them as one rr_phase_reduce_many call
+    (row "ar4_phase"; one GPU's share is helper slice 0 and active slice 0);
+    without it, and in the "job" form, each role is its own call."""
 
-    def __init__(self, xs, dtype, op=AVG, H=4, permille=500, mode="group"):
-        self.dtype, self.op = dtype, op
+    def __init__(self, xs, dtype, op=AVG, H=4, permille=500, mode="group", phase=True):
+        self.dtype, self.op, self.phase = dtype, op, phase
         self._set_mode(mode)
         self.count = xs[0].numel()
         self.relay = Relay(4, H, 0, permille, self.count)
@@ -189,6 +193,14 @@ class AR4(_Row):
         hjobs = [(r, h, [x[h * c:(h + 1) * c] for x in self.x], self.red[h]) for h in range(r.H)] if c else []
         sizes = [g["dslice"] if a < 3 else g["direct_len"] - 3 * g["dslice"] for a in range(4)]
         ajobs = [(r, a, self.x, self.out[a]) for a in range(4) if sizes[a]]
+        if self.phase and self.mode != "job":
+            n = None if self.mode == "group" else 1
+            hj, aj = hjobs[:n], ajobs[:n]
+            if not hj and not aj:
+                return []
+            b = 5 * es * (c * len(hj) + sum(sizes[j[1]] for j in aj))
+            return [("ar4_phase", k, b,
+                     rr_phase_reduce_many(ALLREDUCE, dt, op, hj, aj, stream=stream, prepare=True))]
         return (self._roles(stream, "ar4_helper", k, [5 * c * es] * len(hjobs), hjobs,
                             lambda j, **kw: rr_helper_reduce_many(ALLREDUCE, dt, op, j, **kw),
                             lambda j, **kw: rr_helper_reduce(j[0], ALLREDUCE, dt, op, *j[1:], **kw))

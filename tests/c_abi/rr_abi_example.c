@@ -124,6 +124,10 @@ static int host_checks(void)
     CHECK(rr_a2a_pack(&r4, RR_BF16, 0, src, dst, NULL) == RR_EALIAS, "in-place pack accepted");
     CHECK(rr_helper_reduce_many(RR_ALLREDUCE, RR_BF16, RR_SUM, NULL, 1, NULL) == RR_EINVAL,
           "null job array accepted");
+    CHECK(rr_phase_reduce_many(RR_ALLREDUCE, RR_BF16, RR_SUM, NULL, 0, NULL, 1, NULL) == RR_EINVAL,
+          "null active job array accepted");
+    CHECK(rr_phase_reduce_many(RR_ALLREDUCE, RR_BF16, RR_SUM, NULL, 0, NULL, 0, NULL) == RR_OK,
+          "empty phase call rejected: %s", rr_last_error());
     return 0;
 }
 

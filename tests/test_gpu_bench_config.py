@@ -29,7 +29,7 @@ def test_benchmark_step_matches_the_oracle(orc, variant, dtype):
     inp = bench.host_inputs(M, dtype)
     wls = bench.build_rows(inp, mode=variant, dtype=dtype)
     calls = [c for w in wls.values() for c in w.calls()]
-    assert len(calls) == 9
+    assert len(calls) == 8   # the A=4 allreduce's helper and active slices share one launch
     for w in wls.values():
         w.run()
     torch.cuda.synchronize()

@@ -486,6 +486,54 @@ def test_many_calls_over_heterogeneous_groups(orc):
         check_bf16(host(o4[a]), ref, f"A=4 active {a}")
 
 
+def test_phase_call_runs_a4_helper_and_active_slices(orc):
+    """One rank's phase of the fused A=4 allreduce as one call: its helper
+    slices of the other group and its own direct slices, at a count whose
+    direct slices start off a 16-byte boundary (those take the realigning
+    launch), plus an A=2 helper job of a third group; every output equal to
+    the oracle's, and the call equal to the two per-role calls."""
+    say("phase call A=4 allreduce")
+    n = 2 ** 21 + 4 * 128 * 5 + 7
+    xs = [synth.as_bf16_bits(synth.uniform(n, -2, 2, 62, a)) for a in range(4)]
+    ys = [synth.as_bf16_bits(synth.uniform(n, -2, 2, 63, a)) for a in range(4)]
+    n2 = 8 * 128 * 40 + 3
+    zs = [synth.as_bf16_bits(synth.normal(n2, 64, a)) for a in range(2)]
+    dx, dy, dz = [dev(x) for x in xs], [dev(y) for y in ys], [dev(z) for z in zs]
+    r4, r2 = rr.Relay(4, 4, 0, 500, n), rr.Relay(2, 6, 8, 0, n2)
+    c, c2 = rr.rr_geometry(r4, AR, BF16)["chunk"], rr.rr_geometry(r2, AR, BF16)["chunk"]
+    assert c > 0 and c2 > 0
+
+    def run(fused):
+        red = [torch.zeros(c, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+        red2 = torch.zeros(c2, dtype=torch.bfloat16, device="cuda")
+        outs = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+        hj = [(r4, h, [y[h * c:(h + 1) * c] for y in dy], red[h]) for h in range(4)] + \
+             [(r2, 5, [z[5 * c2:6 * c2] for z in dz], red2)]
+        aj = [(r4, a, dx, outs[a]) for a in range(4)]
+        if fused:
+            rr.rr_phase_reduce_many(AR, BF16, AVG, hj, aj)
+        else:
+            rr.rr_helper_reduce_many(AR, BF16, AVG, hj)
+            rr.rr_active_add_scale_many(AR, BF16, AVG, aj)
+        return [host(t) for t in red + [red2] + outs]
+
+    got, apart = run(True), run(False)
+    for h in range(4):
+        check_bf16(got[h], orc.ar4_helper(BF16, AVG, [y[h * c:(h + 1) * c].copy() for y in ys]), f"helper {h}")
+    check_bf16(got[4], orc.ar2_helper(BF16, AVG, zs[0][5 * c2:6 * c2].copy(), zs[1][5 * c2:6 * c2].copy()),
+               "A=2 helper 5")
+    for a in range(4):
+        check_bf16(got[5 + a], orc.ar_active(BF16, AVG, 4, 4, 0, 500, n, a, xs, np.zeros(n, np.uint16)),
+                   f"active {a}")
+    for i, (g, p) in enumerate(zip(got, apart)):
+        assert np.array_equal(g, p), f"output {i}: the phase call differs from the per-role calls"
+    # an active writing what a helper reads is rejected before any launch
+    out = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(rr.RRError, match="RR_EALIAS"):
+        rr.rr_phase_reduce_many(AR, BF16, AVG, [(r4, 0, [out[4 * c:5 * c]] + [y[:c] for y in dy[1:]], dy[0][:1].new_zeros(c))],
+                                [(r4, 0, dx, out)])
+
+
 def test_workload_modes_agree(orc):
     """One call per job, one call over the whole group's jobs and one call
     over one GPU's share write the same bytes where they overlap, each checked

@@ -227,6 +227,75 @@ def test_active_many_mixes_a2_and_a4_groups(sim, orc):
         assert np.array_equal(o4[a], orc.ar_active(BF16, AVG, 4, 4, 0, 500, n4, a, x4, np.zeros(n4, np.uint16)))
 
 
+def test_phase_reduce_runs_a4_helper_and_active_slices_in_one_launch(sim, orc):
+    """The A=4 allreduce phase of one rank: its helper slice of the other
+    group and its own direct slice, one call, one launch, each output equal
+    to the oracle's; then every helper and active job of a group at once."""
+    sim.reset()
+    # above the 2 MiB pure-direct floor; every slice starts 16-byte aligned
+    # (other offsets take a second, realigning launch) and the last active
+    # slice has a 3-element tail
+    A, H, n = 4, 4, 2 ** 20 + 2 ** 15 + 3
+    xs = [synth.as_bf16_bits(synth.uniform(n, -2, 2, 3, r)) for r in range(A)]
+    ys = [synth.as_bf16_bits(synth.uniform(n, -2, 2, 4, r)) for r in range(A)]
+    bx = [sim.buf(x.copy(), writable=False) for x in xs]
+    by = [sim.buf(y.copy(), writable=False) for y in ys]
+    c = orc.geometry(A, H, 0, 500, n, AR, BF16)["chunk"]
+    assert c > 0
+
+    def helper_jobs(hs, src):
+        jobs = (_rr._HelperJob * len(hs))()
+        outs = []
+        for j, h in enumerate(hs):
+            o = sim.buf(np.zeros(c, np.uint16))
+            jobs[j].relay, jobs[j].helper, jobs[j].nSlots = _relay(A, H, 0, 500, n), h, A
+            for i, b in enumerate(src):
+                jobs[j].slots[i] = ptr(b, h * c).value
+            jobs[j].out = ptr(o).value
+            outs.append(o)
+        return jobs, outs
+
+    def active_jobs(as_, src):
+        jobs = (_rr._ActiveJob * len(as_))()
+        outs = []
+        for j, a in enumerate(as_):
+            o = sim.buf(np.zeros(n, np.uint16))
+            jobs[j].relay, jobs[j].activeIdx, jobs[j].nIn = _relay(A, H, 0, 500, n), a, A
+            for i, b in enumerate(src):
+                jobs[j].inp[i] = ptr(b).value
+            jobs[j].out = ptr(o).value
+            outs.append(o)
+        return jobs, outs
+
+    for hs, as_ in (([1], [2]), (list(range(H)), list(range(A)))):
+        hj, ho = helper_jobs(hs, by)     # the other group's offload region
+        aj, ao = active_jobs(as_, bx)    # this group's direct slices
+        L0 = sim.L.sim_launches()
+        sim.call("rr_phase_reduce_many", AR, BF16, AVG, hj, len(hs), aj, len(as_), None)
+        assert sim.L.sim_launches() - L0 == 1
+        for h, o in zip(hs, ho):
+            assert np.array_equal(o, orc.ar4_helper(BF16, AVG, [y[h * c:(h + 1) * c].copy() for y in ys]))
+        for a, o in zip(as_, ao):
+            assert np.array_equal(o, orc.ar_active(BF16, AVG, A, H, 0, 500, n, a, xs, np.zeros(n, np.uint16)))
+
+    # a helper job reading what an active job writes (active 0's direct
+    # slice starts after the H relay chunks) names the active job with its
+    # number after the helper jobs'; an empty call launches nothing
+    hj, _ = helper_jobs([0], by)
+    aj, ao = active_jobs([0], bx)
+    hj[0].slots[1] = ptr(ao[0], H * c).value
+    L = sim.L
+    L0 = L.sim_launches()
+    assert L.rr_phase_reduce_many(AR, BF16, AVG, hj, 1, aj, 1, None) == 2      # RR_EALIAS
+    assert L.rr_last_error().decode().startswith("jobs 0 and 1: ")
+    aj[0].activeIdx = 7
+    assert L.rr_phase_reduce_many(AR, BF16, AVG, hj, 1, aj, 1, None) == 1      # RR_EINVAL
+    assert L.rr_last_error().decode().startswith("job 1:")
+    assert L.rr_phase_reduce_many(AR, BF16, AVG, None, 0, None, 0, None) == 0
+    assert L.rr_phase_reduce_many(AR, BF16, AVG, None, 1, None, 0, None) == 1
+    assert L.sim_launches() == L0
+
+
 def test_many_rejects_cross_job_overlap_and_names_the_job(sim):
     sim.reset()
     n = 8 * 128 * 4
