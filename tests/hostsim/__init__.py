@@ -2,6 +2,7 @@
 layer (pack_rr_helper_amd/csrc/rr_api.cpp) linked with a host-memory replay
 of the kernels' index arithmetic (sim_launch.cpp)."""
 import ctypes
+import fcntl
 import os
 import subprocess
 
@@ -23,7 +24,7 @@ CAPPED_DEFINES = ("RR_MAX_TILES_PER_LAUNCH=5",)
 
 
 def build(lib=LIB, defines=()):
-    tmp = lib + ".tmp"
+    tmp = f"{lib}.{os.getpid()}.tmp"   # private to this process: parallel test workers may build too
     subprocess.run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-D__HIP_PLATFORM_AMD__",
                     *[f"-D{d}" for d in defines],
                     "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
@@ -36,9 +37,12 @@ def build(lib=LIB, defines=()):
 class Sim:
     def __init__(self, capped=False):
         lib, defines = (CAPPED_LIB, CAPPED_DEFINES) if capped else (LIB, ())
-        if not os.path.exists(lib) or any(os.path.getmtime(s) > os.path.getmtime(lib)
-                                          for s in SOURCES + HEADERS):
-            build(lib, defines)
+        # one builder at a time; the others wait and then find the library fresh
+        with open(lib + ".lock", "w") as lk:
+            fcntl.flock(lk, fcntl.LOCK_EX)
+            if not os.path.exists(lib) or any(os.path.getmtime(s) > os.path.getmtime(lib)
+                                              for s in SOURCES + HEADERS):
+                build(lib, defines)
         self.L = ctypes.CDLL(lib)
         self.L.sim_message.restype = ctypes.c_char_p
         self.L.sim_register.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
