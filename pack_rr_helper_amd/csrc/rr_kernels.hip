@@ -12,7 +12,8 @@
 // its destination disagree modulo 16 bytes (strided all-to-all chunks, views
 // at other element offsets) the data is realigned in registers
 // (v_alignbyte), each lane taking its neighbouring source word from the next
-// lane (ds_bpermute) instead of loading it a second time or staging the tile.
+// lane (a DPP wave shift) instead of loading it a second time or staging the
+// tile.
 //
 // Tiling: one workgroup of 256 threads processes one tile of one segment.  A
 // launch's segments live in the kernel arguments; how a workgroup finds its
@@ -115,15 +116,19 @@ __device__ __forceinline__ Seg load_seg(const Seg &p)
 
 constexpr int kWave = 64;  // gfx950 runs wave64
 
-// The 16-byte vector held by the next lane of this wave (ds_bpermute).  Call
-// it outside any lane-dependent branch: a lane reading from a lane that is
-// switched off gets no data.  The last lane receives its own value.
+// The 16-byte vector held by the next lane of this wave: a DPP move with the
+// whole-wave left shift by one lane (wave_shl:1, lane i reads lane i + 1), a
+// plain VALU operation with no LDS access and no wait counter.  Call it outside
+// any lane-dependent branch: a lane reading from a lane that is switched off
+// gets no data.  The last lane, which has no next lane, receives 0.
+constexpr int kDppWaveShl1 = 0x130;
+
 __device__ __forceinline__ u32x4 next_lane(u32x4 x)
 {
     u32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        o[j] = (unsigned)__shfl_down((int)x[j], 1, kWave);
+        o[j] = (unsigned)__builtin_amdgcn_update_dpp(0, (int)x[j], kDppWaveShl1, 0xf, 0xf, false);
     return o;
 }
 

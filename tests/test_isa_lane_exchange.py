@@ -1,9 +1,11 @@
-"""The realigning kernels take a neighbouring lane's word with ds_bpermute,
-which returns nothing useful from a lane that is switched off.  This test
-compiles rr_kernels.hip for gfx950 to assembly (no GPU needed) and walks the
-control-flow graph of every realigning kernel: on every path, each
-ds_bpermute must run outside any divergent region (no s_*_saveexec without
-its restore), i.e. with every lane of the wave active."""
+"""The realigning kernels take a neighbouring lane's word with a DPP wave
+shift (wave_shl:1), which reads nothing useful from a lane that is switched
+off.  This test compiles rr_kernels.hip for gfx950 to assembly (no GPU
+needed) and walks the control-flow graph of every realigning kernel: on every
+path, each instruction carrying the wave shift (the DPP move, or a VALU
+operation the compiler folded it into) must run outside any divergent region
+(no s_*_saveexec without its restore), i.e. with every lane of the wave
+active.  No ds_bpermute remains."""
 import os
 import re
 import shutil
@@ -64,8 +66,12 @@ def _blocks(body):
     return order, blocks, succ
 
 
+def _is_exchange(t):
+    return "wave_shl:1" in t
+
+
 def _exchanges_in_divergent_code(body):
-    """(ds_bpermute count, those reachable at a nonzero exec nesting depth)."""
+    """(lane-exchange count, those reachable at a nonzero exec nesting depth)."""
     order, blocks, succ = _blocks(body)
     seen = {b: set() for b in order}
     seen["entry"].add(0)
@@ -79,13 +85,13 @@ def _exchanges_in_divergent_code(body):
                     d += 1
                 elif re.match(r"s_or_b64\s+exec,\s*exec,", t) or re.match(r"s_mov_b64\s+exec,\s*s", t):
                     d = max(0, d - 1)
-                if t.startswith("ds_bpermute") and d:
+                if _is_exchange(t) and d:
                     bad.add((b, j))
             for s in succ[b]:
                 if d not in seen[s] and d < 8:
                     seen[s].add(d)
                     work.append(s)
-    total = sum(1 for b in order for t in blocks[b] if t.startswith("ds_bpermute"))
+    total = sum(1 for b in order for t in blocks[b] if _is_exchange(t))
     return total, len(bad)
 
 
@@ -97,7 +103,8 @@ def test_lane_exchanges_run_with_every_lane_active(tmp_path):
         if kern is None:
             continue
         total, bad = _exchanges_in_divergent_code(body)
-        assert total > 0, f"{name}: no ds_bpermute found (the realignment changed shape)"
-        assert bad == 0, f"{name}: {bad} of {total} ds_bpermute run inside a divergent region"
+        assert total > 0, f"{name}: no wave_shl:1 exchange found (the realignment changed shape)"
+        assert bad == 0, f"{name}: {bad} of {total} lane exchanges run inside a divergent region"
+        assert not any(t.strip().startswith("ds_bpermute") for t in body), f"{name}: ds_bpermute is back"
         checked.add(kern)
     assert checked == set(KERNELS)
