@@ -74,9 +74,11 @@ VARIANTS = {
 METRIC = "achieved HBM GB/s (and % of peak) of relay reduce/pack kernels, 2MB-1GB msgs"
 MIB = 1 << 20
 BF16_CODE, F32_CODE = 1, 0  # dtype codes of the C ABI and the oracle
-# rows of the per-role sweep (one workload each; the _shifted rows place every
-# input at an odd element offset, the a2a_ragged row has segmentCount = 5 mod 8)
-SWEEP_ROWS = ("ar2", "rs2", "ar4", "rs4", "a2a", "a2a_ragged", "rs2_shifted", "ar4_shifted")
+# rows of the per-role sweep (one workload each; "ar4" times the A=4 allreduce's
+# helper and active launches apart, "ar4_phase" the launch they share in the
+# step; the _shifted rows place every input at an odd element offset, the
+# a2a_ragged row has segmentCount = 5 mod 8)
+SWEEP_ROWS = ("ar2", "rs2", "ar4", "ar4_phase", "rs4", "a2a", "a2a_ragged", "rs2_shifted", "ar4_shifted")
 
 
 def parse():
@@ -244,10 +246,13 @@ def oracle_prep(inp, dt):
     return prep
 
 
-def oracle_jobs(inp, prep, dt, variant="share"):
+def oracle_jobs(inp, prep, dt, variant="share", phase=True):
     """The GPU step's jobs through the oracle, as (role, algorithmic bytes,
     callable) in launch order: one GPU's share (3 A=2 helper jobs, one job in
     every other role) or, for the other variants, every job of the group.
+    The A=4 allreduce's helper and active jobs carry the role of their shared
+    launch, "ar4_phase", unless ``phase`` is False or every job is its own
+    launch.
     Outputs are private to the returned list; inputs are only read.  Every
     callable binds its arguments when it is made."""
     import functools
@@ -283,7 +288,7 @@ def oracle_jobs(inp, prep, dt, variant="share"):
         g = orc.geometry(4, 4, 0, 500, count, orc.ALLREDUCE, dt)
         c = g["chunk"]
         # one launch for both roles of the phase, except with one launch per job
-        roles = ("ar4_helper", "ar4_active") if variant == "job" else ("ar4_phase", "ar4_phase")
+        roles = ("ar4_helper", "ar4_active") if variant == "job" or not phase else ("ar4_phase", "ar4_phase")
         for h in range(n_a4):
             jobs.append((roles[0], 5 * c * es, P(orc.ar4_helper, dt, AVG, [v[h * c:(h + 1) * c] for v in x])))
         out = np.zeros_like(x[0])
@@ -383,7 +388,8 @@ def oracle_role_rates(M, dt_name, variant, budget_s=0.3):
     """The oracle's GB/s per role at message M, on one thread and on
     host_threads() threads, over the jobs the GPU launch of that role covers
     (same shapes, host inputs from the same recipe).  Roles are named as the
-    sweep names them."""
+    sweep names them (the A=4 allreduce both as its shared launch and as
+    separate roles)."""
     dt = F32_CODE if dt_name == "f32" else BF16_CODE
     rows = ("ar2", "rs2", "ar4", "rs4", "a2a", "a2a_ragged")
     inp = host_inputs(M, dt_name, rows)
@@ -392,9 +398,12 @@ def oracle_role_rates(M, dt_name, variant, budget_s=0.3):
     for row in rows:
         sub = {row: inp[row]}
         prep = oracle_prep(sub, dt)
-        for role in sorted({j[0] for j in oracle_jobs(sub, prep, dt, variant)}):
-            def make(role=role, sub=sub, prep=prep):
-                return [j for j in oracle_jobs(sub, prep, dt, variant) if j[0] == role]
+        for role, phase in sorted({(j[0], ph) for ph in (True, False)
+                                   for j in oracle_jobs(sub, prep, dt, variant, ph)}):
+            if role in rates:
+                continue
+            def make(role=role, sub=sub, prep=prep, phase=phase):
+                return [j for j in oracle_jobs(sub, prep, dt, variant, phase) if j[0] == role]
             t1, b1, _ = oracle_one_thread(make(), budget_s)
             tT, bT, _ = oracle_threads(make, T, budget_s)
             rates[role] = {"threads": T, "gbs": round(bT / tT / 1e9, 3), "gbs_1t": round(b1 / t1 / 1e9, 3),
@@ -788,10 +797,10 @@ def sweep(args):
                     xs = [torch.randn(n, device="cuda", generator=gen).to(tdt) for _ in range(ranks)]
                 mode = mode_of(args)
                 wl = {"ar2": lambda: W.AR2(xs, dt, rr.AVG, mode=mode), "rs2": lambda: W.RS2(xs, dt, rr.AVG, mode=mode),
-                      "ar4": lambda: W.AR4(xs, dt, rr.AVG, mode=mode, phase=False), "rs4": lambda: W.RS4(xs, dt, rr.SUM, mode=mode),
+                      "ar4": lambda: W.AR4(xs, dt, rr.AVG, mode=mode, phase=row == "ar4_phase"), "rs4": lambda: W.RS4(xs, dt, rr.SUM, mode=mode),
                       "a2a": lambda: W.A2A(xs, dt, mode=mode)}[base]()
                 calls = wl.calls(stream)
-                suffix = row[len(base):]
+                suffix = "" if row == "ar4_phase" else row[len(base):]
                 for role in sorted({c[0] for c in calls}):
                     role_call = next(c for c in calls if c[0] == role)
                     name = role + suffix

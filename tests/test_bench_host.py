@@ -79,6 +79,16 @@ def test_oracle_jobs_cover_the_step_bytes_per_role():
     assert _role_bytes(bench.oracle_jobs(inp, prep, bench.BF16_CODE, "job")) == job
 
 
+def test_oracle_rates_cover_every_sweep_role():
+    """The sweep's oracle column has a rate for every role it times: the A=4
+    allreduce as its shared phase launch and as separate helper and active
+    launches, beside every other role of one GPU's share."""
+    rates = bench.oracle_role_rates(M2, "bf16", "share", budget_s=0.0)
+    assert {"ar4_phase", "ar4_helper", "ar4_active"} <= set(rates)
+    assert set(bench.STEP_MIX) <= set(rates)
+    assert all(r["gbs"] > 0 and r["gbs_1t"] > 0 for r in rates.values())
+
+
 def test_oracle_timers_run_on_one_and_several_threads():
     inp = bench.host_inputs(M2, rows=("ar2",))
     prep = bench.oracle_prep(inp, bench.BF16_CODE)
