@@ -14,10 +14,12 @@ by the step before:
   A=4 reduce-scatter (H=4):           helper pass 1, owner pass 2
   A=4 all-to-all (H=4, numChunks=5):  helper-slice pack and unpack (segmentCount = M/8)
 
---variant chooses the jobs each role's launch covers (one launch per role):
+--variant chooses the jobs each launch covers (one launch per role, except
+that the A=4 allreduce's helper and active reductions, which a rank runs in
+the same phase, share one launch):
   share  (default) one GPU's share of the fused call: a GPU is a helper for
          the three other A=2 groups (3 helper jobs) and runs one job in
-         every other role; 9 launches per step;
+         every other role; 8 launches per step;
   group  every job of one simulated group in one launch (2-4x a GPU's share);
   job    one launch per job of the group (34 launches per step).
 
@@ -67,7 +69,8 @@ KERNEL_FORMS = {
 }
 VARIANTS = {
     "share": "each role's launch covers one GPU's share of the fused 8-GPU call (3 A=2 helper "
-             "jobs, one job in every other role)",
+             "jobs, one job in every other role; the A=4 allreduce's helper and active job share "
+             "one launch)",
     "group": "each role's launch covers every job of one simulated group (2-4x one GPU's share)",
     "job": "one launch per job",
 }
