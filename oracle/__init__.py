@@ -262,7 +262,7 @@ def a2a_group(es, A, H, numChunks, seg, src):
 
 
 def plain_sum(dt, op, x, off, n):
-    """RND(scale * sum_s x_s[off:off+n]) in fp64 with one correct rounding."""
+    """RND(sum_s x_s[off:off+n] / D), D = A for AVG: the exact sum, rounded once."""
     for s in x:
         _check(s, dt)
     out = np.empty(n, np_dtype(dt))

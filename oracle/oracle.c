@@ -26,7 +26,6 @@
  * closed forms, printed constants, exact rational brute force or library
  * routines -- never against this file's own formulas.
  */
-#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -59,28 +58,6 @@ uint16_t orc_f32_to_bf16(float f)
     return (uint16_t)(u >> 16);
 }
 
-/* Correct rounding of a double to the buffer dtype, used only by the plain
- * (fp64) collective definitions.  binary64 -> binary32 uses round-to-odd and
- * then binary32 -> bf16 uses round-to-nearest-even; rounding to odd with at
- * least two extra bits before the final rounding gives the correctly rounded
- * result (Boldo and Melquiond, "Emulation of FMA and correctly rounded sums:
- * proved algorithms using rounding to odd", IEEE TC 2008). */
-static float f64_to_f32_odd(double d)
-{
-    float t = (float)d;
-    if (isnan(d) || isinf(d) || (double)t == d)
-        return t;
-    if (isinf(t))  /* overflowed in nearest mode: take the largest finite */
-        t = copysignf(3.40282347e+38f, t);
-    else if (fabs((double)t) > fabs(d))
-        t = nextafterf(t, 0.0f);
-    uint32_t u;
-    memcpy(&u, &t, sizeof u);
-    u |= 1u;
-    memcpy(&t, &u, sizeof t);
-    return t;
-}
-
 static float ld(const void *p, int dt, int64_t i)
 {
     if (dt == ORC_F32)
@@ -94,14 +71,6 @@ static void st(void *p, int dt, int64_t i, float v)
         ((float *)p)[i] = v;
     else
         ((uint16_t *)p)[i] = orc_f32_to_bf16(v);
-}
-
-static void st64(void *p, int dt, int64_t i, double v)
-{
-    if (dt == ORC_F32)
-        ((float *)p)[i] = (float)v; /* one rounding, nearest-even */
-    else
-        ((uint16_t *)p)[i] = orc_f32_to_bf16(f64_to_f32_odd(v));
 }
 
 static int64_t esize(int dt) { return dt == ORC_F32 ? 4 : 2; }
@@ -546,19 +515,211 @@ int orc_a2a_group(int es, int A, int H, int numChunks, int64_t seg,
 }
 
 /* ------------------------------------------------------------------------- */
-/* Plain collective definitions, fp64 accumulation, one correct rounding.      */
+/* Plain collective definitions: the exact sum, rounded once.                  */
 /* ------------------------------------------------------------------------- */
 
-/* out[i] = RND(scale * sum_s x_s[off + i]) */
+/*
+ * Every finite binary32 value (and so every bf16 value) is an integer multiple
+ * of 2^-149, the least binary32 subnormal, and is smaller than 2^128 in
+ * magnitude.  The plain definition therefore sums the inputs exactly as a
+ * two's complement fixed-point integer whose unit is 2^-149: FX_LIMBS words of
+ * 32 bits hold 2^277 times any number of terms up to 2^42 with room for the
+ * sign.  No floating-point operation is involved until the single rounding.
+ */
+#define FX_LIMBS 10
+typedef struct { uint32_t w[FX_LIMBS]; } fx_int;  /* w[0] least significant */
+
+/* acc += sign * (mag << sh), mag < 2^32, 0 <= sh < 32*FX_LIMBS - 64. */
+static void fx_add_shifted(fx_int *acc, int negative, uint32_t mag, int sh)
+{
+    int limb = sh / 32;
+    uint64_t v = (uint64_t)mag << (sh % 32);  /* at most 63 bits */
+    uint32_t part[3] = {(uint32_t)v, (uint32_t)(v >> 32), 0};
+    if (!negative) {
+        uint64_t carry = 0;
+        for (int i = limb; i < FX_LIMBS; i++) {
+            uint64_t t = (uint64_t)acc->w[i] + (i - limb < 3 ? part[i - limb] : 0) + carry;
+            acc->w[i] = (uint32_t)t;
+            carry = t >> 32;
+        }
+    } else {
+        uint64_t borrow = 0;
+        for (int i = limb; i < FX_LIMBS; i++) {
+            uint64_t sub = (uint64_t)(i - limb < 3 ? part[i - limb] : 0) + borrow;
+            borrow = (uint64_t)acc->w[i] < sub;
+            acc->w[i] = (uint32_t)((uint64_t)acc->w[i] - sub);
+        }
+    }
+}
+
+static int fx_is_negative(const fx_int *a) { return (a->w[FX_LIMBS - 1] >> 31) & 1u; }
+
+static int fx_is_zero(const fx_int *a)
+{
+    for (int i = 0; i < FX_LIMBS; i++)
+        if (a->w[i])
+            return 0;
+    return 1;
+}
+
+static void fx_negate(fx_int *a)
+{
+    uint64_t carry = 1;
+    for (int i = 0; i < FX_LIMBS; i++) {
+        uint64_t t = (uint64_t)(uint32_t)~a->w[i] + carry;
+        a->w[i] = (uint32_t)t;
+        carry = t >> 32;
+    }
+}
+
+/* a = a / d (a >= 0, 0 < d < 2^31); returns the remainder. */
+static uint32_t fx_divmod_small(fx_int *a, uint32_t d)
+{
+    uint64_t rem = 0;
+    for (int i = FX_LIMBS - 1; i >= 0; i--) {
+        uint64_t cur = (rem << 32) | a->w[i];
+        a->w[i] = (uint32_t)(cur / d);
+        rem = cur % d;
+    }
+    return (uint32_t)rem;
+}
+
+static int fx_bit(const fx_int *a, int i) { return (int)((a->w[i / 32] >> (i % 32)) & 1u); }
+
+/* Number of significant bits of a >= 0 (0 for a == 0). */
+static int fx_bitlen(const fx_int *a)
+{
+    for (int i = FX_LIMBS - 1; i >= 0; i--)
+        if (a->w[i])
+            for (int b = 31; b >= 0; b--)
+                if ((a->w[i] >> b) & 1u)
+                    return 32 * i + b + 1;
+    return 0;
+}
+
+/* Any of bits [0, n) of a >= 0 set. */
+static int fx_any_below(const fx_int *a, int n)
+{
+    for (int i = 0; i < n; i++)
+        if (fx_bit(a, i))
+            return 1;
+    return 0;
+}
+
+/* Bits [lo, lo + 32) of a >= 0 (lo >= 0). */
+static uint32_t fx_bits_at(const fx_int *a, int lo)
+{
+    uint32_t r = 0;
+    for (int b = 0; b < 32 && lo + b < 32 * FX_LIMBS; b++)
+        r |= (uint32_t)fx_bit(a, lo + b) << b;
+    return r;
+}
+
+/*
+ * Round the exact value  sign * (q + rem/d) * 2^-149  to the binary format
+ * with p significant bits (24: binary32, 8: bf16), exponent range
+ * [-126, 127], round-to-nearest with ties to even (IEEE 754-2019 clause
+ * 4.3.1), gradual underflow, overflow to infinity.  Returns the format's bit
+ * pattern (32 or 16 bits wide).
+ */
+static uint32_t fx_round(const fx_int *q, uint32_t rem, uint32_t d, int negative, int p)
+{
+    const int width = p == 24 ? 32 : 16, man = p - 1;
+    const uint32_t sign = negative ? 1u << (width - 1) : 0u;
+    const int L = fx_bitlen(q);
+    /* exponent of the leading bit, in units of 2^-149; values under 2^-126 use
+       the subnormal quantum */
+    int lead = L - 1 - 149;
+    if (L == 0 || lead < -126)
+        lead = -126;
+    const int s = lead - (p - 1) + 149;  /* quantum = 2^(s - 149), s >= 0 */
+    /* q >> s: at most p bits, since s >= L - p */
+    uint64_t r = (uint64_t)fx_bits_at(q, s) & ((1ull << p) - 1);
+    int above_half, at_half;
+    if (s == 0) {
+        above_half = 2ull * rem > d;
+        at_half = 2ull * rem == d;
+    } else {
+        const int round_bit = fx_bit(q, s - 1);
+        const int sticky = fx_any_below(q, s - 1) || rem != 0;
+        above_half = round_bit && sticky;
+        at_half = round_bit && !sticky;
+    }
+    if (above_half || (at_half && (r & 1u)))
+        r += 1;
+    int e = s;
+    if (r == (1ull << p)) {  /* carried into the next binade */
+        r >>= 1;
+        e += 1;
+    }
+    if (r == 0)
+        return sign;  /* underflow to a zero of the value's sign */
+    if (r < (1ull << man))  /* subnormal: exponent field 0 */
+        return sign | (uint32_t)r;
+    const int biased = e - 149 + (p - 1) + 127;  /* exponent of r * 2^(e-149) */
+    if (biased >= 255)
+        return sign | (0xFFu << man);
+    return sign | ((uint32_t)biased << man) | ((uint32_t)r - (1u << man));
+}
+
+/* out[i] = RND(sum_s x_s[off + i] / D), D = A for AVG and 1 for SUM: the
+ * inputs summed exactly, then rounded once to the buffer dtype.  NaN inputs,
+ * and +inf with -inf, give the default quiet NaN; otherwise an infinite input
+ * gives that infinity.  An exact zero sum is -0 only when every input is -0. */
 void orc_plain_sum(int dt, int op, int A, const void *const *x, int64_t off,
                    int64_t n, void *out)
 {
-    double scale = op == ORC_AVG ? 1.0 / (double)A : 1.0;
+    const uint32_t d = op == ORC_AVG ? (uint32_t)A : 1u;
+    const int p = dt == ORC_F32 ? 24 : 8;
     for (int64_t i = 0; i < n; i++) {
-        double acc = 0.0;
-        for (int s = 0; s < A; s++)
-            acc += (double)ld(x[s], dt, off + i);
-        st64(out, dt, i, acc * scale);
+        fx_int acc;
+        memset(&acc, 0, sizeof acc);
+        int nan = 0, pinf = 0, ninf = 0, all_neg_zero = 1;
+        for (int s = 0; s < A; s++) {
+            uint32_t u;
+            if (dt == ORC_F32)
+                memcpy(&u, (const float *)x[s] + off + i, sizeof u);
+            else
+                u = (uint32_t)((const uint16_t *)x[s])[off + i] << 16;
+            const int neg = (int)(u >> 31), ef = (int)((u >> 23) & 0xFFu);
+            const uint32_t mf = u & 0x7FFFFFu;
+            if (u != 0x80000000u)
+                all_neg_zero = 0;
+            if (ef == 0xFF) {
+                if (mf)
+                    nan = 1;
+                else if (neg)
+                    ninf = 1;
+                else
+                    pinf = 1;
+                continue;
+            }
+            /* value = M * 2^sh units of 2^-149 */
+            const uint32_t M = ef ? (mf | 0x800000u) : mf;
+            const int sh = ef ? ef - 1 : 0;
+            if (M)
+                fx_add_shifted(&acc, neg, M, sh);
+        }
+        uint32_t bits;
+        if (nan || (pinf && ninf)) {
+            bits = p == 24 ? 0x7FC00000u : 0x7FC0u;
+        } else if (pinf || ninf) {
+            bits = p == 24 ? 0x7F800000u : 0x7F80u;
+            if (ninf)
+                bits |= p == 24 ? 0x80000000u : 0x8000u;
+        } else if (fx_is_zero(&acc)) {
+            bits = all_neg_zero ? (p == 24 ? 0x80000000u : 0x8000u) : 0u;
+        } else {
+            const int negative = fx_is_negative(&acc);
+            if (negative)
+                fx_negate(&acc);
+            const uint32_t rem = fx_divmod_small(&acc, d);
+            bits = fx_round(&acc, rem, d, negative, p);
+        }
+        if (dt == ORC_F32)
+            memcpy((float *)out + i, &bits, sizeof bits);
+        else
+            ((uint16_t *)out)[i] = (uint16_t)bits;
     }
 }
 

@@ -7,7 +7,7 @@ oracle's own formulas:
 * exact rational brute force (oracle/brute.py) on tiny random shapes: the
   same fp32 fold, rounded from first principles instead of by hardware;
 * the plain collective definitions: the A=2 and A=4 allreduce and the A=2
-  reduce-scatter compose to the plain fp64 result within one bf16 ulp
+  reduce-scatter compose to the plain result (exact sum, one rounding) within one bf16 ulp
   ("reduce-at-helper" equivalence, PR summary section 2), and the A=4
   reduce-scatter stays within the rounding-error bound of its two roundings;
 * a planted mistake: summing the A=2 reduce-scatter slots at the helper (which
@@ -256,3 +256,116 @@ def test_rs4_group_within_two_rounding_bound(orc):
     outs = orc.rs4_group(BF16, SUM, H, 500, R, xi)
     for o in range(A):
         assert np.array_equal(outs[o], orc.plain_sum(BF16, SUM, xi, o * R, R))
+
+
+# --------------------------------------------------------------------------
+# the plain definition itself: exact sum, one rounding
+# --------------------------------------------------------------------------
+
+def _brute_plain(bit_lists, fmt_bits, d):
+    """Expected plain_sum bits from first principles: decode every input
+    exactly, sum the rationals, divide by d, round once (brute force), and
+    give a rounded-away or exact zero the sign IEEE 754 gives it."""
+    fmt = brute.BINARY32 if fmt_bits == 32 else brute.BFLOAT16
+    sign_bit = 1 << (fmt_bits - 1)
+    out = []
+    for elems in zip(*bit_lists):
+        vals = [brute.decode(b, fmt_bits) for b in elems]
+        exact = sum(vals, Fraction(0)) / d
+        r = brute.round_nearest_even(exact, fmt)
+        bits = brute.encode(r, fmt_bits)
+        if r == 0:
+            if exact != 0:
+                bits = sign_bit if exact < 0 else 0
+            else:
+                bits = sign_bit if all(int(b) == sign_bit for b in elems) else 0
+        out.append(bits)
+    return out
+
+
+def _wide_bits(rng, n, fmt_bits, spread):
+    """n random finite bit patterns.  spread=None: biased exponents uniform over
+    the whole range (subnormals included); otherwise within `spread` binades
+    of a random centre, so that the terms overlap and rounding is decided by
+    bits far below the leading one."""
+    man_bits = 23 if fmt_bits == 32 else 7
+    if spread is None:
+        e = rng.integers(0, 255, n)
+    else:
+        centre = rng.integers(1, 255)
+        e = np.clip(centre + rng.integers(-spread, spread + 1, n), 0, 254)
+    m = rng.integers(0, 1 << man_bits, n)
+    s = rng.integers(0, 2, n)
+    bits = (s << (fmt_bits - 1)) | (e << man_bits) | m
+    return bits.astype(np.uint32 if fmt_bits == 32 else np.uint16)
+
+
+def _plain_bits(orc, dt, op, cols):
+    if dt == F32:
+        xs = [np.ascontiguousarray(c).view(np.float32) for c in cols]
+        return orc.plain_sum(dt, op, xs, 0, len(cols[0])).view(np.uint32)
+    return orc.plain_sum(dt, op, [np.ascontiguousarray(c) for c in cols], 0, len(cols[0]))
+
+
+def test_plain_sum_cases_double_rounding_gets_wrong(orc):
+    """1 + 2^-8 + 2^-80 lies above the bf16 midpoint 1 + 2^-8, so the sum rounds
+    up to 0x3F81; an fp64 accumulator loses the 2^-80 term and rounds the
+    midpoint to even (0x3F80).  The same for binary32 with 1 + 2^-24 + 2^-100."""
+    got = _plain_bits(orc, BF16, SUM, [np.array([0x3F80], np.uint16), np.array([0x3B80], np.uint16),
+                                       np.array([0x1780], np.uint16)])
+    assert int(got[0]) == 0x3F81
+    assert _brute_plain([[0x3F80], [0x3B80], [0x1780]], 16, 1) == [0x3F81]
+    cols = [np.array([v], np.float32).view(np.uint32) for v in (1.0, 2.0 ** -24, 2.0 ** -100)]
+    got = _plain_bits(orc, F32, SUM, cols)
+    assert int(got[0]) == 0x3F800001
+    assert _brute_plain([[int(c[0])] for c in cols], 32, 1) == [0x3F800001]
+
+
+@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("A,op", [(2, SUM), (2, AVG), (3, SUM), (3, AVG), (4, SUM), (4, AVG)])
+def test_plain_sum_against_brute_force_wide_exponents(orc, dt, A, op):
+    """Random finite inputs with exponent spreads from a few binades to the
+    whole binary32 range, subnormals, overflow to infinity and (AVG with
+    A = 3) a quotient that is not a dyadic rational: every output is the
+    correctly rounded value."""
+    fmt_bits = 32 if dt == F32 else 16
+    rng = np.random.default_rng(1000 + 10 * A + op + 100 * dt)
+    cols = [[] for _ in range(A)]
+    for spread in (None, 4, 12, 30, 60, 100):
+        for c in cols:
+            c.append(_wide_bits(rng, 250, fmt_bits, spread))
+    cols = [np.concatenate(c) for c in cols]
+    # cancellation: x, -x and a small remainder
+    k = 200
+    x = _wide_bits(rng, k, fmt_bits, 20)
+    sign = np.array(1 << (fmt_bits - 1), x.dtype)
+    small = _wide_bits(rng, k, fmt_bits, None)
+    extra = [x, x ^ sign] + [small] * (A - 2)
+    cols = [np.concatenate([c, e]) for c, e in zip(cols, extra)]
+    got = _plain_bits(orc, dt, op, cols)
+    exp = _brute_plain([list(map(int, c)) for c in cols], fmt_bits, A if op == AVG else 1)
+    bad = [i for i in range(len(exp)) if int(got[i]) != exp[i]]
+    assert not bad, [(i, [hex(int(c[i])) for c in cols], hex(int(got[i])), hex(exp[i])) for i in bad[:5]]
+
+
+@pytest.mark.parametrize("dt", [F32, BF16])
+def test_plain_sum_special_values(orc, dt):
+    """NaN in, or +inf with -inf: the default quiet NaN; an infinity alone: that
+    infinity; an exact zero: -0 only when every input is -0; a finite sum
+    beyond the largest finite value: infinity of its sign."""
+    if dt == F32:
+        Q, PINF, NINF, NZ, MAX = 0x7FC00000, 0x7F800000, 0xFF800000, 0x80000000, 0x7F7FFFFF
+        one, mone, snan = 0x3F800000, 0xBF800000, 0x7F800001
+        typ = np.uint32
+    else:
+        Q, PINF, NINF, NZ, MAX = 0x7FC0, 0x7F80, 0xFF80, 0x8000, 0x7F7F
+        one, mone, snan = 0x3F80, 0xBF80, 0x7F81
+        typ = np.uint16
+    cases = [
+        ((snan, one), Q), ((one, Q), Q), ((PINF, NINF), Q), ((PINF, one), PINF), ((NINF, MAX), NINF),
+        ((NZ, NZ), NZ), ((NZ, 0), 0), ((one, mone), 0), ((MAX, MAX), PINF), ((MAX | NZ, MAX | NZ), NINF),
+        ((MAX, MAX | NZ), 0),
+    ]
+    cols = [np.array([c[0][j] for c in cases], typ) for j in range(2)]
+    got = _plain_bits(orc, dt, SUM, cols)
+    assert [int(g) for g in got] == [e for _, e in cases]
