@@ -297,7 +297,7 @@ private:
                 s.in[k] = static_cast<const char *>(it.in[k]) + off * es;
             s.out = static_cast<char *>(it.out) + off * es;
             const rr::RedSplit sp = rr::red_split(s.out, n, es);
-            int64_t tiles = std::max<int64_t>(1, (sp.nv + tv - 1) / tv);
+            int64_t tiles = rr::body_tiles(sp.nv, tv);
             int64_t take = n;
             const int64_t room = rr::kMaxTilesPerLaunch - q.tiles;
             if (tiles > room) {
@@ -625,7 +625,7 @@ private:
             if (b_.nseg == rr::kMaxCopySegs || tiles_ >= rr::kMaxTilesPerLaunch)
                 flush();
             const rr::CopySplit sp = rr::copy_split(dst, nbytes);
-            int64_t tiles = std::max<int64_t>(1, (sp.nv + tv - 1) / tv);
+            int64_t tiles = rr::body_tiles(sp.nv, tv);
             int64_t take = nbytes;
             const int64_t room = rr::kMaxTilesPerLaunch - tiles_;
             if (tiles > room) {

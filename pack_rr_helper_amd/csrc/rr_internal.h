@@ -147,6 +147,119 @@ __host__ __device__ inline CopySplit copy_split(const unsigned char *dst, int64_
     return CopySplit{head, nv, nbytes - head - 16 * nv};
 }
 
+// ---------------------------------------------------------------------------
+// Index arithmetic of a tile.  The kernels (rr_kernels.hip) and the host
+// replay of their accesses (the bounds checks of the test suite) both call
+// these functions, so the replay follows the shipped indexing by
+// construction.  `x` is the lane's index in the workgroup (threadIdx.x).
+// ---------------------------------------------------------------------------
+
+constexpr int kWave = 64;  // gfx950 runs wave64
+
+// 16-byte vectors in one tile of a body processed U vectors per lane.
+template <int U>
+__host__ __device__ constexpr int64_t tile_vecs()
+{
+    return int64_t(kBlock) * U;
+}
+
+// Vector index of unroll step u of lane x within tile lt: step u of lane x is
+// x + u*kBlock, so each wave instruction covers 1 KiB and the workgroup's four
+// waves fill each 4 KiB.
+template <int U>
+__host__ __device__ inline int64_t vec_index(int64_t lt, int x, int u)
+{
+    return lt * tile_vecs<U>() + int64_t(x) + int64_t(u) * kBlock;
+}
+
+// Tile lt of a body of nv vectors is full (every lane's every step in range).
+__host__ __device__ inline bool full_tile(int64_t lt, int64_t tv, int64_t nv)
+{
+    return (lt + 1) * tv <= nv;
+}
+
+// Tiles of a body of nv vectors: at least one, which also handles the edges.
+__host__ __device__ inline int64_t body_tiles(int64_t nv, int64_t tv)
+{
+    return nv > tv ? (nv + tv - 1) / tv : 1;
+}
+
+// The last lane of its wave, which has no next lane to take a word from.
+__host__ __device__ inline bool wave_end(int x)
+{
+    return (x & (kWave - 1)) == kWave - 1;
+}
+
+// Which aligned 16-byte words a lane loads for body vector v of a realigning
+// tile (full: the whole tile is in range).  Every lane in range loads its own
+// word v; for an input whose body is not 16-byte aligned (`shifted`) the
+// wave's last lane also loads word v+1, which the other lanes take from their
+// next lane, and in a partial tile a lane whose v == nv still loads word nv
+// (its left neighbour needs it) and stores nothing.
+__host__ __device__ inline bool loads_own_word(bool full, int64_t v, int64_t nv, bool shifted)
+{
+    return full || v < nv || (v == nv && shifted);
+}
+
+__host__ __device__ inline bool loads_next_word(bool full, int64_t v, int64_t nv, bool shifted, bool last_lane)
+{
+    return last_lane && shifted && (full || v < nv);
+}
+
+// The lanes of a segment's tile 0 that compute its edges, element by element
+// (or byte by byte): lane x < head computes head element x; a lane of the
+// second wave with tail_lane(x, tail) computes element tail_elem(x, tail0) of
+// the tail [tail0, tail0 + tail).  Each edge is shorter than one 16-byte
+// vector.
+__host__ __device__ inline bool head_lane(int x, int64_t head)
+{
+    return x < head;
+}
+
+__host__ __device__ inline bool tail_lane(int x, int64_t tail)
+{
+    return x >= kWave && x - kWave < tail;
+}
+
+__host__ __device__ inline int64_t tail_elem(int x, int64_t tail0)
+{
+    return tail0 + (x - kWave);
+}
+
+// Index of the segment that owns tile t in a table form launch: the number of
+// later segment starts at or before t.  Unrolled over the table so the scalar
+// loads issue together.
+template <int MAXS>
+__host__ __device__ inline int find_seg(const int32_t (&tile0)[MAXS], int nseg, int32_t t)
+{
+    int s = 0;
+#pragma unroll
+    for (int i = 1; i < MAXS; ++i)
+        s += (i < nseg && t >= tile0[i]) ? 1 : 0;
+    return s;
+}
+
+// The aligned 16-byte word holding byte p, and p's offset in it (0..15).
+// The base stays a pointer derived from p (not an integer), so device code
+// keeps p's address space and loads through it as global memory.
+struct WordAt {
+    const unsigned char *base;
+    unsigned shift;
+};
+
+__host__ __device__ inline WordAt word_at(const unsigned char *p)
+{
+    const unsigned s = unsigned(reinterpret_cast<uintptr_t>(p) & 15u);
+    return WordAt{p - s, s};
+}
+
+// Work per tile (one workgroup) of each segment mode: a segment spans
+// body_tiles(nv, tile vectors) tiles.
+__host__ __device__ constexpr int64_t red_tile_vecs(int32_t mode)
+{
+    return mode == kRedShifted ? tile_vecs<kShiftRedUnroll>() : tile_vecs<kUnroll>();
+}
+
 template <int CAP>
 struct CopyBatchT {
     int32_t tile0[CAP];
@@ -157,10 +270,10 @@ struct CopyBatchT {
 constexpr int kSmallCopySegs = 16;
 using CopyBatch = CopyBatchT<kMaxCopySegs>;
 
-// Work per tile (one workgroup), matching the kernels' tiling: a segment
-// spans max(1, ceil(nv / tile vectors)) tiles.
-int64_t red_tile_vecs(int32_t mode);
-int64_t copy_tile_vecs(int32_t mode);
+__host__ __device__ constexpr int64_t copy_tile_vecs(int32_t mode)
+{
+    return mode == kCopyShifted ? tile_vecs<kShiftUnroll>() : tile_vecs<kCopyUnroll>();
+}
 
 // How a batch is launched.  Every form runs the same work per tile; they
 // differ in how a workgroup learns its segment before its first load:

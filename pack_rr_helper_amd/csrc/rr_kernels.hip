@@ -78,27 +78,6 @@ __device__ __forceinline__ void store_elem(void *p, int64_t i, float v)
         static_cast<float *>(p)[i] = v;
 }
 
-// Vector index of unroll step u of this thread within tile lt (a tile is
-// kBlock*U vectors): step u of thread t is t + u*kBlock, so each wave
-// instruction covers 1 KiB and the workgroup's four waves fill each 4 KiB.
-template <int U>
-__device__ __forceinline__ int64_t vec_index(int64_t lt, int u)
-{
-    return lt * (int64_t)(kBlock * U) + (int64_t)threadIdx.x + (int64_t)u * kBlock;
-}
-
-// Index of the segment that owns tile t: the number of later segment starts
-// at or before t.  Unrolled over the table so the scalar loads issue together.
-template <int MAXS>
-__device__ __forceinline__ int find_seg(const int32_t (&tile0)[MAXS], int nseg, int32_t t)
-{
-    int s = 0;
-#pragma unroll
-    for (int i = 1; i < MAXS; ++i)
-        s += (i < nseg && t >= tile0[i]) ? 1 : 0;
-    return s;
-}
-
 // A segment descriptor read as one vector, so it arrives in a single scalar
 // load (s_load_dwordx16 / x8) before the workgroup branches on its fields;
 // read field by field, the loads are issued one dependent round at a time.
@@ -110,11 +89,12 @@ __device__ __forceinline__ Seg load_seg(const Seg &p)
     return __builtin_bit_cast(Seg, *reinterpret_cast<const words *>(&p));
 }
 
+// This lane's index in its workgroup.
+__device__ __forceinline__ int lane() { return (int)threadIdx.x; }
+
 // ---------------------------------------------------------------------------
 // Cross-lane realignment (the realigning reduction and copy)
 // ---------------------------------------------------------------------------
-
-constexpr int kWave = 64;  // gfx950 runs wave64
 
 // The 16-byte vector held by the next lane of this wave: a DPP move with the
 // whole-wave left shift by one lane (wave_shl:1, lane i reads lane i + 1), a
@@ -193,11 +173,11 @@ __device__ __forceinline__ void reduce_elem(const RedSeg &sg, int64_t i)
 template <bool BF16, int K>
 __device__ __forceinline__ void reduce_edges(const RedSeg &sg, int64_t head, int64_t tail0, int64_t tail)
 {
-    const int x = (int)threadIdx.x;
-    if (x < head)
+    const int x = lane();
+    if (head_lane(x, head))
         reduce_elem<BF16, K>(sg, x);
-    else if (x >= kWave && x - kWave < tail)
-        reduce_elem<BF16, K>(sg, tail0 + (x - kWave));
+    else if (tail_lane(x, tail))
+        reduce_elem<BF16, K>(sg, tail_elem(x, tail0));
 }
 
 // kRedAligned segment: every pointer 16-byte aligned.
@@ -205,7 +185,6 @@ template <bool BF16, int K>
 __device__ __forceinline__ void reduce_vec(const RedSeg &sg, int64_t lt)
 {
     constexpr int kVecElems = BF16 ? 8 : 4;
-    constexpr int64_t kTileVecs = int64_t(kBlock) * kUnroll;
     const int64_t nv = sg.n / kVecElems;
     const float scale = sg.scale;
 
@@ -215,21 +194,21 @@ __device__ __forceinline__ void reduce_vec(const RedSeg &sg, int64_t lt)
         in[k] = static_cast<const u32x4 *>(sg.in[k]);
     u32x4 *out = static_cast<u32x4 *>(sg.out);
 
-    if ((lt + 1) * kTileVecs <= nv) {
+    if (full_tile(lt, tile_vecs<kUnroll>(), nv)) {
         // Full tile: issue every load before any arithmetic.
         u32x4 x[kUnroll][K];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
             for (int k = 0; k < K; ++k)
-                x[u][k] = ld16(in[k] + vec_index<kUnroll>(lt, u));
+                x[u][k] = ld16(in[k] + vec_index<kUnroll>(lt, lane(), u));
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            st16(out + vec_index<kUnroll>(lt, u), fold_vec<BF16, K>(x[u], scale));
+            st16(out + vec_index<kUnroll>(lt, lane(), u), fold_vec<BF16, K>(x[u], scale));
     } else {
         // The segment's last, partial tile (indices grow with u).
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t v = vec_index<kUnroll>(lt, u);
+            const int64_t v = vec_index<kUnroll>(lt, lane(), u);
             if (v >= nv)
                 break;
             u32x4 x[K];
@@ -247,12 +226,12 @@ __device__ __forceinline__ void reduce_vec(const RedSeg &sg, int64_t lt)
 // workgroup) past aligned word v: bytes [s, 16) of word v (a) and [0, s) of
 // word v+1, which the next lane holds; the wave's last lane loaded word v+1
 // itself (c).
-__device__ __forceinline__ u32x4 shifted_word(u32x4 a, u32x4 c, unsigned s, bool wave_end)
+__device__ __forceinline__ u32x4 shifted_word(u32x4 a, u32x4 c, unsigned s, bool last)
 {
     if (s == 0)
         return a;
     const u32x4 nb = next_lane(a);  // every lane is active here: s is uniform
-    const u32x4 b = wave_end ? c : nb;
+    const u32x4 b = last ? c : nb;
     switch (s >> 2) {
     case 0: return realign<0>(a, b, s & 3);
     case 1: return realign<1>(a, b, s & 3);
@@ -271,30 +250,25 @@ __device__ __forceinline__ void shifted_tile(const u32x4 *const (&base)[K], cons
                                              u32x4 *out, int64_t lt, int64_t nv, float scale)
 {
     constexpr int U = kShiftRedUnroll;
-    const bool wave_end = (threadIdx.x & (kWave - 1)) == kWave - 1;
+    const bool last = wave_end(lane());
     const u32x4 zero = {0u, 0u, 0u, 0u};
     u32x4 a[U][K], c[U][K];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t v = vec_index<U>(lt, u);
+        const int64_t v = vec_index<U>(lt, lane(), u);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            if (kFull) {
-                a[u][k] = ld16(base[k] + v);
-                c[u][k] = wave_end && sh[k] != 0 ? ld16(base[k] + v + 1) : zero;
-            } else {
-                a[u][k] = v < nv || (v == nv && sh[k] != 0) ? ld16(base[k] + v) : zero;
-                c[u][k] = wave_end && sh[k] != 0 && v < nv ? ld16(base[k] + v + 1) : zero;
-            }
+            a[u][k] = loads_own_word(kFull, v, nv, sh[k] != 0) ? ld16(base[k] + v) : zero;
+            c[u][k] = loads_next_word(kFull, v, nv, sh[k] != 0, last) ? ld16(base[k] + v + 1) : zero;
         }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t v = vec_index<U>(lt, u);
+        const int64_t v = vec_index<U>(lt, lane(), u);
         u32x4 x[K];
 #pragma unroll
         for (int k = 0; k < K; ++k)
-            x[k] = shifted_word(a[u][k], c[u][k], sh[k], wave_end);
+            x[k] = shifted_word(a[u][k], c[u][k], sh[k], last);
         if (kFull || v < nv)
             st16(out + v, fold_vec<BF16, K>(x, scale));
     }
@@ -307,18 +281,17 @@ template <bool BF16, int K>
 __device__ __forceinline__ void reduce_shifted(const RedSeg &sg, int64_t lt)
 {
     constexpr int64_t es = BF16 ? 2 : 4;
-    constexpr int64_t kTileVecs = int64_t(kBlock) * kShiftRedUnroll;
     const RedSplit sp = red_split(sg.out, sg.n, es);
     const u32x4 *base[K];
     unsigned sh[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const unsigned char *p = static_cast<const unsigned char *>(sg.in[k]) + sp.head * es;
-        sh[k] = (unsigned)(reinterpret_cast<uintptr_t>(p) & 15u);
-        base[k] = reinterpret_cast<const u32x4 *>(p - sh[k]);
+        const WordAt w = word_at(static_cast<const unsigned char *>(sg.in[k]) + sp.head * es);
+        sh[k] = w.shift;
+        base[k] = reinterpret_cast<const u32x4 *>(w.base);
     }
     u32x4 *out = reinterpret_cast<u32x4 *>(static_cast<unsigned char *>(sg.out) + sp.head * es);
-    if ((lt + 1) * kTileVecs <= sp.nv)
+    if (full_tile(lt, tile_vecs<kShiftRedUnroll>(), sp.nv))
         shifted_tile<BF16, K, true>(base, sh, out, lt, sp.nv, sg.scale);
     else if (sp.nv > 0)  // uniform across the workgroup
         shifted_tile<BF16, K, false>(base, sh, out, lt, sp.nv, sg.scale);
@@ -417,33 +390,32 @@ __global__ __launch_bounds__(kBlock) void reduce_one_kernel(const void *in0, con
 // each): the first wave's lanes the head, the second wave's the tail.
 __device__ __forceinline__ void copy_edges(const CopySeg &sg, const CopySplit &sp)
 {
-    const int x = (int)threadIdx.x;
-    if (x < sp.head) {
+    const int x = lane();
+    if (head_lane(x, sp.head)) {
         sg.dst[x] = sg.src[x];
-    } else if (x >= kWave && x - kWave < sp.tail) {
-        const int64_t i = sp.head + 16 * sp.nv + (x - kWave);
+    } else if (tail_lane(x, sp.tail)) {
+        const int64_t i = tail_elem(x, sp.head + 16 * sp.nv);
         sg.dst[i] = sg.src[i];
     }
 }
 
 __device__ __forceinline__ void copy_aligned(const CopySeg &sg, int64_t lt)
 {
-    constexpr int64_t kTileVecs = int64_t(kBlock) * kCopyUnroll;
     const CopySplit sp = copy_split(sg.dst, sg.nbytes);
     const int64_t nv = sp.nv;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(sg.src + sp.head);
     u32x4 *dst = reinterpret_cast<u32x4 *>(sg.dst + sp.head);
-    if ((lt + 1) * kTileVecs <= nv) {
+    if (full_tile(lt, tile_vecs<kCopyUnroll>(), nv)) {
         u32x4 x[kCopyUnroll];
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u)
-            x[u] = ld16(src + vec_index<kCopyUnroll>(lt, u));
+            x[u] = ld16(src + vec_index<kCopyUnroll>(lt, lane(), u));
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u)
-            st16(dst + vec_index<kCopyUnroll>(lt, u), x[u]);
+            st16(dst + vec_index<kCopyUnroll>(lt, lane(), u), x[u]);
     } else {
         for (int u = 0; u < kCopyUnroll; ++u) {
-            const int64_t v = vec_index<kCopyUnroll>(lt, u);
+            const int64_t v = vec_index<kCopyUnroll>(lt, lane(), u);
             if (v >= nv)
                 break;
             st16(dst + v, ld16(src + v));
@@ -466,40 +438,39 @@ __device__ __forceinline__ void copy_aligned(const CopySeg &sg, int64_t lt)
 template <int Q>
 __device__ __forceinline__ void copy_shifted(const CopySeg &sg, int64_t lt)
 {
-    constexpr int64_t kTileVecs = int64_t(kBlock) * kShiftUnroll;
     const CopySplit sp = copy_split(sg.dst, sg.nbytes);
     const int64_t nv = sp.nv;
     const unsigned r = (unsigned)(sg.shift & 3);
     const u32x4 *src = reinterpret_cast<const u32x4 *>(sg.src + sp.head - sg.shift);
     u32x4 *dst = reinterpret_cast<u32x4 *>(sg.dst + sp.head);
-    const bool wave_end = (threadIdx.x & (kWave - 1)) == kWave - 1;
+    const bool last = wave_end(lane());
     const u32x4 zero = {0u, 0u, 0u, 0u};
     u32x4 a[kShiftUnroll], c[kShiftUnroll];
-    if ((lt + 1) * kTileVecs <= nv) {
+    if (full_tile(lt, tile_vecs<kShiftUnroll>(), nv)) {
 #pragma unroll
         for (int u = 0; u < kShiftUnroll; ++u) {
-            const int64_t v = vec_index<kShiftUnroll>(lt, u);
-            a[u] = ld16(src + v);
-            c[u] = wave_end ? ld16(src + v + 1) : zero;
+            const int64_t v = vec_index<kShiftUnroll>(lt, lane(), u);
+            a[u] = loads_own_word(true, v, nv, true) ? ld16(src + v) : zero;
+            c[u] = loads_next_word(true, v, nv, true, last) ? ld16(src + v + 1) : zero;
         }
 #pragma unroll
         for (int u = 0; u < kShiftUnroll; ++u) {
             const u32x4 nb = next_lane(a[u]);  // on every lane: the source lane must be active
-            const u32x4 b = wave_end ? c[u] : nb;
-            st16(dst + vec_index<kShiftUnroll>(lt, u), realign<Q>(a[u], b, r));
+            const u32x4 b = last ? c[u] : nb;
+            st16(dst + vec_index<kShiftUnroll>(lt, lane(), u), realign<Q>(a[u], b, r));
         }
     } else if (nv > 0) {  // uniform across the workgroup
 #pragma unroll
         for (int u = 0; u < kShiftUnroll; ++u) {
-            const int64_t v = vec_index<kShiftUnroll>(lt, u);
-            a[u] = v <= nv ? ld16(src + v) : zero;
-            c[u] = wave_end && v < nv ? ld16(src + v + 1) : zero;
+            const int64_t v = vec_index<kShiftUnroll>(lt, lane(), u);
+            a[u] = loads_own_word(false, v, nv, true) ? ld16(src + v) : zero;
+            c[u] = loads_next_word(false, v, nv, true, last) ? ld16(src + v + 1) : zero;
         }
 #pragma unroll
         for (int u = 0; u < kShiftUnroll; ++u) {
-            const int64_t v = vec_index<kShiftUnroll>(lt, u);
+            const int64_t v = vec_index<kShiftUnroll>(lt, lane(), u);
             const u32x4 nb = next_lane(a[u]);
-            const u32x4 b = wave_end ? c[u] : nb;
+            const u32x4 b = last ? c[u] : nb;
             if (v < nv)
                 st16(dst + v, realign<Q>(a[u], b, r));
         }
@@ -562,16 +533,6 @@ __global__ __launch_bounds__(kBlock) void copy_mixed_uniform_kernel(CopyBatchT<C
 }
 
 }  // namespace
-
-int64_t red_tile_vecs(int32_t mode)
-{
-    return int64_t(kBlock) * (mode == kRedShifted ? kShiftRedUnroll : kUnroll);
-}
-
-int64_t copy_tile_vecs(int32_t mode)
-{
-    return int64_t(kBlock) * (mode == kCopyShifted ? kShiftUnroll : kCopyUnroll);
-}
 
 namespace {
 

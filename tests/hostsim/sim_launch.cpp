@@ -108,15 +108,6 @@ void copy_byte(const unsigned char *src, unsigned char *dst, int64_t i)
         dst[i] = src[i];
 }
 
-template <int MAXS>
-int find_seg(const int32_t (&tile0)[MAXS], int nseg, int32_t t)
-{
-    int s = 0;
-    for (int i = 1; i < MAXS; ++i)
-        s += (i < nseg && t >= tile0[i]) ? 1 : 0;
-    return s;
-}
-
 // The (segment, tile) pairs that the workgroups of a launch process, in the
 // launch form the library chose: the table form walks the batch's tiles, the
 // uniform form its (tile, segment) grid, the single-segment form segment 0.
@@ -144,26 +135,107 @@ std::vector<std::pair<int, int64_t>> tiles_of(const Batch &b, int64_t total, con
         if (sh.gx != total || sh.gy != 1)
             violation("table grid differs from the tile count", 0, sh.gx);
         for (int64_t t = 0; t < total; ++t) {
-            const int s = find_seg(b.tile0, b.nseg, int32_t(t));
+            const int s = rr::find_seg(b.tile0, b.nseg, int32_t(t));
             out.emplace_back(s, t - b.tile0[s]);
         }
     }
     return out;
 }
 
+// Tiles of segment s of a launch of `total` tiles.
+template <typename Batch>
+int64_t seg_tiles(const Batch &b, int s, int64_t total)
+{
+    return (s + 1 < b.nseg ? int64_t(b.tile0[s + 1]) : total) - b.tile0[s];
+}
+
+// Replay of tile lt of a reduction segment, lane by lane, with the kernels'
+// own index functions (rr_internal.h): which body vectors each lane folds,
+// which aligned input words it loads, and which edge elements tile 0's lanes
+// compute.  U is the segment mode's vectors per lane.
+template <int U>
+void replay_red_tile(const rr::RedBatch &b, int s, int64_t total, int64_t lt, const rr::RedSeg &sg, int64_t head,
+                     int64_t nv, int64_t tail, bool bf16)
+{
+    using namespace rr;
+    const int64_t es = bf16 ? 2 : 4, ve = 16 / es;
+    constexpr int64_t tv = tile_vecs<U>();
+    if (seg_tiles(b, s, total) != body_tiles(nv, tv))
+        violation("reduction segment tile count differs from its body", uintptr_t(sg.out), seg_tiles(b, s, total));
+    const bool shift_mode = sg.mode == kRedShifted;
+    const unsigned char *base[kMaxIn];
+    bool shifted[kMaxIn];
+    for (int k = 0; k < sg.k; ++k) {
+        const WordAt w = word_at(static_cast<const unsigned char *>(sg.in[k]) + head * es);
+        shifted[k] = shift_mode && w.shift != 0;
+        base[k] = shift_mode ? w.base : static_cast<const unsigned char *>(sg.in[k]) + head * es;
+    }
+    const bool full = full_tile(lt, tv, nv);
+    if (full || nv > 0)
+        for (int x = 0; x < kBlock; ++x)
+            for (int u = 0; u < U; ++u) {
+                const int64_t v = vec_index<U>(lt, x, u);
+                for (int k = 0; k < sg.k; ++k) {
+                    if (!shift_mode)
+                        continue;  // aligned inputs: the fold below checks every element read
+                    if (loads_own_word(full, v, nv, shifted[k]) && !touches(uintptr_t(base[k] + v * 16), 16))
+                        violation("realigned input word outside every buffer", uintptr_t(base[k] + v * 16), 16);
+                    if (loads_next_word(full, v, nv, shifted[k], wave_end(x)) &&
+                        !touches(uintptr_t(base[k] + (v + 1) * 16), 16))
+                        violation("realigned input word outside every buffer", uintptr_t(base[k] + (v + 1) * 16), 16);
+                }
+                if (full || v < nv)  // the lanes that store
+                    for (int64_t e = 0; e < ve; ++e)
+                        fold(sg, head + v * ve + e, bf16);
+            }
+    if (lt == 0)
+        for (int x = 0; x < kBlock; ++x) {
+            if (head_lane(x, head))
+                fold(sg, x, bf16);
+            else if (tail_lane(x, tail))
+                fold(sg, tail_elem(x, head + nv * ve), bf16);
+        }
+}
+
+// Replay of tile lt of a copy segment, lane by lane, with the kernels' own
+// index functions.
+template <int U>
+void replay_copy_tile(const rr::CopyBatch &b, int s, int64_t total, int64_t lt, const rr::CopySeg &sg,
+                      const rr::CopySplit &sp, bool shift_mode)
+{
+    using namespace rr;
+    constexpr int64_t tv = tile_vecs<U>();
+    const int64_t nv = sp.nv;
+    if (seg_tiles(b, s, total) != body_tiles(nv, tv))
+        violation("copy segment tile count differs from its body", uintptr_t(sg.dst), seg_tiles(b, s, total));
+    const unsigned char *base = sg.src + sp.head - (shift_mode ? sg.shift : 0);  // aligned words read
+    const bool full = full_tile(lt, tv, nv);
+    if (full || nv > 0)
+        for (int x = 0; x < kBlock; ++x)
+            for (int u = 0; u < U; ++u) {
+                const int64_t v = vec_index<U>(lt, x, u);
+                if (shift_mode) {
+                    if (loads_own_word(full, v, nv, true) && !touches(uintptr_t(base + v * 16), 16))
+                        violation("realigned word outside every buffer", uintptr_t(base + v * 16), 16);
+                    if (loads_next_word(full, v, nv, true, wave_end(x)) && !touches(uintptr_t(base + (v + 1) * 16), 16))
+                        violation("realigned word outside every buffer", uintptr_t(base + (v + 1) * 16), 16);
+                }
+                if (full || v < nv)
+                    for (int e = 0; e < 16; ++e)
+                        copy_byte(sg.src, sg.dst, sp.head + v * 16 + e);
+            }
+    if (lt == 0)
+        for (int x = 0; x < kBlock; ++x) {
+            if (head_lane(x, sp.head))
+                copy_byte(sg.src, sg.dst, x);
+            else if (tail_lane(x, sp.tail))
+                copy_byte(sg.src, sg.dst, tail_elem(x, sp.head + 16 * sp.nv));
+        }
+}
+
 }  // namespace
 
 namespace rr {
-
-int64_t red_tile_vecs(int32_t mode)
-{
-    return int64_t(kBlock) * (mode == kRedShifted ? kShiftRedUnroll : kUnroll);
-}
-
-int64_t copy_tile_vecs(int32_t mode)
-{
-    return int64_t(kBlock) * (mode == kCopyShifted ? kShiftUnroll : kCopyUnroll);
-}
 
 hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, bool shifted, hipStream_t)
 {
@@ -194,58 +266,17 @@ hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, bool shifted, h
             if (!aligned)
                 violation("unaligned pointer in an aligned reduction", o, sg.n);
         }
-        // the split, recomputed from its definition: head elements up to the
-        // output's 16-byte boundary, whole output vectors, tail elements
-        const int64_t head = std::min<int64_t>(sg.n, int64_t((16 - o % 16) % 16) / es);
-        const int64_t nv = (sg.n - head) / ve, tail = sg.n - head - nv * ve;
-        const int unroll = shift_mode ? kShiftRedUnroll : kUnroll;
-        const int64_t tv = int64_t(kBlock) * unroll;
-        const int s = st.first;
-        const int64_t seg_tiles = (s + 1 < b.nseg ? int64_t(b.tile0[s + 1]) : total_tiles) - b.tile0[s];
-        if (seg_tiles != std::max<int64_t>(1, (nv + tv - 1) / tv))
-            violation("reduction segment tile count differs from its body", o, seg_tiles);
-        // realigned inputs: the aligned words each lane reads
-        uintptr_t base[kMaxIn];
-        int64_t shift[kMaxIn];
-        for (int k = 0; k < sg.k; ++k) {
-            const uintptr_t p = uintptr_t(sg.in[k]) + uintptr_t(head * es);
-            shift[k] = shift_mode ? int64_t(p % 16) : 0;
-            base[k] = p - uintptr_t(shift[k]);
-        }
-        const bool full = (lt + 1) * tv <= nv;
-        if (full || nv > 0) {
-            for (int x = 0; x < kBlock; ++x)
-                for (int u = 0; u < unroll; ++u) {
-                    const int64_t v = lt * tv + x + int64_t(u) * kBlock;
-                    if (!full && v >= nv)
-                        break;
-                    const bool wave_end = x % 64 == 63;
-                    for (int k = 0; k < sg.k; ++k)
-                        if (shift[k] && (!touches(base[k] + uintptr_t(v * 16), 16) ||
-                                         (wave_end && !touches(base[k] + uintptr_t((v + 1) * 16), 16))))
-                            violation("realigned input word outside every buffer", base[k] + v * 16, 32);
-                    for (int64_t e = 0; e < ve; ++e)
-                        fold(sg, head + v * ve + e, bf16);
-                }
-            if (!full)
-                // a partial tile's lanes also load word nv for their left neighbour
-                for (int x = 0; x < kBlock; ++x)
-                    for (int u = 0; u < unroll; ++u) {
-                        const int64_t v = lt * tv + x + int64_t(u) * kBlock;
-                        for (int k = 0; k < sg.k; ++k)
-                            if (v == nv && shift[k] && !touches(base[k] + uintptr_t(v * 16), 16))
-                                violation("realigned input word outside every buffer", base[k] + v * 16, 16);
-                    }
-        }
-        if (lt == 0) {
-            // tile 0's first wave computes the head elements, its second wave the tail
-            if (head >= ve || tail >= ve)
-                violation("reduction head or tail of a whole vector or more", o, head + tail);
-            for (int64_t i = 0; i < head; ++i)
-                fold(sg, i, bf16);
-            for (int64_t i = 0; i < tail; ++i)
-                fold(sg, head + nv * ve + i, bf16);
-        }
+        const RedSplit sp = red_split(sg.out, sg.n, es);
+        const int64_t head = sp.head, nv = sp.nv, tail = sp.tail;
+        // the split against its definition: head elements up to the output's
+        // 16-byte boundary, whole output vectors, the remaining tail elements
+        if (head != std::min<int64_t>(sg.n, int64_t((16 - o % 16) % 16) / es) || head + nv * ve + tail != sg.n ||
+            tail < 0 || tail >= ve)
+            violation("reduction split differs from its definition", o, sg.n);
+        if (shift_mode)
+            replay_red_tile<kShiftRedUnroll>(b, st.first, total_tiles, lt, sg, head, nv, tail, bf16);
+        else
+            replay_red_tile<kUnroll>(b, st.first, total_tiles, lt, sg, head, nv, tail, bf16);
     }
     return hipSuccess;
 }
@@ -264,61 +295,25 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
             violation("realigned copy segment in the aligned-only kernel", uintptr_t(sg.dst), sg.mode);
         if (sg.mode != kCopyAligned && sg.mode != kCopyShifted)
             violation("unknown copy mode", uintptr_t(sg.dst), sg.mode);
-        // the move's split, recomputed from its definition: head bytes up to
-        // the destination's 16-byte boundary, whole 16-byte body vectors, tail
         const uintptr_t d = uintptr_t(sg.dst);
-        const int64_t head = std::min<int64_t>(sg.nbytes, int64_t((16 - d % 16) % 16));
-        const int64_t nv = (sg.nbytes - head) / 16, tail = sg.nbytes - head - 16 * nv;
-        const unsigned char *bsrc = sg.src + head;
+        const CopySplit sp = copy_split(sg.dst, sg.nbytes);
+        // the split against its definition: head bytes up to the destination's
+        // 16-byte boundary, whole 16-byte body vectors, the remaining tail
+        if (sp.head != std::min<int64_t>(sg.nbytes, int64_t((16 - d % 16) % 16)) ||
+            sp.head + 16 * sp.nv + sp.tail != sg.nbytes || sp.tail < 0 || sp.tail > 15)
+            violation("copy split differs from its definition", d, sg.nbytes);
+        const unsigned char *bsrc = sg.src + sp.head;
         const bool shift_mode = sg.mode == kCopyShifted;
-        if ((d + uintptr_t(head)) % 16 && nv > 0)
-            violation("copy body destination not 16-byte aligned", d, head);
-        if (!shift_mode && uintptr_t(bsrc) % 16 && nv > 0)
+        if ((d + uintptr_t(sp.head)) % 16 && sp.nv > 0)
+            violation("copy body destination not 16-byte aligned", d, sp.head);
+        if (!shift_mode && uintptr_t(bsrc) % 16 && sp.nv > 0)
             violation("aligned copy body with an unaligned source", uintptr_t(bsrc), 16);
         if (shift_mode && (sg.shift < 1 || sg.shift > 15 || int64_t(uintptr_t(bsrc) % 16) != sg.shift))
             violation("realigned copy with a wrong source shift", uintptr_t(bsrc), sg.shift);
-        const int unroll = shift_mode ? kShiftUnroll : kCopyUnroll;
-        const int64_t tv = int64_t(kBlock) * unroll;
-        const int s = st.first;
-        const int64_t seg_tiles = (s + 1 < b.nseg ? int64_t(b.tile0[s + 1]) : total_tiles) - b.tile0[s];
-        if (seg_tiles != std::max<int64_t>(1, (nv + tv - 1) / tv))
-            violation("copy segment tile count differs from its body", d, seg_tiles);
-        const unsigned char *base = bsrc - (shift_mode ? sg.shift : 0);  // aligned words read
-        const bool full = (lt + 1) * tv <= nv;
-        if (full || nv > 0)
-            for (int x = 0; x < kBlock; ++x)
-                for (int u = 0; u < unroll; ++u) {
-                    const int64_t v = lt * tv + x + int64_t(u) * kBlock;
-                    if (!full && v >= nv)
-                        break;
-                    if (shift_mode) {
-                        // each lane loads aligned word v whole; the wave's last lane
-                        // also loads word v+1 (the others take it from the next lane)
-                        const bool wave_end = x % 64 == 63;
-                        if (!touches(uintptr_t(base) + uintptr_t(v * 16), 16) ||
-                            (wave_end && !touches(uintptr_t(base) + uintptr_t((v + 1) * 16), 16)))
-                            violation("realigned word outside every buffer", uintptr_t(base) + v * 16, 32);
-                    }
-                    for (int e = 0; e < 16; ++e)
-                        copy_byte(sg.src, sg.dst, head + v * 16 + e);
-                }
-        if (shift_mode && !full && nv > 0)
-            // a partial tile's lanes also load word nv for their left neighbour
-            for (int x = 0; x < kBlock; ++x)
-                for (int u = 0; u < unroll; ++u) {
-                    const int64_t v = lt * tv + x + int64_t(u) * kBlock;
-                    if (v == nv && !touches(uintptr_t(base) + uintptr_t(v * 16), 16))
-                        violation("realigned word outside every buffer", uintptr_t(base) + v * 16, 16);
-                }
-        if (lt == 0) {
-            // tile 0's first wave copies the head bytes, its second wave the tail
-            if (head > 15 || tail > 15)
-                violation("copy head or tail longer than 15 bytes", d, head + tail);
-            for (int64_t i = 0; i < head; ++i)
-                copy_byte(sg.src, sg.dst, i);
-            for (int64_t i = 0; i < tail; ++i)
-                copy_byte(sg.src, sg.dst, head + 16 * nv + i);
-        }
+        if (shift_mode)
+            replay_copy_tile<kShiftUnroll>(b, st.first, total_tiles, lt, sg, sp, true);
+        else
+            replay_copy_tile<kCopyUnroll>(b, st.first, total_tiles, lt, sg, sp, false);
     }
     return hipSuccess;
 }

@@ -576,13 +576,21 @@ def test_reduction_beyond_2_31_elements(orc):
     4 GiB per input): 64-bit offsets and tile counts across one launch.
     Outputs are read back as windows by slicing (contiguous device-to-host
     copies); torch's advanced indexing into a tensor of more than 2^31
-    elements faulted on this software stack, so it is not used here."""
+    elements faulted on this software stack, so it is not used here.  The
+    output sits between two guard bands of eight 16 KiB tiles each inside one
+    sentinel-filled allocation, and both bands are read back (by slicing)
+    after the launch: nothing may be written before or past the output."""
     R = 2 ** 31 + 8 * 128 * 3 + 5
+    G = 65536
     say("beyond 2^31", R)
     a, b = _pattern(R, 3), _pattern(R, 7)
-    out = torch.empty(R, dtype=torch.bfloat16, device="cuda")
+    whole = torch.empty(R + 2 * G, dtype=torch.int16, device="cuda")
+    whole.fill_(SENTINEL)
+    out = whole[G:G + R].view(torch.bfloat16)
     rr.rr_active_add_scale(rr.Relay(2, 6, 8, 0, R), RS, BF16, AVG, 0, [a, b], out)
     torch.cuda.synchronize()
+    assert np.all(synth.to_host(whole[:G]) == SENTINEL), "write before the output"
+    assert np.all(synth.to_host(whole[G + R:]) == SENTINEL), "write past the output"
     rng = np.random.default_rng(5)
     starts = [0, 2 ** 31 - 4096, R - 4096] + sorted(int(v) for v in rng.integers(0, R - 2048, 32))
     for lo in starts:
@@ -591,7 +599,7 @@ def test_reduction_beyond_2_31_elements(orc):
         idx = np.arange(lo, hi, dtype=np.int64)
         ref = orc.rs2_active(BF16, AVG, _pattern_host(idx, 3), _pattern_host(idx, 7))
         check_bf16(got, ref, f"window [{lo}, {hi}) past 2^31")
-    del a, b, out
+    del a, b, out, whole
     torch.cuda.empty_cache()
 
 
