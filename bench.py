@@ -122,6 +122,17 @@ def parse():
     p.add_argument("--flush", choices=("read", "write", "none"), default="read",
                    help="how the sweep and calibration evict inputs from the caches before each rep")
     p.add_argument("--sweep-out", default=None)
+    p.add_argument("--role-fit", action="store_true",
+                   help="time every launch of the step alone at --fit-sizes messages (1x to 8x a 64 MiB "
+                        "message's bytes) and fit t = t0 + bytes/BW per role")
+    p.add_argument("--fit-sizes", default="16,32,64,128,256,512")
+    p.add_argument("--fit-reps", type=int, default=10)
+    p.add_argument("--fit-log", default=None,
+                   help="--role-fit: write the launch log (role, message, bytes of every relay launch in "
+                        "issue order) here, to match a rocprofv3 kernel trace of the same run")
+    p.add_argument("--fit-trace", default=None,
+                   help="with --fit-log: fit per role from this rocprofv3 kernel_trace.csv instead of "
+                        "running anything on the GPU; prints the table")
     return p.parse_args()
 
 
@@ -1081,13 +1092,184 @@ def step_sweep(args):
         torch.cuda.empty_cache()
 
 
+# --------------------------------------------------------------------------
+# per-role fixed cost and asymptotic bandwidth: t = t0 + bytes / BW
+# --------------------------------------------------------------------------
+
+RELAY_KERNEL = re.compile(r"rr::\(anonymous namespace\)::(reduce|copy)\w*kernel")
+
+
+def linear_fit(xs, ys):
+    """Least squares y = a + b*x; returns (a, b, r^2)."""
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    sxy = sum((x - mx) * (y - my) for x, y in zip(xs, ys))
+    b = sxy / sxx
+    a = my - b * mx
+    ss = sum((y - my) ** 2 for y in ys)
+    res = sum((y - a - b * x) ** 2 for x, y in zip(xs, ys))
+    return a, b, (1.0 - res / ss) if ss > 0 else 1.0
+
+
+def fit_table(samples, ref_mib=64.0):
+    """samples: {role: {message_mib: (bytes, [seconds...])}} -> rows of the
+    fit over every size, with the decomposition at ref_mib: the launch's
+    fraction of peak = (BW / peak) x (streaming time / (t0 + streaming time))."""
+    rows = []
+    for role, by in samples.items():
+        sizes = sorted(by)
+        xs = [by[m][0] for m in sizes]
+        ys = [statistics.median(by[m][1]) for m in sizes]
+        t0, inv_bw, r2 = linear_fit(xs, ys)
+        bw = 1.0 / inv_bw / 1e9 if inv_bw > 0 else float("inf")
+        row = {"role": role, "t0_us": round(t0 * 1e6, 3), "bw_gbs": round(bw, 1),
+               "bw_pct_of_peak": round(100 * bw / PEAK_GBS, 2), "r2": round(r2, 5),
+               "sizes_mib": sizes, "median_us": [round(y * 1e6, 3) for y in ys],
+               "bytes": xs, "pct_of_peak": [round(100 * x / y / 1e9 / PEAK_GBS, 2) for x, y in zip(xs, ys)]}
+        if ref_mib in by:
+            b, y = by[ref_mib][0], statistics.median(by[ref_mib][1])
+            stream_t = b * inv_bw
+            row["at_ref"] = {"message_mib": ref_mib, "bytes": b, "measured_us": round(y * 1e6, 3),
+                             "fit_us": round((t0 + stream_t) * 1e6, 3), "streaming_us": round(stream_t * 1e6, 3),
+                             "pct_of_peak": round(100 * b / y / 1e9 / PEAK_GBS, 2),
+                             "streaming_share": round(stream_t / (t0 + stream_t), 4)}
+        rows.append(row)
+    return rows
+
+
+def role_fit(args):
+    """Every launch of the step (one GPU's share, --variant) alone, at each
+    --fit-sizes message, --fit-reps times after 2 warm-ups, each rep after a
+    1 GiB read that clears the caches of its inputs, timed with a fence-free
+    HIP event pair (which adds about 1.2 us to a launch).  Also a one-tile
+    reduction launch (the smallest launch the library makes) for the fixed
+    cost of a kernel.  Prints the event-timed fit; --fit-log records every
+    relay launch in issue order so that a rocprofv3 kernel trace of this run
+    can be fitted on kernel durations alone (--fit-trace)."""
+    import ctypes
+    import torch
+    import pack_rr_helper_amd as rr
+    rr.load()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    hip = hip_runtime()
+    evs = []
+    for _ in range(2):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        evs.append(e)
+    f = ctypes.c_float()
+    evict = cache_evictor(torch, "read")
+    log, samples = [], {}
+
+    def run(role, mib, b, fn):
+        for rep in range(args.fit_reps + 2):
+            evict()
+            hip.hipEventRecord(evs[0], sp)
+            fn()
+            hip.hipEventRecord(evs[1], sp)
+            torch.cuda.synchronize()
+            hip.hipEventElapsedTime(ctypes.byref(f), evs[0], evs[1])
+            log.append({"role": role, "message_mib": mib, "bytes": b, "warmup": rep < 2})
+            if rep >= 2:
+                samples.setdefault(role, {}).setdefault(mib, (b, []))[1].append(f.value * 1e-3)
+
+    # the smallest launch: one tile of a two-input bf16 reduction (A=2 helper,
+    # count = 8 chunks of 128 elements)
+    tiny = [torch.randn(1024, device="cuda").to(torch.bfloat16) for _ in range(2)]
+    tiny_out = torch.empty(128, dtype=torch.bfloat16, device="cuda")
+    relay = rr.Relay(2, 6, 8, 0, 1024)
+    tiny_fn = rr.rr_helper_reduce(relay, rr.ALLREDUCE, rr.BF16, rr.SUM, 0, [t[:128] for t in tiny], tiny_out,
+                                  prepare=True)
+    run("one_tile", 0.0, 3 * 128 * 2, tiny_fn)
+    print(f"[fit] one-tile launch: {statistics.median(samples['one_tile'][0.0][1]) * 1e6:.2f} us (event pair)",
+          file=sys.stderr, flush=True)
+    for mib in [float(v) for v in args.fit_sizes.split(",")]:
+        M = int(mib * MIB)
+        inp = device_inputs(M, 2000 + int(mib * 16))
+        wls = build_rows(inp, mode=mode_of(args))
+        del inp
+        calls = [c for wl in wls.values() for c in wl.calls(stream)]
+        for row, _, b, fn in calls:
+            run(row, mib, b, fn)
+        print(f"[fit] {mib:g} MiB: " + ", ".join(
+            f"{row} {statistics.median(samples[row][mib][1]) * 1e6:.2f} us" for row, _, _, _ in calls),
+            file=sys.stderr, flush=True)
+        del wls, calls
+        torch.cuda.empty_cache()
+    for e in evs:
+        hip.hipEventDestroy(e)
+    if args.fit_log:
+        with open(args.fit_log, "w") as fh:
+            json.dump({"variant": mode_of(args), "launches": log}, fh)
+    by_role = {r: v for r, v in samples.items() if r != "one_tile"}
+    print(json.dumps({"role_fit": True, "timing": "fence-free HIP event pair per launch (adds ~1.2 us)",
+                      "variant": mode_of(args), "reps": args.fit_reps,
+                      "one_tile_us": round(statistics.median(samples["one_tile"][0.0][1]) * 1e6, 3),
+                      "roles": fit_table(by_role)}), flush=True)
+
+
+def fit_from_trace(args):
+    """Fit t = t0 + bytes/BW per role on the kernel durations of a rocprofv3
+    kernel trace (End - Start of each dispatch) of a --role-fit run, matched
+    launch by launch with that run's --fit-log; prints a markdown table."""
+    import csv
+    with open(args.fit_log) as fh:
+        log = json.load(fh)
+    with open(args.fit_trace) as fh:
+        rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Dispatch_Id"]))
+    relay = [r for r in rows if RELAY_KERNEL.search(r["Kernel_Name"])]
+    launches = log["launches"]
+    if len(relay) != len(launches):
+        raise SystemExit(f"trace holds {len(relay)} relay dispatches, the log {len(launches)} launches")
+    samples, kernels = {}, {}
+    for r, l in zip(relay, launches):
+        if l["warmup"]:
+            continue
+        t = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        samples.setdefault(l["role"], {}).setdefault(l["message_mib"], (l["bytes"], []))[1].append(t)
+        kernels.setdefault(l["role"], set()).add(re.sub(r"^void rr::\(anonymous namespace\)::", "",
+                                                        r["Kernel_Name"]).split("(")[0])
+    tiny = samples.pop("one_tile", {})
+    fit = fit_table(samples)
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as fh:
+            json.dump({"variant": log["variant"], "one_tile_us": round(statistics.median(tiny[0.0][1]) * 1e6, 3)
+                       if tiny else None, "roles": fit}, fh)
+    print(f"one-tile reduction launch (kernel duration, median): "
+          f"{statistics.median(tiny[0.0][1]) * 1e6:.2f} us\n" if tiny else "")
+    print("| role | kernel | t0 us | BW GB/s | BW % of peak | r^2 | " +
+          " | ".join(f"{m:g} MiB us (% peak)" for m in fit[0]["sizes_mib"]) + " |")
+    print("|---|---|---:|---:|---:|---:|" + "---:|" * len(fit[0]["sizes_mib"]))
+    for row in fit:
+        print(f"| {row['role']} | {', '.join(sorted(kernels[row['role']]))} | {row['t0_us']:.2f} | "
+              f"{row['bw_gbs']:.0f} | {row['bw_pct_of_peak']:.1f} | {row['r2']:.4f} | " +
+              " | ".join(f"{u:.2f} ({p:.1f})" for u, p in zip(row["median_us"], row["pct_of_peak"])) + " |")
+    print()
+    print("| role at 64 MiB | bytes | measured us | t0 us | bytes/BW us | % of peak | = BW % of peak | x streaming share |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|")
+    for row in fit:
+        a = row.get("at_ref")
+        if a:
+            print(f"| {row['role']} | {a['bytes']} | {a['measured_us']:.2f} | {row['t0_us']:.2f} | "
+                  f"{a['streaming_us']:.2f} | {a['pct_of_peak']:.1f} | {row['bw_pct_of_peak']:.1f} | "
+                  f"{a['streaming_share']:.3f} |")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (--gpus {args.gpus} "
               "requested). The relay's local kernels shard per rank; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    if args.step_sweep:
+    if args.fit_trace:
+        fit_from_trace(args)
+    elif args.role_fit:
+        role_fit(args)
+    elif args.step_sweep:
         step_sweep(args)
     elif args.sweep:
         sweep(args)
