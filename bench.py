@@ -1097,6 +1097,7 @@ def step_sweep(args):
 # --------------------------------------------------------------------------
 
 RELAY_KERNEL = re.compile(r"rr::\(anonymous namespace\)::(reduce|copy)\w*kernel")
+EVICT_KERNEL = re.compile(r"at::native::.*reduce_kernel")  # cache_evictor("read"): torch.sum
 
 
 def linear_fit(xs, ys):
@@ -1221,10 +1222,13 @@ def fit_from_trace(args):
         log = json.load(fh)
     with open(args.fit_trace) as fh:
         rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Dispatch_Id"]))
-    relay = [r for r in rows if RELAY_KERNEL.search(r["Kernel_Name"])]
+    # every timed launch directly follows the cache-clearing read (a torch sum);
+    # relay launches made while a workload stages its inputs do not
+    relay = [r for prev, r in zip(rows, rows[1:]) if RELAY_KERNEL.search(r["Kernel_Name"])
+             and EVICT_KERNEL.search(prev["Kernel_Name"])]
     launches = log["launches"]
     if len(relay) != len(launches):
-        raise SystemExit(f"trace holds {len(relay)} relay dispatches, the log {len(launches)} launches")
+        raise SystemExit(f"trace holds {len(relay)} timed relay dispatches, the log {len(launches)} launches")
     samples, kernels = {}, {}
     for r, l in zip(relay, launches):
         if l["warmup"]:
