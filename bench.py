@@ -97,6 +97,16 @@ def parse():
     p.add_argument("--buffer-sets", type=int, default=3,
                    help="independent copies of every buffer, used by consecutive steps in turn "
                         "(3: no step finds its data left in a cache by the previous steps)")
+    p.add_argument("--sizes", default="256,1024",
+                   help="also time the step at these messages (MiB), share and group, each with its own "
+                        "roofline block under 'sizes'; '' for none")
+    p.add_argument("--device-inputs", action="store_true",
+                   help="draw the step's inputs on the device (timing only) instead of seeded host arrays")
+    p.add_argument("--traffic-from", default=None,
+                   help="FETCH_CSV,WRITE_CSV: rocprofv3 --pmc passes of a --calibrate-copy-mib run; with "
+                        "--traffic-bench, record that run's HBM bytes per launch in profiles/traffic.json")
+    p.add_argument("--traffic-bench", default=None,
+                   help="the JSON line bench.py printed in the FETCH_SIZE pass of --traffic-from")
     p.add_argument("--no-other-variants", action="store_true",
                    help="skip timing the other variants and the plain-stream stand-in step")
     p.add_argument("--calibrate-copy-mib", type=float, default=0.0,
@@ -161,16 +171,22 @@ def host_inputs(M, dtype="bf16", rows=("ar2", "rs2", "ar4", "rs4", "a2a")):
     return {r: make[r]() for r in rows}
 
 
-def device_inputs(M, seed):
+def device_inputs(M, seed, dtype="bf16"):
     """Seeded inputs of every row at message M drawn on the device, for timing
     only (the kernels' work does not depend on the values): N(0,1) rounded to
-    bf16, raw 16-bit patterns for the all-to-all."""
+    the dtype, raw 16- or 32-bit patterns for the all-to-all."""
     import torch
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
-    n = M // 2
-    normal = lambda: torch.randn(n, device="cuda", generator=g).to(torch.bfloat16)
-    bits = lambda: torch.randint(-32768, 32768, (n,), dtype=torch.int16, device="cuda", generator=g)
+    f32 = dtype == "f32"
+    n = M // (4 if f32 else 2)
+    tdt = torch.float32 if f32 else torch.bfloat16
+    normal = lambda: torch.randn(n, device="cuda", generator=g).to(tdt)
+    if f32:
+        bits = lambda: torch.randint(-2 ** 31, 2 ** 31 - 1, (n,), dtype=torch.int32, device="cuda",
+                                     generator=g).view(torch.float32)
+    else:
+        bits = lambda: torch.randint(-32768, 32768, (n,), dtype=torch.int16, device="cuda", generator=g)
     return {"ar2": [normal() for _ in range(2)], "rs2": [normal() for _ in range(2)],
             "ar4": [normal() for _ in range(4)], "rs4": [normal() for _ in range(4)],
             "a2a": [bits() for _ in range(4)]}
@@ -450,25 +466,128 @@ def kernel_source_digest():
     return code_digest(texts)
 
 
-def traffic_for(kernel, message_mib, variant, algo_bytes_per_launch, launches_per_step):
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def traffic_for(kernel, message_mib, variant, algo_bytes_per_launch, launches_per_step, dtype="bf16",
+                path=TRAFFIC_JSON):
     """HBM bytes per launch of `kernel` (counter-measured, scaled by a plain
     copy of known size) from profiles/traffic.json, or None if absent, taken
-    on another workload or launch sequence (other launches per step, or other
-    algorithmic bytes per launch), or taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    on another workload or launch sequence (other message, variant or dtype,
+    other launches per step, or other algorithmic bytes per launch), or taken
+    on other kernel sources."""
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         t = json.load(fh)
     if t.get("kernel_source_digest") != kernel_source_digest():
         return None
-    if t.get("message_mib") != message_mib or t.get("variant") != variant:
+    for e in t.get("entries", []):
+        if e.get("message_mib") != message_mib or e.get("variant") != variant or e.get("dtype") != dtype:
+            continue
+        k = e.get("kernels", {}).get(kernel)
+        if not k or k.get("algorithmic_bytes_per_launch") != algo_bytes_per_launch \
+                or k.get("launches_per_step") != launches_per_step:
+            return None
+        return k.get("hbm_bytes_per_launch")
+    return None
+
+
+def counter_rows(path, counter):
+    """(kernel name, value) per dispatch of a rocprofv3 --pmc CSV, in dispatch order."""
+    import csv
+    with open(path) as fh:
+        rows = [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows]
+
+
+def kernel_family(name):
+    """The roofline family of a relay kernel symbol: reduce<bf16>, reduce<f32> or copy."""
+    m = RELAY_KERNEL.search(name)
+    if not m:
         return None
-    k = t.get("kernels", {}).get(kernel)
-    if not k or k.get("algorithmic_bytes_per_launch") != algo_bytes_per_launch \
-            or k.get("launches_per_step") != launches_per_step:
-        return None
-    return k.get("hbm_bytes_per_launch")
+    if m.group(1) == "copy":
+        return "copy"
+    return "reduce<bf16>" if "<true" in name else "reduce<f32>"
+
+
+def traffic_from(args):
+    """HBM bytes per launch of one step from two rocprofv3 --pmc passes
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of a bench.py run with
+    --calibrate-copy-mib C: the counters are scaled so that the run's plain
+    C MiB device copy reads as C MiB fetched and C MiB written; the last
+    (warmup + 2 x steps) steps of relay dispatches are the timed ones, and
+    each launch of the step is averaged over them.  Records the entry in
+    profiles/traffic.json (replacing one of the same message, variant and
+    dtype) and prints a markdown table."""
+    fetch_csv, write_csv = args.traffic_from.split(",")
+    with open(args.traffic_bench) as fh:
+        run = json.loads(fh.read().strip().splitlines()[-1])
+    cfg = run["config"]
+    order = cfg["launch_order"]
+    L = len(order)
+    nsteps = run["warmup"] + 2 * run["steps"]
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = counter_rows(path, counter)
+        relay_at = [i for i, (n, _) in enumerate(rows) if RELAY_KERNEL.search(n)]
+        timed = relay_at[-nsteps * L:]
+        if len(timed) != nsteps * L:
+            raise SystemExit(f"{path}: {len(relay_at)} relay dispatches, fewer than {nsteps} steps of {L}")
+        copies = [v for n, v in rows[:timed[0]] if "copyBuffer" in n][-3:]
+        expect_kib = args.calibrate_copy_mib * 1024.0
+        scale = expect_kib / statistics.median(copies)
+        per = []
+        for j in range(L):
+            vals = [rows[timed[s * L + j]] for s in range(nsteps)]
+            if len({n for n, _ in vals}) != 1:
+                raise SystemExit(f"launch {j} of the step runs different kernels across steps")
+            per.append((vals[0][0], statistics.mean(v for _, v in vals)))
+        out[counter] = (scale, per)
+    fscale, fper = out["FETCH_SIZE"]
+    wscale, wper = out["WRITE_SIZE"]
+    algo = cfg["rows_bytes_per_launch"]
+    launches, fam = [], {}
+    for j, row in enumerate(order):
+        name = fper[j][0]
+        hbm = (fper[j][1] * fscale + wper[j][1] * wscale) * 1024.0
+        launches.append({"row": row, "kernel": re.sub(r"^void rr::\(anonymous namespace\)::", "", name).split("(")[0],
+                         "fetch_kib": round(fper[j][1], 1), "write_kib": round(wper[j][1], 1),
+                         "hbm_bytes": round(hbm), "algorithmic_bytes": algo[row],
+                         "ratio": round(hbm / algo[row], 4)})
+        f = fam.setdefault(kernel_family(name), [0.0, 0, 0])
+        f[0] += hbm
+        f[1] += algo[row]
+        f[2] += 1
+    entry = {"message_mib": run["config"]["message_bytes"] / MIB, "variant": cfg["variant"], "dtype": run["dtype"],
+             "fetch_scale": fscale, "write_scale": wscale,
+             "kernels": {k: {"hbm_bytes_per_launch": round(v[0] / v[2]), "algorithmic_bytes_per_launch": v[1] // v[2],
+                             "launches_per_step": v[2]} for k, v in fam.items()},
+             "launches": launches}
+    t = {"kernel_source_digest": kernel_source_digest(), "entries": []}
+    if os.path.exists(TRAFFIC_JSON):
+        with open(TRAFFIC_JSON) as fh:
+            old = json.load(fh)
+        if old.get("kernel_source_digest") == t["kernel_source_digest"]:
+            t["entries"] = [e for e in old.get("entries", []) if (e["message_mib"], e["variant"], e["dtype"]) !=
+                            (entry["message_mib"], entry["variant"], entry["dtype"])]
+    t["entries"].append(entry)
+    t["entries"].sort(key=lambda e: (e["dtype"], e["variant"], e["message_mib"]))
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(t, fh, indent=1)
+        fh.write("\n")
+    print(f"scale: fetch x{fscale:.4f}, write x{wscale:.4f} (plain {args.calibrate_copy_mib:g} MiB copy)\n")
+    print("| launch | kernel | FETCH KiB | WRITE KiB | HBM bytes (scaled) | algorithmic bytes | ratio |")
+    print("|---|---|---:|---:|---:|---:|---:|")
+    for l in launches:
+        print(f"| {l['row']} | `{l['kernel']}` | {l['fetch_kib']} | {l['write_kib']} | {l['hbm_bytes']} | "
+              f"{l['algorithmic_bytes']} | {l['ratio']:.4f} |")
+    print("\n| kernel | launches | HBM bytes/launch | algorithmic bytes/launch | ratio |")
+    print("|---|---:|---:|---:|---:|")
+    for k, v in entry["kernels"].items():
+        print(f"| `{k}` | {v['launches_per_step']} | {v['hbm_bytes_per_launch']} | {v['algorithmic_bytes_per_launch']} | "
+              f"{v['hbm_bytes_per_launch'] / v['algorithmic_bytes_per_launch']:.4f} |")
 
 
 # --------------------------------------------------------------------------
@@ -513,15 +632,148 @@ def time_variant(inp, mode, steps, warmup, stream, buffer_sets, dtype="bf16"):
             "variant_means": VARIANTS[mode]}
 
 
-def step_bench(args):
+def time_launches(step_fns, calls, steps, warmup, stream):
+    """The step timed twice: region 1 runs K steps with nothing between the
+    launches (ms per step); region 2 runs K more with one timing-only HIP event
+    (no system-scope fence) between consecutive launches on the kernels'
+    stream, so launch i lasts from event i to event i+1.  An event between two
+    launches delays the second one, so an interval is a launch plus the
+    events' own cost; that cost per launch is region 2's step time less region
+    1's, spread over the step's launches, and is subtracted from every
+    interval.  step_fns(i) gives step i's launches; calls the (row, kernel,
+    bytes, fn) of one step."""
     import ctypes
+    import torch
+    for i in range(warmup):
+        for fn in step_fns(i):
+            fn()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        for fn in step_fns(i):
+            fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / steps
+
+    hip = hip_runtime()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    evs = []
+    for _ in range(steps * len(calls) + 1):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        evs.append(e)
+    i = 0
+    hip.hipEventRecord(evs[0], sp)
+    for step in range(steps):
+        for fn in step_fns(step):
+            fn()
+            i += 1
+            hip.hipEventRecord(evs[i], sp)
+    torch.cuda.synchronize()
+    per_row, per_kernel = {}, {}
+    f = ctypes.c_float()
+    i = 0
+    for _ in range(steps):
+        for row, kern, b, _ in calls:
+            hip.hipEventElapsedTime(ctypes.byref(f), evs[i], evs[i + 1])
+            i += 1
+            for key, table in ((row, per_row), (kern, per_kernel)):
+                r = table.setdefault(key, [0.0, 0, 0])
+                r[0] += f.value
+                r[1] += b
+                r[2] += 1
+    for e in evs:
+        hip.hipEventDestroy(e)
+    events_ms_step = sum(r[0] for r in per_row.values()) / steps
+    event_cost_ms = max(0.0, events_ms_step - ms_step) / len(calls)
+    return {"ms_step": ms_step, "wall_s": wall, "per_row": per_row, "per_kernel": per_kernel,
+            "event_cost_ms": event_cost_ms}
+
+
+def launch_ms(t, ms, n):
+    """Average launch duration (ms) of n launches whose event intervals sum to ms."""
+    return ms / n - t["event_cost_ms"]
+
+
+def roofline_of(t, steps, message_mib, variant, dtype):
+    """The roofline block for the kernel family with the largest share of the
+    step's time: algorithmic bytes per launch / average launch duration."""
+    per_kernel = t["per_kernel"]
+    dom = max(per_kernel, key=lambda k: per_kernel[k][0])
+    d_ms, d_b, d_n = per_kernel[dom]
+    dur = launch_ms(t, d_ms, d_n)
+    achieved = (d_b / d_n) / (dur * 1e-3) / 1e9
+    return {
+        "kernel": dom,
+        "kernel_symbols": KERNEL_FORMS.get(dom, dom),
+        "timing": ("timing-only HIP events between consecutive launches on the kernels' stream "
+                   "(second timed region), less the events' own cost per launch: (second region's "
+                   "step time - event-free first region's) / launches per step"),
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / PEAK_GBS, 4),
+        "traffic": traffic_for(dom, message_mib, variant, d_b // d_n, d_n // steps, dtype),
+        "algorithmic_bytes_per_launch": d_b // d_n,
+        "avg_launch_us": round(1e3 * dur, 3),
+        "avg_event_interval_us": round(1e3 * d_ms / d_n, 3),
+        "event_cost_us_per_launch": round(1e3 * t["event_cost_ms"], 3),
+        "launches": d_n,
+    }
+
+
+def rows_of(t):
+    per_row = t["per_row"]
+    return {
+        "rows_gbs": {row: round(b / n / (launch_ms(t, ms, n) * 1e-3) / 1e9, 1) for row, (ms, b, n) in per_row.items()},
+        "rows_us_per_launch": {row: round(1e3 * launch_ms(t, ms, n), 2) for row, (ms, b, n) in per_row.items()},
+        "rows_bytes_per_launch": {row: b // n for row, (ms, b, n) in per_row.items()},
+    }
+
+
+def size_block(mib, variant, steps, warmup, stream, dtype):
+    """The step at another message size, inputs drawn on the device (the
+    kernels' work does not depend on the values): three buffer sets in turn
+    while a step moves under 2 GB, one above (a step then streams many times
+    the 256 MB Infinity Cache); fewer steps for steps over 4 GB."""
+    import torch
+    M = int(mib * MIB)
+    inp = device_inputs(M, 3000 + int(mib * 16), dtype)
+    first = build_rows(inp, mode=variant, dtype=dtype)
+    calls = [c for wl in first.values() for c in wl.calls(stream)]
+    step_bytes = sum(c[2] for c in calls)
+    nsets = 3 if step_bytes < 2e9 else 1
+    sets = [first] + [build_rows(inp, mode=variant, dtype=dtype) for _ in range(nsets - 1)]
+    del inp
+    set_calls = [calls] + [[c for wl in wls.values() for c in wl.calls(stream)] for wls in sets[1:]]
+    k = steps if step_bytes < 4e9 else max(10, steps // 5)
+    t = time_launches(lambda i: [c[3] for c in set_calls[i % nsets]], calls, k, warmup, stream)
+    value = step_bytes / (t["ms_step"] * 1e-3) / 1e9
+    out = {"message_mib": mib, "variant": variant, "value": round(value, 1), "unit": "GB/s",
+           "pct_of_peak": round(100.0 * value / PEAK_GBS, 2), "ms_per_step": round(t["ms_step"], 5),
+           "steps": k, "warmup": warmup, "buffer_sets": nsets, "launches_per_step": len(calls),
+           "algorithmic_bytes_per_step": step_bytes, "inputs": "drawn on the device (seeded), timing only",
+           **rows_of(t), "roofline": roofline_of(t, k, mib, variant, dtype)}
+    del sets, set_calls, calls, first
+    torch.cuda.empty_cache()
+    return out
+
+
+def step_bench(args):
     import torch
     import pack_rr_helper_amd as rr
     rr.load()
     torch.cuda.set_device(0)
     M = int(args.message_mib * MIB)
     print(f"[bench] generating inputs, M={args.message_mib} MiB", file=sys.stderr, flush=True)
-    inp = host_inputs(M, args.dtype)
+    inp = device_inputs(M, 1000 + int(args.message_mib * 16), args.dtype) if args.device_inputs \
+        else host_inputs(M, args.dtype)
     # --buffer-sets N: N independent copies of every buffer, used by
     # consecutive steps in turn, so that no step finds its data in a cache
     # left warm by the previous one
@@ -545,76 +797,12 @@ def step_bench(args):
         torch.cuda.synchronize()
         del a, b
 
-    print(f"[bench] warmup {args.warmup} steps, {len(calls)} launches per step", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        for fn in step_fns(i):
-            fn()
-    torch.cuda.synchronize()
-
-    # Timed region 1 -- the value: K whole steps, nothing between launches.
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    for i in range(args.steps):
-        for fn in step_fns(i):
-            fn()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t0.elapsed_time(t1) / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)", file=sys.stderr,
+    print(f"[bench] warmup {args.warmup} steps, then 2 x {args.steps} timed steps, {len(calls)} launches per step",
+          file=sys.stderr, flush=True)
+    t = time_launches(step_fns, calls, args.steps, args.warmup, stream)
+    ms_step = t["ms_step"]
+    print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step (wall {t['wall_s']:.3f} s)", file=sys.stderr,
           flush=True)
-
-    # Timed region 2 -- per launch: K more steps with one timing-only HIP event
-    # (no system-scope fence) between consecutive launches on the stream the
-    # kernels run on; launch i lasts from event i to event i+1.
-    hip = hip_runtime()
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    nev = args.steps * len(calls) + 1
-    evs = []
-    for _ in range(nev):
-        e = ctypes.c_void_p()
-        if hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
-            raise RuntimeError("hipEventCreateWithFlags failed")
-        evs.append(e)
-    i = 0
-    hip.hipEventRecord(evs[0], sp)
-    for step in range(args.steps):
-        for fn in step_fns(step):
-            fn()
-            i += 1
-            hip.hipEventRecord(evs[i], sp)
-    torch.cuda.synchronize()
-    per_row, per_kernel = {}, {}
-    f = ctypes.c_float()
-    i = 0
-    for _ in range(args.steps):
-        for row, kern, b, _ in calls:
-            hip.hipEventElapsedTime(ctypes.byref(f), evs[i], evs[i + 1])
-            ms = f.value
-            i += 1
-            for key, table in ((row, per_row), (kern, per_kernel)):
-                r = table.setdefault(key, [0.0, 0, 0])
-                r[0] += ms
-                r[1] += b
-                r[2] += 1
-    for e in evs:
-        hip.hipEventDestroy(e)
-    # An event between two launches delays the second one (the event is
-    # processed after the first kernel ends, the next dispatch after it), so
-    # an interval is a launch plus the events' own cost.  That cost per launch
-    # is the second region's step time minus the event-free first region's,
-    # spread over the step's launches; it is subtracted from every interval.
-    events_ms_step = sum(r[0] for r in per_row.values()) / args.steps
-    event_cost_ms = max(0.0, events_ms_step - ms_step) / len(calls)
-    def launch_ms(ms, n):
-        return ms / n - event_cost_ms
-    dom = max(per_kernel, key=lambda k: per_kernel[k][0])
-    d_ms, d_b, d_n = per_kernel[dom]
-    achieved = (d_b / d_n) / (launch_ms(d_ms, d_n) * 1e-3) / 1e9
-    traffic = traffic_for(dom, args.message_mib, args.variant, d_b // d_n, d_n // args.steps)
-
     value = step_bytes / (ms_step * 1e-3) / 1e9
     result = {
         "metric": METRIC,
@@ -640,31 +828,13 @@ def step_bench(args):
             "launches_per_step": len(calls),
             "algorithmic_bytes_per_step": step_bytes,
             "buffer_sets": args.buffer_sets,
+            "inputs": ("drawn on the device (seeded), timing only" if args.device_inputs else
+                       "seeded host arrays (pack_rr_helper_amd.synth), uploaded before timing"),
             "timed_region_1": "K steps, no events between launches (value, ms_per_step)",
-            "rows_gbs": {row: round(b / n / (launch_ms(ms, n) * 1e-3) / 1e9, 1)
-                         for row, (ms, b, n) in per_row.items()},
-            "rows_us_per_launch": {row: round(1e3 * launch_ms(ms, n), 2) for row, (ms, b, n) in per_row.items()},
-            "rows_bytes_per_launch": {row: b // n for row, (ms, b, n) in per_row.items()},
+            **rows_of(t),
             "launch_order": [row for row, _, _, _ in calls],
         },
-        "roofline": {
-            "kernel": dom,
-            "kernel_symbols": KERNEL_FORMS.get(dom, dom),
-            "timing": ("timing-only HIP events between consecutive launches on the kernels' stream "
-                       "(second timed region), less the events' own cost per launch: (second region's "
-                       "step time - event-free first region's) / launches per step"),
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / PEAK_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": d_b // d_n,
-            "avg_launch_us": round(1e3 * launch_ms(d_ms, d_n), 3),
-            "avg_event_interval_us": round(1e3 * d_ms / d_n, 3),
-            "event_cost_us_per_launch": round(1e3 * event_cost_ms, 3),
-            "launches": d_n,
-        },
+        "roofline": roofline_of(t, args.steps, args.message_mib, args.variant, args.dtype),
         "cpu_baseline": None,
     }
     if not args.no_other_variants:
@@ -679,18 +849,26 @@ def step_bench(args):
     if not args.no_other_variants:
         # the same launch sequence as plain stream kernels of each launch's
         # read/write mix and bytes (bench_calib.hip), timed like timed region 1
-        print("[bench] timing the plain-stream stand-in step", file=sys.stderr, flush=True)
-        st_sets, _, st_bytes = stand_in_step(calls, args.buffer_sets, stream)
-        st_ms = time_steps(lambda i: st_sets[i % len(st_sets)], args.steps, args.warmup, stream)
-        st_gbs = st_bytes / (st_ms * 1e-3) / 1e9
+        print("[bench] timing the plain-stream stand-in steps", file=sys.stderr, flush=True)
         result["stand_in_step"] = {
             "what": ("the same launch sequence with every launch replaced by a plain stream kernel "
-                     "(bench_calib.hip) of its read/write mix and bytes, timed like timed region 1"),
-            "value": round(st_gbs, 1), "unit": "GB/s", "pct_of_peak": round(100.0 * st_gbs / PEAK_GBS, 2),
-            "ms_per_step": round(st_ms, 5), "relay_over_stand_in": round(value / st_gbs, 4)}
-        del st_sets
+                     "(bench_calib.hip) of its read/write mix and bytes, in each of the calibration's access "
+                     "patterns and with the fastest pattern per launch, timed like timed region 1; "
+                     "relay_over_stand_in compares with the fastest of them"),
+            "unit": "GB/s",
+            **stand_in_ceiling(calls, args.buffer_sets, stream, args.steps, args.warmup, value)}
+    if args.sizes:
+        # the same step at the larger messages of the configurations (the A=4
+        # allreduce's 256 MiB, the all-to-all's 1 GiB), one GPU's share and
+        # the whole group, each with its own roofline block
+        del sets, set_calls, calls
         torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
+        result["sizes"] = []
+        for mib in [float(v) for v in args.sizes.split(",")]:
+            for variant in ("share", "group"):
+                print(f"[bench] {mib:g} MiB message, {variant} variant", file=sys.stderr, flush=True)
+                result["sizes"].append(size_block(mib, variant, args.steps, args.warmup, stream, args.dtype))
+    if not args.no_cpu_baseline and not args.device_inputs:
         print(f"[bench] timing the CPU oracle on the step's jobs: one thread, then {host_threads()} threads",
               file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, F32_CODE if args.dtype == "f32" else BF16_CODE, args.variant,
@@ -819,15 +997,19 @@ def sweep(args):
                     role_call = next(c for c in calls if c[0] == role)
                     name = role + suffix
                     rec = record(mib, dt_name, name, role_call[1], role_call[2], times_of(role_call[3]))
-                    # the plain stream of this launch's read/write mix and bytes, timed alike
-                    st_sets, st_launch, st_bytes = stand_in_step([role_call], 1, stream)
-                    st_ts = times_of(st_sets[0][0])
-                    st_gbs = st_bytes / statistics.median(st_ts) / 1e9
+                    # plain streams of this launch's read/write mix and bytes in every
+                    # access pattern of the calibration, timed alike; the fastest is
+                    # the ceiling the row is compared with
+                    pats = {}
+                    for pi, pname in enumerate(CALIB_PATTERNS):
+                        st_sets, st_launch, st_bytes = stand_in_step([role_call], 1, stream, pi)
+                        pats[pname] = round(st_bytes / statistics.median(times_of(st_sets[0][0])) / 1e9, 1)
+                        del st_sets
+                    top = max(pats, key=pats.get)
                     rec["stand_in"] = {"reads": st_launch[0][1], "writes": st_launch[0][2], "bytes": st_bytes,
-                                       "gbs_median": round(st_gbs, 1),
-                                       "gbs_best": round(st_bytes / min(st_ts) / 1e9, 1),
-                                       "relay_over_stand_in": round(rec["gbs_median"] / st_gbs, 3)}
-                    del st_sets
+                                       "gbs_median": pats[top], "pattern": top, "patterns": pats,
+                                       "relay_over_stand_in": round(rec["gbs_median"] / pats[top], 3),
+                                       "relay_over_relay_pattern": round(rec["gbs_median"] / pats["relay"], 3)}
                     # a realigned view changes where the data sits, not the oracle's work
                     oname = name if name in orates else role
                     if oname in orates:
@@ -853,13 +1035,19 @@ def sweep(args):
 # --------------------------------------------------------------------------
 
 CALIB_MIXES = [(1, 0), (2, 0), (4, 0), (0, 1), (1, 1), (2, 1), (3, 1), (4, 1), (2, 2)]
+# bench_calib.hip's access patterns, by index: the relay kernels' own (16 KiB
+# tiles, one per workgroup, non-temporal), smaller tiles, several tiles per
+# workgroup with the next tile's loads before the current stores, a persistent
+# double-buffered grid, and write-back stores
+CALIB_PATTERNS = ["relay", "tile8k", "tile4k", "multi2", "multi4", "persistent", "persist_wb", "relay_wb"]
 
 
 def calibrate(args):
-    """R reads + W writes per element with the relay kernels' access pattern
-    (bench_calib.hip), each mix timed alone with a fence-free HIP event pair
-    after the caches are cleared of its inputs (--flush); best and median of
-    the reps."""
+    """R reads + W writes per element (bench_calib.hip) in every access
+    pattern of CALIB_PATTERNS, each mix timed alone with a fence-free HIP
+    event pair after the caches are cleared of its inputs (--flush); best and
+    median of the reps per pattern, then one line per (size, mix) naming the
+    fastest pattern by median: the ceiling for that mix."""
     import ctypes
     import torch
     lib = _calib_lib()
@@ -867,15 +1055,7 @@ def calibrate(args):
     vp = ctypes.c_void_p
     stream = torch.cuda.current_stream()
     sp = vp(stream.cuda_stream)
-    hip = hip_runtime()
-    evs = []
-    for _ in range(2):
-        e = vp()
-        if hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
-            raise RuntimeError("hipEventCreateWithFlags failed")
-        evs.append(e)
-    f = ctypes.c_float()
-    evict = cache_evictor(torch, args.flush)
+    times_of = alone_timer(cache_evictor(torch, args.flush), reps=args.sweep_reps, warm=3)
     sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
     out = open(args.calibrate_out, "w") if args.calibrate_out else sys.stdout
     for mib in [int(v) for v in args.calibrate_sizes.split(",")]:
@@ -884,29 +1064,27 @@ def calibrate(args):
         for R, W in CALIB_MIXES:
             ins = (vp * 4)(*[b.data_ptr() for b in bufs[:4]])
             outs = (vp * 4)(*[b.data_ptr() for b in bufs[4:]] + [0, 0])
-            ts = []
-            for rep in range(args.sweep_reps + 3):
-                evict()
-                hip.hipEventRecord(evs[0], sp)
-                rc = lib.calib_stream(R, W, ins, outs, vp(sink.data_ptr()), vectors, sp)
-                hip.hipEventRecord(evs[1], sp)
-                if rc != 0:
-                    raise RuntimeError(f"calib_stream({R}, {W}) failed: {rc}")
-                torch.cuda.synchronize()
-                hip.hipEventElapsedTime(ctypes.byref(f), evs[0], evs[1])
-                if rep >= 3:
-                    ts.append(f.value * 1e-3)
             b = (R + W) * vectors * 16
-            print(json.dumps({"mib_per_stream": mib, "reads": R, "writes": W, "flush": args.flush,
-                              "bytes": b, "reps": len(ts),
-                              "gbs_best": round(b / min(ts) / 1e9, 1),
-                              "gbs_median": round(b / statistics.median(ts) / 1e9, 1),
-                              "pct_peak_median": round(100 * b / statistics.median(ts) / 1e9 / PEAK_GBS, 1)}),
-                  file=out, flush=True)
+            best = None
+            for pi, pname in enumerate(CALIB_PATTERNS):
+                def fn(pi=pi):
+                    rc = lib.calib_stream_pattern(pi, R, W, ins, outs, vp(sink.data_ptr()), vectors, sp)
+                    if rc != 0:
+                        raise RuntimeError(f"calib_stream_pattern({pi}, {R}, {W}) failed: {rc}")
+                ts = times_of(fn)
+                rec = {"mib_per_stream": mib, "reads": R, "writes": W, "pattern": pname, "flush": args.flush,
+                       "bytes": b, "reps": len(ts),
+                       "gbs_best": round(b / min(ts) / 1e9, 1),
+                       "gbs_median": round(b / statistics.median(ts) / 1e9, 1),
+                       "pct_peak_median": round(100 * b / statistics.median(ts) / 1e9 / PEAK_GBS, 1)}
+                print(json.dumps(rec), file=out, flush=True)
+                if best is None or rec["gbs_median"] > best["gbs_median"]:
+                    best = rec
+            print(json.dumps({"mib_per_stream": mib, "reads": R, "writes": W, "ceiling": True,
+                              "best_pattern": best["pattern"], "gbs_median": best["gbs_median"],
+                              "pct_peak_median": best["pct_peak_median"]}), file=out, flush=True)
         del bufs
         torch.cuda.empty_cache()
-    for e in evs:
-        hip.hipEventDestroy(e)
 
 
 # Read and write streams per element of each launch of the step, for its
@@ -927,6 +1105,9 @@ def _calib_lib():
     vp = ctypes.c_void_p
     lib.calib_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), vp,
                                  ctypes.c_int64, vp]
+    lib.calib_stream_pattern.argtypes = [ctypes.c_int] + lib.calib_stream.argtypes
+    if lib.calib_patterns() != len(CALIB_PATTERNS):
+        raise RuntimeError(f"{path} has {lib.calib_patterns()} patterns; rebuild it")
     return lib
 
 
@@ -948,11 +1129,13 @@ def time_steps(step_fns, steps, warmup, stream):
     return t0.elapsed_time(t1) / steps
 
 
-def stand_in_step(calls, nsets, stream):
+def stand_in_step(calls, nsets, stream, pattern=0):
     """Plain-stream stand-ins for a step's launches (row, kernel, bytes, fn):
     per buffer set, one bench_calib.hip launch per relay launch with the row's
-    read/write mix and bytes.  Returns (per-set launch lists, launches as
-    (row, reads, writes, vectors per stream, relay bytes), stand-in bytes)."""
+    read/write mix and bytes, in access pattern `pattern` (an index into
+    CALIB_PATTERNS, or one per launch).  Returns (per-set launch lists,
+    launches as (row, reads, writes, vectors per stream, relay bytes),
+    stand-in bytes)."""
     import ctypes
     import functools
     import torch
@@ -964,20 +1147,96 @@ def stand_in_step(calls, nsets, stream):
     for row, _, b, _ in calls:
         R, W = STEP_MIX[row]
         launches.append((row, R, W, max(1024, round(b / (16 * (R + W)) / 1024) * 1024), b))
+    pats = list(pattern) if isinstance(pattern, (list, tuple)) else [pattern] * len(launches)
     sets = []
     for _ in range(nsets):
         fns = []
-        for row, R, W, vectors, _ in launches:
+        for (row, R, W, vectors, _), pat in zip(launches, pats):
             bufs = [torch.empty(vectors * 16, dtype=torch.uint8, device="cuda") for _ in range(R + W)]
             ins = (vp * 4)(*([x.data_ptr() for x in bufs[:R]] + [0] * (4 - R)))
             outs = (vp * 4)(*([x.data_ptr() for x in bufs[R:]] + [0] * (4 - W)))
-            fn = functools.partial(lib.calib_stream, R, W, ins, outs, vp(sink.data_ptr()), vectors, sp)
+            fn = functools.partial(lib.calib_stream_pattern, pat, R, W, ins, outs, vp(sink.data_ptr()), vectors, sp)
             fn.keep = (bufs, ins, outs, sink)
             if fn() != 0:
-                raise RuntimeError(f"calib_stream({R}, {W}, {vectors}) failed")
+                raise RuntimeError(f"calib_stream_pattern({pat}, {R}, {W}, {vectors}) failed")
             fns.append(fn)
         sets.append(fns)
     return sets, launches, sum((R + W) * v * 16 for _, R, W, v, _ in launches)
+
+
+def alone_timer(evict, reps, warm=2):
+    """A function timing one launch function alone: `reps` times after `warm`
+    warm-ups, each after evict() (clearing the caches of its inputs), with a
+    fence-free HIP event pair; returns the durations in seconds."""
+    import ctypes
+    import torch
+    hip = hip_runtime()
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    evs = []
+    for _ in range(2):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        evs.append(e)
+    f = ctypes.c_float()
+
+    def times_of(fn):
+        ts = []
+        for rep in range(reps + warm):
+            evict()
+            hip.hipEventRecord(evs[0], sp)
+            fn()
+            hip.hipEventRecord(evs[1], sp)
+            torch.cuda.synchronize()
+            hip.hipEventElapsedTime(ctypes.byref(f), evs[0], evs[1])
+            if rep >= warm:
+                ts.append(f.value * 1e-3)
+        return ts
+    times_of.events = evs  # kept alive with the function
+    return times_of
+
+
+def stand_in_ceiling(calls, nsets, stream, steps, warmup, value):
+    """The step's launch sequence replaced by plain streams of each launch's
+    read/write mix and bytes, in every access pattern of bench_calib.hip
+    (the same pattern for every launch), and once with each launch in the
+    pattern that ran its mix and bytes fastest alone; each timed like timed
+    region 1.  The fastest of these is the ceiling the relay step is compared
+    with."""
+    import torch
+    out = {"patterns": {}}
+    for pi, name in enumerate(CALIB_PATTERNS):
+        st_sets, _, st_bytes = stand_in_step(calls, nsets, stream, pi)
+        ms = time_steps(lambda i: st_sets[i % nsets], steps, warmup, stream)
+        gbs = st_bytes / (ms * 1e-3) / 1e9
+        out["patterns"][name] = {"value": round(gbs, 1), "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
+                                 "ms_per_step": round(ms, 5)}
+        del st_sets
+        torch.cuda.empty_cache()
+    times_of = alone_timer(cache_evictor(torch, "read"), reps=5)
+    best = []
+    for c in calls:
+        med = {}
+        for pi in range(len(CALIB_PATTERNS)):
+            st_sets, _, _ = stand_in_step([c], 1, stream, pi)
+            med[pi] = statistics.median(times_of(st_sets[0][0]))
+            del st_sets
+        best.append(min(med, key=med.get))
+    torch.cuda.empty_cache()
+    st_sets, _, st_bytes = stand_in_step(calls, nsets, stream, best)
+    ms = time_steps(lambda i: st_sets[i % nsets], steps, warmup, stream)
+    gbs = st_bytes / (ms * 1e-3) / 1e9
+    out["best_per_launch"] = {"value": round(gbs, 1), "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
+                              "ms_per_step": round(ms, 5),
+                              "patterns": {c[0]: CALIB_PATTERNS[b] for c, b in zip(calls, best)}}
+    del st_sets
+    torch.cuda.empty_cache()
+    cands = [(v["value"], k) for k, v in out["patterns"].items()] + [(gbs, "best_per_launch")]
+    ceil, which = max(cands)
+    out["ceiling"] = {"value": round(ceil, 1), "pct_of_peak": round(100.0 * ceil / PEAK_GBS, 2), "from": which}
+    out["relay_over_stand_in"] = round(value / ceil, 4)
+    out["relay_over_relay_pattern"] = round(value / out["patterns"]["relay"]["value"], 4)
+    return out
 
 
 def calibrate_step(args):
@@ -1269,7 +1528,9 @@ def main():
         print(f"bench.py measures one GPU: the library has no multi-GPU path (--gpus {args.gpus} "
               "requested). The relay's local kernels shard per rank; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    if args.fit_trace:
+    if args.traffic_from:
+        traffic_from(args)
+    elif args.fit_trace:
         fit_from_trace(args)
     elif args.role_fit:
         role_fit(args)

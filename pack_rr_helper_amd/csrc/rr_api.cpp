@@ -586,10 +586,12 @@ rr_status check_moves(const std::vector<Move> &mv, size_t culprit[2])
 
 class CopyLauncher {
 public:
-    explicit CopyLauncher(hipStream_t st) : st_(st)
+    // long_call: the call moves at least kCopyLongBytes, so its aligned moves
+    // use the long-call tiles.
+    CopyLauncher(hipStream_t st, bool long_call) : st_(st)
     {
         b_.nseg = 0;
-        b_.pad = 0;
+        b_.long_tiles = long_call ? 1 : 0;
     }
 
     // One segment per move (tile 0 also copies its head and tail bytes), all
@@ -620,7 +622,7 @@ private:
     void piece(const unsigned char *src, unsigned char *dst, int64_t nbytes, int32_t mode,
                int32_t shift)
     {
-        const int64_t tv = rr::copy_tile_vecs(mode);
+        const int64_t tv = rr::copy_tile_vecs(mode, b_.long_tiles != 0);
         while (nbytes > 0) {
             if (b_.nseg == rr::kMaxCopySegs || tiles_ >= rr::kMaxTilesPerLaunch)
                 flush();
@@ -677,7 +679,10 @@ rr_status run_copy(const std::vector<Move> &mv, void *stream, bool batch)
     rr_status st = check_moves(mv, culprit);
     if (st != RR_OK)
         return batch ? jobs_error(mv[culprit[0]].job, mv[culprit[1]].job, st) : st;
-    CopyLauncher L(static_cast<hipStream_t>(stream));
+    int64_t total = 0;
+    for (const Move &m : mv)
+        total += m.nbytes;
+    CopyLauncher L(static_cast<hipStream_t>(stream), total >= rr::kCopyLongBytes);
     for (const Move &m : mv)
         L.add(m.src, m.dst, m.nbytes);
     const hipError_t e = L.finish();

@@ -39,8 +39,16 @@ constexpr int64_t kMaxTilesPerLaunch = RR_MAX_TILES_PER_LAUNCH;
 #ifndef RR_COPY_UNROLL
 #define RR_COPY_UNROLL 2             // 16-byte vectors per thread in a copy tile:
                                      // 8 KiB tiles measured faster than 16 and 32 KiB
-                                     // from 16 MiB to 1 GiB; 4 KiB keeps too few loads
-                                     // in flight
+                                     // from 16 MiB to 1 GiB
+#endif
+#ifndef RR_COPY_UNROLL_LONG
+#define RR_COPY_UNROLL_LONG 1        // the same for calls that move at least
+                                     // RR_COPY_LONG_BYTES: 4 KiB tiles moved a 1 GiB
+                                     // message's all-to-all 5% faster than 8 KiB tiles,
+                                     // equal at 256 MiB, 5% slower at 64 MiB
+#endif
+#ifndef RR_COPY_LONG_BYTES
+#define RR_COPY_LONG_BYTES (int64_t(1) << 29)
 #endif
 
 #ifndef RR_SHIFT_RED_UNROLL
@@ -51,6 +59,8 @@ constexpr int64_t kMaxTilesPerLaunch = RR_MAX_TILES_PER_LAUNCH;
 constexpr int kUnroll = RR_UNROLL;
 constexpr int kShiftRedUnroll = RR_SHIFT_RED_UNROLL;
 constexpr int kCopyUnroll = RR_COPY_UNROLL;
+constexpr int kCopyUnrollLong = RR_COPY_UNROLL_LONG;
+constexpr int64_t kCopyLongBytes = RR_COPY_LONG_BYTES;
 #ifndef RR_SHIFT_UNROLL
 #define RR_SHIFT_UNROLL 2            // 16-byte vectors per thread in a realigning copy tile
                                      // (8 KiB tiles; measured faster than 16 and 32 KiB)
@@ -61,8 +71,14 @@ constexpr int kShiftUnroll = RR_SHIFT_UNROLL;
 // (unused) LDS per workgroup, which lets 6 of them share a CU's 160 KiB
 // instead of 8: with fewer loads and stores in flight, HBM serves a long copy
 // 2-4% faster.  Reductions and short copies measured best at full occupancy.
-constexpr int64_t kCopyThrottleTiles = 4096;
-constexpr unsigned kCopyThrottleLds = 26 * 1024;
+#ifndef RR_COPY_THROTTLE_TILES
+#define RR_COPY_THROTTLE_TILES 4096
+#endif
+#ifndef RR_COPY_THROTTLE_LDS
+#define RR_COPY_THROTTLE_LDS (26 * 1024)
+#endif
+constexpr int64_t kCopyThrottleTiles = RR_COPY_THROTTLE_TILES;
+constexpr unsigned kCopyThrottleLds = RR_COPY_THROTTLE_LDS;
 
 enum RedMode : int32_t { kRedAligned = 1, kRedShifted = 2 };
 
@@ -260,19 +276,22 @@ __host__ __device__ constexpr int64_t red_tile_vecs(int32_t mode)
     return mode == kRedShifted ? tile_vecs<kShiftRedUnroll>() : tile_vecs<kUnroll>();
 }
 
+// long_tiles: the batch belongs to a call that moves at least kCopyLongBytes,
+// whose aligned moves use tiles of kCopyUnrollLong vectors per lane.
 template <int CAP>
 struct CopyBatchT {
     int32_t tile0[CAP];
     int32_t nseg;
-    int32_t pad;
+    int32_t long_tiles;
     CopySeg seg[CAP];
 };
 constexpr int kSmallCopySegs = 16;
 using CopyBatch = CopyBatchT<kMaxCopySegs>;
 
-__host__ __device__ constexpr int64_t copy_tile_vecs(int32_t mode)
+__host__ __device__ constexpr int64_t copy_tile_vecs(int32_t mode, bool long_tiles)
 {
-    return mode == kCopyShifted ? tile_vecs<kShiftUnroll>() : tile_vecs<kCopyUnroll>();
+    return mode == kCopyShifted ? tile_vecs<kShiftUnroll>()
+                                : long_tiles ? tile_vecs<kCopyUnrollLong>() : tile_vecs<kCopyUnroll>();
 }
 
 // How a batch is launched.  Every form runs the same work per tile; they

@@ -399,23 +399,26 @@ __device__ __forceinline__ void copy_edges(const CopySeg &sg, const CopySplit &s
     }
 }
 
+// U: 16-byte vectors per lane in a tile (kCopyUnroll, or kCopyUnrollLong
+// for the batches of a long call).
+template <int U>
 __device__ __forceinline__ void copy_aligned(const CopySeg &sg, int64_t lt)
 {
     const CopySplit sp = copy_split(sg.dst, sg.nbytes);
     const int64_t nv = sp.nv;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(sg.src + sp.head);
     u32x4 *dst = reinterpret_cast<u32x4 *>(sg.dst + sp.head);
-    if (full_tile(lt, tile_vecs<kCopyUnroll>(), nv)) {
-        u32x4 x[kCopyUnroll];
+    if (full_tile(lt, tile_vecs<U>(), nv)) {
+        u32x4 x[U];
 #pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u)
-            x[u] = ld16(src + vec_index<kCopyUnroll>(lt, lane(), u));
+        for (int u = 0; u < U; ++u)
+            x[u] = ld16(src + vec_index<U>(lt, lane(), u));
 #pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u)
-            st16(dst + vec_index<kCopyUnroll>(lt, lane(), u), x[u]);
+        for (int u = 0; u < U; ++u)
+            st16(dst + vec_index<U>(lt, lane(), u), x[u]);
     } else {
-        for (int u = 0; u < kCopyUnroll; ++u) {
-            const int64_t v = vec_index<kCopyUnroll>(lt, lane(), u);
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = vec_index<U>(lt, lane(), u);
             if (v >= nv)
                 break;
             st16(dst + v, ld16(src + v));
@@ -480,23 +483,18 @@ __device__ __forceinline__ void copy_shifted(const CopySeg &sg, int64_t lt)
 }
 
 // Segments whose source and destination agree modulo 16 bytes.
-__device__ __forceinline__ void copy_seg(const CopySeg &sg, int64_t lt)
-{
-    copy_aligned(sg, lt);
-}
-
-template <int CAP>
+template <int CAP, int U>
 __global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatchT<CAP> b)
 {
     const int32_t t = (int32_t)blockIdx.x;
     const int s = find_seg(b.tile0, b.nseg, t);
-    copy_seg(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
+    copy_aligned<U>(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
 }
 
-template <int CAP>
+template <int CAP, int U>
 __global__ __launch_bounds__(kBlock) void copy_uniform_kernel(CopyBatchT<CAP> b)
 {
-    copy_seg(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
+    copy_aligned<U>(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
 }
 
 // Any segment: realigned (source and destination disagree modulo 16 bytes)
@@ -504,10 +502,11 @@ __global__ __launch_bounds__(kBlock) void copy_uniform_kernel(CopyBatchT<CAP> b)
 // both (a segmentCount that is not a multiple of 8) takes one launch.  The
 // aligned-only kernels above keep the smaller register budget for calls
 // without realigned moves.
+template <int U>
 __device__ __forceinline__ void copy_mixed_seg(const CopySeg &sg, int64_t lt)
 {
     if (sg.mode != kCopyShifted) {  // uniform across the workgroup
-        copy_aligned(sg, lt);
+        copy_aligned<U>(sg, lt);
         return;
     }
     switch (sg.shift >> 2) {
@@ -518,18 +517,18 @@ __device__ __forceinline__ void copy_mixed_seg(const CopySeg &sg, int64_t lt)
     }
 }
 
-template <int CAP>
+template <int CAP, int U>
 __global__ __launch_bounds__(kBlock) void copy_mixed_kernel(CopyBatchT<CAP> b)
 {
     const int32_t t = (int32_t)blockIdx.x;
     const int s = find_seg(b.tile0, b.nseg, t);
-    copy_mixed_seg(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
+    copy_mixed_seg<U>(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
 }
 
-template <int CAP>
+template <int CAP, int U>
 __global__ __launch_bounds__(kBlock) void copy_mixed_uniform_kernel(CopyBatchT<CAP> b)
 {
-    copy_mixed_seg(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
+    copy_mixed_seg<U>(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
 }
 
 }  // namespace
@@ -610,7 +609,7 @@ void launch_reduce_sized(const RedBatch &b, const LaunchShape &sh, int64_t total
     }
 }
 
-template <int CAP>
+template <int CAP, int U>
 void launch_copy_table(const CopyBatchT<CAP> &b, const LaunchShape &sh, int64_t total_tiles, bool shifted,
                        hipStream_t stream)
 {
@@ -618,18 +617,28 @@ void launch_copy_table(const CopyBatchT<CAP> &b, const LaunchShape &sh, int64_t 
     if (sh.form == kFormUniform) {
         const dim3 grid((unsigned)sh.gx, (unsigned)sh.gy);
         if (shifted) {
-            copy_mixed_uniform_kernel<CAP><<<grid, block, 0, stream>>>(b);
+            copy_mixed_uniform_kernel<CAP, U><<<grid, block, 0, stream>>>(b);
         } else {
             const unsigned lds = total_tiles >= kCopyThrottleTiles ? kCopyThrottleLds : 0u;
-            copy_uniform_kernel<CAP><<<grid, block, lds, stream>>>(b);
+            copy_uniform_kernel<CAP, U><<<grid, block, lds, stream>>>(b);
         }
     } else {
         const dim3 grid((unsigned)total_tiles);
         if (shifted)
-            copy_mixed_kernel<CAP><<<grid, block, 0, stream>>>(b);
+            copy_mixed_kernel<CAP, U><<<grid, block, 0, stream>>>(b);
         else
-            copy_kernel<CAP><<<grid, block, 0, stream>>>(b);
+            copy_kernel<CAP, U><<<grid, block, 0, stream>>>(b);
     }
+}
+
+template <int CAP>
+void launch_copy_sized(const CopyBatchT<CAP> &b, const LaunchShape &sh, int64_t total_tiles, bool shifted,
+                       hipStream_t stream)
+{
+    if (b.long_tiles)
+        launch_copy_table<CAP, kCopyUnrollLong>(b, sh, total_tiles, shifted, stream);
+    else
+        launch_copy_table<CAP, kCopyUnroll>(b, sh, total_tiles, shifted, stream);
 }
 
 }  // namespace
@@ -659,10 +668,13 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
         return hipSuccess;
     (void)hipGetLastError();  // report this launch's status only
     const LaunchShape sh = copy_shape(b, total_tiles);
-    if (b.nseg <= kSmallCopySegs)
-        launch_copy_table(shrink<CopyBatchT<kSmallCopySegs>>(b), sh, total_tiles, shifted, stream);
-    else
-        launch_copy_table(b, sh, total_tiles, shifted, stream);
+    if (b.nseg <= kSmallCopySegs) {
+        CopyBatchT<kSmallCopySegs> t = shrink<CopyBatchT<kSmallCopySegs>>(b);
+        t.long_tiles = b.long_tiles;
+        launch_copy_sized(t, sh, total_tiles, shifted, stream);
+    } else {
+        launch_copy_sized(b, sh, total_tiles, shifted, stream);
+    }
     return hipGetLastError();
 }
 

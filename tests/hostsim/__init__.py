@@ -21,6 +21,11 @@ HEADERS = [os.path.join(ROOT, "pack_rr_helper_amd", "csrc", "rr_internal.h"),
 # items longer than that continue in further launches
 CAPPED_LIB = os.path.join(HERE, "libhostsim_cap5.so")
 CAPPED_DEFINES = ("RR_MAX_TILES_PER_LAUNCH=5",)
+# variants in which every copy call takes the long-call tiling (the library
+# switches to it only for calls that move hundreds of MiB)
+LONG_LIB = os.path.join(HERE, "libhostsim_long.so")
+LONG_DEFINES = ("RR_COPY_LONG_BYTES=1",)
+CAPPED_LONG_LIB = os.path.join(HERE, "libhostsim_cap5_long.so")
 
 
 def build(lib=LIB, defines=()):
@@ -35,14 +40,17 @@ def build(lib=LIB, defines=()):
 
 
 class Sim:
-    def __init__(self, capped=False):
-        lib, defines = (CAPPED_LIB, CAPPED_DEFINES) if capped else (LIB, ())
+    def __init__(self, capped=False, long_copies=False):
+        lib, defines = {(False, False): (LIB, ()), (True, False): (CAPPED_LIB, CAPPED_DEFINES),
+                        (False, True): (LONG_LIB, LONG_DEFINES),
+                        (True, True): (CAPPED_LONG_LIB, CAPPED_DEFINES + LONG_DEFINES)}[(capped, long_copies)]
         # one builder at a time; the others wait and then find the library fresh
         with open(lib + ".lock", "w") as lk:
             fcntl.flock(lk, fcntl.LOCK_EX)
             if not os.path.exists(lib) or any(os.path.getmtime(s) > os.path.getmtime(lib)
                                               for s in SOURCES + HEADERS):
                 build(lib, defines)
+        self.long_copies = long_copies
         self.L = ctypes.CDLL(lib)
         self.L.sim_message.restype = ctypes.c_char_p
         self.L.sim_register.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]

@@ -47,6 +47,7 @@ bool touches(uintptr_t a, int64_t n)
 }
 
 long g_forms[2][3];  // launches per (copy?, launch form)
+long g_long_copies[2];  // copy launches per tiling (0 default, 1 long-call)
 
 void violation(const char *what, uintptr_t a, int64_t n)
 {
@@ -288,6 +289,9 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
     ++g_forms[1][sh.form];
     if (sh.form == kFormOne)
         violation("single-segment form for a copy", 0, 0);
+    if (b.long_tiles != 0 && b.long_tiles != 1)
+        violation("copy batch with an unknown tiling", 0, b.long_tiles);
+    ++g_long_copies[b.long_tiles != 0];
     for (const auto &st : tiles_of(b, total_tiles, sh)) {
         const CopySeg &sg = b.seg[st.first];
         const int64_t lt = st.second;
@@ -312,6 +316,8 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
             violation("realigned copy with a wrong source shift", uintptr_t(bsrc), sg.shift);
         if (shift_mode)
             replay_copy_tile<kShiftUnroll>(b, st.first, total_tiles, lt, sg, sp, true);
+        else if (b.long_tiles)
+            replay_copy_tile<kCopyUnrollLong>(b, st.first, total_tiles, lt, sg, sp, false);
         else
             replay_copy_tile<kCopyUnroll>(b, st.first, total_tiles, lt, sg, sp, false);
     }
@@ -327,6 +333,7 @@ void sim_reset(void)
     g_violations = 0;
     g_launches = 0;
     memset(g_forms, 0, sizeof g_forms);
+    memset(g_long_copies, 0, sizeof g_long_copies);
     g_msg[0] = '\0';
 }
 void sim_register(const void *p, int64_t bytes, int writable)
@@ -339,4 +346,6 @@ long sim_launches(void) { return g_launches; }
 // 2 single segment) of the reduction (copy == 0) or copy (copy == 1) kernels
 long sim_form_launches(int copy, int form) { return g_forms[copy != 0][form]; }
 const char *sim_message(void) { return g_msg; }
+// copy launches since the last reset with the default (0) or long-call (1) tiling
+long sim_copy_launches(int long_tiles) { return g_long_copies[long_tiles != 0]; }
 }

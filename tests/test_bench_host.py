@@ -20,25 +20,131 @@ def test_code_digest_ignores_comments_and_spacing_only():
     assert bench.code_digest([code, same]) != bench.code_digest([code])
 
 
-def test_stored_traffic_is_used_only_for_its_own_workload():
-    with open(os.path.join(ROOT, "profiles", "traffic.json")) as fh:
-        t = json.load(fh)
-    kernel = next(iter(t["kernels"]))
-    k = t["kernels"][kernel]
-    seq = (k["algorithmic_bytes_per_launch"], k["launches_per_step"])
-    got = bench.traffic_for(kernel, t["message_mib"], t["variant"], *seq)
-    if t["kernel_source_digest"] == bench.kernel_source_digest():
-        assert got == k["hbm_bytes_per_launch"]
-    else:
-        assert got is None          # counters taken on other kernel code
-    other = "group" if t["variant"] != "group" else "share"
-    assert bench.traffic_for(kernel, t["message_mib"], other, *seq) is None
-    assert bench.traffic_for(kernel, t["message_mib"] * 2, t["variant"], *seq) is None
-    assert bench.traffic_for("no such kernel", t["message_mib"], t["variant"], *seq) is None
+def _traffic_file(tmp_path, digest=None):
+    t = {"kernel_source_digest": digest or bench.kernel_source_digest(), "entries": [
+        {"message_mib": 64.0, "variant": "share", "dtype": "bf16",
+         "kernels": {"reduce<bf16>": {"hbm_bytes_per_launch": 1001, "algorithmic_bytes_per_launch": 1000,
+                                      "launches_per_step": 6}}},
+        {"message_mib": 1024.0, "variant": "group", "dtype": "bf16",
+         "kernels": {"copy": {"hbm_bytes_per_launch": 2002, "algorithmic_bytes_per_launch": 2000,
+                              "launches_per_step": 2}}}]}
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps(t))
+    return str(path)
+
+
+def test_stored_traffic_is_used_only_for_its_own_workload(tmp_path):
+    path = _traffic_file(tmp_path)
+    get = lambda *a, **k: bench.traffic_for(*a, path=path, **k)
+    assert get("reduce<bf16>", 64.0, "share", 1000, 6) == 1001
+    assert get("copy", 1024.0, "group", 2000, 2) == 2002
+    assert get("reduce<bf16>", 64.0, "group", 1000, 6) is None       # other variant
+    assert get("reduce<bf16>", 128.0, "share", 1000, 6) is None      # other message
+    assert get("reduce<bf16>", 64.0, "share", 1000, 6, "f32") is None  # other dtype
+    assert get("copy", 64.0, "share", 1000, 6) is None               # no such kernel there
     # another launch sequence of the same kernel (other launches per step or
     # bytes per launch) gets no stored figure either
-    assert bench.traffic_for(kernel, t["message_mib"], t["variant"], seq[0], seq[1] - 1) is None
-    assert bench.traffic_for(kernel, t["message_mib"], t["variant"], seq[0] + 16, seq[1]) is None
+    assert get("reduce<bf16>", 64.0, "share", 1000, 5) is None
+    assert get("reduce<bf16>", 64.0, "share", 1016, 6) is None
+    # counters taken on other kernel code are never used
+    stale = _traffic_file(tmp_path, digest="0" * 16)
+    assert bench.traffic_for("reduce<bf16>", 64.0, "share", 1000, 6, path=stale) is None
+
+
+def test_committed_traffic_matches_its_kernel_code():
+    """The committed counter figures carry the digest of the kernel code they
+    were taken on; bench.py uses them only while that code is unchanged."""
+    with open(bench.TRAFFIC_JSON) as fh:
+        t = json.load(fh)
+    for e in t["entries"]:
+        for kern, k in e["kernels"].items():
+            got = bench.traffic_for(kern, e["message_mib"], e["variant"], k["algorithmic_bytes_per_launch"],
+                                    k["launches_per_step"], e["dtype"])
+            assert got == (k["hbm_bytes_per_launch"] if t["kernel_source_digest"] == bench.kernel_source_digest()
+                           else None)
+
+
+_REL = "void rr::(anonymous namespace)::{}(rr::RedBatchT<8>)"
+
+
+def _pmc_csv(path, counter, dispatches):
+    lines = ['"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value"']
+    for i, (name, v) in enumerate(dispatches, 1):
+        lines.append(f'{i},"{name}","{counter}",{v}')
+    path.write_text("\n".join(lines) + "\n")
+    return str(path)
+
+
+def test_traffic_from_scales_by_the_plain_copy_and_averages_the_timed_steps(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_JSON", str(tmp_path / "traffic.json"))
+    red, cp = _REL.format("reduce_uniform_kernel<true, 8>"), _REL.format("copy_uniform_kernel<16>")
+    order, algo = ["ar2_helper", "a2a_pack"], {"ar2_helper": 3 * 1024 * 100, "a2a_pack": 2 * 1024 * 50}
+    run = {"steps": 2, "warmup": 1, "dtype": "bf16",
+           "config": {"launch_order": order, "rows_bytes_per_launch": algo, "message_bytes": 64 << 20,
+                      "variant": "share"}}
+    (tmp_path / "run.json").write_text("[bench] noise\n" + json.dumps(run) + "\n")
+    # a relay launch while staging inputs, the copy of 256 MiB three times,
+    # then warmup + 2 x 2 steps of the two launches
+    setup = [(red, 999.0), ("__amd_rocclr_copyBuffer", 1.0)]
+    fetch = setup + [("__amd_rocclr_copyBuffer", 256 * 1024 / 2)] * 3 + [(red, 100.0), (cp, 25.0)] * 5
+    write = setup + [("__amd_rocclr_copyBuffer", 256 * 1024)] * 3 + [(red, 100.0), (cp, 50.0)] * 5
+    args = type("A", (), {})()
+    args.traffic_from = ",".join([_pmc_csv(tmp_path / "f.csv", "FETCH_SIZE", fetch),
+                                  _pmc_csv(tmp_path / "w.csv", "WRITE_SIZE", write)])
+    args.traffic_bench = str(tmp_path / "run.json")
+    args.calibrate_copy_mib = 256.0
+    bench.traffic_from(args)
+    t = json.loads((tmp_path / "traffic.json").read_text())
+    e = t["entries"][0]
+    assert t["kernel_source_digest"] == bench.kernel_source_digest()
+    assert e["fetch_scale"] == 2.0 and e["write_scale"] == 1.0
+    assert [l["hbm_bytes"] for l in e["launches"]] == [300 * 1024, 100 * 1024]
+    assert e["kernels"]["reduce<bf16>"] == {"hbm_bytes_per_launch": 300 * 1024,
+                                            "algorithmic_bytes_per_launch": 300 * 1024, "launches_per_step": 1}
+    assert e["kernels"]["copy"]["hbm_bytes_per_launch"] == 100 * 1024
+
+
+def test_linear_fit_recovers_fixed_cost_and_bandwidth():
+    t0, bw = 1.5e-6, 6.4e12
+    samples = {"r": {m: (int(m * 2 ** 20), [t0 + m * 2 ** 20 / bw]) for m in (64.0, 128.0, 256.0, 512.0)}}
+    row = bench.fit_table(samples)[0]
+    assert abs(row["t0_us"] - 1.5) < 1e-3 and abs(row["bw_gbs"] - 6400.0) < 0.1 and row["r2"] > 0.99999
+    a = row["at_ref"]
+    assert abs(a["pct_of_peak"] / 100 - (bw / 8e12) * a["streaming_share"]) < 1e-3
+
+
+def test_fit_from_trace_uses_only_launches_after_the_cache_clearing_read(tmp_path, capsys):
+    evict = "void at::native::reduce_kernel<512, 1, at::native::ReduceOp<long, at::native::func_wrapper<long> > >"
+    red = _REL.format("reduce_one_kernel<true, 2>")
+    log, rows, ts = [], [], 0
+
+    def disp(name, dur_ns):
+        nonlocal ts
+        rows.append((name, ts, ts + dur_ns))
+        ts += dur_ns + 1000
+
+    disp(red, 5)  # a launch made while staging inputs: not timed
+    for role, t0_ns, bw in (("one_tile", 3560, None), ("a", 1000, 6400.0), ("b", 2000, 8000.0)):
+        for mib in ((0.0,) if bw is None else (64.0, 128.0, 256.0, 512.0)):
+            b = 768 if bw is None else int(mib * 2 ** 20)
+            for rep in range(4):
+                disp(evict, 200000)
+                disp(red, t0_ns if bw is None else int(t0_ns + b / bw))
+                log.append({"role": role, "message_mib": mib, "bytes": b, "warmup": rep < 2})
+    lines = ['"Dispatch_Id","Kernel_Name","Start_Timestamp","End_Timestamp"']
+    lines += [f'{i},"{n}",{a},{b}' for i, (n, a, b) in enumerate(rows, 1)]
+    (tmp_path / "trace.csv").write_text("\n".join(lines) + "\n")
+    (tmp_path / "log.json").write_text(json.dumps({"variant": "share", "launches": log}))
+    args = type("A", (), {})()
+    args.fit_trace, args.fit_log, args.sweep_out = str(tmp_path / "trace.csv"), str(tmp_path / "log.json"), \
+        str(tmp_path / "fit.json")
+    bench.fit_from_trace(args)
+    fit = json.loads((tmp_path / "fit.json").read_text())
+    assert fit["one_tile_us"] == 3.56
+    got = {r["role"]: r for r in fit["roles"]}
+    assert abs(got["a"]["t0_us"] - 1.0) < 0.01 and abs(got["a"]["bw_gbs"] - 6400) < 1
+    assert abs(got["b"]["t0_us"] - 2.0) < 0.01 and abs(got["b"]["bw_gbs"] - 8000) < 1
+    assert "| a |" in capsys.readouterr().out
 
 
 def test_more_than_one_gpu_is_refused():

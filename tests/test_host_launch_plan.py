@@ -137,9 +137,24 @@ def test_rs4_passes(sim, orc, H, R, lead):
             assert sim.L.sim_launches() - launches0 >= 2
 
 
-@pytest.mark.parametrize("seg,lead", [(5 * 128 * 4 + 8, 0), (5 * 128 * 2 + 3, 0), (5 * 128 * 3, 5), (400, 0)])
+@pytest.fixture(scope="module", params=["default", "long"])
+def copy_sim(request):
+    """The replay with the default copy tiling, and with the long-call tiling
+    (4 KiB tiles for aligned moves) that the library takes for calls of
+    hundreds of MiB, forced here for every call."""
+    return Sim(long_copies=request.param == "long")
+
+
+def _tiling_used(sim, long_copies):
+    n_long, n_default = sim.L.sim_copy_launches(1), sim.L.sim_copy_launches(0)
+    assert (n_long > 0 and n_default == 0) if long_copies else (n_long == 0 and n_default > 0)
+
+
+@pytest.mark.parametrize("seg,lead", [(5 * 128 * 4 + 8, 0), (5 * 128 * 2 + 3, 0), (5 * 128 * 3, 5), (400, 0),
+                                      (5 * 128 * 9 + 8, 0)])
 @pytest.mark.parametrize("es", [2, 4])
-def test_a2a_pack_unpack(sim, orc, seg, lead, es):
+def test_a2a_pack_unpack(copy_sim, orc, seg, lead, es):
+    sim = copy_sim
     sim.reset()
     A, H, nc = 4, 4, 5
     dt = BF16 if es == 2 else F32
@@ -164,6 +179,8 @@ def test_a2a_pack_unpack(sim, orc, seg, lead, es):
     for d in range(A):
         assert np.array_equal(outs[d][1:1 + A * seg], expect[d])
         assert outs[d][0] == 0x5A and np.all(outs[d][1 + A * seg:] == 0x5A)
+    if c > 0:
+        _tiling_used(sim, sim.long_copies)
 
 
 # --------------------------------------------------------------------------
@@ -592,13 +609,19 @@ def capped():
     return Sim(capped=True)
 
 
+@pytest.fixture(scope="module", params=["default", "long"])
+def capped_copy(request):
+    return Sim(capped=True, long_copies=request.param == "long")
+
+
 @pytest.mark.parametrize("seg,out_lead", [(5 * 128 * 200, 0), (5 * 128 * 200 + 3, 0), (5 * 128 * 200, 1),
                                           (5 * 128 * 37 + 5, 3)])
-def test_copies_longer_than_a_launch_continue(capped, orc, seg, out_lead):
-    """Each chunk move spans 7 body tiles, more than one launch holds: the
-    launcher cuts it after whole tiles, and the rest starts on a 16-byte
-    destination boundary with the same source shift in the next launch."""
-    sim = capped
+def test_copies_longer_than_a_launch_continue(capped_copy, orc, seg, out_lead):
+    """Each chunk move spans several body tiles (7 or 13 in the aligned
+    moves, by tiling), more than one launch holds: the launcher cuts it after
+    whole tiles, and the rest starts on a 16-byte destination boundary with the
+    same source shift in the next launch."""
+    sim = capped_copy
     sim.reset()
     A, H, nc, h = 4, 4, 5, 1
     c = orc.geometry(A, H, nc, 0, seg, A2A, BF16)["chunk"]
@@ -609,6 +632,8 @@ def test_copies_longer_than_a_launch_continue(capped, orc, seg, out_lead):
              parr(*[ptr(d) for d in dst]), None)
     tiles = -(-(c * 2) // 8192)
     assert sim.L.sim_launches() - L0 >= 12 * tiles // 5
+    if seg % 8 == 0 and out_lead == 0:
+        _tiling_used(sim, sim.long_copies)
     ref = orc.a2a_pack(2, A, seg, c, h, src)
     for d in range(A):
         assert np.array_equal(dst[d].view(np.uint8), ref[d])
