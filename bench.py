@@ -1111,9 +1111,11 @@ def _calib_lib():
     return lib
 
 
-def time_steps(step_fns, steps, warmup, stream):
+def time_steps(step_fns, steps, warmup, stream, host=False):
     """ms per step of K steps back to back (nothing between the launches),
-    after the warm-up steps; step_fns(i) gives step i's launches."""
+    after the warm-up steps; step_fns(i) gives step i's launches.  host=True
+    also returns the host's issue time per step in us (the loop that enqueues
+    the K steps, before the final synchronisation)."""
     import torch
     for i in range(warmup):
         for fn in step_fns(i):
@@ -1121,12 +1123,15 @@ def time_steps(step_fns, steps, warmup, stream):
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
+    h0 = time.perf_counter()
     for i in range(steps):
         for fn in step_fns(i):
             fn()
+    h1 = time.perf_counter()
     t1.record(stream)
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    ms = t0.elapsed_time(t1) / steps
+    return (ms, (h1 - h0) * 1e6 / steps) if host else ms
 
 
 def stand_in_step(calls, nsets, stream, pattern=0):
@@ -1300,9 +1305,11 @@ def step_sweep(args):
     """The step (one GPU's share and the whole group) and its plain-stream
     stand-in at each message size: K steps back to back, three buffer sets in
     turn while a step moves under 2 GB (one set above: a step then streams far
-    more than the 256 MB Infinity Cache holds), issued from Python and
-    replayed from HIP graphs.  Inputs are drawn on the device (timing only).
-    One JSON line per (size, variant)."""
+    more than the 256 MB Infinity Cache holds), issued from Python as one
+    prepared call (plan) per launch, as one plan per step (a single C call),
+    and replayed from HIP graphs; the host's issue time per step is recorded
+    beside the GPU's time per step.  Inputs are drawn on the device (timing
+    only).  One JSON line per (size, variant)."""
     import torch
     import pack_rr_helper_amd as rr
     rr.load()
@@ -1320,7 +1327,17 @@ def step_sweep(args):
             sets = [first] + [build_rows(inp, mode=variant) for _ in range(nsets - 1)]
             set_calls = [calls0] + [[c for wl in wls.values() for c in wl.calls(stream)] for wls in sets[1:]]
             steps = max(args.steps, 50)
-            relay_ms = time_steps(lambda i: [c[3] for c in set_calls[i % nsets]], steps, args.warmup, stream)
+            relay_ms, relay_host = time_steps(lambda i: [c[3] for c in set_calls[i % nsets]], steps, args.warmup,
+                                              stream, host=True)
+            # one plan per step: every call's recorded launches appended into one
+            # plan, issued with a single C call
+            step_plans = []
+            for sc in set_calls:
+                p = rr.Plan(sum(c[3].launches for c in sc))
+                with p:
+                    pass
+                step_plans.append(p.extend(*[c[3] for c in sc]))
+            plan_ms, plan_host = time_steps(lambda i: [step_plans[i % nsets]], steps, args.warmup, stream, host=True)
             st_sets, _, st_bytes = stand_in_step(calls0, nsets, stream)
             st_ms = time_steps(lambda i: st_sets[i % nsets], steps, args.warmup, stream)
             # the same steps replayed from HIP graphs (one per buffer set): no
@@ -1338,6 +1355,11 @@ def step_sweep(args):
                               "launches": len(calls0), "bytes_per_step": step_bytes,
                               "relay_ms_per_step": round(relay_ms, 5), "relay_gbs": round(rg, 1),
                               "relay_pct_of_peak": round(100 * rg / PEAK_GBS, 2),
+                              "relay_host_us_per_step": round(relay_host, 2),
+                              "step_plan_ms_per_step": round(plan_ms, 5),
+                              "step_plan_gbs": round(step_bytes / (plan_ms * 1e-3) / 1e9, 1),
+                              "step_plan_pct_of_peak": round(100 * step_bytes / (plan_ms * 1e-3) / 1e9 / PEAK_GBS, 2),
+                              "step_plan_host_us_per_step": round(plan_host, 2),
                               "stand_in_gbs": round(sg, 1), "stand_in_pct_of_peak": round(100 * sg / PEAK_GBS, 2),
                               "relay_over_stand_in": round(rg / sg, 4),
                               "graph_relay_gbs": round(rgg, 1), "graph_relay_pct_of_peak": round(100 * rgg / PEAK_GBS, 2),
@@ -1345,7 +1367,7 @@ def step_sweep(args):
                               "graph_relay_over_stand_in": round(rgg / sgg, 4)}), file=out, flush=True)
             torch.cuda.synchronize()
             del g_relay, g_st          # the graphs go before the buffers they write
-            del first, sets, set_calls, calls0, st_sets, relay_cs, st_cs
+            del first, sets, set_calls, calls0, st_sets, relay_cs, st_cs, step_plans
             torch.cuda.empty_cache()
         del inp
         torch.cuda.empty_cache()

@@ -49,6 +49,7 @@
 #ifndef RR_H
 #define RR_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -329,6 +330,53 @@ rr_status rr_phase_reduce_many(int coll, int dtype, int op,
                                const rr_helper_job *helperJobs, int nHelper,
                                const rr_active_job *activeJobs, int nActive,
                                void *stream);
+
+/*
+ * Plans -- validate once, launch many times.  For callers that issue the same
+ * relay steps on the same buffers over and over (a training or serving loop at
+ * small messages, where the host's per-call work -- argument checks, geometry,
+ * aliasing, segment tables -- would otherwise take longer than the kernels),
+ * every entry point above can be recorded into a plan and the plan re-issued
+ * with one call.  A plan is a HOST buffer owned by the caller; the library
+ * allocates nothing and keeps no pointer to it after rr_plan_end.
+ *
+ *   rr_plan_bytes(n): bytes a plan buffer needs to hold n kernel launches
+ *     (1 <= n <= RR_PLAN_MAX_LAUNCHES; 0 otherwise).  A call is one launch per
+ *     kernel body it uses (reductions: aligned and realigned items; copies:
+ *     one), or more when it exceeds a launch's segment table (40 reduction
+ *     items, 64 chunk moves) or 2^22 tiles.
+ *   rr_plan_begin(plan, bytes): starts recording on the calling thread into
+ *     `plan` (8-byte aligned, at least rr_plan_bytes(1) bytes).  Until
+ *     rr_plan_end, every entry point called on this thread validates its
+ *     arguments as usual (a rejected call records nothing and returns its
+ *     status) and appends its launches to the plan instead of enqueuing them;
+ *     their `stream` argument is ignored.  RR_EINVAL if this thread is already
+ *     recording.
+ *   rr_plan_end(&launches): stops recording; stores the number of recorded
+ *     launches if `launches` is not null.  RR_EINVAL if the thread is not
+ *     recording, or if a call ran out of records (that call returned RR_EINVAL
+ *     too); such a plan cannot be launched.
+ *   rr_plan_append(plan, bytes, other): appends the launches of the finished
+ *     plan `other` to the finished plan `plan` (whose buffer is `bytes` long),
+ *     so that one rr_plan_launch issues both in order -- for instance every
+ *     relay step of one phase or of one benchmark step.  RR_EINVAL, with
+ *     nothing changed, if either is not a finished, unbroken plan, if they are
+ *     the same buffer, or if `plan` lacks room.
+ *   rr_plan_launch(plan, stream): enqueues the recorded launches, in recording
+ *     order, on `stream`, with no validation: the device buffers named by the
+ *     recorded calls must still be allocated at the same addresses with the
+ *     same sizes.  RR_EINVAL for a buffer that is not a finished, unbroken
+ *     plan; RR_EHIP if a launch fails.  Launching is read-only on the plan, so
+ *     one plan may be launched from several threads (on streams that do not
+ *     write the same buffers concurrently), and the plan buffer may be copied.
+ */
+#define RR_PLAN_MAX_LAUNCHES 4096
+
+size_t rr_plan_bytes(int32_t max_launches);
+rr_status rr_plan_begin(void *plan, size_t bytes);
+rr_status rr_plan_end(int32_t *launches);
+rr_status rr_plan_append(void *plan, size_t bytes, const void *other);
+rr_status rr_plan_launch(const void *plan, void *stream);
 
 #ifdef __cplusplus
 }

@@ -10,16 +10,20 @@ contiguous, has the buffer dtype and is large enough -- and raises
 ``ValueError`` for a rejected argument and ``RuntimeError`` for a HIP failure
 or a missing library.  There is no CPU fallback.
 
-Every entry point also accepts ``prepare=True``: the checks and the ctypes
-marshalling then run once and a zero-argument callable is returned that only
-re-issues the C call (on the stream chosen at preparation; the tensors are
-kept alive by the callable).  The ``*_many`` forms take lists of per-group jobs
-and enqueue them together, typically as one kernel launch.
+Every entry point also accepts ``prepare=True``: the checks, the ctypes
+marshalling and the library's own validation and segment tables then run
+once, recorded into a plan (rr_plan_* in rr.h), and a zero-argument callable
+is returned that only re-issues the recorded launches (on the stream chosen at
+preparation; the tensors are kept alive by the callable).  ``Plan`` records
+several calls into one plan that is launched with a single C call.  The
+``*_many`` forms take lists of per-group jobs and enqueue them together,
+typically as one kernel launch.
 
 Pointer/layout semantics of each call are documented in include/rr.h.
 """
 import ctypes
 import os
+import threading
 from dataclasses import dataclass
 
 import torch
@@ -30,6 +34,7 @@ __all__ = [
     "rr_helper_reduce", "rr_active_add_scale", "rr_rs_multi_reduce", "rr_a2a_pack",
     "rr_a2a_unpack", "rr_helper_reduce_many", "rr_active_add_scale_many",
     "rr_rs_multi_reduce_many", "rr_a2a_pack_many", "rr_a2a_unpack_many", "rr_phase_reduce_many",
+    "Plan",
 ]
 
 F32, BF16 = 0, 1
@@ -129,6 +134,11 @@ def load():
         ("rr_a2a_unpack_many", ci, [ci, ctypes.POINTER(_A2AJob), ci, vp]),
         ("rr_phase_reduce_many", ci, [ci, ci, ci, ctypes.POINTER(_HelperJob), ci,
                                       ctypes.POINTER(_ActiveJob), ci, vp]),
+        ("rr_plan_bytes", ctypes.c_size_t, [i32]),
+        ("rr_plan_begin", ci, [vp, ctypes.c_size_t]),
+        ("rr_plan_end", ci, [ctypes.POINTER(i32)]),
+        ("rr_plan_append", ci, [vp, ctypes.c_size_t, vp]),
+        ("rr_plan_launch", ci, [vp, vp]),
     ]:
         f = getattr(L, name)
         f.restype, f.argtypes = res, args
@@ -220,16 +230,91 @@ def rr_passthrough_helper_size(count_g, A, num_chunks):
     return v
 
 
+_tls = threading.local()
+PLAN_MAX_LAUNCHES = 4096  # RR_PLAN_MAX_LAUNCHES
+
+
+class Plan:
+    """Relay calls validated once and re-issued together with one C call.
+
+    ``with Plan(n) as p:`` records every entry point called on this thread in
+    the block (each validates as usual; nothing is enqueued), then ``p()`` or
+    ``p.launch(stream)`` enqueues all recorded kernel launches in order, with
+    no checks: the tensors the recorded calls named are kept alive by the plan
+    and must keep their contents' meaning (same buffers, same sizes).  ``n``
+    bounds the launches the plan holds (rr_plan_bytes); the plan's memory is a
+    host buffer owned by this object."""
+
+    def __init__(self, max_launches=64):
+        nbytes = load().rr_plan_bytes(max_launches)
+        if nbytes == 0:
+            raise RRError(RR_EINVAL, f"a plan holds 1..{PLAN_MAX_LAUNCHES} launches, not {max_launches}")
+        self._buf = (ctypes.c_uint64 * ((nbytes + 7) // 8))()  # 8-byte aligned host memory
+        self._bytes = nbytes
+        self._keep = []
+        self.launches = None
+        self.stream = None
+
+    def __enter__(self):
+        if getattr(_tls, "plan", None) is not None:
+            raise RRError(RR_EINVAL, "this thread is already recording a plan")
+        _raise(load().rr_plan_begin(self._buf, self._bytes))
+        _tls.plan = self
+        return self
+
+    def __exit__(self, et, ev, tb):
+        _tls.plan = None
+        n = ctypes.c_int32()
+        st = load().rr_plan_end(ctypes.byref(n))
+        self.launches = n.value
+        if et is None:
+            _raise(st)
+        return False
+
+    def extend(self, *others):
+        """Append the launches of finished plans (or prepared calls) to this
+        finished plan, so that one launch issues them all in order."""
+        for o in others:
+            _raise(load().rr_plan_append(self._buf, self._bytes, o._buf))
+            self._keep.append(o._keep)
+            self.launches += o.launches
+        return self
+
+    def launch(self, stream=None):
+        """Enqueue the recorded launches on `stream` (default: the stream
+        chosen at preparation, else torch's current stream)."""
+        s = _stream(stream) if stream is not None or self.stream is None else self.stream
+        _raise(load().rr_plan_launch(self._buf, s))
+
+    __call__ = launch
+
+
 def _issue(fn, args, keep, prepare):
-    """Call the C entry point now, or return a callable that re-issues it."""
+    """Call the C entry point now (recording it if a Plan is being recorded on
+    this thread), or record it alone into a plan and return a callable that
+    re-issues its launches on the stream of the call (its last argument)."""
+    plan = getattr(_tls, "plan", None)
+    if plan is not None:
+        if prepare:
+            raise RRError(RR_EINVAL, "prepare=True inside a Plan recording")
+        _raise(fn(*args))
+        plan._keep.append(keep)
+        return None
     if not prepare:
         _raise(fn(*args))
         return None
-
-    def call():
+    # recorded once to count its launches, then into a plan of that size
+    scratch = getattr(_tls, "scratch", None)
+    if scratch is None:
+        scratch = _tls.scratch = Plan(PLAN_MAX_LAUNCHES)
+    with scratch:
         _raise(fn(*args))
-    call.keep = keep
-    return call
+    p = Plan(max(scratch.launches, 1))
+    with p:
+        _raise(fn(*args))
+    p.stream = args[-1]
+    p._keep.append(keep)
+    return p
 
 
 def _helper_need(relay, coll, dtype):

@@ -42,6 +42,71 @@ int64_t align_down_128(int64_t x) { return (x / 128) * 128; }
 uintptr_t addr(const void *p) { return reinterpret_cast<uintptr_t>(p); }
 
 // ---------------------------------------------------------------------------
+// Plans: between rr_plan_begin and rr_plan_end the launchers of this thread
+// append their batches to the caller's plan buffer instead of launching them.
+// ---------------------------------------------------------------------------
+
+thread_local rr::PlanHeader *g_plan = nullptr;
+
+rr::PlanRec *plan_records(rr::PlanHeader *h)
+{
+    return reinterpret_cast<rr::PlanRec *>(reinterpret_cast<char *>(h) + sizeof(rr::PlanHeader));
+}
+
+// A batch goes to the plan being recorded, or to the GPU.  A full plan is
+// marked broken and the call reports it (hipErrorOutOfMemory stands for "no
+// record left" inside this file).
+hipError_t emit_reduce(const rr::RedBatch &b, int64_t tiles, bool shifted, hipStream_t st)
+{
+    if (!g_plan)
+        return rr::launch_reduce(b, tiles, shifted, st);
+    if (g_plan->count >= g_plan->capacity) {
+        g_plan->broken = 1;
+        return hipErrorOutOfMemory;
+    }
+    rr::PlanRec &r = plan_records(g_plan)[g_plan->count++];
+    r.kind = rr::kPlanReduce;
+    r.shifted = shifted ? 1 : 0;
+    r.tiles = tiles;
+    r.red.nseg = b.nseg;
+    r.red.bf16 = b.bf16;
+    for (int i = 0; i < b.nseg; ++i) {
+        r.red.tile0[i] = b.tile0[i];
+        r.red.seg[i] = b.seg[i];
+    }
+    return hipSuccess;
+}
+
+hipError_t emit_copy(const rr::CopyBatch &b, int64_t tiles, bool shifted, hipStream_t st)
+{
+    if (!g_plan)
+        return rr::launch_copy(b, tiles, shifted, st);
+    if (g_plan->count >= g_plan->capacity) {
+        g_plan->broken = 1;
+        return hipErrorOutOfMemory;
+    }
+    rr::PlanRec &r = plan_records(g_plan)[g_plan->count++];
+    r.kind = rr::kPlanCopy;
+    r.shifted = shifted ? 1 : 0;
+    r.tiles = tiles;
+    r.copy.nseg = b.nseg;
+    r.copy.long_tiles = b.long_tiles;
+    for (int i = 0; i < b.nseg; ++i) {
+        r.copy.tile0[i] = b.tile0[i];
+        r.copy.seg[i] = b.seg[i];
+    }
+    return hipSuccess;
+}
+
+rr_status launch_failed(hipError_t e)
+{
+    if (e == hipErrorOutOfMemory && g_plan)
+        return fail(RR_EINVAL, "the plan buffer holds %d launches and this call needs more; the plan is "
+                    "unusable (record it again into a larger buffer)", g_plan->capacity);
+    return fail(RR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
 // Geometry (pull request summary sections 1, 4 and 6; zero-chunk fallback)
 // ---------------------------------------------------------------------------
 
@@ -322,7 +387,7 @@ private:
     {
         if (q.b.nseg == 0)
             return;
-        const hipError_t e = rr::launch_reduce(q.b, q.tiles, q.shifted, st_);
+        const hipError_t e = emit_reduce(q.b, q.tiles, q.shifted, st_);
         if (e != hipSuccess && err_ == hipSuccess)
             err_ = e;
         q.b.nseg = 0;
@@ -349,7 +414,7 @@ rr_status run_reduce(const std::vector<RedItem> &items, int dtype, void *stream,
         L.add(it, es);
     const hipError_t e = L.finish();
     if (e != hipSuccess)
-        return fail(RR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+        return launch_failed(e);
     return ok();
 }
 
@@ -656,7 +721,7 @@ private:
     {
         if (b_.nseg == 0)
             return;
-        const hipError_t e = rr::launch_copy(b_, tiles_, shifted_, st_);
+        const hipError_t e = emit_copy(b_, tiles_, shifted_, st_);
         if (e != hipSuccess && err_ == hipSuccess)
             err_ = e;
         b_.nseg = 0;
@@ -687,7 +752,7 @@ rr_status run_copy(const std::vector<Move> &mv, void *stream, bool batch)
         L.add(m.src, m.dst, m.nbytes);
     const hipError_t e = L.finish();
     if (e != hipSuccess)
-        return fail(RR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+        return launch_failed(e);
     return ok();
 }
 
@@ -984,6 +1049,116 @@ rr_status rr_a2a_pack_many(int dtype, const rr_a2a_job *jobs, int nJobs, void *s
 rr_status rr_a2a_unpack_many(int dtype, const rr_a2a_job *jobs, int nJobs, void *stream)
 {
     return a2a_many(dtype, jobs, nJobs, true, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Plans
+// ---------------------------------------------------------------------------
+
+size_t rr_plan_bytes(int32_t max_launches)
+{
+    if (max_launches < 1 || max_launches > RR_PLAN_MAX_LAUNCHES)
+        return 0;
+    return sizeof(rr::PlanHeader) + size_t(max_launches) * sizeof(rr::PlanRec);
+}
+
+rr_status rr_plan_begin(void *plan, size_t bytes)
+{
+    if (g_plan)
+        return fail(RR_EINVAL, "this thread is already recording a plan");
+    if (!plan)
+        return fail(RR_EINVAL, "plan buffer is null");
+    if (addr(plan) % alignof(rr::PlanRec) != 0)
+        return fail(RR_EINVAL, "plan buffer is not %zu-byte aligned", alignof(rr::PlanRec));
+    if (bytes < rr_plan_bytes(1))
+        return fail(RR_EINVAL, "plan buffer of %zu bytes holds no launch (rr_plan_bytes(1) = %zu)", bytes,
+                    rr_plan_bytes(1));
+    auto *h = static_cast<rr::PlanHeader *>(plan);
+    const size_t cap = (bytes - sizeof(rr::PlanHeader)) / sizeof(rr::PlanRec);
+    h->magic = rr::kPlanMagic;
+    h->capacity = int32_t(std::min<size_t>(cap, RR_PLAN_MAX_LAUNCHES));
+    h->count = 0;
+    h->recording = 1;
+    h->broken = 0;
+    g_plan = h;
+    return ok();
+}
+
+rr_status rr_plan_end(int32_t *launches)
+{
+    if (!g_plan)
+        return fail(RR_EINVAL, "this thread is not recording a plan");
+    rr::PlanHeader *h = g_plan;
+    g_plan = nullptr;
+    h->recording = 0;
+    if (launches)
+        *launches = h->count;
+    if (h->broken)
+        return fail(RR_EINVAL, "a call ran out of plan records; the plan is unusable");
+    return ok();
+}
+
+namespace {
+
+// A finished, unbroken plan (RR_OK) or the reason it is not one.
+rr_status check_plan(const void *plan, const char *what)
+{
+    if (!plan)
+        return fail(RR_EINVAL, "%s is null", what);
+    if (addr(plan) % alignof(rr::PlanRec) != 0)
+        return fail(RR_EINVAL, "%s buffer is not %zu-byte aligned", what, alignof(rr::PlanRec));
+    const auto *h = static_cast<const rr::PlanHeader *>(plan);
+    if (h->magic != rr::kPlanMagic)
+        return fail(RR_EINVAL, "%s is not a plan (record one with rr_plan_begin/rr_plan_end)", what);
+    if (h->recording)
+        return fail(RR_EINVAL, "%s is still being recorded", what);
+    if (h->broken)
+        return fail(RR_EINVAL, "%s ran out of records while it was recorded and is unusable", what);
+    return RR_OK;
+}
+
+}  // namespace
+
+rr_status rr_plan_append(void *plan, size_t bytes, const void *other)
+{
+    rr_status st = check_plan(plan, "plan");
+    if (st == RR_OK)
+        st = check_plan(other, "appended plan");
+    if (st != RR_OK)
+        return st;
+    auto *h = static_cast<rr::PlanHeader *>(plan);
+    const auto *o = static_cast<const rr::PlanHeader *>(other);
+    const size_t room = bytes >= sizeof(rr::PlanHeader) ? (bytes - sizeof(rr::PlanHeader)) / sizeof(rr::PlanRec) : 0;
+    const int64_t cap = std::min<int64_t>(std::min<int64_t>(h->capacity, int64_t(room)), RR_PLAN_MAX_LAUNCHES);
+    if (int64_t(h->count) + o->count > cap)
+        return fail(RR_EINVAL, "the plan holds %lld launches; it has %d and the appended plan %d",
+                    (long long)cap, h->count, o->count);
+    if (plan == other)
+        return fail(RR_EINVAL, "a plan cannot be appended to itself");
+    const auto *src = reinterpret_cast<const rr::PlanRec *>(reinterpret_cast<const char *>(o) +
+                                                            sizeof(rr::PlanHeader));
+    memcpy(plan_records(h) + h->count, src, size_t(o->count) * sizeof(rr::PlanRec));
+    h->count += o->count;
+    return ok();
+}
+
+rr_status rr_plan_launch(const void *plan, void *stream)
+{
+    const rr_status chk = check_plan(plan, "plan");
+    if (chk != RR_OK)
+        return chk;
+    const auto *h = static_cast<const rr::PlanHeader *>(plan);
+    const auto *rec = reinterpret_cast<const rr::PlanRec *>(reinterpret_cast<const char *>(h) +
+                                                            sizeof(rr::PlanHeader));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int i = 0; i < h->count; ++i) {
+        const rr::PlanRec &r = rec[i];
+        const hipError_t e = r.kind == rr::kPlanReduce ? rr::launch_reduce(r.red, r.tiles, r.shifted != 0, st)
+                                                       : rr::launch_copy(r.copy, r.tiles, r.shifted != 0, st);
+        if (e != hipSuccess)
+            return fail(RR_EHIP, "kernel launch %d of the plan failed: %s", i, hipGetErrorString(e));
+    }
+    return ok();
 }
 
 }  // extern "C"

@@ -309,6 +309,29 @@ struct LaunchShape {
     int32_t form;
     int64_t gx, gy;
 };
+// One recorded launch of a plan (rr_plan_begin .. rr_plan_launch): the batch
+// as the launcher built it, and how it is launched.
+enum PlanKind : int32_t { kPlanReduce = 1, kPlanCopy = 2 };
+struct PlanRec {
+    int32_t kind;
+    int32_t shifted;
+    int64_t tiles;
+    union {
+        RedBatch red;
+        CopyBatch copy;
+    };
+};
+
+// Header of a plan buffer, followed by `capacity` PlanRec records.
+constexpr uint64_t kPlanMagic = 0x3150524c4559414cull;  // a tag for caller-owned plan memory
+struct PlanHeader {
+    uint64_t magic;
+    int32_t capacity;   // records the buffer holds
+    int32_t count;      // records written
+    int32_t recording;  // 1 between rr_plan_begin and rr_plan_end
+    int32_t broken;     // a call ran out of records; the plan cannot be launched
+};
+
 // Host-side choice of the form for a filled batch (rr_api.cpp).
 LaunchShape reduce_shape(const RedBatch &b, int64_t total_tiles);
 LaunchShape copy_shape(const CopyBatch &b, int64_t total_tiles);

@@ -126,6 +126,16 @@ static int host_checks(void)
           "null job array accepted");
     CHECK(rr_phase_reduce_many(RR_ALLREDUCE, RR_BF16, RR_SUM, NULL, 0, NULL, 1, NULL) == RR_EINVAL,
           "null active job array accepted");
+    /* plans: sizes, and misuse rejected before anything runs */
+    CHECK(rr_plan_bytes(0) == 0 && rr_plan_bytes(RR_PLAN_MAX_LAUNCHES + 1) == 0 &&
+              rr_plan_bytes(2) > rr_plan_bytes(1), "plan sizes");
+    CHECK(rr_plan_end(NULL) == RR_EINVAL, "plan end without a recording accepted");
+    CHECK(rr_plan_launch(NULL, NULL) == RR_EINVAL, "null plan launched");
+    {
+        uint64_t small[4] = {0, 0, 0, 0};
+        CHECK(rr_plan_begin(small, sizeof small) == RR_EINVAL, "plan buffer without room accepted");
+        CHECK(rr_plan_launch(small, NULL) == RR_EINVAL, "a buffer that is no plan launched");
+    }
     CHECK(rr_phase_reduce_many(RR_ALLREDUCE, RR_BF16, RR_SUM, NULL, 0, NULL, 0, NULL) == RR_OK,
           "empty phase call rejected: %s", rr_last_error());
     return 0;
@@ -259,9 +269,26 @@ static int gpu_a2a(hipStream_t st)
         uj[h].in = uin[h];
         uj[h].out = uout[h];
     }
+    /* both calls recorded into one caller-owned plan (validated once), then
+       launched with a single call */
+    const size_t plan_bytes = rr_plan_bytes(8);
+    void *plan = malloc(plan_bytes);
+    int32_t launches = -1;
+    CHECK(plan != NULL && plan_bytes > 0, "plan allocation");
+    CHECK(rr_plan_begin(plan, plan_bytes) == RR_OK, "%s", rr_last_error());
     CHECK(rr_a2a_pack_many(RR_BF16, pj, H, st) == RR_OK, "%s", rr_last_error());
     CHECK(rr_a2a_unpack_many(RR_BF16, uj, H, st) == RR_OK, "%s", rr_last_error());
+    CHECK(rr_plan_end(&launches) == RR_OK && launches == 2, "plan end: %d launches, %s", launches,
+          rr_last_error());
     HIP(hipStreamSynchronize(st));
+    for (int d = 0; d < A; ++d) {  /* recording enqueued nothing */
+        HIP(hipMemcpy(hout[d], dout[d], full, hipMemcpyDeviceToHost));
+        if (same(hout[d], ref_out[d], full, "all-to-all output before the plan is launched"))
+            return 1;
+    }
+    CHECK(rr_plan_launch(plan, st) == RR_OK, "%s", rr_last_error());
+    HIP(hipStreamSynchronize(st));
+    free(plan);
 
     const void *srcs[A] = {hs[0], hs[1], hs[2], hs[3]};
     void *pks[A] = {ref_pk[0], ref_pk[1], ref_pk[2], ref_pk[3]};
@@ -289,7 +316,7 @@ static int gpu_a2a(hipStream_t st)
         for (int d = 0; d < A; ++d)
             HIP(hipFree(dpk[h][d]));
     free(got);
-    printf("A=4 all-to-all pack + unpack, segmentCount %" PRId64 ": bit-exact\n", seg);
+    printf("A=4 all-to-all pack + unpack, segmentCount %" PRId64 ", one recorded plan: bit-exact\n", seg);
     return 0;
 }
 

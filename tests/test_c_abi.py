@@ -39,6 +39,7 @@ def test_c_program_host_checks(example):
 def test_c_program_gpu_parity(example):
     rc, out = run(example, "gpu", 120)
     assert rc == 0, out
-    for what in ("A=2 allreduce helpers", "A=4 reduce-scatter pass 1", "all-to-all pack + unpack"):
+    for what in ("A=2 allreduce helpers", "A=4 reduce-scatter pass 1", "all-to-all pack + unpack",
+                 "one recorded plan"):
         assert what in out and "bit-exact" in out, out
     assert "gpu checks passed" in out

@@ -891,3 +891,55 @@ def test_copy_batches_at_the_segment_table_sizes(orc, nslices, ragged):
         ref = orc.a2a_pack(2, A, seg, c, h, src)
         for d in range(A):
             assert np.array_equal(host(packed[h][d]).view(np.uint8), ref[d]), f"slice {h} dest {d}"
+
+
+# --------------------------------------------------------------------------
+# plans: validated once, launched many times
+# --------------------------------------------------------------------------
+
+def test_plan_records_calls_and_launches_them_later(orc):
+    """Three calls recorded into one rr.Plan (an A=2 reduce-scatter owner, a
+    batched A=2 allreduce helper call over three groups, an all-to-all pack)
+    enqueue nothing while they are recorded; the launched plan writes the
+    oracle's bytes, and launched again after the inputs change in place it
+    writes the new result."""
+    R = 2 ** 20 + 8 * 128 * 3 + 5
+    count = 2 ** 20
+    c = count // 8
+    seg = 5 * 128 * 4096 + 3
+    say("plan", R, count, seg)
+    xs = [dev(synth.as_bf16_bits(synth.normal(R, 80, a))) for a in range(2)]
+    ss = [dev(synth.as_bf16_bits(synth.normal(count, 81, a))) for a in range(2)]
+    src_h = [synth.bits16(4 * seg, 82, s) for s in range(4)]
+    src = [synth.to_device(h, None) for h in src_h]
+    ac = orc.geometry(4, 4, 5, 0, seg, A2A, BF16)["chunk"]
+    out = torch.zeros(R, dtype=torch.bfloat16, device="cuda")
+    hout = [torch.zeros(c, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    dst = [torch.zeros(3 * ac, dtype=torch.int16, device="cuda") for _ in range(4)]
+    relay2, relay4 = rr.Relay(2, 6, 8, 0, count), rr.Relay(4, 4, 5, 0, seg)
+    plan = rr.Plan(16)
+    with plan:
+        rr.rr_active_add_scale(rr.Relay(2, 6, 8, 0, R), RS, BF16, AVG, 0, xs, out)
+        rr.rr_helper_reduce_many(AR, BF16, SUM, [(relay2, h, [s[h * c:(h + 1) * c] for s in ss], hout[h])
+                                                 for h in range(3)])
+        rr.rr_a2a_pack(relay4, BF16, 1, src, dst)
+    assert plan.launches == 3
+    torch.cuda.synchronize()
+    assert not out.any() and not any(h.any() for h in hout) and not any(d.any() for d in dst)
+
+    def check(tag):
+        xh, sh = [host(x) for x in xs], [host(s) for s in ss]
+        check_bf16(host(out), orc.rs2_active(BF16, AVG, xh[0], xh[1]), f"plan {tag}: reduce-scatter owner")
+        for h in range(3):
+            ref = orc.ar2_helper(BF16, SUM, sh[0][h * c:(h + 1) * c].copy(), sh[1][h * c:(h + 1) * c].copy())
+            check_bf16(host(hout[h]), ref, f"plan {tag}: helper {h}")
+        ref = orc.a2a_pack(2, 4, seg, ac, 1, [host(s) for s in src])
+        for d in range(4):
+            assert np.array_equal(host(dst[d]).view(np.uint8), ref[d]), f"plan {tag}: pack destination {d}"
+
+    plan()
+    check("first launch")
+    for t in xs + ss + src:
+        t.copy_(torch.roll(t, 11))
+    plan.launch(torch.cuda.current_stream())
+    check("after new inputs")
