@@ -1106,6 +1106,7 @@ def _calib_lib():
     lib.calib_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), vp,
                                  ctypes.c_int64, vp]
     lib.calib_stream_pattern.argtypes = [ctypes.c_int] + lib.calib_stream.argtypes
+    lib.calib_fixed.argtypes = [ctypes.c_int, ctypes.c_int64, vp, vp, vp]
     if lib.calib_patterns() != len(CALIB_PATTERNS):
         raise RuntimeError(f"{path} has {lib.calib_patterns()} patterns; rebuild it")
     return lib
@@ -1378,6 +1379,7 @@ def step_sweep(args):
 # --------------------------------------------------------------------------
 
 RELAY_KERNEL = re.compile(r"rr::\(anonymous namespace\)::(reduce|copy)\w*kernel")
+FIXED_KERNEL = re.compile(r"(empty_kernel|touch_kernel)")  # bench_calib.hip's fixed-cost kernels
 EVICT_KERNEL = re.compile(r"at::native::.*reduce_kernel")  # cache_evictor("read"): torch.sum
 
 
@@ -1467,6 +1469,18 @@ def role_fit(args):
     tiny_fn = rr.rr_helper_reduce(relay, rr.ALLREDUCE, rr.BF16, rr.SUM, 0, [t[:128] for t in tiny], tiny_out,
                                   prepare=True)
     run("one_tile", 0.0, 3 * 128 * 2, tiny_fn)
+    # a launch's fixed cost apart from the relay kernels: workgroups that touch
+    # no memory, or load or store one 16-byte vector per lane (bench_calib.hip)
+    lib = _calib_lib()
+    buf = torch.empty(2048 * 4096, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    for kind, name in ((0, "empty"), (1, "load_only"), (2, "store_only")):
+        for blocks in (1, 2048):
+            def fixed(kind=kind, blocks=blocks):
+                if lib.calib_fixed(kind, blocks, ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(sink.data_ptr()),
+                                   sp) != 0:
+                    raise RuntimeError("calib_fixed failed")
+            run(f"{name}_{blocks}wg", 0.0, 0 if kind == 0 else blocks * 4096, fixed)
     print(f"[fit] one-tile launch: {statistics.median(samples['one_tile'][0.0][1]) * 1e6:.2f} us (event pair)",
           file=sys.stderr, flush=True)
     for mib in [float(v) for v in args.fit_sizes.split(",")]:
@@ -1487,7 +1501,7 @@ def role_fit(args):
     if args.fit_log:
         with open(args.fit_log, "w") as fh:
             json.dump({"variant": mode_of(args), "launches": log}, fh)
-    by_role = {r: v for r, v in samples.items() if r != "one_tile"}
+    by_role = {r: v for r, v in samples.items() if r != "one_tile" and not r.endswith("wg")}
     print(json.dumps({"role_fit": True, "timing": "fence-free HIP event pair per launch (adds ~1.2 us)",
                       "variant": mode_of(args), "reps": args.fit_reps,
                       "one_tile_us": round(statistics.median(samples["one_tile"][0.0][1]) * 1e6, 3),
@@ -1505,7 +1519,8 @@ def fit_from_trace(args):
         rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Dispatch_Id"]))
     # every timed launch directly follows the cache-clearing read (a torch sum);
     # relay launches made while a workload stages its inputs do not
-    relay = [r for prev, r in zip(rows, rows[1:]) if RELAY_KERNEL.search(r["Kernel_Name"])
+    relay = [r for prev, r in zip(rows, rows[1:])
+             if (RELAY_KERNEL.search(r["Kernel_Name"]) or FIXED_KERNEL.search(r["Kernel_Name"]))
              and EVICT_KERNEL.search(prev["Kernel_Name"])]
     launches = log["launches"]
     if len(relay) != len(launches):
@@ -1519,13 +1534,20 @@ def fit_from_trace(args):
         kernels.setdefault(l["role"], set()).add(re.sub(r"^void rr::\(anonymous namespace\)::", "",
                                                         r["Kernel_Name"]).split("(")[0])
     tiny = samples.pop("one_tile", {})
+    fixed = {r: statistics.median(samples.pop(r)[0.0][1]) * 1e6 for r in list(samples) if r.endswith("wg")}
     fit = fit_table(samples)
     if args.sweep_out:
         with open(args.sweep_out, "w") as fh:
             json.dump({"variant": log["variant"], "one_tile_us": round(statistics.median(tiny[0.0][1]) * 1e6, 3)
-                       if tiny else None, "roles": fit}, fh)
+                       if tiny else None, "fixed_us": {k: round(v, 3) for k, v in fixed.items()}, "roles": fit}, fh)
     print(f"one-tile reduction launch (kernel duration, median): "
           f"{statistics.median(tiny[0.0][1]) * 1e6:.2f} us\n" if tiny else "")
+    if fixed:
+        print("| fixed-cost kernel | kernel us (median) |")
+        print("|---|---:|")
+        for name, us in fixed.items():
+            print(f"| {name} | {us:.2f} |")
+        print()
     print("| role | kernel | t0 us | BW GB/s | BW % of peak | r^2 | " +
           " | ".join(f"{m:g} MiB us (% peak)" for m in fit[0]["sizes_mib"]) + " |")
     print("|---|---|---:|---:|---:|---:|" + "---:|" * len(fit[0]["sizes_mib"]))
