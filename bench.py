@@ -105,6 +105,9 @@ def parse():
     p.add_argument("--traffic-from", default=None,
                    help="FETCH_CSV,WRITE_CSV: rocprofv3 --pmc passes of a --calibrate-copy-mib run; with "
                         "--traffic-bench, record that run's HBM bytes per launch in profiles/traffic.json")
+    p.add_argument("--trace-summary", default=None,
+                   help="KERNEL_TRACE_CSV: with --traffic-bench naming the JSON line of the traced run, print "
+                        "per-family kernel averages and the last step launch by launch")
     p.add_argument("--traffic-bench", default=None,
                    help="the JSON line bench.py printed in the FETCH_SIZE pass of --traffic-from")
     p.add_argument("--no-other-variants", action="store_true",
@@ -510,6 +513,47 @@ def kernel_family(name):
     if m.group(1) == "copy":
         return "copy"
     return "reduce<bf16>" if "<true" in name else "reduce<f32>"
+
+
+def trace_summary(args):
+    """Per kernel family, the call-weighted average duration of every relay
+    dispatch in a rocprofv3 kernel trace of a bench.py run, and the run's last
+    step launch by launch (its launch order from the run's JSON line), as
+    markdown."""
+    import csv
+    with open(args.traffic_bench) as fh:
+        run = json.loads(fh.read().strip().splitlines()[-1])
+    cfg = run["config"]
+    order, algo = cfg["launch_order"], cfg["rows_bytes_per_launch"]
+    with open(args.trace_summary) as fh:
+        rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Dispatch_Id"]))
+    relay = [r for r in rows if RELAY_KERNEL.search(r["Kernel_Name"])]
+    fam = {}
+    for r in relay:
+        f = fam.setdefault(kernel_family(r["Kernel_Name"]), [0, 0.0])
+        f[0] += 1
+        f[1] += (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+    print("| family | relay dispatches | avg us |")
+    print("|---|---:|---:|")
+    for k, (n, us) in fam.items():
+        print(f"| `{k}` | {n} | {us / n:.3f} |")
+    rl = run["roofline"]
+    print(f"\nbench.py's roofline kernel in the same run: `{rl['kernel']}`, {rl['avg_launch_us']} us per launch "
+          f"(timing-only event intervals of {rl['avg_event_interval_us']} us less {rl['event_cost_us_per_launch']} us)\n")
+    last = relay[-len(order):]
+    print("| launch | kernel | workgroups | duration us | algorithmic MB | GB/s | % of 8 TB/s |")
+    print("|---|---|---:|---:|---:|---:|---:|")
+    tot_us = tot_b = 0.0
+    for row, r in zip(order, last):
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+        wg = (int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])) // int(r["Workgroup_Size_X"])
+        name = re.sub(r"^void rr::\(anonymous namespace\)::", "", r["Kernel_Name"]).split("(")[0]
+        b = algo[row]
+        tot_us += us
+        tot_b += b
+        print(f"| {row} | `{name}` | {wg} | {us:.2f} | {b / 1e6:.1f} | {b / us / 1e3:.0f} | {100 * b / us / 1e3 / PEAK_GBS:.1f} |")
+    print(f"| **step (kernels only)** | | | {tot_us:.2f} | {tot_b / 1e6:.1f} | {tot_b / tot_us / 1e3:.0f} | "
+          f"{100 * tot_b / tot_us / 1e3 / PEAK_GBS:.1f} |")
 
 
 def traffic_from(args):
@@ -1572,7 +1616,9 @@ def main():
         print(f"bench.py measures one GPU: the library has no multi-GPU path (--gpus {args.gpus} "
               "requested). The relay's local kernels shard per rank; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    if args.traffic_from:
+    if args.trace_summary:
+        trace_summary(args)
+    elif args.traffic_from:
         traffic_from(args)
     elif args.fit_trace:
         fit_from_trace(args)
