@@ -105,6 +105,11 @@ def parse():
     p.add_argument("--traffic-from", default=None,
                    help="FETCH_CSV,WRITE_CSV: rocprofv3 --pmc passes of a --calibrate-copy-mib run; with "
                         "--traffic-bench, record that run's HBM bytes per launch in profiles/traffic.json")
+    p.add_argument("--sweep-summary", default=None,
+                   help="JSONL of a --sweep run: print its tables (GB/s, %% of peak, best, relay / fastest stand-in, "
+                        "oracle rates) as markdown")
+    p.add_argument("--ragged-a2a", action="store_true",
+                   help="the step's all-to-all with segmentCount = 5 mod 8 (its chunk moves realigned)")
     p.add_argument("--trace-summary", default=None,
                    help="KERNEL_TRACE_CSV: with --traffic-bench naming the JSON line of the traced run, print "
                         "per-family kernel averages and the last step launch by launch")
@@ -126,6 +131,8 @@ def parse():
                    help="time the step beside a stand-in step of plain streams with the same mixes and bytes")
     p.add_argument("--calibrate-sizes", default="256,1024", help="MiB per stream")
     p.add_argument("--calibrate-out", default=None)
+    p.add_argument("--calibrate-alone", action="store_true",
+                   help="--calibrate: time each launch alone after a 1 GiB read instead of back to back")
     p.add_argument("--sweep-sizes", default="2,4,8,16,32,64,128,256,512,1024")
     p.add_argument("--sweep-reps", type=int, default=20)
     p.add_argument("--sweep-dtypes", default="bf16,f32")
@@ -133,7 +140,7 @@ def parse():
                    help="rows of the per-role sweep; the _shifted rows put every input at an odd "
                         "element offset (the realigning reduction kernels)")
     p.add_argument("--flush", choices=("read", "write", "none"), default="read",
-                   help="how the sweep and calibration evict inputs from the caches before each rep")
+                   help="--calibrate-alone: how a launch's inputs are pushed out of the caches before it is timed")
     p.add_argument("--sweep-out", default=None)
     p.add_argument("--role-fit", action="store_true",
                    help="time every launch of the step alone at --fit-sizes messages (1x to 8x a 64 MiB "
@@ -472,27 +479,36 @@ def kernel_source_digest():
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def workload_name(message_mib, dtype="bf16", ragged_a2a=False):
+    """The benchmark step's workload, as its JSON line and its counter entries name it."""
+    return (f"relay hot path, {message_mib:g} MiB per-rank {dtype} message: A=2 allreduce (H=6) + A=2 "
+            "reduce-scatter + A=4 allreduce (H=4, 500 permille) + A=4 reduce-scatter + A=4 all-to-all "
+            "pack/unpack" + (" (segmentCount = 5 mod 8)" if ragged_a2a else "") + ", one GPU")
+
+
 def traffic_for(kernel, message_mib, variant, algo_bytes_per_launch, launches_per_step, dtype="bf16",
-                path=TRAFFIC_JSON):
+                path=TRAFFIC_JSON, workload=None):
     """HBM bytes per launch of `kernel` (counter-measured, scaled by a plain
     copy of known size) from profiles/traffic.json, or None if absent, taken
-    on another workload or launch sequence (other message, variant or dtype,
-    other launches per step, or other algorithmic bytes per launch), or taken
-    on other kernel sources."""
+    on another workload or launch sequence (other message, variant, dtype or
+    workload, other launches per step, or other algorithmic bytes per launch),
+    or taken on other kernel sources.  workload: the step's workload_name
+    (default: the plain step's)."""
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         t = json.load(fh)
     if t.get("kernel_source_digest") != kernel_source_digest():
         return None
+    workload = workload or workload_name(message_mib, dtype)
     for e in t.get("entries", []):
-        if e.get("message_mib") != message_mib or e.get("variant") != variant or e.get("dtype") != dtype:
+        if e.get("message_mib") != message_mib or e.get("variant") != variant or e.get("dtype") != dtype \
+                or e.get("workload", workload) != workload:
             continue
         k = e.get("kernels", {}).get(kernel)
-        if not k or k.get("algorithmic_bytes_per_launch") != algo_bytes_per_launch \
-                or k.get("launches_per_step") != launches_per_step:
-            return None
-        return k.get("hbm_bytes_per_launch")
+        if k and k.get("algorithmic_bytes_per_launch") == algo_bytes_per_launch \
+                and k.get("launches_per_step") == launches_per_step:
+            return k.get("hbm_bytes_per_launch")
     return None
 
 
@@ -513,6 +529,67 @@ def kernel_family(name):
     if m.group(1) == "copy":
         return "copy"
     return "reduce<bf16>" if "<true" in name else "reduce<f32>"
+
+
+SWEEP_ORDER = ["ar2_active", "ar2_helper", "rs2_owner", "ar4_active", "ar4_helper", "ar4_phase", "rs4_pass1",
+               "rs4_pass2", "a2a_pack", "a2a_unpack", "a2a_pack_ragged", "a2a_unpack_ragged", "rs2_owner_shifted",
+               "ar4_active_shifted", "ar4_helper_shifted", "torch_copy_calibration"]
+
+
+def sweep_summary(args):
+    """Markdown tables of a --sweep JSONL: per dtype, GB/s and % of peak
+    (median), GB/s (best), relay / fastest plain-stream stand-in (and the
+    pattern that was fastest), and the CPU oracle's rates."""
+    recs = [json.loads(l) for l in open(args.sweep_summary)]
+    sizes = sorted({r["message_mib"] for r in recs})
+
+    def table(vals, cols, fmt, roles, unit="MiB"):
+        out = ["| role | " + " | ".join(f"{c:g} {unit}" for c in cols) + " |", "|---|" + "---:|" * len(cols)]
+        for role in roles:
+            cells = ["" if vals.get((role, c)) is None else fmt(vals[(role, c)]) for c in cols]
+            if any(cells):
+                out.append(f"| {role} | " + " | ".join(cells) + " |")
+        return out
+
+    out = []
+    for dt in ("bf16", "f32"):
+        g = {(r["row"], r["message_mib"]): r for r in recs if r["dtype"] in (dt, "u8")}
+        if not any(r["dtype"] == dt for r in recs):
+            continue
+        for title, key, fmt in (("GB/s, median", "gbs_median", lambda v: f"{v:.0f}"),
+                                ("percent of 8 TB/s, median", "pct_peak_median", lambda v: f"{v:.1f}"),
+                                ("GB/s, best of the reps", "gbs_best", lambda v: f"{v:.0f}")):
+            out += [f"## {dt}: {title}", ""] + table({k: r[key] for k, r in g.items()}, sizes, fmt, SWEEP_ORDER) + [""]
+        st = {k: r["stand_in"] for k, r in g.items() if r.get("stand_in")}
+        out += [f"## {dt}: relay launch / fastest plain-stream stand-in of the same read/write mix and bytes (median)",
+                ""] + table({k: v["relay_over_stand_in"] for k, v in st.items()}, sizes, lambda v: f"{v:.2f}",
+                            SWEEP_ORDER) + [""]
+        out += [f"## {dt}: fastest stand-in pattern", ""] + table({k: v.get("pattern", "relay") for k, v in st.items()},
+                                                                  sizes, str, SWEEP_ORDER) + [""]
+        # write-back stores timed alone end with written lines still in the
+        # Infinity Cache; the non-temporal patterns have no such deferral
+        nt = {}
+        for k, v in st.items():
+            pats = {p: g for p, g in v.get("patterns", {}).items() if not p.endswith("_wb")}
+            if pats:
+                nt[k] = g_row[k] / max(pats.values()) if (g_row := {kk: r["gbs_median"] for kk, r in g.items()}) else None
+        out += [f"## {dt}: relay launch / fastest non-temporal stand-in (median)", ""] + table(
+            nt, sizes, lambda v: f"{v:.2f}", SWEEP_ORDER) + [""]
+        orc = {k: r for k, r in g.items() if r.get("oracle")}
+        if orc:
+            samples = sorted({r["oracle"]["sample_mib"] for r in orc.values()})
+            thr = next(iter(orc.values()))["oracle"]["threads"]
+            ofmt = lambda v: f"{v:.2f}" if v < 100 else f"{v:.1f}"
+            out += [f"## {dt}: CPU oracle GB/s on {thr} threads (by sample message)", ""] + table(
+                {(k[0], r["oracle"]["sample_mib"]): r["oracle"]["gbs"] for k, r in orc.items()}, samples, ofmt,
+                SWEEP_ORDER) + [""]
+            out += [f"## {dt}: CPU oracle GB/s on one thread (by sample message)", ""] + table(
+                {(k[0], r["oracle"]["sample_mib"]): r["oracle"]["gbs_1t"] for k, r in orc.items()}, samples, ofmt,
+                SWEEP_ORDER) + [""]
+            out += [f"## {dt}: GPU / oracle ({thr} threads), median", ""] + table(
+                {k: r["oracle"]["gpu_over_oracle"] for k, r in orc.items()}, sizes, lambda v: f"{v:.0f}",
+                SWEEP_ORDER) + [""]
+    print("\n".join(out).rstrip())
 
 
 def trace_summary(args):
@@ -605,6 +682,7 @@ def traffic_from(args):
         f[1] += algo[row]
         f[2] += 1
     entry = {"message_mib": run["config"]["message_bytes"] / MIB, "variant": cfg["variant"], "dtype": run["dtype"],
+             "workload": cfg["workload"],
              "fetch_scale": fscale, "write_scale": wscale,
              "kernels": {k: {"hbm_bytes_per_launch": round(v[0] / v[2]), "algorithmic_bytes_per_launch": v[1] // v[2],
                              "launches_per_step": v[2]} for k, v in fam.items()},
@@ -614,7 +692,8 @@ def traffic_from(args):
         with open(TRAFFIC_JSON) as fh:
             old = json.load(fh)
         if old.get("kernel_source_digest") == t["kernel_source_digest"]:
-            t["entries"] = [e for e in old.get("entries", []) if (e["message_mib"], e["variant"], e["dtype"]) !=
+            t["entries"] = [e for e in old.get("entries", []) if e.get("workload") != entry["workload"] or
+                            (e["message_mib"], e["variant"], e["dtype"]) !=
                             (entry["message_mib"], entry["variant"], entry["dtype"])]
     t["entries"].append(entry)
     t["entries"].sort(key=lambda e: (e["dtype"], e["variant"], e["message_mib"]))
@@ -744,7 +823,7 @@ def launch_ms(t, ms, n):
     return ms / n - t["event_cost_ms"]
 
 
-def roofline_of(t, steps, message_mib, variant, dtype):
+def roofline_of(t, steps, message_mib, variant, dtype, workload=None):
     """The roofline block for the kernel family with the largest share of the
     step's time: algorithmic bytes per launch / average launch duration."""
     per_kernel = t["per_kernel"]
@@ -763,7 +842,7 @@ def roofline_of(t, steps, message_mib, variant, dtype):
         "peak": PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / PEAK_GBS, 4),
-        "traffic": traffic_for(dom, message_mib, variant, d_b // d_n, d_n // steps, dtype),
+        "traffic": traffic_for(dom, message_mib, variant, d_b // d_n, d_n // steps, dtype, workload=workload),
         "algorithmic_bytes_per_launch": d_b // d_n,
         "avg_launch_us": round(1e3 * dur, 3),
         "avg_event_interval_us": round(1e3 * d_ms / d_n, 3),
@@ -818,6 +897,13 @@ def step_bench(args):
     print(f"[bench] generating inputs, M={args.message_mib} MiB", file=sys.stderr, flush=True)
     inp = device_inputs(M, 1000 + int(args.message_mib * 16), args.dtype) if args.device_inputs \
         else host_inputs(M, args.dtype)
+    if args.ragged_a2a:
+        # segmentCount = 5 mod 8: sources and destinations of the helper
+        # slice's chunk moves disagree modulo 16 bytes (the realigning copy)
+        if args.device_inputs:
+            inp["a2a"] = [x[:4 * (x.numel() // 4 - 3)].clone() for x in inp["a2a"]]
+        else:
+            inp["a2a"] = host_inputs(M, args.dtype, rows=("a2a_ragged",))["a2a_ragged"]
     # --buffer-sets N: N independent copies of every buffer, used by
     # consecutive steps in turn, so that no step finds its data in a cache
     # left warm by the previous one
@@ -863,9 +949,7 @@ def step_bench(args):
         "data": "synthetic",
         "pct_of_peak": round(100.0 * value / PEAK_GBS, 2),
         "config": {
-            "workload": (f"relay hot path, {args.message_mib:g} MiB per-rank {args.dtype} message: A=2 allreduce "
-                         "(H=6) + A=2 reduce-scatter + A=4 allreduce (H=4, 500 permille) + A=4 "
-                         "reduce-scatter + A=4 all-to-all pack/unpack, one GPU"),
+            "workload": workload_name(args.message_mib, args.dtype, args.ragged_a2a),
             "variant": args.variant,
             "variant_means": VARIANTS[args.variant],
             "message_bytes": M,
@@ -878,7 +962,8 @@ def step_bench(args):
             **rows_of(t),
             "launch_order": [row for row, _, _, _ in calls],
         },
-        "roofline": roofline_of(t, args.steps, args.message_mib, args.variant, args.dtype),
+        "roofline": roofline_of(t, args.steps, args.message_mib, args.variant, args.dtype,
+                                workload_name(args.message_mib, args.dtype, args.ragged_a2a)),
         "cpu_baseline": None,
     }
     if not args.no_other_variants:
@@ -946,12 +1031,11 @@ def mode_of(args):
 
 def sweep(args):
     """Per-role GB/s over message sizes and dtypes: one launch of each role
-    (covering the jobs --variant selects), timed alone with a fence-free HIP
-    event pair after the caches are cleared of its inputs (--flush); best and
-    median of the reps after 3 warm-ups.  Beside each row: the plain stream
-    of the launch's read/write mix and bytes timed alike, and the CPU oracle
-    on the same jobs."""
-    import ctypes
+    (covering the jobs --variant selects), timed back to back over buffer
+    sets that rotate through at least 1 GiB (b2b_timer), median and best of
+    the trials.  Beside each row: plain streams of the launch's read/write mix
+    and bytes in every calibration pattern, timed alike, and the CPU oracle on
+    the same jobs."""
     import zlib
     import torch
     import pack_rr_helper_amd as rr
@@ -959,35 +1043,12 @@ def sweep(args):
     rr.load()
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    hip = hip_runtime()
-    evs = []
-    for _ in range(2):
-        e = ctypes.c_void_p()
-        if hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
-            raise RuntimeError("hipEventCreateWithFlags failed")
-        evs.append(e)
-    f = ctypes.c_float()
-    evict = cache_evictor(torch, args.flush)
+    times_of = b2b_timer()
 
-    def times_of(fn):
-        ts = []
-        for rep in range(args.sweep_reps + 3):
-            evict()
-            hip.hipEventRecord(evs[0], sp)
-            fn()
-            hip.hipEventRecord(evs[1], sp)
-            torch.cuda.synchronize()
-            hip.hipEventElapsedTime(ctypes.byref(f), evs[0], evs[1])
-            if rep >= 3:
-                ts.append(f.value * 1e-3)
-        return ts
-
-    def record(mib, dt_name, role, kernel, b, ts):
-        return {"message_mib": mib, "dtype": dt_name, "variant": mode_of(args),
-                "flush": args.flush,
-                "row": role, "kernel": kernel, "bytes_per_launch": b,
-                "reps": len(ts), "us_min": round(min(ts) * 1e6, 2),
+    def record(mib, dt_name, role, kernel, b, ts, nsets):
+        return {"message_mib": mib, "dtype": dt_name, "variant": mode_of(args), "timing": "back to back",
+                "buffer_sets": nsets, "row": role, "kernel": kernel, "bytes_per_launch": b,
+                "trials": len(ts), "us_min": round(min(ts) * 1e6, 2),
                 "us_median": round(statistics.median(ts) * 1e6, 2),
                 "gbs_best": round(b / min(ts) / 1e9, 1),
                 "gbs_median": round(b / statistics.median(ts) / 1e9, 1),
@@ -1017,37 +1078,49 @@ def sweep(args):
                 gen.manual_seed(zlib.crc32(f"{row}/{dt_name}/{M}".encode()))
                 base = row.split("_")[0]
                 ranks = 2 if base in ("ar2", "rs2") else 4
-                if row.startswith("a2a"):
-                    # ragged: segmentCount = 5 mod 8, so odd destinations' chunks sit at
-                    # byte offsets that disagree with the packed buffer modulo 16
-                    nr = n if row == "a2a" else 4 * (n // 4 - 3)
-                    lim = 1 << (8 * W.ESIZE[dt] - 1)
-                    xs = [torch.randint(-lim, lim - 1, (nr,), dtype=bits_dt, device="cuda", generator=gen)
-                          for _ in range(ranks)]
-                elif row.endswith("_shifted"):
-                    # rank r's input starts 2r + 1 elements into its buffer: every
-                    # input sits at another offset modulo 16 bytes
-                    xs = [torch.randn(n + 16, device="cuda", generator=gen).to(tdt)[2 * r + 1:2 * r + 1 + n]
-                          for r in range(ranks)]
-                else:
-                    xs = [torch.randn(n, device="cuda", generator=gen).to(tdt) for _ in range(ranks)]
                 mode = mode_of(args)
-                wl = {"ar2": lambda: W.AR2(xs, dt, rr.AVG, mode=mode), "rs2": lambda: W.RS2(xs, dt, rr.AVG, mode=mode),
-                      "ar4": lambda: W.AR4(xs, dt, rr.AVG, mode=mode, phase=row == "ar4_phase"), "rs4": lambda: W.RS4(xs, dt, rr.SUM, mode=mode),
-                      "a2a": lambda: W.A2A(xs, dt, mode=mode)}[base]()
-                calls = wl.calls(stream)
+
+                def make_xs():
+                    if row.startswith("a2a"):
+                        # ragged: segmentCount = 5 mod 8, so odd destinations' chunks sit
+                        # at byte offsets that disagree with the packed buffer modulo 16
+                        nr = n if row == "a2a" else 4 * (n // 4 - 3)
+                        lim = 1 << (8 * W.ESIZE[dt] - 1)
+                        return [torch.randint(-lim, lim - 1, (nr,), dtype=bits_dt, device="cuda", generator=gen)
+                                for _ in range(ranks)]
+                    if row.endswith("_shifted"):
+                        # rank r's input starts 2r + 1 elements into its buffer: every
+                        # input sits at another offset modulo 16 bytes
+                        return [torch.randn(n + 16, device="cuda", generator=gen).to(tdt)[2 * r + 1:2 * r + 1 + n]
+                                for r in range(ranks)]
+                    return [torch.randn(n, device="cuda", generator=gen).to(tdt) for _ in range(ranks)]
+
+                def make_wl(xs):
+                    return {"ar2": lambda: W.AR2(xs, dt, rr.AVG, mode=mode),
+                            "rs2": lambda: W.RS2(xs, dt, rr.AVG, mode=mode),
+                            "ar4": lambda: W.AR4(xs, dt, rr.AVG, mode=mode, phase=row == "ar4_phase"),
+                            "rs4": lambda: W.RS4(xs, dt, rr.SUM, mode=mode),
+                            "a2a": lambda: W.A2A(xs, dt, mode=mode)}[base]()
+
+                wls = [make_wl(make_xs())]
+                calls0 = wls[0].calls(stream)
+                nsets = rotation_sets(sum(c[2] for c in calls0))
+                wls += [make_wl(make_xs()) for _ in range(nsets - 1)]
+                set_calls = [wl.calls(stream) for wl in wls]
                 suffix = "" if row == "ar4_phase" else row[len(base):]
-                for role in sorted({c[0] for c in calls}):
-                    role_call = next(c for c in calls if c[0] == role)
+                for role in sorted({c[0] for c in calls0}):
+                    idx = next(i for i, c in enumerate(calls0) if c[0] == role)
+                    role_call = calls0[idx]
                     name = role + suffix
-                    rec = record(mib, dt_name, name, role_call[1], role_call[2], times_of(role_call[3]))
+                    rec = record(mib, dt_name, name, role_call[1], role_call[2],
+                                 times_of([sc[idx][3] for sc in set_calls]), nsets)
                     # plain streams of this launch's read/write mix and bytes in every
                     # access pattern of the calibration, timed alike; the fastest is
                     # the ceiling the row is compared with
-                    pats = {}
+                    pats, k = {}, rotation_sets(role_call[2])
                     for pi, pname in enumerate(CALIB_PATTERNS):
-                        st_sets, st_launch, st_bytes = stand_in_step([role_call], 1, stream, pi)
-                        pats[pname] = round(st_bytes / statistics.median(times_of(st_sets[0][0])) / 1e9, 1)
+                        st_sets, st_launch, st_bytes = stand_in_step([role_call], k, stream, pi)
+                        pats[pname] = round(st_bytes / statistics.median(times_of([fs[0] for fs in st_sets])) / 1e9, 1)
                         del st_sets
                     top = max(pats, key=pats.get)
                     rec["stand_in"] = {"reads": st_launch[0][1], "writes": st_launch[0][2], "bytes": st_bytes,
@@ -1061,17 +1134,17 @@ def sweep(args):
                         o["gpu_over_oracle"] = round(rec["gbs_median"] / o["gbs"], 1)
                         rec["oracle"] = o
                     print(json.dumps(rec), file=out, flush=True)
-                del wl, xs, calls
+                del wls, set_calls, calls0
                 torch.cuda.empty_cache()
         # calibration: the runtime's own device-to-device copy of M bytes
-        a = torch.empty(M, dtype=torch.uint8, device="cuda")
-        bb = torch.empty_like(a)
-        rec = record(mib, "u8", "torch_copy_calibration", "hipMemcpyAsync D2D", 2 * M, times_of(lambda: bb.copy_(a)))
+        k = rotation_sets(2 * M)
+        pairs = [(torch.empty(M, dtype=torch.uint8, device="cuda"), torch.empty(M, dtype=torch.uint8, device="cuda"))
+                 for _ in range(k)]
+        rec = record(mib, "u8", "torch_copy_calibration", "hipMemcpyAsync D2D", 2 * M,
+                     times_of([(lambda a=a, bb=bb: bb.copy_(a)) for a, bb in pairs]), k)
         print(json.dumps(rec), file=out, flush=True)
-        del a, bb
+        del pairs
         torch.cuda.empty_cache()
-    for e in evs:
-        hip.hipEventDestroy(e)
 
 
 # --------------------------------------------------------------------------
@@ -1088,36 +1161,49 @@ CALIB_PATTERNS = ["relay", "tile8k", "tile4k", "multi2", "multi4", "persistent",
 
 def calibrate(args):
     """R reads + W writes per element (bench_calib.hip) in every access
-    pattern of CALIB_PATTERNS, each mix timed alone with a fence-free HIP
-    event pair after the caches are cleared of its inputs (--flush); best and
-    median of the reps per pattern, then one line per (size, mix) naming the
-    fastest pattern by median: the ceiling for that mix."""
+    pattern of CALIB_PATTERNS, each timed back to back over buffer sets that
+    rotate through at least 1 GiB (b2b_timer: no cache clearing, no event per
+    launch), median and best of the trials per pattern, then one line per
+    (size, mix) naming the fastest pattern by median: the ceiling for that
+    mix.  --calibrate-alone times each launch alone after a 1 GiB read
+    instead (the method of the per-role sweep before), which lets written
+    data still sit in the Infinity Cache when a kernel ends."""
     import ctypes
+    import functools
     import torch
     lib = _calib_lib()
     torch.cuda.set_device(0)
     vp = ctypes.c_void_p
     stream = torch.cuda.current_stream()
     sp = vp(stream.cuda_stream)
-    times_of = alone_timer(cache_evictor(torch, args.flush), reps=args.sweep_reps, warm=3)
+    if args.calibrate_alone:
+        alone = alone_timer(cache_evictor(torch, args.flush), reps=args.sweep_reps, warm=3)
+        times_of = lambda fns: alone(fns[0])
+    else:
+        times_of = b2b_timer()
     sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
     out = open(args.calibrate_out, "w") if args.calibrate_out else sys.stdout
     for mib in [int(v) for v in args.calibrate_sizes.split(",")]:
         vectors = (mib * MIB // 16) // 1024 * 1024
-        bufs = [torch.ones(vectors * 16, dtype=torch.uint8, device="cuda") for _ in range(6)]
         for R, W in CALIB_MIXES:
-            ins = (vp * 4)(*[b.data_ptr() for b in bufs[:4]])
-            outs = (vp * 4)(*[b.data_ptr() for b in bufs[4:]] + [0, 0])
             b = (R + W) * vectors * 16
+            nsets = 1 if args.calibrate_alone else rotation_sets(b)
+            sets = []
+            for _ in range(nsets):
+                bufs = [torch.ones(vectors * 16, dtype=torch.uint8, device="cuda") for _ in range(R + W)]
+                ins = (vp * 4)(*([x.data_ptr() for x in bufs[:R]] + [0] * (4 - R)))
+                outs = (vp * 4)(*([x.data_ptr() for x in bufs[R:]] + [0] * (4 - W)))
+                sets.append((bufs, ins, outs))
             best = None
             for pi, pname in enumerate(CALIB_PATTERNS):
-                def fn(pi=pi):
+                def launch(ins, outs, pi=pi):
                     rc = lib.calib_stream_pattern(pi, R, W, ins, outs, vp(sink.data_ptr()), vectors, sp)
                     if rc != 0:
                         raise RuntimeError(f"calib_stream_pattern({pi}, {R}, {W}) failed: {rc}")
-                ts = times_of(fn)
-                rec = {"mib_per_stream": mib, "reads": R, "writes": W, "pattern": pname, "flush": args.flush,
-                       "bytes": b, "reps": len(ts),
+                ts = times_of([functools.partial(launch, ins, outs) for _, ins, outs in sets])
+                rec = {"mib_per_stream": mib, "reads": R, "writes": W, "pattern": pname,
+                       "timing": "alone" if args.calibrate_alone else "back to back", "buffer_sets": nsets,
+                       "bytes": b, "trials": len(ts),
                        "gbs_best": round(b / min(ts) / 1e9, 1),
                        "gbs_median": round(b / statistics.median(ts) / 1e9, 1),
                        "pct_peak_median": round(100 * b / statistics.median(ts) / 1e9 / PEAK_GBS, 1)}
@@ -1127,8 +1213,8 @@ def calibrate(args):
             print(json.dumps({"mib_per_stream": mib, "reads": R, "writes": W, "ceiling": True,
                               "best_pattern": best["pattern"], "gbs_median": best["gbs_median"],
                               "pct_peak_median": best["pct_peak_median"]}), file=out, flush=True)
-        del bufs
-        torch.cuda.empty_cache()
+            del sets
+            torch.cuda.empty_cache()
 
 
 # Read and write streams per element of each launch of the step, for its
@@ -1246,11 +1332,64 @@ def alone_timer(evict, reps, warm=2):
     return times_of
 
 
+# Launch sequences timed back to back rotate over buffer sets that together
+# hold at least this much (four times the 256 MB Infinity Cache), so that no
+# launch finds its inputs, or room for its outputs, left in a cache by the
+# launches before it.
+ROTATE_BYTES = 1 << 30
+MAX_SETS = 256
+
+
+def rotation_sets(bytes_per_set):
+    """Buffer sets for a back-to-back sequence: enough to rotate through
+    ROTATE_BYTES, at least 2, at most MAX_SETS."""
+    return max(2, min(MAX_SETS, -(-ROTATE_BYTES // max(1, int(bytes_per_set)))))
+
+
+def b2b_timer(trials=5, min_launches=30):
+    """A function timing launches back to back: given one launch function per
+    buffer set, it issues max(min_launches, 2 x sets) launches cycling through
+    the sets, with one fence-free HIP event pair around them, `trials` times
+    after one warm-up pass; returns the seconds per launch of each trial.  No
+    per-launch event and no cache clearing: the steady state of a stream of
+    launches, as in the benchmark step."""
+    import ctypes
+    import torch
+    hip = hip_runtime()
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    evs = []
+    for _ in range(2):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        evs.append(e)
+    f = ctypes.c_float()
+
+    def times_of(fns):
+        n = max(min_launches, 2 * len(fns))
+        for fn in fns:
+            fn()
+        ts = []
+        for _ in range(trials):
+            torch.cuda.synchronize()
+            hip.hipEventRecord(evs[0], sp)
+            for i in range(n):
+                fns[i % len(fns)]()
+            hip.hipEventRecord(evs[1], sp)
+            torch.cuda.synchronize()
+            hip.hipEventElapsedTime(ctypes.byref(f), evs[0], evs[1])
+            ts.append(f.value * 1e-3 / n)
+        return ts
+    times_of.events = evs
+    return times_of
+
+
 def stand_in_ceiling(calls, nsets, stream, steps, warmup, value):
     """The step's launch sequence replaced by plain streams of each launch's
     read/write mix and bytes, in every access pattern of bench_calib.hip
     (the same pattern for every launch), and once with each launch in the
-    pattern that ran its mix and bytes fastest alone; each timed like timed
+    pattern that ran its mix and bytes fastest (each launch's patterns timed
+    back to back over rotating buffer sets); each step timed like timed
     region 1.  The fastest of these is the ceiling the relay step is compared
     with."""
     import torch
@@ -1263,13 +1402,14 @@ def stand_in_ceiling(calls, nsets, stream, steps, warmup, value):
                                  "ms_per_step": round(ms, 5)}
         del st_sets
         torch.cuda.empty_cache()
-    times_of = alone_timer(cache_evictor(torch, "read"), reps=5)
+    times_of = b2b_timer()
     best = []
     for c in calls:
         med = {}
+        k = rotation_sets(c[2])
         for pi in range(len(CALIB_PATTERNS)):
-            st_sets, _, _ = stand_in_step([c], 1, stream, pi)
-            med[pi] = statistics.median(times_of(st_sets[0][0]))
+            st_sets, _, _ = stand_in_step([c], k, stream, pi)
+            med[pi] = statistics.median(times_of([fs[0] for fs in st_sets]))
             del st_sets
         best.append(min(med, key=med.get))
     torch.cuda.empty_cache()
@@ -1616,7 +1756,9 @@ def main():
         print(f"bench.py measures one GPU: the library has no multi-GPU path (--gpus {args.gpus} "
               "requested). The relay's local kernels shard per rank; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    if args.trace_summary:
+    if args.sweep_summary:
+        sweep_summary(args)
+    elif args.trace_summary:
         trace_summary(args)
     elif args.traffic_from:
         traffic_from(args)

@@ -22,10 +22,10 @@ def test_code_digest_ignores_comments_and_spacing_only():
 
 def _traffic_file(tmp_path, digest=None):
     t = {"kernel_source_digest": digest or bench.kernel_source_digest(), "entries": [
-        {"message_mib": 64.0, "variant": "share", "dtype": "bf16",
+        {"message_mib": 64.0, "variant": "share", "dtype": "bf16", "workload": bench.workload_name(64.0),
          "kernels": {"reduce<bf16>": {"hbm_bytes_per_launch": 1001, "algorithmic_bytes_per_launch": 1000,
                                       "launches_per_step": 6}}},
-        {"message_mib": 1024.0, "variant": "group", "dtype": "bf16",
+        {"message_mib": 1024.0, "variant": "group", "dtype": "bf16", "workload": bench.workload_name(1024.0),
          "kernels": {"copy": {"hbm_bytes_per_launch": 2002, "algorithmic_bytes_per_launch": 2000,
                               "launches_per_step": 2}}}]}
     path = tmp_path / "traffic.json"
@@ -46,6 +46,10 @@ def test_stored_traffic_is_used_only_for_its_own_workload(tmp_path):
     # bytes per launch) gets no stored figure either
     assert get("reduce<bf16>", 64.0, "share", 1000, 5) is None
     assert get("reduce<bf16>", 64.0, "share", 1016, 6) is None
+    # an entry of another workload at the same message (the ragged all-to-all
+    # step) is not used for the plain step, and the other way round
+    assert bench.traffic_for("reduce<bf16>", 64.0, "share", 1000, 6, path=path,
+                             workload=bench.workload_name(64.0, "bf16", True)) is None
     # counters taken on other kernel code are never used
     stale = _traffic_file(tmp_path, digest="0" * 16)
     assert bench.traffic_for("reduce<bf16>", 64.0, "share", 1000, 6, path=stale) is None
@@ -59,7 +63,7 @@ def test_committed_traffic_matches_its_kernel_code():
     for e in t["entries"]:
         for kern, k in e["kernels"].items():
             got = bench.traffic_for(kern, e["message_mib"], e["variant"], k["algorithmic_bytes_per_launch"],
-                                    k["launches_per_step"], e["dtype"])
+                                    k["launches_per_step"], e["dtype"], workload=e["workload"])
             assert got == (k["hbm_bytes_per_launch"] if t["kernel_source_digest"] == bench.kernel_source_digest()
                            else None)
 
@@ -81,7 +85,7 @@ def test_traffic_from_scales_by_the_plain_copy_and_averages_the_timed_steps(tmp_
     order, algo = ["ar2_helper", "a2a_pack"], {"ar2_helper": 3 * 1024 * 100, "a2a_pack": 2 * 1024 * 50}
     run = {"steps": 2, "warmup": 1, "dtype": "bf16",
            "config": {"launch_order": order, "rows_bytes_per_launch": algo, "message_bytes": 64 << 20,
-                      "variant": "share"}}
+                      "variant": "share", "workload": "two launches"}}
     (tmp_path / "run.json").write_text("[bench] noise\n" + json.dumps(run) + "\n")
     # a relay launch while staging inputs, the copy of 256 MiB three times,
     # then warmup + 2 x 2 steps of the two launches
