@@ -651,8 +651,8 @@ rr_status check_moves(const std::vector<Move> &mv, size_t culprit[2])
 
 class CopyLauncher {
 public:
-    // long_call: the call moves at least kCopyLongBytes, so its aligned moves
-    // use the long-call tiles.
+    // long_call: the call moves at least kCopyLongBytes, all of it in aligned
+    // moves, which then use the long-call tiles.
     CopyLauncher(hipStream_t st, bool long_call) : st_(st)
     {
         b_.nseg = 0;
@@ -744,10 +744,16 @@ rr_status run_copy(const std::vector<Move> &mv, void *stream, bool batch)
     rr_status st = check_moves(mv, culprit);
     if (st != RR_OK)
         return batch ? jobs_error(mv[culprit[0]].job, mv[culprit[1]].job, st) : st;
+    // Long-call tiles only when every move is aligned: a realigned move keeps
+    // its own tile size, and moves of one size with unequal tiles would leave
+    // the uniform launch form for the table form.
     int64_t total = 0;
-    for (const Move &m : mv)
+    bool aligned = true;
+    for (const Move &m : mv) {
         total += m.nbytes;
-    CopyLauncher L(static_cast<hipStream_t>(stream), total >= rr::kCopyLongBytes);
+        aligned = aligned && (m.nbytes <= 0 || addr(m.src) % 16 == addr(m.dst) % 16);
+    }
+    CopyLauncher L(static_cast<hipStream_t>(stream), aligned && total >= rr::kCopyLongBytes);
     for (const Move &m : mv)
         L.add(m.src, m.dst, m.nbytes);
     const hipError_t e = L.finish();
@@ -868,7 +874,8 @@ LaunchShape uniform_or_table(const Batch &b, int64_t total_tiles)
 
 LaunchShape reduce_shape(const RedBatch &b, int64_t total_tiles)
 {
-    if (b.nseg == 1 && b.seg[0].mode == kRedAligned && b.seg[0].k >= 1 && b.seg[0].k <= kMaxIn)
+    if (b.nseg == 1 && (b.seg[0].mode == kRedAligned || b.seg[0].mode == kRedShifted) && b.seg[0].k >= 1 &&
+        b.seg[0].k <= kMaxIn)
         return LaunchShape{kFormOne, total_tiles, 1};
     return uniform_or_table(b, total_tiles);
 }

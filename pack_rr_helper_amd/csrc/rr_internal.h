@@ -67,18 +67,21 @@ constexpr int64_t kCopyLongBytes = RR_COPY_LONG_BYTES;
 #endif
 constexpr int kShiftUnroll = RR_SHIFT_UNROLL;
 
-// Copies of at least kCopyThrottleTiles tiles reserve kCopyThrottleLds bytes of
-// (unused) LDS per workgroup, which lets 6 of them share a CU's 160 KiB
-// instead of 8: with fewer loads and stores in flight, HBM serves a long copy
-// 2-4% faster.  Reductions and short copies measured best at full occupancy.
-#ifndef RR_COPY_THROTTLE_TILES
-#define RR_COPY_THROTTLE_TILES 4096
+// Launches of at least kThrottleTiles tiles in the uniform copy kernels
+// (aligned and mixed) and in the realigning single-segment reduction reserve
+// kThrottleLds bytes of (unused) LDS per workgroup, which lets 6 of them
+// share a CU's 160 KiB instead of 8: with fewer loads and stores in flight,
+// HBM serves a long stream 1-4% faster.  Aligned reductions and short
+// launches measured best at full occupancy; the other realigning reductions
+// already run 6 per CU (their register count).
+#ifndef RR_THROTTLE_TILES
+#define RR_THROTTLE_TILES 4096
 #endif
-#ifndef RR_COPY_THROTTLE_LDS
-#define RR_COPY_THROTTLE_LDS (26 * 1024)
+#ifndef RR_THROTTLE_LDS
+#define RR_THROTTLE_LDS (26 * 1024)
 #endif
-constexpr int64_t kCopyThrottleTiles = RR_COPY_THROTTLE_TILES;
-constexpr unsigned kCopyThrottleLds = RR_COPY_THROTTLE_LDS;
+constexpr int64_t kThrottleTiles = RR_THROTTLE_TILES;
+constexpr unsigned kThrottleLds = RR_THROTTLE_LDS;
 
 enum RedMode : int32_t { kRedAligned = 1, kRedShifted = 2 };
 
@@ -243,16 +246,20 @@ __host__ __device__ inline int64_t tail_elem(int x, int64_t tail0)
 }
 
 // Index of the segment that owns tile t in a table form launch: the number of
-// later segment starts at or before t.  Unrolled over the table so the scalar
-// loads issue together.
+// later segment starts at or before t.  Unrolled over the table, one bit per
+// start in a 64-bit mask, then a population count: on the GPU every step stays
+// on the scalar unit (a running sum of the compares was compiled to a chain of
+// 64-bit vector adds, several hundred cycles before a workgroup's first load).
 template <int MAXS>
 __host__ __device__ inline int find_seg(const int32_t (&tile0)[MAXS], int nseg, int32_t t)
 {
-    int s = 0;
+    static_assert(MAXS >= 1 && MAXS <= 64, "one mask bit per segment");
+    uint64_t m = 0;
 #pragma unroll
     for (int i = 1; i < MAXS; ++i)
-        s += (i < nseg && t >= tile0[i]) ? 1 : 0;
-    return s;
+        m |= uint64_t(t >= tile0[i]) << i;
+    const uint64_t valid = nseg >= 64 ? ~uint64_t(0) : (uint64_t(1) << nseg) - 1;
+    return __builtin_popcountll(m & valid);
 }
 
 // The aligned 16-byte word holding byte p, and p's offset in it (0..15).
@@ -276,8 +283,8 @@ __host__ __device__ constexpr int64_t red_tile_vecs(int32_t mode)
     return mode == kRedShifted ? tile_vecs<kShiftRedUnroll>() : tile_vecs<kUnroll>();
 }
 
-// long_tiles: the batch belongs to a call that moves at least kCopyLongBytes,
-// whose aligned moves use tiles of kCopyUnrollLong vectors per lane.
+// long_tiles: the batch belongs to a call that moves at least kCopyLongBytes
+// in aligned moves only; they use tiles of kCopyUnrollLong vectors per lane.
 template <int CAP>
 struct CopyBatchT {
     int32_t tile0[CAP];
@@ -301,7 +308,7 @@ __host__ __device__ constexpr int64_t copy_tile_vecs(int32_t mode, bool long_til
 //                 loads from the kernel arguments);
 //   kFormUniform: every segment has gx tiles: 2-D grid (gx, nseg), the
 //                 segment is blockIdx.y and the tile blockIdx.x;
-//   kFormOne:     one kRedAligned reduction segment: 1-D grid of gx
+//   kFormOne:     one reduction segment (either mode): 1-D grid of gx
 //                 tiles, the descriptor passed as scalar kernel arguments
 //                 that the hardware preloads into registers.
 enum LaunchForm : int32_t { kFormTable = 0, kFormUniform = 1, kFormOne = 2 };

@@ -382,6 +382,26 @@ __global__ __launch_bounds__(kBlock) void reduce_one_kernel(const void *in0, con
     reduce_vec<BF16, K>(sg, (int64_t)blockIdx.x);
 }
 
+// The same for one realigning (kRedShifted) segment.
+template <bool BF16, int K>
+__global__ __launch_bounds__(kBlock) void reduce_shifted_one_kernel(const void *in0, const void *in1,
+                                                                    const void *in2, const void *in3,
+                                                                    void *out, int64_t n, float scale)
+{
+    RedSeg sg;
+    sg.in[0] = in0;
+    sg.in[1] = in1;
+    sg.in[2] = in2;
+    sg.in[3] = in3;
+    sg.out = out;
+    sg.n = n;
+    sg.k = K;
+    sg.mode = kRedShifted;
+    sg.scale = scale;
+    sg.pad = 0;
+    reduce_shifted<BF16, K>(sg, (int64_t)blockIdx.x);
+}
+
 // ---------------------------------------------------------------------------
 // Copy
 // ---------------------------------------------------------------------------
@@ -535,27 +555,28 @@ __global__ __launch_bounds__(kBlock) void copy_mixed_uniform_kernel(CopyBatchT<C
 
 namespace {
 
-template <bool BF16>
-void launch_one(const RedSeg &sg, int64_t tiles, hipStream_t stream)
+template <bool BF16, int K>
+void launch_one_k(const RedSeg &sg, const dim3 &grid, bool shifted, hipStream_t stream)
 {
-    const dim3 grid((unsigned)tiles), block(kBlock);
+    const dim3 block(kBlock);
+    const unsigned lds = grid.x >= kThrottleTiles ? kThrottleLds : 0u;
+    if (shifted)
+        reduce_shifted_one_kernel<BF16, K><<<grid, block, lds, stream>>>(sg.in[0], sg.in[1], sg.in[2], sg.in[3],
+                                                                         sg.out, sg.n, sg.scale);
+    else
+        reduce_one_kernel<BF16, K><<<grid, block, 0, stream>>>(sg.in[0], sg.in[1], sg.in[2], sg.in[3], sg.out,
+                                                               sg.n, sg.scale);
+}
+
+template <bool BF16>
+void launch_one(const RedSeg &sg, int64_t tiles, bool shifted, hipStream_t stream)
+{
+    const dim3 grid((unsigned)tiles);
     switch (sg.k) {
-    case 1:
-        reduce_one_kernel<BF16, 1><<<grid, block, 0, stream>>>(sg.in[0], sg.in[1], sg.in[2], sg.in[3],
-                                                               sg.out, sg.n, sg.scale);
-        break;
-    case 2:
-        reduce_one_kernel<BF16, 2><<<grid, block, 0, stream>>>(sg.in[0], sg.in[1], sg.in[2], sg.in[3],
-                                                               sg.out, sg.n, sg.scale);
-        break;
-    case 3:
-        reduce_one_kernel<BF16, 3><<<grid, block, 0, stream>>>(sg.in[0], sg.in[1], sg.in[2], sg.in[3],
-                                                               sg.out, sg.n, sg.scale);
-        break;
-    default:
-        reduce_one_kernel<BF16, 4><<<grid, block, 0, stream>>>(sg.in[0], sg.in[1], sg.in[2], sg.in[3],
-                                                               sg.out, sg.n, sg.scale);
-        break;
+    case 1: launch_one_k<BF16, 1>(sg, grid, shifted, stream); break;
+    case 2: launch_one_k<BF16, 2>(sg, grid, shifted, stream); break;
+    case 3: launch_one_k<BF16, 3>(sg, grid, shifted, stream); break;
+    default: launch_one_k<BF16, 4>(sg, grid, shifted, stream); break;
     }
 }
 
@@ -616,12 +637,11 @@ void launch_copy_table(const CopyBatchT<CAP> &b, const LaunchShape &sh, int64_t 
     const dim3 block(kBlock);
     if (sh.form == kFormUniform) {
         const dim3 grid((unsigned)sh.gx, (unsigned)sh.gy);
-        if (shifted) {
-            copy_mixed_uniform_kernel<CAP, U><<<grid, block, 0, stream>>>(b);
-        } else {
-            const unsigned lds = total_tiles >= kCopyThrottleTiles ? kCopyThrottleLds : 0u;
+        const unsigned lds = total_tiles >= kThrottleTiles ? kThrottleLds : 0u;
+        if (shifted)
+            copy_mixed_uniform_kernel<CAP, U><<<grid, block, lds, stream>>>(b);
+        else
             copy_uniform_kernel<CAP, U><<<grid, block, lds, stream>>>(b);
-        }
     } else {
         const dim3 grid((unsigned)total_tiles);
         if (shifted)
@@ -649,11 +669,11 @@ hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, bool shifted, h
         return hipSuccess;
     (void)hipGetLastError();  // report this launch's status only
     const LaunchShape sh = reduce_shape(b, total_tiles);
-    if (!shifted && sh.form == kFormOne) {
+    if (sh.form == kFormOne) {
         if (b.bf16)
-            launch_one<true>(b.seg[0], sh.gx, stream);
+            launch_one<true>(b.seg[0], sh.gx, shifted, stream);
         else
-            launch_one<false>(b.seg[0], sh.gx, stream);
+            launch_one<false>(b.seg[0], sh.gx, shifted, stream);
     } else if (b.bf16) {
         launch_reduce_sized<true>(b, sh, total_tiles, shifted, stream);
     } else {

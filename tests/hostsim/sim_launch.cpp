@@ -48,6 +48,7 @@ bool touches(uintptr_t a, int64_t n)
 
 long g_forms[2][3];  // launches per (copy?, launch form)
 long g_long_copies[2];  // copy launches per tiling (0 default, 1 long-call)
+long g_shifted_copies;  // copy launches in the mixed-mode (realigning) kernels
 
 void violation(const char *what, uintptr_t a, int64_t n)
 {
@@ -245,7 +246,8 @@ hipError_t launch_reduce(const RedBatch &b, int64_t total_tiles, bool shifted, h
     const int64_t es = bf16 ? 2 : 4, ve = 16 / es;
     const LaunchShape sh = reduce_shape(b, total_tiles);
     ++g_forms[0][sh.form];
-    if (sh.form == kFormOne && (shifted || b.seg[0].mode != kRedAligned || b.seg[0].k < 1 || b.seg[0].k > kMaxIn))
+    if (sh.form == kFormOne && (b.nseg != 1 || b.seg[0].mode != (shifted ? kRedShifted : kRedAligned) ||
+                                b.seg[0].k < 1 || b.seg[0].k > kMaxIn))
         violation("single-segment form for a segment it cannot run", uintptr_t(b.seg[0].out), b.seg[0].k);
     for (const auto &st : tiles_of(b, total_tiles, sh)) {
         const RedSeg &sg = b.seg[st.first];
@@ -292,6 +294,9 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
     if (b.long_tiles != 0 && b.long_tiles != 1)
         violation("copy batch with an unknown tiling", 0, b.long_tiles);
     ++g_long_copies[b.long_tiles != 0];
+    g_shifted_copies += shifted ? 1 : 0;
+    if (b.long_tiles && shifted)
+        violation("long-call tiling in a launch with a realigned move", 0, 0);
     for (const auto &st : tiles_of(b, total_tiles, sh)) {
         const CopySeg &sg = b.seg[st.first];
         const int64_t lt = st.second;
@@ -334,6 +339,7 @@ void sim_reset(void)
     g_launches = 0;
     memset(g_forms, 0, sizeof g_forms);
     memset(g_long_copies, 0, sizeof g_long_copies);
+    g_shifted_copies = 0;
     g_msg[0] = '\0';
 }
 void sim_register(const void *p, int64_t bytes, int writable)
@@ -348,4 +354,6 @@ long sim_form_launches(int copy, int form) { return g_forms[copy != 0][form]; }
 const char *sim_message(void) { return g_msg; }
 // copy launches since the last reset with the default (0) or long-call (1) tiling
 long sim_copy_launches(int long_tiles) { return g_long_copies[long_tiles != 0]; }
+// copy launches since the last reset in the mixed-mode (realigning) kernels
+long sim_shifted_copy_launches(void) { return g_shifted_copies; }
 }

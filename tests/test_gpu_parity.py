@@ -295,6 +295,36 @@ def _guards_ok(whole, view_lead, n, dt):
     return bool(np.all(b[:16 + view_lead] == g) and np.all(b[16 + view_lead + n:] == g))
 
 
+def test_long_realigned_single_segment_reductions(orc):
+    """A realigning reduction of one segment runs in the single-segment form;
+    from 4096 tiles (32 MiB of bf16 output) the launch also reserves LDS to
+    run fewer workgroups per CU.  The 2-input A=2 reduce-scatter owner and the
+    4-input A=4 allreduce helper past that size, inputs and output at
+    different element offsets, bit for bit, guards untouched."""
+    say("long realigned single-segment reductions")
+    vals = lambda n, seed, r: synth.as_bf16_bits(synth.normal(n, seed, r))
+    R = (1 << 24) + 8 * 128 * 3 + 77
+    relay = rr.Relay(2, 6, 8, 0, R)
+    b0, b1 = vals(R, 24, 0), vals(R, 24, 1)
+    v0, _ = _view(b0, 5, BF16)
+    v1, _ = _view(b1, 2, BF16)
+    ov, ow = _view(np.zeros(R, np.uint16), 7, BF16)
+    rr.rr_active_add_scale(relay, RS, BF16, AVG, 1, [v0, v1], ov)
+    assert np.array_equal(host(ov), orc.rs2_active(BF16, AVG, b0, b1)), "owner"
+    assert _guards_ok(ow, 7, R, BF16)
+    # the helper reads only its chunk of each input: those chunks are drawn alone
+    count = (1 << 27) + 8 * 128 * 3 + 40
+    relay = rr.Relay(4, 4, 0, 500, count)
+    c = rr.rr_geometry(relay, AR, BF16)["chunk"]
+    assert c > 4096 * 4096
+    chunks = [vals(c, 26, a) for a in range(4)]
+    slots = [_view(x, lead, BF16)[0] for x, lead in zip(chunks, (3, 0, 6, 1))]
+    ov, ow = _view(np.zeros(c, np.uint16), 2, BF16)
+    rr.rr_helper_reduce(relay, AR, BF16, AVG, 1, slots, ov)
+    assert np.array_equal(host(ov), orc.ar4_helper(BF16, AVG, chunks)), "4-input helper"
+    assert _guards_ok(ow, 2, c, BF16)
+
+
 @pytest.mark.parametrize("dt", [BF16, F32])
 def test_realigned_reductions_every_input_shift(orc, dt):
     """Reductions whose inputs each start at a different element offset from
@@ -943,3 +973,32 @@ def test_plan_records_calls_and_launches_them_later(orc):
         t.copy_(torch.roll(t, 11))
     plan.launch(torch.cuda.current_stream())
     check("after new inputs")
+
+
+def test_plan_of_a_call_that_spans_several_launches(orc):
+    """A batched A=2 allreduce helper call of 50 jobs, every tenth job's slots
+    and output at odd element offsets (the realigning kernels), so the 45
+    aligned jobs exceed one launch's 40 reduction segments: prepared with
+    prepare=True, the plan holds every launch of the call (two aligned, one
+    realigning), and launched it writes the oracle's bytes for every job."""
+    count = 8 * 128 * 24
+    c = count // 8
+    relay = rr.Relay(2, 6, 8, 0, count)
+    say("plan, 50 jobs", count)
+    jobs, refs = [], []
+    for j in range(50):
+        lead = 1 + (j % 7) if j % 10 == 0 else 0
+        xs = [synth.as_bf16_bits(synth.normal(c + 8, 90 + j, a)) for a in range(2)]
+        dx = [dev(x) for x in xs]
+        out = torch.zeros(c + 8, dtype=torch.bfloat16, device="cuda")
+        jobs.append((relay, j % 6, [x[lead:lead + c] for x in dx], out[lead:lead + c]))
+        refs.append((out, lead, orc.ar2_helper(BF16, AVG, xs[0][lead:lead + c].copy(), xs[1][lead:lead + c].copy())))
+    fn = rr.rr_helper_reduce_many(AR, BF16, AVG, jobs, prepare=True)
+    assert fn.launches == 3      # two aligned launches (45 > 40 segments) and a realigning one
+    torch.cuda.synchronize()
+    assert not any(o.any() for o, _, _ in refs)
+    fn()
+    for j, (out, lead, ref) in enumerate(refs):
+        got = host(out)
+        check_bf16(got[lead:lead + c], ref, f"plan job {j}")
+        assert not got[:lead].any() and not got[lead + c:].any(), f"plan job {j} wrote outside its output"

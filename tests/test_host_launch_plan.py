@@ -150,6 +150,23 @@ def _tiling_used(sim, long_copies):
     assert (n_long > 0 and n_default == 0) if long_copies else (n_long == 0 and n_default > 0)
 
 
+def _copy_call(sim, name, *args):
+    """Issues one copy call; checks that it took the long-call tiling exactly
+    when the library forces it and none of its moves is realigned (every launch
+    in the aligned-only kernels).  Returns whether it did (False for a call
+    with nothing to move)."""
+    L = sim.L
+    before = (L.sim_copy_launches(1), L.sim_copy_launches(0), L.sim_shifted_copy_launches())
+    sim.call(name, *args)
+    n_long, n_default, n_shifted = (L.sim_copy_launches(1) - before[0], L.sim_copy_launches(0) - before[1],
+                                    L.sim_shifted_copy_launches() - before[2])
+    if n_long + n_default == 0:  # nothing to move
+        return False
+    want_long = sim.long_copies and n_shifted == 0
+    assert (n_long > 0 and n_default == 0) if want_long else n_long == 0
+    return want_long
+
+
 @pytest.mark.parametrize("seg,lead", [(5 * 128 * 4 + 8, 0), (5 * 128 * 2 + 3, 0), (5 * 128 * 3, 5), (400, 0),
                                       (5 * 128 * 9 + 8, 0)])
 @pytest.mark.parametrize("es", [2, 4])
@@ -163,24 +180,26 @@ def test_a2a_pack_unpack(copy_sim, orc, seg, lead, es):
     src = [synth.rng(4, s).integers(0, 2 ** (8 * es), A * seg, dtype=npdt) for s in range(A)]
     sb = [sim.buf(padded(s, lead), writable=False) for s in src]
     outs = [sim.buf(np.full(A * seg + 16, 0x5A, npdt)) for _ in range(A)]
+    longs = []
     for h in range(H):
         dst = [sim.buf(np.zeros(max((A - 1) * c, 1) + 8, npdt)) for _ in range(A)]
-        sim.call("rr_a2a_pack", rel(A, H, nc, 0, seg), dt, h, parr(*[ptr(b, lead) for b in sb]),
-                 parr(*[ptr(d) for d in dst]), None)
+        longs.append(_copy_call(sim, "rr_a2a_pack", rel(A, H, nc, 0, seg), dt, h, parr(*[ptr(b, lead) for b in sb]),
+                                parr(*[ptr(d) for d in dst]), None))
         ref = orc.a2a_pack(es, A, seg, c, h, src)
         for d in range(A):
             assert np.array_equal(dst[d][:(A - 1) * c].view(np.uint8), ref[d])
         recv = [sim.buf(d.copy(), writable=False) for d in dst]
-        sim.call("rr_a2a_unpack", rel(A, H, nc, 0, seg), dt, h, parr(*[ptr(r) for r in recv]),
-                 parr(*[ptr(o, 1) for o in outs]), None)
+        longs.append(_copy_call(sim, "rr_a2a_unpack", rel(A, H, nc, 0, seg), dt, h,
+                                parr(*[ptr(r) for r in recv]), parr(*[ptr(o, 1) for o in outs]), None))
     expect = [np.full(A * seg, 0x5A, npdt) for _ in range(A)]
     for h in range(H):
         orc.a2a_unpack(es, A, seg, c, h, orc.a2a_pack(es, A, seg, c, h, src), expect)
     for d in range(A):
         assert np.array_equal(outs[d][1:1 + A * seg], expect[d])
         assert outs[d][0] == 0x5A and np.all(outs[d][1 + A * seg:] == 0x5A)
-    if c > 0:
-        _tiling_used(sim, sim.long_copies)
+    if c > 0 and lead == 0 and (seg * es) % 16 == 0:
+        # every pack move is aligned: the long-call tiling runs where forced
+        assert any(longs) == sim.long_copies
 
 
 # --------------------------------------------------------------------------
@@ -509,9 +528,8 @@ def test_random_all_to_all_round_trip(sim, orc, seed):
 # --------------------------------------------------------------------------
 
 def test_every_launch_form_is_replayed(sim, orc):
-    """The library launches a batch in one of three forms (one aligned
-    segment with preloaded arguments, a uniform (tile, segment) grid, the
-    tile table).  Each form, replayed here, writes the oracle's values and
+    """The library launches a batch in one of three forms (one segment with
+    preloaded arguments, a uniform (tile, segment) grid, the tile table).  Each form, replayed here, writes the oracle's values and
     touches only the registered buffers."""
     def forms(copy):
         return [sim.L.sim_form_launches(copy, f) for f in range(3)]   # table, uniform, one
@@ -544,7 +562,7 @@ def test_every_launch_form_is_replayed(sim, orc):
     assert forms(0) == [0, 1, 1]
 
     # every buffer 6 bytes past a 16-byte boundary: one realigning segment
-    # (element-wise head and tail in tile 0) on a uniform grid of one row
+    # (element-wise head and tail in tile 0), also in the single-segment form
     lead = 3
     xb = [sim.buf(padded(bits(R, 43, s), lead), writable=False) for s in range(2)]
     ob = sim.buf(np.zeros(R + lead + 16, np.uint16))
@@ -552,7 +570,7 @@ def test_every_launch_form_is_replayed(sim, orc):
              parr(ptr(xb[0], lead), ptr(xb[1], lead)), 2, ptr(ob, lead), None)
     ref = orc.rs2_active(BF16, SUM, xb[0][lead:lead + R].copy(), xb[1][lead:lead + R].copy())
     assert np.array_equal(ob[lead:lead + R], ref)
-    assert forms(0) == [0, 2, 1]
+    assert forms(0) == [0, 1, 2]
 
     # unequal segments: helper jobs of two groups whose chunks span different
     # tile counts take the tile table
@@ -570,7 +588,7 @@ def test_every_launch_form_is_replayed(sim, orc):
     sim.call("rr_helper_reduce_many", AR, BF16, AVG, hj, 2, None)
     for o2, ref2 in hrefs:
         assert np.array_equal(o2, ref2)
-    assert forms(0) == [1, 2, 1]
+    assert forms(0) == [1, 1, 2]
 
     # copies: pack and unpack issue one segment per chunk move (tile 0 also
     # copies its head and tail bytes) and one launch per call, so the aligned
