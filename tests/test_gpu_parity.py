@@ -923,6 +923,30 @@ def test_copy_batches_at_the_segment_table_sizes(orc, nslices, ragged):
             assert np.array_equal(host(packed[h][d]).view(np.uint8), ref[d]), f"slice {h} dest {d}"
 
 
+def test_copy_batches_of_unequal_moves_fill_the_table(orc):
+    """Six all-to-all pack jobs over groups of different segmentCounts (some 5
+    mod 8): 72 chunk moves of unequal tile counts, so the first launch runs a
+    full 64-entry tile table in the mixed-mode copy kernel and the rest
+    continues in a second launch; every job bit for bit against the oracle."""
+    say("copy table of unequal moves")
+    A, H, nc = 4, 4, 5
+    jobs, refs = [], []
+    for j in range(6):
+        seg = 5 * 128 * (40 + 24 * j) + (5 if j % 2 else 0)   # chunks of 2-9 copy tiles
+        c = orc.geometry(A, H, nc, 0, seg, A2A, BF16)["chunk"]
+        src = [synth.bits16(A * seg, 320 + j, s) for s in range(A)]
+        dst = [torch.zeros((A - 1) * c, dtype=torch.int16, device="cuda") for _ in range(A)]
+        h = j % H
+        jobs.append((rr.Relay(A, H, nc, 0, seg), h, [dev(x, None) for x in src], dst))
+        refs.append(orc.a2a_pack(2, A, seg, c, h, src))
+    fn = rr.rr_a2a_pack_many(BF16, jobs, prepare=True)
+    assert fn.launches == 2
+    fn()
+    for j, (job, ref) in enumerate(zip(jobs, refs)):
+        for d in range(A):
+            assert np.array_equal(host(job[3][d]).view(np.uint8), ref[d]), f"job {j} dest {d}"
+
+
 # --------------------------------------------------------------------------
 # plans: validated once, launched many times
 # --------------------------------------------------------------------------

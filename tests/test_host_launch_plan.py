@@ -527,6 +527,37 @@ def test_random_all_to_all_round_trip(sim, orc, seed):
 # launch forms
 # --------------------------------------------------------------------------
 
+def test_copy_batch_of_unequal_moves_fills_the_table(sim, orc):
+    """Six pack jobs over groups of different segmentCounts (some 5 mod 8):
+    72 chunk moves of 2-6 tiles.  The first launch holds a full 64-entry tile
+    table in the mixed-mode kernel, the last 8 moves (of one job, equal)
+    follow in a uniform mixed-mode launch; every job's bytes as the oracle's,
+    every access inside the registered buffers."""
+    sim.reset()
+    A, H, nc = 4, 4, 5
+    aj = (_rr._A2AJob * 6)()
+    keep, outs, refs = [], [], []
+    for j in range(6):
+        seg = 5 * 128 * (40 + 24 * j) + (5 if j % 2 else 0)
+        c = orc.geometry(A, H, nc, 0, seg, A2A, BF16)["chunk"]
+        src = [sim.buf(synth.bits16(A * seg, 320 + j, s), writable=False) for s in range(A)]
+        dst = [sim.buf(np.zeros((A - 1) * c, np.uint16)) for _ in range(A)]
+        pi, po = parr(*[ptr(b) for b in src]), parr(*[ptr(b) for b in dst])
+        keep += [pi, po]
+        aj[j].relay, aj[j].helper = _relay(A, H, nc, 0, seg), j % H
+        aj[j].inp = ctypes.cast(pi, ctypes.POINTER(ctypes.c_void_p))
+        aj[j].out = ctypes.cast(po, ctypes.POINTER(ctypes.c_void_p))
+        outs.append(dst)
+        refs.append(orc.a2a_pack(2, A, seg, c, j % H, src))
+    sim.call("rr_a2a_pack_many", BF16, aj, 6, None)
+    assert sim.L.sim_launches() == 2
+    assert [sim.L.sim_form_launches(1, f) for f in range(3)] == [1, 1, 0]
+    assert sim.L.sim_shifted_copy_launches() == 2
+    for j in range(6):
+        for d in range(A):
+            assert np.array_equal(outs[j][d].view(np.uint8), refs[j][d]), f"job {j} dest {d}"
+
+
 def test_every_launch_form_is_replayed(sim, orc):
     """The library launches a batch in one of three forms (one segment with
     preloaded arguments, a uniform (tile, segment) grid, the tile table).  Each form, replayed here, writes the oracle's values and
