@@ -18,9 +18,9 @@
 // Tiling: one workgroup of 256 threads processes one tile of one segment.  A
 // launch's segments live in the kernel arguments; how a workgroup finds its
 // segment depends on the launch form the host chose (rr_internal.h): a single
-// aligned segment arrives as plain arguments preloaded into scalar registers,
-// equal segments are the rows of a 2-D grid, and otherwise a branch-free
-// count over the table's tile offsets finds it.
+// reduction segment arrives as plain arguments preloaded into scalar
+// registers, equal segments are the rows of a 2-D grid, and otherwise a
+// branch-free count over the table's tile offsets finds it.
 #include "rr_internal.h"
 
 namespace rr {
