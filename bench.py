@@ -567,13 +567,14 @@ def sweep_summary(args):
         out += [f"## {dt}: fastest stand-in pattern", ""] + table({k: v.get("pattern", "relay") for k, v in st.items()},
                                                                   sizes, str, SWEEP_ORDER) + [""]
         # write-back stores timed alone end with written lines still in the
-        # Infinity Cache; the non-temporal patterns have no such deferral
+        # caches; the non-temporal and write-through patterns have no such
+        # deferral
         nt = {}
         for k, v in st.items():
             pats = {p: g for p, g in v.get("patterns", {}).items() if not p.endswith("_wb")}
             if pats:
                 nt[k] = g_row[k] / max(pats.values()) if (g_row := {kk: r["gbs_median"] for kk, r in g.items()}) else None
-        out += [f"## {dt}: relay launch / fastest non-temporal stand-in (median)", ""] + table(
+        out += [f"## {dt}: relay launch / fastest stand-in without write-back stores (median)", ""] + table(
             nt, sizes, lambda v: f"{v:.2f}", SWEEP_ORDER) + [""]
         orc = {k: r for k, r in g.items() if r.get("oracle")}
         if orc:
@@ -1152,11 +1153,13 @@ def sweep(args):
 # --------------------------------------------------------------------------
 
 CALIB_MIXES = [(1, 0), (2, 0), (4, 0), (0, 1), (1, 1), (2, 1), (3, 1), (4, 1), (2, 2)]
-# bench_calib.hip's access patterns, by index: the relay kernels' own (16 KiB
-# tiles, one per workgroup, non-temporal), smaller tiles, several tiles per
+# bench_calib.hip's access patterns, by index: the relay reductions' own (16
+# KiB tiles, one per workgroup, non-temporal), smaller tiles, several tiles per
 # workgroup with the next tile's loads before the current stores, a persistent
-# double-buffered grid, and write-back stores
-CALIB_PATTERNS = ["relay", "tile8k", "tile4k", "multi2", "multi4", "persistent", "persist_wb", "relay_wb"]
+# double-buffered grid, write-back stores, and agent-scope (write-through)
+# stores with 16 and 8 KiB tiles (the relay copies' stores)
+CALIB_PATTERNS = ["relay", "tile8k", "tile4k", "multi2", "multi4", "persistent", "persist_wb", "relay_wb",
+                  "relay_wt", "tile8k_wt"]
 
 
 def calibrate(args):

@@ -21,7 +21,11 @@
 //                 over 8 KiB tiles with a stride of the grid, register double
 //                 buffered as multi4;
 //   6 persist_wb  persistent with write-back (cached) stores;
-//   7 relay_wb    the relay pattern with write-back stores.
+//   7 relay_wb    the relay pattern with write-back stores;
+//   8 relay_wt    the relay pattern with agent-scope stores (the sc1
+//                 cache-policy bit: the L2 writes each line through at once);
+//   9 tile8k_wt   8 KiB tiles with agent-scope stores (the relay copies'
+//                 pattern for calls under the long-call size).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,7 +58,11 @@ __device__ __forceinline__ void load_tile(const Streams &s, int64_t t, Tile<R> &
             d.x[u][r] = __builtin_nontemporal_load(s.in[r] + base + u * kBlock);
 }
 
-template <int R, int W, int U, bool NT>
+// Store policies: non-temporal, write-back (cached), agent scope (a buffer
+// store with the sc1 cache-policy bit, resource on the tile).
+enum StorePolicy { kNT = 0, kWB = 1, kWT = 2 };
+
+template <int R, int W, int U, int SP>
 __device__ __forceinline__ void store_tile(const Streams &s, int64_t t, const Tile<R> &d)
 {
     const int64_t base = t * (kBlock * U) + threadIdx.x;
@@ -66,10 +74,15 @@ __device__ __forceinline__ void store_tile(const Streams &s, int64_t t, const Ti
             v ^= d.x[u][r];
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-            if (NT)
+            if (SP == kNT) {
                 __builtin_nontemporal_store(v, s.out[w] + base + u * kBlock);
-            else
+            } else if (SP == kWB) {
                 s.out[w][base + u * kBlock] = v;
+            } else {
+                __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(s.out[w] + t * (kBlock * U), (short)0,
+                                                                              kBlock * U * 16, 0x00020000);
+                __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)((threadIdx.x + u * kBlock) * 16), 0, 16);
+            }
         }
         if (W == 0 && v.x == 0x9E3779B9u && v.y == 0x7F4A7C15u && v.z == 0xF39CC060u)
             s.sink[0] = v;  // keeps the loads of a read-only stream alive
@@ -79,7 +92,7 @@ __device__ __forceinline__ void store_tile(const Streams &s, int64_t t, const Ti
 // Tiles first, first + step, first + 2*step, ... below ntiles, each tile's
 // successor loaded before the tile is stored.  Every tile index is checked
 // against ntiles before it is touched.
-template <int R, int W, int U, bool NT>
+template <int R, int W, int U, int SP>
 __device__ __forceinline__ void run_tiles(const Streams &s, int64_t first, int64_t step, int64_t last,
                                           int64_t ntiles)
 {
@@ -92,18 +105,18 @@ __device__ __forceinline__ void run_tiles(const Streams &s, int64_t first, int64
         const int64_t t1 = t + step;
         if (t1 < end)
             load_tile<R, U>(s, t1, b);
-        store_tile<R, W, U, NT>(s, t, a);
+        store_tile<R, W, U, SP>(s, t, a);
         if (t1 >= end)
             break;
         const int64_t t2 = t1 + step;
         if (t2 < end)
             load_tile<R, U>(s, t2, a);
-        store_tile<R, W, U, NT>(s, t1, b);
+        store_tile<R, W, U, SP>(s, t1, b);
     }
 }
 
-// One tile per workgroup (patterns 0, 1, 2, 7).
-template <int R, int W, int U, bool NT>
+// One tile per workgroup (patterns 0, 1, 2, 7, 8, 9).
+template <int R, int W, int U, int SP>
 __global__ __launch_bounds__(kBlock) void one_tile_kernel(Streams s, int64_t ntiles)
 {
     const int64_t t = blockIdx.x;
@@ -111,7 +124,7 @@ __global__ __launch_bounds__(kBlock) void one_tile_kernel(Streams s, int64_t nti
         return;
     Tile<R> a;
     load_tile<R, U>(s, t, a);
-    store_tile<R, W, U, NT>(s, t, a);
+    store_tile<R, W, U, SP>(s, t, a);
 }
 
 // TPW consecutive tiles per workgroup (patterns 3, 4).
@@ -119,14 +132,14 @@ template <int R, int W, int U, int TPW>
 __global__ __launch_bounds__(kBlock) void multi_tile_kernel(Streams s, int64_t ntiles)
 {
     const int64_t first = (int64_t)blockIdx.x * TPW;
-    run_tiles<R, W, U, true>(s, first, 1, first + TPW, ntiles);
+    run_tiles<R, W, U, kNT>(s, first, 1, first + TPW, ntiles);
 }
 
 // A grid of resident workgroups striding over the tiles (patterns 5, 6).
-template <int R, int W, int U, bool NT>
+template <int R, int W, int U, int SP>
 __global__ __launch_bounds__(kBlock) void persistent_kernel(Streams s, int64_t ntiles)
 {
-    run_tiles<R, W, U, NT>(s, blockIdx.x, gridDim.x, ntiles, ntiles);
+    run_tiles<R, W, U, SP>(s, blockIdx.x, gridDim.x, ntiles, ntiles);
 }
 
 // The fixed cost of a launch, apart: a kernel that touches no memory, and
@@ -150,7 +163,7 @@ __global__ __launch_bounds__(kBlock) void touch_kernel(const u32x4 *in, u32x4 *o
     }
 }
 
-constexpr int kPatterns = 8;
+constexpr int kPatterns = 10;
 
 template <int R, int W>
 hipError_t launch(int pattern, const Streams &s, int64_t vectors, hipStream_t st)
@@ -183,14 +196,16 @@ hipError_t launch(int pattern, const Streams &s, int64_t vectors, hipStream_t st
         return hipGetLastError();
     };
     switch (pattern) {
-    case 0: return one(one_tile_kernel<R, W, 4, true>, 4);
-    case 1: return one(one_tile_kernel<R, W, 2, true>, 2);
-    case 2: return one(one_tile_kernel<R, W, 1, true>, 1);
+    case 0: return one(one_tile_kernel<R, W, 4, kNT>, 4);
+    case 1: return one(one_tile_kernel<R, W, 2, kNT>, 2);
+    case 2: return one(one_tile_kernel<R, W, 1, kNT>, 1);
     case 3: return multi(multi_tile_kernel<R, W, 4, 2>, 4, 2);
     case 4: return multi(multi_tile_kernel<R, W, 2, 4>, 2, 4);
-    case 5: return persist(persistent_kernel<R, W, 2, true>, 2);
-    case 6: return persist(persistent_kernel<R, W, 2, false>, 2);
-    case 7: return one(one_tile_kernel<R, W, 4, false>, 4);
+    case 5: return persist(persistent_kernel<R, W, 2, kNT>, 2);
+    case 6: return persist(persistent_kernel<R, W, 2, kWB>, 2);
+    case 7: return one(one_tile_kernel<R, W, 4, kWB>, 4);
+    case 8: return one(one_tile_kernel<R, W, 4, kWT>, 4);
+    case 9: return one(one_tile_kernel<R, W, 2, kWT>, 2);
     default: return hipErrorInvalidValue;
     }
 }
@@ -202,7 +217,7 @@ extern "C" {
 int calib_patterns(void) { return kPatterns; }
 
 // Streams `vectors` 16-byte vectors (a positive multiple of 1024) through R
-// inputs and W outputs in access pattern `pattern` (0..7, listed above), all
+// inputs and W outputs in access pattern `pattern` (0..9, listed above), all
 // device buffers owned by the caller.  Returns a hipError_t.
 int calib_stream_pattern(int pattern, int R, int W, const void *const *in, void *const *out, void *sink,
                          int64_t vectors, void *stream)

@@ -91,6 +91,7 @@ hipError_t emit_copy(const rr::CopyBatch &b, int64_t tiles, bool shifted, hipStr
     r.tiles = tiles;
     r.copy.nseg = b.nseg;
     r.copy.long_tiles = b.long_tiles;
+    r.copy.nt_stores = b.nt_stores;
     for (int i = 0; i < b.nseg; ++i) {
         r.copy.tile0[i] = b.tile0[i];
         r.copy.seg[i] = b.seg[i];
@@ -651,12 +652,15 @@ rr_status check_moves(const std::vector<Move> &mv, size_t culprit[2])
 
 class CopyLauncher {
 public:
-    // long_call: the call moves at least kCopyLongBytes, all of it in aligned
-    // moves, which then use the long-call tiles.
-    CopyLauncher(hipStream_t st, bool long_call) : st_(st)
+    // long_call: the call moves at least kCopyLongBytes; aligned: all of it
+    // in aligned moves.  A long call stores non-temporally, and takes the
+    // long-call tiles if it is aligned.
+    CopyLauncher(hipStream_t st, bool long_call, bool aligned) : st_(st)
     {
         b_.nseg = 0;
-        b_.long_tiles = long_call ? 1 : 0;
+        b_.long_tiles = long_call && aligned ? 1 : 0;
+        b_.nt_stores = long_call ? 1 : 0;
+        b_.pad = 0;
     }
 
     // One segment per move (tile 0 also copies its head and tail bytes), all
@@ -753,7 +757,7 @@ rr_status run_copy(const std::vector<Move> &mv, void *stream, bool batch)
         total += m.nbytes;
         aligned = aligned && (m.nbytes <= 0 || addr(m.src) % 16 == addr(m.dst) % 16);
     }
-    CopyLauncher L(static_cast<hipStream_t>(stream), aligned && total >= rr::kCopyLongBytes);
+    CopyLauncher L(static_cast<hipStream_t>(stream), total >= rr::kCopyLongBytes, aligned);
     for (const Move &m : mv)
         L.add(m.src, m.dst, m.nbytes);
     const hipError_t e = L.finish();

@@ -191,6 +191,20 @@ __host__ __device__ inline int64_t vec_index(int64_t lt, int x, int u)
     return lt * tile_vecs<U>() + int64_t(x) + int64_t(u) * kBlock;
 }
 
+// The body vectors of tile lt (tiles of tv vectors, body of nv vectors, the
+// tile holding at least one): the first one and how many.  A copy tile's
+// stores address its vectors relative to `first` (vec_index with lt = 0), in
+// a buffer range of `count` vectors.
+struct TileBody {
+    int64_t first, count;
+};
+
+__host__ __device__ inline TileBody tile_body(int64_t lt, int64_t tv, int64_t nv)
+{
+    const int64_t first = lt * tv;
+    return TileBody{first, nv - first < tv ? nv - first : tv};
+}
+
 // Tile lt of a body of nv vectors is full (every lane's every step in range).
 __host__ __device__ inline bool full_tile(int64_t lt, int64_t tv, int64_t nv)
 {
@@ -285,11 +299,16 @@ __host__ __device__ constexpr int64_t red_tile_vecs(int32_t mode)
 
 // long_tiles: the batch belongs to a call that moves at least kCopyLongBytes
 // in aligned moves only; they use tiles of kCopyUnrollLong vectors per lane.
+// nt_stores: the batch belongs to a call that moves at least kCopyLongBytes
+// (aligned or not); its stores are non-temporal, those of every other call
+// agent-scope write-through stores.
 template <int CAP>
 struct CopyBatchT {
     int32_t tile0[CAP];
     int32_t nseg;
     int32_t long_tiles;
+    int32_t nt_stores;
+    int32_t pad;
     CopySeg seg[CAP];
 };
 constexpr int kSmallCopySegs = 16;

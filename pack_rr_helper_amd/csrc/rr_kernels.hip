@@ -406,6 +406,43 @@ __global__ __launch_bounds__(kBlock) void reduce_shifted_one_kernel(const void *
 // Copy
 // ---------------------------------------------------------------------------
 
+// The destination of one copy tile.  Copies of calls under kCopyLongBytes
+// store with agent scope (WT: the sc1 cache-policy bit, no non-temporal
+// hint): the L2 writes each line through to memory at once instead of holding
+// it dirty until the end-of-kernel release, so less is left to drain between
+// this launch and the next.  A buffer store carries that policy; its resource
+// starts at the tile's first destination vector (uniform across the
+// workgroup) and spans the tile's body vectors.  Long calls keep
+// non-temporal stores, which measured faster there.
+constexpr int kBufferFormat = 0x00020000;  // raw buffer: 32-bit data format, no swizzle
+constexpr int kStoreAgentScope = 16;       // cache-policy operand: sc1
+
+template <bool WT>
+struct TileOut {
+    u32x4 *first;
+    __amdgpu_buffer_rsrc_t r;
+    __device__ TileOut(u32x4 *first_, int64_t nvec)
+        : first(first_), r(__builtin_amdgcn_make_buffer_rsrc(first_, (short)0, (int)(nvec * 16), kBufferFormat))
+    {
+    }
+    // Vector i of the tile (0 <= i < nvec).
+    __device__ void put(int64_t i, u32x4 v) const
+    {
+        if constexpr (WT)
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)(i * 16), 0, kStoreAgentScope);
+        else
+            st16(first + i, v);
+    }
+};
+
+// Tile lt of a body of nv vectors in tiles of tv vectors.
+template <bool WT>
+__device__ __forceinline__ TileOut<WT> tile_out(u32x4 *dst, int64_t lt, int64_t tv, int64_t nv)
+{
+    const TileBody tb = tile_body(lt, tv, nv);
+    return TileOut<WT>(dst + tb.first, tb.count);
+}
+
 // Tile 0 of a copy segment also moves its head and tail bytes (at most 15
 // each): the first wave's lanes the head, the second wave's the tail.
 __device__ __forceinline__ void copy_edges(const CopySeg &sg, const CopySplit &sp)
@@ -420,8 +457,8 @@ __device__ __forceinline__ void copy_edges(const CopySeg &sg, const CopySplit &s
 }
 
 // U: 16-byte vectors per lane in a tile (kCopyUnroll, or kCopyUnrollLong
-// for the batches of a long call).
-template <int U>
+// for the batches of a long call); WT: agent-scope stores (TileOut).
+template <int U, bool WT>
 __device__ __forceinline__ void copy_aligned(const CopySeg &sg, int64_t lt)
 {
     const CopySplit sp = copy_split(sg.dst, sg.nbytes);
@@ -429,19 +466,21 @@ __device__ __forceinline__ void copy_aligned(const CopySeg &sg, int64_t lt)
     const u32x4 *src = reinterpret_cast<const u32x4 *>(sg.src + sp.head);
     u32x4 *dst = reinterpret_cast<u32x4 *>(sg.dst + sp.head);
     if (full_tile(lt, tile_vecs<U>(), nv)) {
+        const TileOut<WT> out = tile_out<WT>(dst, lt, tile_vecs<U>(), nv);
         u32x4 x[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
             x[u] = ld16(src + vec_index<U>(lt, lane(), u));
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            st16(dst + vec_index<U>(lt, lane(), u), x[u]);
-    } else {
+            out.put(vec_index<U>(0, lane(), u), x[u]);
+    } else if (nv > 0) {  // uniform across the workgroup
+        const TileOut<WT> out = tile_out<WT>(dst, lt, tile_vecs<U>(), nv);
         for (int u = 0; u < U; ++u) {
             const int64_t v = vec_index<U>(lt, lane(), u);
             if (v >= nv)
                 break;
-            st16(dst + v, ld16(src + v));
+            out.put(vec_index<U>(0, lane(), u), ld16(src + v));
         }
     }
     if (lt == 0)
@@ -458,7 +497,7 @@ __device__ __forceinline__ void copy_aligned(const CopySeg &sg, int64_t lt)
 // nothing.  Word nv always holds at least one byte of the body (shift > 0),
 // and an aligned 16-byte word never straddles a page, so that read stays in
 // mapped memory even where the source buffer ends inside the word.
-template <int Q>
+template <int Q, bool WT>
 __device__ __forceinline__ void copy_shifted(const CopySeg &sg, int64_t lt)
 {
     const CopySplit sp = copy_split(sg.dst, sg.nbytes);
@@ -476,11 +515,12 @@ __device__ __forceinline__ void copy_shifted(const CopySeg &sg, int64_t lt)
             a[u] = loads_own_word(true, v, nv, true) ? ld16(src + v) : zero;
             c[u] = loads_next_word(true, v, nv, true, last) ? ld16(src + v + 1) : zero;
         }
+        const TileOut<WT> out = tile_out<WT>(dst, lt, tile_vecs<kShiftUnroll>(), nv);
 #pragma unroll
         for (int u = 0; u < kShiftUnroll; ++u) {
             const u32x4 nb = next_lane(a[u]);  // on every lane: the source lane must be active
             const u32x4 b = last ? c[u] : nb;
-            st16(dst + vec_index<kShiftUnroll>(lt, lane(), u), realign<Q>(a[u], b, r));
+            out.put(vec_index<kShiftUnroll>(0, lane(), u), realign<Q>(a[u], b, r));
         }
     } else if (nv > 0) {  // uniform across the workgroup
 #pragma unroll
@@ -489,32 +529,34 @@ __device__ __forceinline__ void copy_shifted(const CopySeg &sg, int64_t lt)
             a[u] = loads_own_word(false, v, nv, true) ? ld16(src + v) : zero;
             c[u] = loads_next_word(false, v, nv, true, last) ? ld16(src + v + 1) : zero;
         }
+        const TileOut<WT> out = tile_out<WT>(dst, lt, tile_vecs<kShiftUnroll>(), nv);
 #pragma unroll
         for (int u = 0; u < kShiftUnroll; ++u) {
             const int64_t v = vec_index<kShiftUnroll>(lt, lane(), u);
             const u32x4 nb = next_lane(a[u]);
             const u32x4 b = last ? c[u] : nb;
             if (v < nv)
-                st16(dst + v, realign<Q>(a[u], b, r));
+                out.put(vec_index<kShiftUnroll>(0, lane(), u), realign<Q>(a[u], b, r));
         }
     }
     if (lt == 0)
         copy_edges(sg, sp);
 }
 
-// Segments whose source and destination agree modulo 16 bytes.
-template <int CAP, int U>
+// Segments whose source and destination agree modulo 16 bytes.  U and WT
+// as in copy_aligned.
+template <int CAP, int U, bool WT>
 __global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatchT<CAP> b)
 {
     const int32_t t = (int32_t)blockIdx.x;
     const int s = find_seg(b.tile0, b.nseg, t);
-    copy_aligned<U>(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
+    copy_aligned<U, WT>(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
 }
 
-template <int CAP, int U>
+template <int CAP, int U, bool WT>
 __global__ __launch_bounds__(kBlock) void copy_uniform_kernel(CopyBatchT<CAP> b)
 {
-    copy_aligned<U>(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
+    copy_aligned<U, WT>(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
 }
 
 // Any segment: realigned (source and destination disagree modulo 16 bytes)
@@ -522,33 +564,33 @@ __global__ __launch_bounds__(kBlock) void copy_uniform_kernel(CopyBatchT<CAP> b)
 // both (a segmentCount that is not a multiple of 8) takes one launch.  The
 // aligned-only kernels above keep the smaller register budget for calls
 // without realigned moves.
-template <int U>
+template <int U, bool WT>
 __device__ __forceinline__ void copy_mixed_seg(const CopySeg &sg, int64_t lt)
 {
     if (sg.mode != kCopyShifted) {  // uniform across the workgroup
-        copy_aligned<U>(sg, lt);
+        copy_aligned<U, WT>(sg, lt);
         return;
     }
     switch (sg.shift >> 2) {
-    case 0: copy_shifted<0>(sg, lt); break;
-    case 1: copy_shifted<1>(sg, lt); break;
-    case 2: copy_shifted<2>(sg, lt); break;
-    default: copy_shifted<3>(sg, lt); break;
+    case 0: copy_shifted<0, WT>(sg, lt); break;
+    case 1: copy_shifted<1, WT>(sg, lt); break;
+    case 2: copy_shifted<2, WT>(sg, lt); break;
+    default: copy_shifted<3, WT>(sg, lt); break;
     }
 }
 
-template <int CAP, int U>
+template <int CAP, int U, bool WT>
 __global__ __launch_bounds__(kBlock) void copy_mixed_kernel(CopyBatchT<CAP> b)
 {
     const int32_t t = (int32_t)blockIdx.x;
     const int s = find_seg(b.tile0, b.nseg, t);
-    copy_mixed_seg<U>(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
+    copy_mixed_seg<U, WT>(load_seg(b.seg[s]), (int64_t)(t - b.tile0[s]));
 }
 
-template <int CAP, int U>
+template <int CAP, int U, bool WT>
 __global__ __launch_bounds__(kBlock) void copy_mixed_uniform_kernel(CopyBatchT<CAP> b)
 {
-    copy_mixed_seg<U>(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
+    copy_mixed_seg<U, WT>(load_seg(b.seg[blockIdx.y]), (int64_t)blockIdx.x);
 }
 
 }  // namespace
@@ -630,7 +672,7 @@ void launch_reduce_sized(const RedBatch &b, const LaunchShape &sh, int64_t total
     }
 }
 
-template <int CAP, int U>
+template <int CAP, int U, bool WT>
 void launch_copy_table(const CopyBatchT<CAP> &b, const LaunchShape &sh, int64_t total_tiles, bool shifted,
                        hipStream_t stream)
 {
@@ -639,26 +681,30 @@ void launch_copy_table(const CopyBatchT<CAP> &b, const LaunchShape &sh, int64_t 
         const dim3 grid((unsigned)sh.gx, (unsigned)sh.gy);
         const unsigned lds = total_tiles >= kThrottleTiles ? kThrottleLds : 0u;
         if (shifted)
-            copy_mixed_uniform_kernel<CAP, U><<<grid, block, lds, stream>>>(b);
+            copy_mixed_uniform_kernel<CAP, U, WT><<<grid, block, lds, stream>>>(b);
         else
-            copy_uniform_kernel<CAP, U><<<grid, block, lds, stream>>>(b);
+            copy_uniform_kernel<CAP, U, WT><<<grid, block, lds, stream>>>(b);
     } else {
         const dim3 grid((unsigned)total_tiles);
         if (shifted)
-            copy_mixed_kernel<CAP, U><<<grid, block, 0, stream>>>(b);
+            copy_mixed_kernel<CAP, U, WT><<<grid, block, 0, stream>>>(b);
         else
-            copy_kernel<CAP, U><<<grid, block, 0, stream>>>(b);
+            copy_kernel<CAP, U, WT><<<grid, block, 0, stream>>>(b);
     }
 }
 
+// Long calls (the batch's nt_stores) keep non-temporal stores, in the
+// long-call tiles when aligned; every other copy stores with agent scope.
 template <int CAP>
 void launch_copy_sized(const CopyBatchT<CAP> &b, const LaunchShape &sh, int64_t total_tiles, bool shifted,
                        hipStream_t stream)
 {
     if (b.long_tiles)
-        launch_copy_table<CAP, kCopyUnrollLong>(b, sh, total_tiles, shifted, stream);
+        launch_copy_table<CAP, kCopyUnrollLong, false>(b, sh, total_tiles, shifted, stream);
+    else if (b.nt_stores)
+        launch_copy_table<CAP, kCopyUnroll, false>(b, sh, total_tiles, shifted, stream);
     else
-        launch_copy_table<CAP, kCopyUnroll>(b, sh, total_tiles, shifted, stream);
+        launch_copy_table<CAP, kCopyUnroll, true>(b, sh, total_tiles, shifted, stream);
 }
 
 }  // namespace
@@ -691,6 +737,7 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
     if (b.nseg <= kSmallCopySegs) {
         CopyBatchT<kSmallCopySegs> t = shrink<CopyBatchT<kSmallCopySegs>>(b);
         t.long_tiles = b.long_tiles;
+        t.nt_stores = b.nt_stores;
         launch_copy_sized(t, sh, total_tiles, shifted, stream);
     } else {
         launch_copy_sized(b, sh, total_tiles, shifted, stream);

@@ -49,6 +49,7 @@ bool touches(uintptr_t a, int64_t n)
 long g_forms[2][3];  // launches per (copy?, launch form)
 long g_long_copies[2];  // copy launches per tiling (0 default, 1 long-call)
 long g_shifted_copies;  // copy launches in the mixed-mode (realigning) kernels
+long g_nt_copies[2];    // copy launches per store policy (0 agent scope, 1 non-temporal)
 
 void violation(const char *what, uintptr_t a, int64_t n)
 {
@@ -222,9 +223,15 @@ void replay_copy_tile(const rr::CopyBatch &b, int s, int64_t total, int64_t lt, 
                     if (loads_next_word(full, v, nv, true, wave_end(x)) && !touches(uintptr_t(base + (v + 1) * 16), 16))
                         violation("realigned word outside every buffer", uintptr_t(base + (v + 1) * 16), 16);
                 }
-                if (full || v < nv)
+                if (full || v < nv) {
+                    // the kernel stores vector i of the tile's body range
+                    const TileBody tb = tile_body(lt, tv, nv);
+                    const int64_t i = vec_index<U>(0, x, u);
+                    if (tb.first + i != v || i < 0 || i >= tb.count)
+                        violation("copy store outside its tile's buffer range", uintptr_t(sg.dst), i);
                     for (int e = 0; e < 16; ++e)
-                        copy_byte(sg.src, sg.dst, sp.head + v * 16 + e);
+                        copy_byte(sg.src, sg.dst, sp.head + (tb.first + i) * 16 + e);
+                }
             }
     if (lt == 0)
         for (int x = 0; x < kBlock; ++x) {
@@ -293,6 +300,11 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
         violation("single-segment form for a copy", 0, 0);
     if (b.long_tiles != 0 && b.long_tiles != 1)
         violation("copy batch with an unknown tiling", 0, b.long_tiles);
+    if (b.nt_stores != 0 && b.nt_stores != 1)
+        violation("copy batch with an unknown store policy", 0, b.nt_stores);
+    if (b.long_tiles && !b.nt_stores)
+        violation("long-call tiles without the long call's store policy", 0, 0);
+    ++g_nt_copies[b.nt_stores != 0];
     ++g_long_copies[b.long_tiles != 0];
     g_shifted_copies += shifted ? 1 : 0;
     if (b.long_tiles && shifted)
@@ -340,6 +352,7 @@ void sim_reset(void)
     memset(g_forms, 0, sizeof g_forms);
     memset(g_long_copies, 0, sizeof g_long_copies);
     g_shifted_copies = 0;
+    memset(g_nt_copies, 0, sizeof g_nt_copies);
     g_msg[0] = '\0';
 }
 void sim_register(const void *p, int64_t bytes, int writable)
@@ -356,4 +369,6 @@ const char *sim_message(void) { return g_msg; }
 long sim_copy_launches(int long_tiles) { return g_long_copies[long_tiles != 0]; }
 // copy launches since the last reset in the mixed-mode (realigning) kernels
 long sim_shifted_copy_launches(void) { return g_shifted_copies; }
+// copy launches since the last reset with agent-scope (0) or non-temporal (1) stores
+long sim_nt_copy_launches(int nt) { return g_nt_copies[nt != 0]; }
 }

@@ -153,15 +153,19 @@ def _tiling_used(sim, long_copies):
 def _copy_call(sim, name, *args):
     """Issues one copy call; checks that it took the long-call tiling exactly
     when the library forces it and none of its moves is realigned (every launch
-    in the aligned-only kernels).  Returns whether it did (False for a call
-    with nothing to move)."""
+    in the aligned-only kernels), and the long call's non-temporal stores
+    exactly when the library forces it.  Returns whether it took the long
+    tiling (False for a call with nothing to move)."""
     L = sim.L
-    before = (L.sim_copy_launches(1), L.sim_copy_launches(0), L.sim_shifted_copy_launches())
+    before = (L.sim_copy_launches(1), L.sim_copy_launches(0), L.sim_shifted_copy_launches(),
+              L.sim_nt_copy_launches(1))
     sim.call(name, *args)
-    n_long, n_default, n_shifted = (L.sim_copy_launches(1) - before[0], L.sim_copy_launches(0) - before[1],
-                                    L.sim_shifted_copy_launches() - before[2])
+    n_long, n_default, n_shifted, n_nt = (L.sim_copy_launches(1) - before[0], L.sim_copy_launches(0) - before[1],
+                                          L.sim_shifted_copy_launches() - before[2],
+                                          L.sim_nt_copy_launches(1) - before[3])
     if n_long + n_default == 0:  # nothing to move
         return False
+    assert n_nt == (n_long + n_default if sim.long_copies else 0)
     want_long = sim.long_copies and n_shifted == 0
     assert (n_long > 0 and n_default == 0) if want_long else n_long == 0
     return want_long
