@@ -139,6 +139,10 @@ def parse():
     p.add_argument("--sweep-rows", default=",".join(SWEEP_ROWS),
                    help="rows of the per-role sweep; the _shifted rows put every input at an odd "
                         "element offset (the realigning reduction kernels)")
+    p.add_argument("--library", default=None,
+                   help="run this build of the relay library instead of pack_rr_helper_amd/librr.so (for A/B "
+                        "comparisons of build options); the counter traffic of profiles/traffic.json is then "
+                        "not attached")
     p.add_argument("--flush", choices=("read", "write", "none"), default="read",
                    help="--calibrate-alone: how a launch's inputs are pushed out of the caches before it is timed")
     p.add_argument("--sweep-out", default=None)
@@ -477,6 +481,9 @@ def kernel_source_digest():
 
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+# --library: another build of the relay library is running (its counters are
+# not the stored ones)
+CUSTOM_LIBRARY = None
 
 
 def workload_name(message_mib, dtype="bf16", ragged_a2a=False):
@@ -494,7 +501,7 @@ def traffic_for(kernel, message_mib, variant, algo_bytes_per_launch, launches_pe
     workload, other launches per step, or other algorithmic bytes per launch),
     or taken on other kernel sources.  workload: the step's workload_name
     (default: the plain step's)."""
-    if not os.path.exists(path):
+    if CUSTOM_LIBRARY or not os.path.exists(path):
         return None
     with open(path) as fh:
         t = json.load(fh)
@@ -962,6 +969,7 @@ def step_bench(args):
             "timed_region_1": "K steps, no events between launches (value, ms_per_step)",
             **rows_of(t),
             "launch_order": [row for row, _, _, _ in calls],
+            **({"library": CUSTOM_LIBRARY} if CUSTOM_LIBRARY else {}),
         },
         "roofline": roofline_of(t, args.steps, args.message_mib, args.variant, args.dtype,
                                 workload_name(args.message_mib, args.dtype, args.ragged_a2a)),
@@ -983,10 +991,11 @@ def step_bench(args):
         result["stand_in_step"] = {
             "what": ("the same launch sequence with every launch replaced by a plain stream kernel "
                      "(bench_calib.hip) of its read/write mix and bytes, in each of the calibration's access "
-                     "patterns and with the fastest pattern per launch, timed like timed region 1; "
-                     "relay_over_stand_in compares with the fastest of them"),
+                     "patterns, with the fastest pattern per launch, and with the library's own store "
+                     "policy per launch, timed like timed region 1; relay_over_stand_in compares with the "
+                     "fastest of them"),
             "unit": "GB/s",
-            **stand_in_ceiling(calls, args.buffer_sets, stream, args.steps, args.warmup, value)}
+            **stand_in_ceiling(calls, args.buffer_sets, stream, args.steps, args.warmup, value, args.ragged_a2a)}
     if args.sizes:
         # the same step at the larger messages of the configurations (the A=4
         # allreduce's 256 MiB, the all-to-all's 1 GiB), one GPU's share and
@@ -1387,14 +1396,36 @@ def b2b_timer(trials=5, min_launches=30):
     return times_of
 
 
-def stand_in_ceiling(calls, nsets, stream, steps, warmup, value):
+# the long-call size of the library's copies (RR_COPY_LONG_BYTES): calls that
+# move at least this many bytes store non-temporally (4 KiB tiles when aligned)
+COPY_LONG_BYTES = 512 << 20
+
+
+def library_patterns(calls, ragged=False):
+    """Per launch, the calibration pattern with the relay kernels' own tiles
+    and store policy: the reductions 16 KiB tiles, non-temporal stores; the
+    copies 8 KiB tiles with agent-scope stores, or from the long-call size
+    non-temporal stores in 4 KiB tiles (8 KiB for a ragged all-to-all)."""
+    pats = []
+    for row, _, b, _ in calls:
+        if row.startswith("a2a"):
+            long_call = b // 2 >= COPY_LONG_BYTES
+            name = ("tile8k" if ragged else "tile4k") if long_call else "tile8k_wt"
+        else:
+            name = "relay"
+        pats.append(CALIB_PATTERNS.index(name))
+    return pats
+
+
+def stand_in_ceiling(calls, nsets, stream, steps, warmup, value, ragged=False):
     """The step's launch sequence replaced by plain streams of each launch's
     read/write mix and bytes, in every access pattern of bench_calib.hip
-    (the same pattern for every launch), and once with each launch in the
+    (the same pattern for every launch), once with each launch in the
     pattern that ran its mix and bytes fastest (each launch's patterns timed
-    back to back over rotating buffer sets); each step timed like timed
-    region 1.  The fastest of these is the ceiling the relay step is compared
-    with."""
+    back to back over rotating buffer sets), and once with each launch in the
+    relay kernels' own tiles and store policy (library_patterns); each step
+    timed like timed region 1.  The fastest of these is the ceiling the relay
+    step is compared with."""
     import torch
     out = {"patterns": {}}
     for pi, name in enumerate(CALIB_PATTERNS):
@@ -1424,7 +1455,17 @@ def stand_in_ceiling(calls, nsets, stream, steps, warmup, value):
                               "patterns": {c[0]: CALIB_PATTERNS[b] for c, b in zip(calls, best)}}
     del st_sets
     torch.cuda.empty_cache()
-    cands = [(v["value"], k) for k, v in out["patterns"].items()] + [(gbs, "best_per_launch")]
+    lib_pats = library_patterns(calls, ragged)
+    st_sets, _, st_bytes = stand_in_step(calls, nsets, stream, lib_pats)
+    ms = time_steps(lambda i: st_sets[i % nsets], steps, warmup, stream)
+    lib_gbs = st_bytes / (ms * 1e-3) / 1e9
+    out["library_policy"] = {"value": round(lib_gbs, 1), "pct_of_peak": round(100.0 * lib_gbs / PEAK_GBS, 2),
+                             "ms_per_step": round(ms, 5),
+                             "patterns": {c[0]: CALIB_PATTERNS[b] for c, b in zip(calls, lib_pats)}}
+    del st_sets
+    torch.cuda.empty_cache()
+    cands = [(v["value"], k) for k, v in out["patterns"].items()] + [(gbs, "best_per_launch"),
+                                                                      (lib_gbs, "library_policy")]
     ceil, which = max(cands)
     out["ceiling"] = {"value": round(ceil, 1), "pct_of_peak": round(100.0 * ceil / PEAK_GBS, 2), "from": which}
     out["relay_over_stand_in"] = round(value / ceil, 4)
@@ -1755,6 +1796,10 @@ def fit_from_trace(args):
 
 def main():
     args = parse()
+    if args.library:
+        global CUSTOM_LIBRARY
+        import pack_rr_helper_amd
+        CUSTOM_LIBRARY = pack_rr_helper_amd.library_path = os.path.abspath(args.library)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (--gpus {args.gpus} "
               "requested). The relay's local kernels shard per rank; run with --gpus 1.", file=sys.stderr)

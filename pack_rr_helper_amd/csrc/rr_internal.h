@@ -50,6 +50,10 @@ constexpr int64_t kMaxTilesPerLaunch = RR_MAX_TILES_PER_LAUNCH;
 #ifndef RR_COPY_LONG_BYTES
 #define RR_COPY_LONG_BYTES (int64_t(1) << 29)
 #endif
+#ifndef RR_COPY_AGENT_STORES
+#define RR_COPY_AGENT_STORES 1       // copies of calls under RR_COPY_LONG_BYTES store with agent
+                                     // scope (write-through L2); 0: non-temporal like long calls
+#endif
 
 #ifndef RR_SHIFT_RED_UNROLL
 #define RR_SHIFT_RED_UNROLL 2        // 16-byte vectors per thread per input in a realigning
@@ -61,6 +65,7 @@ constexpr int kShiftRedUnroll = RR_SHIFT_RED_UNROLL;
 constexpr int kCopyUnroll = RR_COPY_UNROLL;
 constexpr int kCopyUnrollLong = RR_COPY_UNROLL_LONG;
 constexpr int64_t kCopyLongBytes = RR_COPY_LONG_BYTES;
+constexpr bool kCopyAgentStores = RR_COPY_AGENT_STORES != 0;
 #ifndef RR_SHIFT_UNROLL
 #define RR_SHIFT_UNROLL 2            // 16-byte vectors per thread in a realigning copy tile
                                      // (8 KiB tiles; measured faster than 16 and 32 KiB)

@@ -701,7 +701,7 @@ void launch_copy_sized(const CopyBatchT<CAP> &b, const LaunchShape &sh, int64_t 
 {
     if (b.long_tiles)
         launch_copy_table<CAP, kCopyUnrollLong, false>(b, sh, total_tiles, shifted, stream);
-    else if (b.nt_stores)
+    else if (b.nt_stores || !kCopyAgentStores)
         launch_copy_table<CAP, kCopyUnroll, false>(b, sh, total_tiles, shifted, stream);
     else
         launch_copy_table<CAP, kCopyUnroll, true>(b, sh, total_tiles, shifted, stream);
