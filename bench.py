@@ -154,6 +154,8 @@ def parse():
     p.add_argument("--fit-log", default=None,
                    help="--role-fit: write the launch log (role, message, bytes of every relay launch in "
                         "issue order) here, to match a rocprofv3 kernel trace of the same run")
+    p.add_argument("--fit-min-mib", type=float, default=0.0,
+                   help="with --fit-trace: fit only the messages of at least this many MiB")
     p.add_argument("--fit-trace", default=None,
                    help="with --fit-log: fit per role from this rocprofv3 kernel_trace.csv instead of "
                         "running anything on the GPU; prints the table")
@@ -1763,6 +1765,8 @@ def fit_from_trace(args):
                                                         r["Kernel_Name"]).split("(")[0])
     tiny = samples.pop("one_tile", {})
     fixed = {r: statistics.median(samples.pop(r)[0.0][1]) * 1e6 for r in list(samples) if r.endswith("wg")}
+    if args.fit_min_mib:
+        samples = {r: {m: v for m, v in by.items() if m >= args.fit_min_mib} for r, by in samples.items()}
     fit = fit_table(samples)
     if args.sweep_out:
         with open(args.sweep_out, "w") as fh:
@@ -1799,7 +1803,9 @@ def main():
     if args.library:
         global CUSTOM_LIBRARY
         import pack_rr_helper_amd
-        CUSTOM_LIBRARY = pack_rr_helper_amd.library_path = os.path.abspath(args.library)
+        pack_rr_helper_amd.library_path = os.path.abspath(args.library)
+        rel = os.path.relpath(pack_rr_helper_amd.library_path, ROOT)
+        CUSTOM_LIBRARY = pack_rr_helper_amd.library_path if rel.startswith("..") else rel
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (--gpus {args.gpus} "
               "requested). The relay's local kernels shard per rank; run with --gpus 1.", file=sys.stderr)
