@@ -1765,7 +1765,7 @@ def fit_from_trace(args):
                                                         r["Kernel_Name"]).split("(")[0])
     tiny = samples.pop("one_tile", {})
     fixed = {r: statistics.median(samples.pop(r)[0.0][1]) * 1e6 for r in list(samples) if r.endswith("wg")}
-    if args.fit_min_mib:
+    if getattr(args, "fit_min_mib", 0):
         samples = {r: {m: v for m, v in by.items() if m >= args.fit_min_mib} for r, by in samples.items()}
     fit = fit_table(samples)
     if args.sweep_out:
