@@ -1398,21 +1398,27 @@ def b2b_timer(trials=5, min_launches=30):
     return times_of
 
 
-# the long-call size of the library's copies (RR_COPY_LONG_BYTES): calls that
-# move at least this many bytes store non-temporally (4 KiB tiles when aligned)
+# the library's copy sizes: calls that move at least COPY_AGENT_MAX_BYTES
+# (RR_COPY_AGENT_MAX_BYTES) store non-temporally, those of at least
+# COPY_LONG_BYTES (RR_COPY_LONG_BYTES) also take 4 KiB tiles when aligned
+COPY_AGENT_MAX_BYTES = 256 << 20
 COPY_LONG_BYTES = 512 << 20
 
 
 def library_patterns(calls, ragged=False):
     """Per launch, the calibration pattern with the relay kernels' own tiles
     and store policy: the reductions 16 KiB tiles, non-temporal stores; the
-    copies 8 KiB tiles with agent-scope stores, or from the long-call size
-    non-temporal stores in 4 KiB tiles (8 KiB for a ragged all-to-all)."""
+    copies 8 KiB tiles with agent-scope stores, non-temporal ones from
+    COPY_AGENT_MAX_BYTES moved, and from the long-call size 4 KiB tiles (8 KiB
+    for a ragged all-to-all)."""
     pats = []
     for row, _, b, _ in calls:
         if row.startswith("a2a"):
-            long_call = b // 2 >= COPY_LONG_BYTES
-            name = ("tile8k" if ragged else "tile4k") if long_call else "tile8k_wt"
+            moved = b // 2
+            if moved >= COPY_LONG_BYTES:
+                name = "tile8k" if ragged else "tile4k"
+            else:
+                name = "tile8k" if moved >= COPY_AGENT_MAX_BYTES else "tile8k_wt"
         else:
             name = "relay"
         pats.append(CALIB_PATTERNS.index(name))

@@ -652,14 +652,16 @@ rr_status check_moves(const std::vector<Move> &mv, size_t culprit[2])
 
 class CopyLauncher {
 public:
-    // long_call: the call moves at least kCopyLongBytes; aligned: all of it
-    // in aligned moves.  A long call stores non-temporally, and takes the
-    // long-call tiles if it is aligned.
-    CopyLauncher(hipStream_t st, bool long_call, bool aligned) : st_(st)
+    // total: the bytes the call moves; aligned: all of them in aligned moves.
+    // A call of at least kCopyLongBytes takes the long-call tiles if it is
+    // aligned; one of at least kCopyAgentMaxBytes (or a long one) stores
+    // non-temporally.
+    CopyLauncher(hipStream_t st, int64_t total, bool aligned) : st_(st)
     {
+        const bool long_call = total >= rr::kCopyLongBytes;
         b_.nseg = 0;
         b_.long_tiles = long_call && aligned ? 1 : 0;
-        b_.nt_stores = long_call ? 1 : 0;
+        b_.nt_stores = long_call || total >= rr::kCopyAgentMaxBytes ? 1 : 0;
         b_.pad = 0;
     }
 
@@ -757,7 +759,7 @@ rr_status run_copy(const std::vector<Move> &mv, void *stream, bool batch)
         total += m.nbytes;
         aligned = aligned && (m.nbytes <= 0 || addr(m.src) % 16 == addr(m.dst) % 16);
     }
-    CopyLauncher L(static_cast<hipStream_t>(stream), total >= rr::kCopyLongBytes, aligned);
+    CopyLauncher L(static_cast<hipStream_t>(stream), total, aligned);
     for (const Move &m : mv)
         L.add(m.src, m.dst, m.nbytes);
     const hipError_t e = L.finish();

@@ -51,8 +51,14 @@ constexpr int64_t kMaxTilesPerLaunch = RR_MAX_TILES_PER_LAUNCH;
 #define RR_COPY_LONG_BYTES (int64_t(1) << 29)
 #endif
 #ifndef RR_COPY_AGENT_STORES
-#define RR_COPY_AGENT_STORES 1       // copies of calls under RR_COPY_LONG_BYTES store with agent
-                                     // scope (write-through L2); 0: non-temporal like long calls
+#define RR_COPY_AGENT_STORES 1       // copies of calls under RR_COPY_AGENT_MAX_BYTES store with
+                                     // agent scope (write-through L2); 0: non-temporal throughout
+#endif
+#ifndef RR_COPY_AGENT_MAX_BYTES
+#define RR_COPY_AGENT_MAX_BYTES (int64_t(1) << 28)  // calls moving this much or more store
+                                                    // non-temporally: the step gained with agent-
+                                                    // scope stores up to 161 MB per call, lost a
+                                                    // point at 322 MB
 #endif
 
 #ifndef RR_SHIFT_RED_UNROLL
@@ -66,6 +72,7 @@ constexpr int kCopyUnroll = RR_COPY_UNROLL;
 constexpr int kCopyUnrollLong = RR_COPY_UNROLL_LONG;
 constexpr int64_t kCopyLongBytes = RR_COPY_LONG_BYTES;
 constexpr bool kCopyAgentStores = RR_COPY_AGENT_STORES != 0;
+constexpr int64_t kCopyAgentMaxBytes = RR_COPY_AGENT_MAX_BYTES;
 #ifndef RR_SHIFT_UNROLL
 #define RR_SHIFT_UNROLL 2            // 16-byte vectors per thread in a realigning copy tile
                                      // (8 KiB tiles; measured faster than 16 and 32 KiB)
@@ -304,9 +311,9 @@ __host__ __device__ constexpr int64_t red_tile_vecs(int32_t mode)
 
 // long_tiles: the batch belongs to a call that moves at least kCopyLongBytes
 // in aligned moves only; they use tiles of kCopyUnrollLong vectors per lane.
-// nt_stores: the batch belongs to a call that moves at least kCopyLongBytes
-// (aligned or not); its stores are non-temporal, those of every other call
-// agent-scope write-through stores.
+// nt_stores: the batch belongs to a call that moves at least
+// kCopyAgentMaxBytes (aligned or not); its stores are non-temporal, those of
+// every other call agent-scope write-through stores.
 template <int CAP>
 struct CopyBatchT {
     int32_t tile0[CAP];

@@ -406,13 +406,13 @@ __global__ __launch_bounds__(kBlock) void reduce_shifted_one_kernel(const void *
 // Copy
 // ---------------------------------------------------------------------------
 
-// The destination of one copy tile.  Copies of calls under kCopyLongBytes
+// The destination of one copy tile.  Copies of calls under kCopyAgentMaxBytes
 // store with agent scope (WT: the sc1 cache-policy bit, no non-temporal
 // hint): the L2 writes each line through to memory at once instead of holding
 // it dirty until the end-of-kernel release, so less is left to drain between
 // this launch and the next.  A buffer store carries that policy; its resource
 // starts at the tile's first destination vector (uniform across the
-// workgroup) and spans the tile's body vectors.  Long calls keep
+// workgroup) and spans the tile's body vectors.  Larger calls keep
 // non-temporal stores, which measured faster there.
 constexpr int kBufferFormat = 0x00020000;  // raw buffer: 32-bit data format, no swizzle
 constexpr int kStoreAgentScope = 16;       // cache-policy operand: sc1
@@ -693,8 +693,8 @@ void launch_copy_table(const CopyBatchT<CAP> &b, const LaunchShape &sh, int64_t 
     }
 }
 
-// Long calls (the batch's nt_stores) keep non-temporal stores, in the
-// long-call tiles when aligned; every other copy stores with agent scope.
+// Large calls (the batch's nt_stores) keep non-temporal stores, long aligned
+// ones in the long-call tiles; every other copy stores with agent scope.
 template <int CAP>
 void launch_copy_sized(const CopyBatchT<CAP> &b, const LaunchShape &sh, int64_t total_tiles, bool shifted,
                        hipStream_t stream)

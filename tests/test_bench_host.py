@@ -224,20 +224,23 @@ def test_stand_in_step_covers_every_launch():
 
 def test_library_stand_in_follows_the_copy_store_policy():
     """The stand-in with the library's own policy per launch: reductions in
-    the 16 KiB non-temporal pattern, copies under the long-call size in 8 KiB
-    tiles with agent-scope stores, long copies non-temporal in 4 KiB tiles
-    (8 KiB when ragged).  The long-call size is the library's own."""
+    the 16 KiB non-temporal pattern, copies moving under 256 MiB in 8 KiB
+    tiles with agent-scope stores, larger ones non-temporal, and long ones in
+    4 KiB tiles (8 KiB when ragged).  The sizes are the library's own."""
     import re
     hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                             "pack_rr_helper_amd", "csrc", "rr_internal.h")).read()
-    m = re.search(r"#define RR_COPY_LONG_BYTES \(int64_t\(1\) << (\d+)\)", hdr)
-    assert m and bench.COPY_LONG_BYTES == 1 << int(m.group(1))
-    long_b = 2 * bench.COPY_LONG_BYTES
+    for name, const in (("RR_COPY_LONG_BYTES", bench.COPY_LONG_BYTES),
+                        ("RR_COPY_AGENT_MAX_BYTES", bench.COPY_AGENT_MAX_BYTES)):
+        m = re.search(r"#define %s \(int64_t\(1\) << (\d+)\)" % name, hdr)
+        assert m and const == 1 << int(m.group(1)), name
+    long_b, wt_b = 2 * bench.COPY_LONG_BYTES, 2 * bench.COPY_AGENT_MAX_BYTES
     calls = [("ar4_phase", "reduce<bf16>", 84 << 20, None), ("a2a_pack", "copy", 80 << 20, None),
-             ("a2a_unpack", "copy", long_b, None), ("a2a_pack", "copy", long_b - 2, None)]
+             ("a2a_unpack", "copy", long_b, None), ("a2a_pack", "copy", long_b - 2, None),
+             ("a2a_pack", "copy", wt_b - 2, None)]
     names = lambda ragged: [bench.CALIB_PATTERNS[p] for p in bench.library_patterns(calls, ragged)]
-    assert names(False) == ["relay", "tile8k_wt", "tile4k", "tile8k_wt"]
-    assert names(True) == ["relay", "tile8k_wt", "tile8k", "tile8k_wt"]
+    assert names(False) == ["relay", "tile8k_wt", "tile4k", "tile8k", "tile8k_wt"]
+    assert names(True) == ["relay", "tile8k_wt", "tile8k", "tile8k", "tile8k_wt"]
 
 
 def test_another_library_build_gets_no_stored_traffic(monkeypatch):
