@@ -25,7 +25,7 @@
 //   8 relay_wt    the relay pattern with agent-scope stores (the sc1
 //                 cache-policy bit: the L2 writes each line through at once);
 //   9 tile8k_wt   8 KiB tiles with agent-scope stores (the relay copies'
-//                 pattern for calls under the long-call size).
+//                 pattern for calls moving under 256 MiB).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
