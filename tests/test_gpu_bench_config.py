@@ -2,13 +2,15 @@
 and launches of one benchmark step at the 64 MiB message, for one GPU's share
 (the default) and for the whole-group variant, in bf16 and (one GPU's share)
 in fp32 as ``--dtype f32`` runs it, every output the step writes against the
-CPU oracle, bit for bit."""
+CPU oracle, bit for bit.  Outputs hold a sentinel before the step runs
+(tests/benchrows.py), so every compared byte was written by the step."""
 import numpy as np
 import pytest
 import torch
 
 import bench
 from pack_rr_helper_amd import synth
+from tests.benchrows import poison_outputs
 
 pytestmark = pytest.mark.gpu
 F32, BF16, SUM, AVG = 0, 1, 0, 1
@@ -30,10 +32,11 @@ def test_benchmark_step_matches_the_oracle(orc, variant, dtype):
     wls = bench.build_rows(inp, mode=variant, dtype=dtype)
     calls = [c for w in wls.values() for c in w.calls()]
     assert len(calls) == 8   # the A=4 allreduce's helper and active slices share one launch
+    share = variant == "share"
+    poison_outputs(wls, share)
     for w in wls.values():
         w.run()
     torch.cuda.synchronize()
-    share = variant == "share"
     # A=2 allreduce: helper reductions, then the actives' direct regions
     x = inp["ar2"]
     ar2 = wls["ar2"]
