@@ -7,6 +7,13 @@
 // segment tables, head/body/tail splits and launch batching on the CPU, so an
 // addressing mistake shows up here as a recorded violation rather than as a
 // fault on the GPU.  It is never part of the product library.
+//
+// In check-only mode (sim_set_check_only) the registered ranges need hold no
+// memory -- they may be made-up device addresses for buffers of any size --
+// and no access is performed: every access is checked as above, except that
+// the aligned body of a tile is checked as one range per input and output
+// after every lane's vector has been shown to land in it exactly once, which
+// keeps full-size launches (tens of GB of accesses) to seconds.
 #include <math.h>
 #include <stdio.h>
 #include <string.h>
@@ -19,6 +26,8 @@
 
 namespace {
 
+using rr::TileBody;
+
 struct Buf {
     uintptr_t lo, hi;
     bool writable;
@@ -27,6 +36,7 @@ std::vector<Buf> g_bufs;
 long g_violations = 0;
 char g_msg[256];
 long g_launches = 0;
+bool g_check_only = false;  // accesses are checked, never performed
 
 bool inside(uintptr_t a, int64_t n, bool write)
 {
@@ -64,6 +74,8 @@ float ld(const void *p, int64_t i, bool bf16)
         violation("read", a, bf16 ? 2 : 4);
         return 0.0f;
     }
+    if (g_check_only)
+        return 0.0f;
     if (bf16) {
         uint32_t u = uint32_t(*reinterpret_cast<const uint16_t *>(a)) << 16;
         float f;
@@ -80,6 +92,8 @@ void st(void *p, int64_t i, float v, bool bf16)
         violation("write", a, bf16 ? 2 : 4);
         return;
     }
+    if (g_check_only)
+        return;
     if (bf16) {
         uint32_t u;
         memcpy(&u, &v, 4);
@@ -107,7 +121,7 @@ void copy_byte(const unsigned char *src, unsigned char *dst, int64_t i)
         violation("copy read", uintptr_t(src + i), 1);
     else if (!inside(uintptr_t(dst + i), 1, true))
         violation("copy write", uintptr_t(dst + i), 1);
-    else
+    else if (!g_check_only)
         dst[i] = src[i];
 }
 
@@ -145,6 +159,36 @@ std::vector<std::pair<int, int64_t>> tiles_of(const Batch &b, int64_t total, con
     return out;
 }
 
+// Check-only mode: the body vectors the lanes of tile lt store (vec_index for
+// every lane and step with v < nv), each exactly once, and exactly the
+// tile's body range.  Returns that range.
+template <int U>
+TileBody stored_body(int64_t lt, int64_t nv, uintptr_t where)
+{
+    using namespace rr;
+    constexpr int64_t tv = tile_vecs<U>();
+    const TileBody tb = tile_body(lt, tv, nv);
+    static std::vector<unsigned char> seen;
+    seen.assign(size_t(tv), 0);
+    int64_t stored = 0;
+    for (int x = 0; x < kBlock; ++x)
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = vec_index<U>(lt, x, u);
+            if (v >= nv)
+                continue;
+            const int64_t i = v - tb.first;
+            if (i < 0 || i >= tb.count || seen[size_t(i)]) {
+                violation("lane vector outside its tile's body or stored twice", where, v);
+                continue;
+            }
+            seen[size_t(i)] = 1;
+            ++stored;
+        }
+    if (stored != tb.count)
+        violation("tile leaves part of its body unstored", where, stored);
+    return tb;
+}
+
 // Tiles of segment s of a launch of `total` tiles.
 template <typename Batch>
 int64_t seg_tiles(const Batch &b, int s, int64_t total)
@@ -174,7 +218,17 @@ void replay_red_tile(const rr::RedBatch &b, int s, int64_t total, int64_t lt, co
         base[k] = shift_mode ? w.base : static_cast<const unsigned char *>(sg.in[k]) + head * es;
     }
     const bool full = full_tile(lt, tv, nv);
-    if (full || nv > 0)
+    if (g_check_only && !shift_mode) {
+        if (nv > 0) {
+            const TileBody tb = stored_body<U>(lt, nv, uintptr_t(sg.out));
+            const int64_t off = (head + tb.first * ve) * es, len = tb.count * 16;
+            for (int k = 0; k < sg.k; ++k)
+                if (!inside(uintptr_t(sg.in[k]) + uintptr_t(off), len, false))
+                    violation("read", uintptr_t(sg.in[k]) + uintptr_t(off), len);
+            if (!inside(uintptr_t(sg.out) + uintptr_t(off), len, true))
+                violation("write", uintptr_t(sg.out) + uintptr_t(off), len);
+        }
+    } else if (full || nv > 0)
         for (int x = 0; x < kBlock; ++x)
             for (int u = 0; u < U; ++u) {
                 const int64_t v = vec_index<U>(lt, x, u);
@@ -213,7 +267,23 @@ void replay_copy_tile(const rr::CopyBatch &b, int s, int64_t total, int64_t lt, 
         violation("copy segment tile count differs from its body", uintptr_t(sg.dst), seg_tiles(b, s, total));
     const unsigned char *base = sg.src + sp.head - (shift_mode ? sg.shift : 0);  // aligned words read
     const bool full = full_tile(lt, tv, nv);
-    if (full || nv > 0)
+    if (g_check_only && !shift_mode) {
+        if (nv > 0) {
+            // every lane stores vector i of its tile's body range (as below)
+            const TileBody tb = stored_body<U>(lt, nv, uintptr_t(sg.dst));
+            for (int x = 0; x < kBlock; ++x)
+                for (int u = 0; u < U; ++u) {
+                    const int64_t v = vec_index<U>(lt, x, u), i = vec_index<U>(0, x, u);
+                    if (v < nv && (tb.first + i != v || i >= tb.count))
+                        violation("copy store outside its tile's buffer range", uintptr_t(sg.dst), i);
+                }
+            const int64_t off = sp.head + tb.first * 16, len = tb.count * 16;
+            if (!inside(uintptr_t(sg.src) + uintptr_t(off), len, false))
+                violation("copy read", uintptr_t(sg.src) + uintptr_t(off), len);
+            if (!inside(uintptr_t(sg.dst) + uintptr_t(off), len, true))
+                violation("copy write", uintptr_t(sg.dst) + uintptr_t(off), len);
+        }
+    } else if (full || nv > 0)
         for (int x = 0; x < kBlock; ++x)
             for (int u = 0; u < U; ++u) {
                 const int64_t v = vec_index<U>(lt, x, u);
@@ -344,6 +414,8 @@ hipError_t launch_copy(const CopyBatch &b, int64_t total_tiles, bool shifted, hi
 }  // namespace rr
 
 extern "C" {
+// 1: registered ranges hold no memory; accesses are checked, never performed
+void sim_set_check_only(int on) { g_check_only = on != 0; }
 void sim_reset(void)
 {
     g_bufs.clear();
