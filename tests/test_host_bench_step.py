@@ -8,7 +8,8 @@ address range, 2 MiB aligned with a 2 MiB gap after it, registered with the
 replay; in check-only mode the replay checks every access of every launch
 against those ranges without performing it.  So the launch configuration
 bench.py times at 64 MiB, 256 MiB and 1 GiB per rank, one GPU's share and the
-whole group, is shown on the CPU to stay inside its buffers (and every body
+whole group, and one GPU's share at 64 MiB with the ragged all-to-all of
+--ragged-a2a, is shown on the CPU to stay inside its buffers (and every body
 vector to be stored exactly once), with the launch count, launch forms, copy
 tiling and copy store policy that the kernel traces of those runs record.
 """
@@ -77,19 +78,32 @@ def meta_inputs(M):
             "a2a": [bits() for _ in range(4)]}
 
 
+def ragged(inp):
+    """The all-to-all rows with segmentCount = 5 (mod 8), as bench.py --ragged-a2a
+    builds them: chunk moves whose source and destination disagree modulo 16 bytes."""
+    n = inp["a2a"][0].numel()
+    inp["a2a"] = [torch.empty(4 * (n // 4 - 3), dtype=torch.int16, device="meta") for _ in range(4)]
+    return inp
+
+
 def counters(sim):
     L = sim.L
     return {"launches": L.sim_launches(),
             "red": [L.sim_form_launches(0, f) for f in range(3)],
             "copy": [L.sim_form_launches(1, f) for f in range(3)],
-            "long": L.sim_copy_launches(1), "nt": L.sim_nt_copy_launches(1)}
+            "long": L.sim_copy_launches(1), "nt": L.sim_nt_copy_launches(1),
+            "shifted": L.sim_shifted_copy_launches()}
 
 
-@pytest.mark.parametrize("mib", [64, 256, 1024])
-@pytest.mark.parametrize("variant", ["share", "group"])
-def test_benchmark_step_launches_stay_inside_their_buffers(fake_gpu, mib, variant):
+@pytest.mark.parametrize("mib,ragged_a2a,variant", [
+    (64, False, "share"), (64, False, "group"), (256, False, "share"), (256, False, "group"),
+    (1024, False, "share"), (1024, False, "group"), (64, True, "share")],
+    ids=["64MiB-share", "64MiB-group", "256MiB-share", "256MiB-group", "1GiB-share", "1GiB-group",
+         "64MiB-ragged-share"])
+def test_benchmark_step_launches_stay_inside_their_buffers(fake_gpu, mib, ragged_a2a, variant):
     sim = fake_gpu
-    wls = bench.build_rows(meta_inputs(mib * MIB), mode=variant, dtype="bf16")
+    inp = meta_inputs(mib * MIB)
+    wls = bench.build_rows(ragged(inp) if ragged_a2a else inp, mode=variant, dtype="bf16")
     calls = [c for w in wls.values() for c in w.calls()]
     assert [c[0] for c in calls] == ["ar2_helper", "ar2_active", "rs2_owner", "ar4_phase", "rs4_pass1",
                                      "rs4_pass2", "a2a_pack", "a2a_unpack"]
@@ -105,10 +119,11 @@ def test_benchmark_step_launches_stay_inside_their_buffers(fake_gpu, mib, varian
     # reductions: single-segment form for the one-job owner and active epilogues
     # of one GPU's share, the uniform grid for everything else, never the table
     share = variant == "share"
-    assert d["red"] == [0, 4, 2] if share else [0, 6, 0]
+    assert d["red"] == ([0, 4, 2] if share else [0, 6, 0])
     assert d["copy"] == [0, 2, 0]
     moved = [b // 2 for row, _, b, _ in calls if row.startswith("a2a")]
     long_call = moved[0] >= bench.COPY_LONG_BYTES
     nt = long_call or moved[0] >= bench.COPY_AGENT_MAX_BYTES
     assert d["long"] == (2 if long_call else 0)
     assert d["nt"] == (2 if nt else 0)
+    assert d["shifted"] == (2 if ragged_a2a else 0)   # ragged: both copies in the realigning kernels
