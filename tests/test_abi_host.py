@@ -188,7 +188,7 @@ def test_a2a_rejections(L):
     dst = ptrs(*[B + 64 * MB + i * 2 * MB for i in range(4)])
     assert L.rr_a2a_pack(r, BF16, 4, src, dst, None) == EINVAL                      # helper
     assert L.rr_a2a_pack(relay(4, 4, 4, 0, MB), BF16, 0, src, dst, None) == EINVAL  # numChunks
-    # in-place (a dst inside a source) is forbidden: all-to-all is out-of-place only
+    # in-place (a dst inside a source) is forbidden: an all-to-all never writes into its own inputs
     assert L.rr_a2a_pack(r, BF16, 0, src, ptrs(B, B + 66 * MB, B + 68 * MB, B + 70 * MB),
                          None) == EALIAS
     assert L.rr_a2a_pack(r, BF16, 0, src, ptrs(B + 64 * MB, B + 64 * MB, B + 68 * MB, B + 70 * MB),
