@@ -794,12 +794,12 @@ rr_status collect_a2a(const rr_relay *relay, int dtype, int helper, const void *
     if ((st = check_array(const_cast<const void *const *>(outs), A, es, out_name)) != RR_OK)
         return st;
     const int64_t in_len = unpack ? packed : full, out_len = unpack ? full : packed;
-    // out-of-place only: no written buffer may overlap a read buffer
+    // no written buffer may overlap a read buffer (nor another written one)
     for (int d = 0; d < A; ++d) {
         const Range ro = range_of(outs[d], 0, out_len, es);
         for (int s = 0; s < A; ++s)
             if (overlap(ro, range_of(ins[s], 0, in_len, es)))
-                return fail(RR_EALIAS, "all-to-all is out-of-place: %s[%d] overlaps %s[%d]", out_name,
+                return fail(RR_EALIAS, "all-to-all output overlaps an input: %s[%d] overlaps %s[%d]", out_name,
                             d, in_name, s);
         for (int e = 0; e < d; ++e)
             if (overlap(ro, range_of(outs[e], 0, out_len, es)))
