@@ -68,6 +68,10 @@ class Sim:
         self.keep.append(a)
         return a
 
+    def register(self, addr, nbytes, writable=True):
+        """Register a raw host address range (memory the caller keeps alive)."""
+        self.L.sim_register(ctypes.c_void_p(addr), nbytes, int(writable))
+
     def check(self):
         assert self.L.sim_violations() == 0, self.L.sim_message().decode()
 

@@ -30,6 +30,7 @@ from tests.hostsim import Sim
 
 AR, RS, A2A = 0, 1, 2
 F32, BF16 = 0, 1
+SLACK = 300   # elements: the largest offset of a partially aliased output
 OK, EINVAL, EALIAS = 0, 1, 2
 KINDS = ("helper", "active", "rs", "pack", "unpack")
 # aliases found over all items (or moves) of a call, after every job's
@@ -59,8 +60,12 @@ class Case:
         # call that accepted one would show up as a replay access violation
         nelem = min(nelem, 1 << 23)
         lead = int(self.rng.integers(0, 8))
-        a = self.rng.integers(0, 256, size=(nelem + lead + 8) * self.es, dtype=np.uint8)
-        self.sim.buf(a)
+        nominal = (nelem + lead + 8) * self.es
+        # SLACK more elements of memory past the registered range: room for an
+        # output placed at a partial alias of this buffer (out_pointer)
+        a = np.concatenate([self.rng.integers(0, 256, size=nominal, dtype=np.uint8),
+                            np.zeros(SLACK * self.es, np.uint8)])
+        self.sim.register(a.ctypes.data, nominal)
         self.bufs.append(a)
         return a.ctypes.data + lead * self.es
 
@@ -93,8 +98,13 @@ class Case:
                 self.faulty = True
         elif inputs and u < 0.09:
             p = int(self.rng.choice(inputs))
-            p = p + int(self.rng.integers(1, 300)) * self.es if p else 0
+            p = p + int(self.rng.integers(1, SLACK)) * self.es if p else 0
             self.faulty = True
+            # the caller's output buffer of nelem elements at p: a call may
+            # accept it when the overlap misses every range it reads (an input
+            # its geometry leaves unused), and then writes all of it
+            if p:
+                self.sim.register(p, min(nelem, 1 << 23) * self.es)   # the cap of fresh()
         else:
             p = self.pointer(nelem)
         o = self.owner(p) if p else None
