@@ -63,7 +63,7 @@ def same_bits(got, ref, what):
     assert np.array_equal(got.view(np.uint8), np.ascontiguousarray(ref).view(np.uint8)), what
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", range(192))
 def test_random_allreduce_batches(orc, seed):
     rng = np.random.default_rng(5000 + seed)
     A = int(rng.choice([2, 4]))
@@ -97,7 +97,7 @@ def test_random_allreduce_batches(orc, seed):
             assert hout[h].guards_intact(), f"helper {h} wrote outside its output"
 
 
-@pytest.mark.parametrize("seed", range(32))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_four_active_reduce_scatter(orc, seed):
     rng = np.random.default_rng(7000 + seed)
     A, H = 4, int(rng.integers(1, 5))
@@ -137,7 +137,7 @@ def test_random_four_active_reduce_scatter(orc, seed):
         assert outs[o].guards_intact(), f"owner {o} wrote outside its output"
 
 
-@pytest.mark.parametrize("seed", range(32))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_all_to_all(orc, seed):
     rng = np.random.default_rng(9000 + seed)
     A, H = 4, int(rng.integers(1, 5))
