@@ -315,7 +315,7 @@ def run_case(sim, seed):
 @pytest.mark.parametrize("block", range(8))
 def test_fuzzed_arguments_keep_the_contract(sims, block):
     seen = {OK: 0, EINVAL: 0, EALIAS: 0}
-    for seed in range(block * 40, block * 40 + 40):
+    for seed in range(block * 80, block * 80 + 80):
         for st in run_case(sims[seed % 7 == 3], seed):
             seen[st] += 1
     # the draws reach every outcome in every block

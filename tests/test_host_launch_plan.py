@@ -435,7 +435,7 @@ def _rand_case(rng):
     return A, H, dt, op
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_active_and_helper_calls_match_the_oracle(sim, orc, seed):
     rng = np.random.default_rng(1000 + seed)
     sim.reset()
@@ -491,7 +491,7 @@ def test_random_active_and_helper_calls_match_the_oracle(sim, orc, seed):
         assert np.array_equal(o[start:start + c].view(np.uint8), ref.view(np.uint8)), (A, H, dt, count, h)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(32))
 def test_random_all_to_all_round_trip(sim, orc, seed):
     rng = np.random.default_rng(3000 + seed)
     sim.reset()
@@ -726,7 +726,7 @@ def _overlap(a, b):
     return a[0] < a[1] and b[0] < b[1] and a[0] < b[1] and b[0] < a[1]
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(200))
 def test_random_views_follow_the_aliasing_rule(sim, orc, seed):
     """Random A=2 helper jobs over views of one buffer, on a coarse grid so
     that overlaps and exact in-place aliases are common: the call is accepted
